@@ -1,0 +1,328 @@
+"""Pins of the fp64 CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against mathematics or the pages:
+
+* central finite differences of l = sum(dO * O) (backward vs forward),
+* an independent library routine (torch CPU scaled_dot_product_attention in
+  float64, the routine [TE-3333]'s and [TE-3216]'s references call),
+* hand-derived closed forms (one key, two keys, identical keys, causal row 0),
+* invariants (softmax rows sum to one, GQA == summed MHA over repeated KV,
+  padding rows inert and exactly zero),
+* values printed on the pages (golden fixtures under tests/golden/).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import workloads
+from oracle import attn_bwd, attn_fwd, attn_fwd_seq
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f64(t):
+    return t.to(torch.float64).numpy() if isinstance(t, torch.Tensor) else np.asarray(t, np.float64)
+
+
+def run_case(c, mode="definition"):
+    args = (c.cu_seqlens_q, c.cu_seqlens_kv, c.cu_seqlens_q_padded, c.cu_seqlens_kv_padded)
+    o, l = attn_fwd(f64(c.q), f64(c.k), f64(c.v), *args, scale=c.scale, causal=c.causal)
+    g = attn_bwd(f64(c.q), f64(c.k), f64(c.v), f64(c.dout), *args, scale=c.scale,
+                 causal=c.causal, out=o, lse=l, mode=mode)
+    return o, l, g
+
+
+def small_case(rng, lq, lk, pq, pk, hq, hkv, d, causal, scale=None):
+    """Random fp64 case with padding rows (filled with noise)."""
+    Tq, Tk = sum(pq), sum(pk)
+    cu = lambda a: np.concatenate([[0], np.cumsum(a)]).astype(np.int32)
+    return dict(q=rng.standard_normal((Tq, hq, d)), k=rng.standard_normal((Tk, hkv, d)),
+                v=rng.standard_normal((Tk, hkv, d)), dout=rng.standard_normal((Tq, hq, d)),
+                cu_q=cu(lq), cu_kv=cu(lk), cu_qp=cu(pq), cu_kp=cu(pk),
+                scale=scale if scale is not None else 1 / math.sqrt(d), causal=causal)
+
+
+def fwd_of(c, q=None, k=None, v=None):
+    return attn_fwd(c["q"] if q is None else q, c["k"] if k is None else k,
+                    c["v"] if v is None else v, c["cu_q"], c["cu_kv"], c["cu_qp"], c["cu_kp"],
+                    scale=c["scale"], causal=c["causal"])
+
+
+def bwd_of(c):
+    return attn_bwd(c["q"], c["k"], c["v"], c["dout"], c["cu_q"], c["cu_kv"], c["cu_qp"],
+                    c["cu_kp"], scale=c["scale"], causal=c["causal"])
+
+
+# ---------------------------------------------------------------- finite differences
+def _fd_check(c, eps=1e-6):
+    """Analytic gradient vs central differences of l = sum(dO*O), every element."""
+    grads = dict(zip("qkv", bwd_of(c)))
+    for name in "qkv":
+        x = c[name]
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            lp = np.sum(c["dout"] * fwd_of(c, **{name: xp})[0])
+            lm = np.sum(c["dout"] * fwd_of(c, **{name: xm})[0])
+            num[idx] = (lp - lm) / (2 * eps)
+        an = grads[name]
+        err = np.linalg.norm(an - num) / max(np.linalg.norm(num), 1e-30)
+        assert err <= 1e-7, (name, err)
+        # padding rows: perturbing them changes l by exactly zero
+        zero_rows = np.all(num == 0.0, axis=(1, 2))
+        assert np.all(an[zero_rows] == 0.0)
+
+
+@pytest.mark.parametrize("call", [0, 1])
+def test_finite_differences_tiny_gqa_calls(call):
+    """The TE-2448 two-call shapes (T=12, hq=2, hkv=1, d=8, padding mask, scale 0.1)."""
+    case = workloads.tiny_gqa_two_calls()[call]
+    c = dict(q=f64(case.q), k=f64(case.k), v=f64(case.v), dout=f64(case.dout),
+             cu_q=case.cu_seqlens_q, cu_kv=case.cu_seqlens_kv, cu_qp=case.cu_seqlens_q_padded,
+             cu_kp=case.cu_seqlens_kv_padded, scale=case.scale, causal=case.causal)
+    _fd_check(c)
+
+
+def test_finite_differences_causal_gqa_with_padding():
+    rng = np.random.default_rng(7)
+    c = small_case(rng, lq=[3, 5], lk=[3, 5], pq=[4, 6], pk=[4, 6], hq=4, hkv=2, d=8, causal=True)
+    _fd_check(c)
+
+
+def test_finite_differences_causal_lq_ne_lk():
+    """Top-left causal with Lq != Lk (a reading; the pages only use Lq == Lk with causal)."""
+    rng = np.random.default_rng(8)
+    c = small_case(rng, lq=[2, 4], lk=[5, 3], pq=[3, 4], pk=[6, 4], hq=2, hkv=1, d=8, causal=True)
+    _fd_check(c)
+
+
+# ---------------------------------------------------------------- library cross-check
+def _sdpa_ref(c):
+    """torch CPU fp64 SDPA per sequence (+ autograd), placed in the padded layout."""
+    q = torch.tensor(c["q"], requires_grad=True)
+    k = torch.tensor(c["k"], requires_grad=True)
+    v = torch.tensor(c["v"], requires_grad=True)
+    out = torch.zeros_like(q)
+    outs = []
+    for b in range(len(c["cu_q"]) - 1):
+        oq, lq = int(c["cu_qp"][b]), int(c["cu_q"][b + 1] - c["cu_q"][b])
+        ok, lk = int(c["cu_kp"][b]), int(c["cu_kv"][b + 1] - c["cu_kv"][b])
+        if lq == 0 or lk == 0:
+            continue
+        qi = q[oq:oq + lq].transpose(0, 1)[None]
+        ki = k[ok:ok + lk].transpose(0, 1)[None]
+        vi = v[ok:ok + lk].transpose(0, 1)[None]
+        o = F.scaled_dot_product_attention(qi, ki, vi, is_causal=c["causal"], scale=c["scale"],
+                                           enable_gqa=True)
+        outs.append((oq, lq, o[0].transpose(0, 1)))
+    for oq, lq, o in outs:
+        out = out.index_put((torch.arange(oq, oq + lq),), o)
+    (out * torch.tensor(c["dout"])).sum().backward()
+    return out.detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [
+    dict(lq=[5, 0, 7], lk=[6, 4, 7], pq=[8, 2, 8], pk=[8, 4, 9], hq=6, hkv=2, d=16),
+    dict(lq=[17], lk=[17], pq=[20], pk=[20], hq=4, hkv=4, d=32),
+    dict(lq=[9, 12], lk=[4, 12], pq=[9, 16], pk=[4, 13], hq=8, hkv=1, d=8),
+])
+def test_matches_torch_sdpa_fp64(shape, causal):
+    rng = np.random.default_rng(11)
+    c = small_case(rng, causal=causal, **shape)
+    o, l = fwd_of(c)
+    dq, dk, dv = bwd_of(c)
+    ro, rdq, rdk, rdv = _sdpa_ref(c)
+    for a, b in [(o, ro), (dq, rdq), (dk, rdk), (dv, rdv)]:
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_single_token_sequence():
+    """Lq = Lk = 1: O = v, LSE = scale*q.k, dQ = dK = 0, dV = dO."""
+    rng = np.random.default_rng(1)
+    c = small_case(rng, lq=[1], lk=[1], pq=[1], pk=[1], hq=2, hkv=1, d=8, causal=False, scale=0.37)
+    o, l = fwd_of(c)
+    dq, dk, dv = bwd_of(c)
+    for h in range(2):
+        np.testing.assert_array_equal(o[0, h], c["v"][0, 0])
+        assert l[0, h] == pytest.approx(0.37 * c["q"][0, h] @ c["k"][0, 0], rel=1e-15)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_allclose(dv[0, 0], c["dout"][0, 0] + c["dout"][0, 1], rtol=1e-15)
+
+
+def test_two_keys_closed_form():
+    """One query, two keys: O = s*v0 + (1-s)*v1 with s = sigmoid(scale*q.(k0-k1)).
+
+    Gradients by hand: with w = s(1-s) dO.(v0-v1),
+    dq = scale*w*(k0-k1), dk0 = scale*w*q = -dk1, dv0 = s*dO, dv1 = (1-s)*dO.
+    """
+    rng = np.random.default_rng(2)
+    d, sc = 8, 0.7
+    c = small_case(rng, lq=[1], lk=[2], pq=[1], pk=[2], hq=1, hkv=1, d=d, causal=False, scale=sc)
+    q, k0, k1 = c["q"][0, 0], c["k"][0, 0], c["k"][1, 0]
+    v0, v1, do = c["v"][0, 0], c["v"][1, 0], c["dout"][0, 0]
+    a = sc * q @ (k0 - k1)
+    s = 1 / (1 + math.exp(-a))
+    o, l = fwd_of(c)
+    np.testing.assert_allclose(o[0, 0], s * v0 + (1 - s) * v1, rtol=1e-13)
+    np.testing.assert_allclose(l[0, 0], math.log(math.exp(sc * q @ k0) + math.exp(sc * q @ k1)),
+                               rtol=1e-13)
+    dq, dk, dv = bwd_of(c)
+    w = s * (1 - s) * do @ (v0 - v1)
+    np.testing.assert_allclose(dq[0, 0], sc * w * (k0 - k1), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk[0, 0], sc * w * q, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk[1, 0], -sc * w * q, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dv[0, 0], s * do, rtol=1e-13)
+    np.testing.assert_allclose(dv[1, 0], (1 - s) * do, rtol=1e-13)
+
+
+def test_identical_keys_give_mean_of_values():
+    """All keys equal: P is uniform over the allowed keys, O = their mean,
+    LSE = scale*q.k + ln(#allowed)."""
+    rng = np.random.default_rng(3)
+    L, d = 6, 8
+    q = rng.standard_normal((L, 1, d))
+    krow = rng.standard_normal(d)
+    k = np.tile(krow, (L, 1, 1))
+    v = rng.standard_normal((L, 1, d))
+    for causal in (False, True):
+        o, l = attn_fwd_seq(q, k, v, 0.5, causal)
+        for i in range(L):
+            n = i + 1 if causal else L
+            np.testing.assert_allclose(o[i, 0], v[:n, 0].mean(axis=0), rtol=1e-12, atol=1e-14)
+            assert l[i, 0] == pytest.approx(0.5 * q[i, 0] @ krow + math.log(n), rel=1e-12)
+
+
+def test_causal_first_row_sees_only_first_key():
+    rng = np.random.default_rng(4)
+    q, k, v = (rng.standard_normal((5, 2, 8)) for _ in range(3))
+    o, l = attn_fwd_seq(q, k, v, 0.3, True)
+    np.testing.assert_array_equal(o[0], v[0])
+    np.testing.assert_allclose(l[0], 0.3 * np.sum(q[0] * k[0], axis=-1), rtol=1e-15)
+
+
+def test_softmax_rows_sum_to_one():
+    """With one-hot value rows, O_i is row i of P: it sums to 1 and is 0 off the allowed set."""
+    rng = np.random.default_rng(5)
+    L = 7
+    q = rng.standard_normal((L, 1, L))
+    k = rng.standard_normal((L, 1, L))
+    v = np.eye(L)[:, None, :]
+    for causal in (False, True):
+        p, _ = attn_fwd_seq(q, k, v, 1.3, causal)
+        p = p[:, 0, :]
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+        if causal:
+            assert np.all(p[np.triu_indices(L, 1)] == 0.0)
+        assert np.all(p >= 0)
+
+
+# ---------------------------------------------------------------- invariants
+def test_gqa_equals_summed_mha_over_repeated_kv():
+    """[TE-3216] repeat_interleave: GQA dK/dV of a group == sum over its heads of MHA."""
+    rng = np.random.default_rng(6)
+    c = small_case(rng, lq=[6, 9], lk=[6, 9], pq=[7, 9], pk=[7, 9], hq=6, hkv=2, d=8, causal=True)
+    G = 3
+    o, l = fwd_of(c)
+    dq, dk, dv = bwd_of(c)
+    kr, vr = np.repeat(c["k"], G, axis=1), np.repeat(c["v"], G, axis=1)
+    o2, l2 = fwd_of(c, k=kr, v=vr)
+    c2 = dict(c, k=kr, v=vr)
+    dq2, dk2, dv2 = bwd_of(c2)
+    np.testing.assert_allclose(o, o2, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(dq, dq2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(dk, dk2.reshape(dk2.shape[0], 2, G, -1).sum(axis=2), rtol=1e-12,
+                               atol=1e-14)
+    np.testing.assert_allclose(dv, dv2.reshape(dv2.shape[0], 2, G, -1).sum(axis=2), rtol=1e-12,
+                               atol=1e-14)
+
+
+def test_padding_rows_exact_zero_and_inert():
+    """Rows outside the real ranges are exactly 0 (lse -inf); redrawing them changes nothing."""
+    rng = np.random.default_rng(9)
+    c = small_case(rng, lq=[3, 0, 5], lk=[4, 2, 5], pq=[5, 3, 8], pk=[6, 2, 7], hq=4, hkv=2, d=8,
+                   causal=False)
+    o, l = fwd_of(c)
+    dq, dk, dv = bwd_of(c)
+    real_q = np.zeros(o.shape[0], bool)
+    real_k = np.zeros(dk.shape[0], bool)
+    for b in range(3):
+        real_q[c["cu_qp"][b]:c["cu_qp"][b] + c["cu_q"][b + 1] - c["cu_q"][b]] = True
+        if c["cu_q"][b + 1] > c["cu_q"][b]:
+            real_k[c["cu_kp"][b]:c["cu_kp"][b] + c["cu_kv"][b + 1] - c["cu_kv"][b]] = True
+    assert np.all(o[~real_q] == 0) and np.all(np.isneginf(l[~real_q]))
+    assert np.all(dq[~real_q] == 0)
+    assert np.all(dk[~real_k] == 0) and np.all(dv[~real_k] == 0)
+    # redraw all padding rows with noise (and NaN in one of them): nothing moves
+    c2 = dict(c)
+    for name, mask in (("q", real_q), ("dout", real_q), ("k", real_k), ("v", real_k)):
+        x = c[name].copy()
+        x[~mask] = rng.standard_normal(x[~mask].shape) * 100
+        c2[name] = x
+    o2, l2 = fwd_of(c2)
+    g2 = bwd_of(c2)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+    for a, b in zip((dq, dk, dv), g2):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_formula_mode_equals_definition_with_own_stats():
+    rng = np.random.default_rng(10)
+    c = small_case(rng, lq=[5, 8], lk=[5, 8], pq=[6, 8], pk=[6, 8], hq=4, hkv=1, d=16, causal=True)
+    o, l = fwd_of(c)
+    a = bwd_of(c)
+    b = attn_bwd(c["q"], c["k"], c["v"], c["dout"], c["cu_q"], c["cu_kv"], c["cu_qp"], c["cu_kp"],
+                 scale=c["scale"], causal=True, out=o, lse=l, mode="formula")
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- values from the pages
+def test_te2448_second_call_first_four_kv_rows_zero():
+    gold = json.load(open(os.path.join(GOLDEN, "te2448_second_call_zero_rows.json")))
+    case = workloads.tiny_gqa_two_calls()[1]
+    assert list(case.cu_seqlens_q) == gold["cu_seqlens_q"]
+    assert list(case.cu_seqlens_kv) == gold["cu_seqlens_kv"]
+    assert list(case.cu_seqlens_q_padded) == gold["cu_seqlens_padded"]
+    _, _, (dq, dk, dv) = run_case(case)
+    rows = gold["zero_rows_dk_dv"]
+    assert np.all(dk[rows] == 0) and np.all(dv[rows] == 0)
+    # the second sequence does have gradient, so the zeros are not vacuous
+    assert np.abs(dk[4:10]).max() > 0 and np.abs(dv[4:10]).max() > 0
+
+
+@pytest.mark.parametrize("lengths", workloads.MHA_CAUSAL_LENGTH_SETS)
+def test_te3333_query_gradient_norms(lengths):
+    gold = json.load(open(os.path.join(GOLDEN, "te3333_qgrad_norms.json")))
+    ref = gold["ref_norms"][",".join(map(str, lengths))]
+    case = workloads.mha_causal_lengths(list(lengths))
+    _, _, (dq, _, _) = run_case(case)
+    nrm = float(np.linalg.norm(dq))
+    assert abs(nrm - ref) <= gold["rel_tol"] * ref, (lengths, nrm, ref)
+
+
+def test_te2448_comment_dk_max_magnitude():
+    gold = json.load(open(os.path.join(GOLDEN, "te2448_dk_max.json")))
+    rng = np.random.default_rng(0)
+    T, hq, hkv, d = 128, 4, 1, 256
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    q = bf(rng.standard_normal((T, hq, d), dtype=np.float32))
+    k = bf(rng.standard_normal((T, hkv, d), dtype=np.float32))
+    v = bf(rng.standard_normal((T, hkv, d), dtype=np.float32))
+    cu = np.array([0, 64, 128], np.int32)
+    dq, dk, dv = attn_bwd(q, k, v, np.ones((T, hq, d)), cu, cu, cu, cu, scale=d ** -0.5,
+                          causal=True)
+    m = float(np.abs(dk).max())
+    lo, hi = gold["range"]
+    assert lo <= m <= hi, m
