@@ -1,0 +1,252 @@
+"""MI355X (gfx950) fused attention over packed variable-length THD sequences.
+
+A thin ctypes binding of ``libattn_thd.so`` (C ABI in ``include/attn_thd.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals arguments: PyTorch supplies device memory (outputs and the
+workspace are ``torch.empty``) and the current stream.  There is no fallback:
+if the library is missing or fails to load, every call raises.
+
+Names follow TransformerEngine's ``DotProductAttention`` / ``fused_attn_bwd``
+arguments (``cu_seqlens_q``, ``cu_seqlens_kv``, ``cu_seqlens_q_padded``,
+``cu_seqlens_kv_padded``, ``max_seqlen_q``, ``max_seqlen_kv``,
+``attn_mask_type`` in {"padding", "padding_causal"}).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd", "fwd", "bwd",
+           "status_string", "read_device_status", "AttnError", "STATUS", "DEV_BAD_SEQLENS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
+_LIB = None
+
+STATUS = {0: "ATTN_THD_OK", 1: "ATTN_THD_EINVAL", 2: "ATTN_THD_EUNSUPPORTED",
+          3: "ATTN_THD_EWORKSPACE", 4: "ATTN_THD_ELAUNCH"}
+DEV_BAD_SEQLENS = 1
+_DTYPE = {torch.bfloat16: 0, torch.float16: 1}
+_MASK = {"padding": 0, "padding_causal": 1}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+_FWD_ARGS = [_P, _P, _P, _P, _P,          # q k v out lse
+             _P, _P, _P, _P,              # cu_q cu_kv cu_q_pad cu_kv_pad
+             _I, _I, _I, _I, _I,          # batch total_q total_kv max_q max_kv
+             _I, _I, _I, _F, _I, _I,      # hq hkv d scale mask dtype
+             _P, _S, _P]                  # workspace bytes stream
+_BWD_ARGS = [_P, _P, _P, _P, _P, _P,      # q k v out dout lse
+             _P, _P, _P,                  # dq dk dv
+             _P, _P, _P, _P,
+             _I, _I, _I, _I, _I,
+             _I, _I, _I, _F, _I, _I,
+             _P, _S, _P]
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libattn_thd.so (built in-tree by ``python -m bwd_thd_varlen_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_LIB_PATH):
+            raise AttnError(f"{_LIB_PATH} is not built: run `python -m bwd_thd_varlen_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.attn_thd_workspace_size.argtypes = [_I] * 6
+        L.attn_thd_workspace_size.restype = _S
+        L.attn_fwd_thd.argtypes = _FWD_ARGS
+        L.attn_fwd_thd.restype = ctypes.c_int
+        L.attn_bwd_thd.argtypes = _BWD_ARGS
+        L.attn_bwd_thd.restype = ctypes.c_int
+        L.attn_thd_status_string.argtypes = [_I]
+        L.attn_thd_status_string.restype = ctypes.c_char_p
+        L.attn_thd_read_device_status.argtypes = [_P, _P, ctypes.POINTER(_I)]
+        L.attn_thd_read_device_status.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().attn_thd_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise AttnError(f"{what}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+# ----------------------------------------------------------------- raw C-ABI mirrors
+def workspace_size(batch: int, total_q: int, total_kv: int, hq: int, hkv: int, d: int) -> int:
+    return int(lib().attn_thd_workspace_size(batch, total_q, total_kv, hq, hkv, d))
+
+
+def attn_fwd_thd(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                 cu_seqlens_kv_padded, batch, total_q, total_kv, max_seqlen_q, max_seqlen_kv,
+                 hq, hkv, d, scale, mask_type, dtype, workspace, workspace_bytes, stream) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_fwd_thd(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv,
+                                  cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q,
+                                  total_kv, max_seqlen_q, max_seqlen_kv, hq, hkv, d, scale,
+                                  mask_type, dtype, workspace, workspace_bytes, stream))
+
+
+def attn_bwd_thd(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
+                 cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv,
+                 max_seqlen_q, max_seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
+                 workspace_bytes, stream) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_bwd_thd(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q,
+                                  cu_seqlens_kv, cu_seqlens_q_padded, cu_seqlens_kv_padded, batch,
+                                  total_q, total_kv, max_seqlen_q, max_seqlen_kv, hq, hkv, d,
+                                  scale, mask_type, dtype, workspace, workspace_bytes, stream))
+
+
+def read_device_status(workspace: torch.Tensor) -> int:
+    """Synchronises the current stream and returns the device status word of the last call."""
+    st = _I(0)
+    stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    _check(lib().attn_thd_read_device_status(workspace.data_ptr(), stream, ctypes.byref(st)),
+           "attn_thd_read_device_status")
+    return int(st.value)
+
+
+# ----------------------------------------------------------------- tensor wrappers
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dev=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise AttnError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise AttnError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise AttnError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise AttnError(f"{name} must be {dtype}, got {t.dtype}")
+    if dev is not None and t.device != dev:
+        raise AttnError(f"{name} must be on {dev}")
+
+
+def _cu(t, name, dev):
+    if t is None:
+        return None
+    _need(t, name, torch.int32, dev)
+    return t
+
+
+def _workspace(ws, batch, tq, tk, hq, hkv, d, dev):
+    need = workspace_size(batch, tq, tk, hq, hkv, d)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if ws.numel() * ws.element_size() < need:
+        raise AttnError(f"workspace of {ws.numel() * ws.element_size()} bytes < {need}")
+    return ws
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+        cu_seqlens_kv: torch.Tensor, cu_seqlens_q_padded: Optional[torch.Tensor] = None,
+        cu_seqlens_kv_padded: Optional[torch.Tensor] = None, max_seqlen_q: int = 0,
+        max_seqlen_kv: int = 0, attn_mask_type: str = "padding",
+        softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward: returns (out [Tq,hq,d] in q's dtype, lse [Tq,hq] float32)."""
+    dev = q.device
+    _need(q, "q", None, dev)
+    if q.dtype not in _DTYPE:
+        raise AttnError(f"q must be bf16 or fp16, got {q.dtype}")
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    tq, hq, d = q.shape
+    tk, hkv, dk_ = k.shape
+    if v.shape != k.shape or dk_ != d:
+        raise AttnError("k and v must be [total_kv, hkv, d] with q's d")
+    cq = _cu(cu_seqlens_q, "cu_seqlens_q", dev)
+    ck = _cu(cu_seqlens_kv, "cu_seqlens_kv", dev)
+    cqp = _cu(cu_seqlens_q_padded, "cu_seqlens_q_padded", dev)
+    ckp = _cu(cu_seqlens_kv_padded, "cu_seqlens_kv_padded", dev)
+    batch = cq.numel() - 1
+    if ck.numel() != batch + 1 or any(c is not None and c.numel() != batch + 1 for c in (cqp, ckp)):
+        raise AttnError("all cu_seqlens arrays need batch + 1 entries")
+    if attn_mask_type not in _MASK:
+        raise AttnError(f"attn_mask_type must be one of {sorted(_MASK)}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=dev)
+    _need(out, "out", q.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = attn_fwd_thd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      cq.data_ptr(), ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk,
+                      int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, d, scale,
+                      _MASK[attn_mask_type], _DTYPE[q.dtype], ws.data_ptr(),
+                      ws.numel() * ws.element_size(), stream)
+    _check(st, "attn_fwd_thd")
+    return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+        dout: torch.Tensor, lse: torch.Tensor, cu_seqlens_q: torch.Tensor,
+        cu_seqlens_kv: torch.Tensor, cu_seqlens_q_padded: Optional[torch.Tensor] = None,
+        cu_seqlens_kv_padded: Optional[torch.Tensor] = None, max_seqlen_q: int = 0,
+        max_seqlen_kv: int = 0, attn_mask_type: str = "padding",
+        softmax_scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+        dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None
+        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward: returns (dq, dk, dv) in q's dtype."""
+    dev = q.device
+    _need(q, "q", None, dev)
+    if q.dtype not in _DTYPE:
+        raise AttnError(f"q must be bf16 or fp16, got {q.dtype}")
+    for t, n in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, q.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or k.shape[2] != d:
+        raise AttnError("shape mismatch among q, k, v, out, dout")
+    if tuple(lse.shape) != (tq, hq):
+        raise AttnError("lse must be [total_q, hq]")
+    cq = _cu(cu_seqlens_q, "cu_seqlens_q", dev)
+    ck = _cu(cu_seqlens_kv, "cu_seqlens_kv", dev)
+    cqp = _cu(cu_seqlens_q_padded, "cu_seqlens_q_padded", dev)
+    ckp = _cu(cu_seqlens_kv_padded, "cu_seqlens_kv_padded", dev)
+    batch = cq.numel() - 1
+    if ck.numel() != batch + 1 or any(c is not None and c.numel() != batch + 1 for c in (cqp, ckp)):
+        raise AttnError("all cu_seqlens arrays need batch + 1 entries")
+    if attn_mask_type not in _MASK:
+        raise AttnError(f"attn_mask_type must be one of {sorted(_MASK)}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q.dtype, dev)
+    _need(dk, "dk", q.dtype, dev)
+    _need(dv, "dv", q.dtype, dev)
+    ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = attn_bwd_thd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cq.data_ptr(),
+                      ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk, int(max_seqlen_q),
+                      int(max_seqlen_kv), hq, hkv, d, scale, _MASK[attn_mask_type],
+                      _DTYPE[q.dtype], ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    _check(st, "attn_bwd_thd")
+    return dq, dk, dv

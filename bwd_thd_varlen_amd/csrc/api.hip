@@ -1,0 +1,266 @@
+// Host side of the C ABI declared in include/attn_thd.h: argument checks,
+// workspace layout and the launch sequence on the caller's stream.  Nothing
+// here allocates device memory, synchronises or keeps state between calls.
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/attn_thd.h"
+#include "common.h"
+
+namespace attn {
+hipError_t launch_sched(const SchedParams& p, hipStream_t st);
+hipError_t launch_zero_fill(const ZeroParams& p, hipStream_t st);
+hipError_t launch_delta(const AttnParams& p, int dtype, int max_q_tiles, hipStream_t st);
+hipError_t launch_fwd(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st);
+hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st);
+hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st);
+int dkdv_tile(int d);
+}  // namespace attn
+
+namespace {
+
+using namespace attn;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// the kernels move rows in 16-byte pieces
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  size_t hdr, seq, q_list, kv_list, delta, total;
+  int64_t q_cap, kv_cap;   // list capacities for the smallest tile
+};
+
+bool sizes_ok(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv, int32_t d) {
+  return batch >= 0 && total_q >= 0 && total_kv >= 0 && hq >= 1 && hkv >= 1 && d >= 1;
+}
+
+Layout layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq) {
+  Layout L;
+  L.q_cap = ((int64_t)total_q + kMinTile - 1) / kMinTile + batch;
+  L.kv_cap = ((int64_t)total_kv + kMinTile - 1) / kMinTile + batch;
+  size_t off = 0;
+  L.hdr = off;
+  off += round_up(kHdrWords * sizeof(int32_t));
+  L.seq = off;
+  off += round_up((size_t)batch * sizeof(SeqInfo));
+  L.q_list = off;
+  off += round_up((size_t)L.q_cap * sizeof(int2));
+  L.kv_list = off;
+  off += round_up((size_t)L.kv_cap * sizeof(int2));
+  L.delta = off;
+  off += round_up((size_t)total_q * (size_t)hq * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+struct Common {
+  Layout L;
+  char* ws;
+  int64_t q_tiles_max, kv_tiles_max;
+};
+
+// Checks shared by both entry points.  Nothing is launched before they pass.
+attn_thd_status check_common(const void* q, const void* k, const void* v,
+                             const int32_t* cu_q, const int32_t* cu_kv, int32_t batch,
+                             int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv,
+                             int32_t d, float scale, int32_t mask_type, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, Common& c) {
+  if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return ATTN_THD_EINVAL;
+  if (hq % hkv != 0) return ATTN_THD_EINVAL;
+  if (d % 8 != 0 || d > 256) return ATTN_THD_EUNSUPPORTED;
+  if (dtype != ATTN_THD_BF16 && dtype != ATTN_THD_FP16) return ATTN_THD_EUNSUPPORTED;
+  if (mask_type != ATTN_THD_MASK_PADDING && mask_type != ATTN_THD_MASK_PADDING_CAUSAL)
+    return ATTN_THD_EUNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_THD_EINVAL;
+  if (!cu_q || !cu_kv) return ATTN_THD_EINVAL;
+  if ((total_q > 0 && !q) || (total_kv > 0 && (!k || !v))) return ATTN_THD_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_THD_EINVAL;
+  // grid sizes and element offsets must fit the kernels' integer types
+  const int64_t q_tiles = ((int64_t)total_q + kQTile - 1) / kQTile + batch;
+  const int64_t kv_tiles = ((int64_t)total_kv + dkdv_tile(d) - 1) / dkdv_tile(d) + batch;
+  if (q_tiles * hq > INT32_MAX || kv_tiles * hkv > INT32_MAX) return ATTN_THD_EINVAL;
+  if ((int64_t)total_q * hq > INT32_MAX || (int64_t)total_kv + 256 > INT32_MAX) return ATTN_THD_EINVAL;
+  c.L = layout(batch, total_q, total_kv, hq);
+  if (!workspace || workspace_bytes < c.L.total) return ATTN_THD_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return ATTN_THD_EWORKSPACE;
+  c.ws = static_cast<char*>(workspace);
+  c.q_tiles_max = q_tiles;
+  c.kv_tiles_max = kv_tiles;
+  return ATTN_THD_OK;
+}
+
+SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu_kv,
+                         const int32_t* cu_qp, const int32_t* cu_kp, int32_t batch,
+                         int32_t total_q, int32_t total_kv, int q_tile, int kv_tile, bool causal) {
+  SchedParams s;
+  s.cu_q = cu_q;
+  s.cu_kv = cu_kv;
+  s.cu_qp = cu_qp;
+  s.cu_kp = cu_kp;
+  s.batch = batch;
+  s.total_q = total_q;
+  s.total_kv = total_kv;
+  s.q_tile = q_tile;
+  s.kv_tile = kv_tile;
+  s.causal = causal ? 1 : 0;
+  s.hdr = reinterpret_cast<int32_t*>(c.ws + c.L.hdr);
+  s.seq = reinterpret_cast<SeqInfo*>(c.ws + c.L.seq);
+  s.q_list = reinterpret_cast<int2*>(c.ws + c.L.q_list);
+  s.kv_list = reinterpret_cast<int2*>(c.ws + c.L.kv_list);
+  return s;
+}
+
+AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, float scale) {
+  AttnParams a = {};
+  a.hdr = reinterpret_cast<const int32_t*>(c.ws + c.L.hdr);
+  a.seq = reinterpret_cast<const SeqInfo*>(c.ws + c.L.seq);
+  a.delta = reinterpret_cast<float*>(c.ws + c.L.delta);
+  a.hq = hq;
+  a.hkv = hkv;
+  a.group = hq / hkv;
+  a.d = d;
+  a.scale = scale;
+  a.scale_log2e = scale * kLog2e;
+  return a;
+}
+
+ZeroParams zero_params(const Common& c, int32_t batch, int rows, int width, bool kv_side,
+                       void* t0, void* t1, float* lse, int lse_heads) {
+  ZeroParams z;
+  z.hdr = reinterpret_cast<const int32_t*>(c.ws + c.L.hdr);
+  z.seq = reinterpret_cast<const SeqInfo*>(c.ws + c.L.seq);
+  z.batch = batch;
+  z.rows = rows;
+  z.width = width;
+  z.kv_side = kv_side ? 1 : 0;
+  z.lse_heads = lse_heads;
+  z.t0 = t0;
+  z.t1 = t1;
+  z.lse = lse;
+  return z;
+}
+
+#define ATTN_TRY(expr)                                   \
+  do {                                                   \
+    if ((expr) != hipSuccess) return ATTN_THD_ELAUNCH;   \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_thd_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq,
+                               int32_t hkv, int32_t d) {
+  if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return 0;
+  return layout(batch, total_q, total_kv, hq).total;
+}
+
+attn_thd_status attn_fwd_thd(const void* q, const void* k, const void* v, void* out, float* lse,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                             const int32_t* cu_seqlens_q_padded,
+                             const int32_t* cu_seqlens_kv_padded, int32_t batch, int32_t total_q,
+                             int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                             int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
+                             int32_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  (void)max_seqlen_q;
+  (void)max_seqlen_kv;
+  Common c;
+  attn_thd_status st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv,
+                                    hq, hkv, d, scale, mask_type, dtype, workspace,
+                                    workspace_bytes, c);
+  if (st != ATTN_THD_OK) return st;
+  if (total_q > 0 && (!out || !lse)) return ATTN_THD_EINVAL;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_THD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool causal = mask_type == ATTN_THD_MASK_PADDING_CAUSAL;
+
+  ATTN_TRY(launch_sched(sched_params(c, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                                     cu_seqlens_kv_padded, batch, total_q, total_kv, kQTile, 0,
+                                     causal), s));
+  AttnParams a = attn_params(c, hq, hkv, d, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse_out = lse;
+  a.list = reinterpret_cast<const int2*>(c.ws + c.L.q_list);
+  ATTN_TRY(launch_fwd(a, dtype, causal, (int)c.q_tiles_max, s));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, out, nullptr, lse, hq), s));
+  return ATTN_THD_OK;
+}
+
+attn_thd_status attn_bwd_thd(const void* q, const void* k, const void* v, const void* out,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                             const int32_t* cu_seqlens_q_padded,
+                             const int32_t* cu_seqlens_kv_padded, int32_t batch, int32_t total_q,
+                             int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                             int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
+                             int32_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  (void)max_seqlen_q;
+  (void)max_seqlen_kv;
+  Common c;
+  attn_thd_status st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv,
+                                    hq, hkv, d, scale, mask_type, dtype, workspace,
+                                    workspace_bytes, c);
+  if (st != ATTN_THD_OK) return st;
+  if (total_q > 0 && (!out || !dout || !lse || !dq)) return ATTN_THD_EINVAL;
+  if (total_kv > 0 && (!dk || !dv)) return ATTN_THD_EINVAL;
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return ATTN_THD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool causal = mask_type == ATTN_THD_MASK_PADDING_CAUSAL;
+  const int kv_tile = dkdv_tile(d);
+
+  ATTN_TRY(launch_sched(sched_params(c, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                                     cu_seqlens_kv_padded, batch, total_q, total_kv, kQTile,
+                                     kv_tile, causal), s));
+  AttnParams a = attn_params(c, hq, hkv, d, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.list = reinterpret_cast<const int2*>(c.ws + c.L.q_list);
+  ATTN_TRY(launch_delta(a, dtype, (int)c.q_tiles_max, s));
+  ATTN_TRY(launch_dq(a, dtype, causal, (int)c.q_tiles_max, s));
+  a.list = reinterpret_cast<const int2*>(c.ws + c.L.kv_list);
+  ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0), s));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0), s));
+  return ATTN_THD_OK;
+}
+
+const char* attn_thd_status_string(int32_t status) {
+  switch (status) {
+    case ATTN_THD_OK: return "ok";
+    case ATTN_THD_EINVAL: return "invalid argument";
+    case ATTN_THD_EUNSUPPORTED: return "unsupported head dim, dtype or mask";
+    case ATTN_THD_EWORKSPACE: return "workspace missing, too small or misaligned";
+    case ATTN_THD_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+attn_thd_status attn_thd_read_device_status(const void* workspace, void* stream, int32_t* status_out) {
+  if (!workspace || !status_out) return ATTN_THD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return ATTN_THD_ELAUNCH;
+  int32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return ATTN_THD_ELAUNCH;
+  *status_out = v;
+  return ATTN_THD_OK;
+}
+
+}  // extern "C"

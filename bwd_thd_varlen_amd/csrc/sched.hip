@@ -1,0 +1,275 @@
+// Varlen tile scheduler, uncovered-row zero fill and the backward
+// preprocess (Delta = rowsum(dO o O)).
+//
+// The scheduler turns the four cu_seqlens arrays into (a) a per-sequence
+// table of padded offsets and real lengths and (b) work lists of
+// (sequence, tile) for the compute kernels.  Real boundaries mask, padded
+// boundaries index (TransformerEngine issue 2892, "Expected Behavior").
+// Sequences without a real query or without a real key get no tile: their
+// rows are written by the zero fill, which also covers padding rows and rows
+// outside every slot (issue 2448, "Expected behavior": KV of a sequence with
+// no valid query must come back as zeros).  Tiles are listed heaviest first
+// so that the long causal tiles start early.
+#include "common.h"
+
+namespace attn {
+
+constexpr int kSchedThreads = 1024;
+
+// ceil(a / b) for a >= 0, b > 0
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Work key of a query tile: keys it visits, in 64-key units.
+__device__ __forceinline__ int q_tile_key(const SeqInfo& s, int m, int tile, int causal) {
+  int hi = min(s.lq, (m + 1) * tile);
+  int keys = causal ? min(s.lk, hi) : s.lk;
+  return min(cdiv(keys, 64), kSchedKeys - 1);
+}
+
+// Work key of a key tile: queries that reach it, in 64-query units.
+__device__ __forceinline__ int kv_tile_key(const SeqInfo& s, int n, int tile, int causal) {
+  int q = causal ? max(0, s.lq - n * tile) : s.lq;
+  return min(cdiv(q, 64), kSchedKeys - 1);
+}
+
+// Exclusive prefix over hist[] in DESCENDING key order, in place:
+// hist[k] becomes the number of tiles with a larger key.  Returns the total.
+__device__ int scan_desc(int* hist, int* part) {
+  const int tid = threadIdx.x;
+  constexpr int per = kSchedKeys / kSchedThreads;  // keys per thread
+  // thread tid owns descending positions [tid*per, tid*per+per)
+  int loc[per];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    loc[i] = hist[kSchedKeys - 1 - (tid * per + i)];
+    sum += loc[i];
+  }
+  part[tid] = sum;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the per-thread sums
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+  const int total = part[kSchedThreads - 1];
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    hist[kSchedKeys - 1 - (tid * per + i)] = run;
+    run += loc[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// Builds one list.  kv_side selects which length is tiled.  The order of
+// tiles with equal keys depends on LDS atomics and is not fixed; every output
+// element is produced by exactly one work item with a fixed internal order,
+// so results do not depend on the list order.
+__device__ int build_list(const SchedParams& p, bool kv_side, int tile, int2* list, int* hist,
+                          int* part) {
+  const int tid = threadIdx.x;
+  for (int k = tid; k < kSchedKeys; k += kSchedThreads) hist[k] = 0;
+  __syncthreads();
+  for (int b = tid; b < p.batch; b += kSchedThreads) {
+    SeqInfo s = p.seq[b];
+    if (s.lq == 0 || s.lk == 0) continue;
+    const int n = cdiv(kv_side ? s.lk : s.lq, tile);
+    for (int t = 0; t < n; ++t) {
+      int key = kv_side ? kv_tile_key(s, t, tile, p.causal) : q_tile_key(s, t, tile, p.causal);
+      atomicAdd(&hist[key], 1);
+    }
+  }
+  __syncthreads();
+  const int total = scan_desc(hist, part);
+  for (int b = tid; b < p.batch; b += kSchedThreads) {
+    SeqInfo s = p.seq[b];
+    if (s.lq == 0 || s.lk == 0) continue;
+    const int n = cdiv(kv_side ? s.lk : s.lq, tile);
+    for (int t = 0; t < n; ++t) {
+      int key = kv_side ? kv_tile_key(s, t, tile, p.causal) : q_tile_key(s, t, tile, p.causal);
+      int pos = atomicAdd(&hist[key], 1);
+      list[pos] = make_int2(b, t);
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
+  __shared__ int hist[kSchedKeys];
+  __shared__ int part[kSchedThreads];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  const int32_t* cqp = p.cu_qp ? p.cu_qp : p.cu_q;
+  const int32_t* ckp = p.cu_kp ? p.cu_kp : p.cu_kv;
+  for (int b = tid; b < p.batch; b += kSchedThreads) {
+    const int64_t q0 = p.cu_q[b], q1 = p.cu_q[b + 1], k0 = p.cu_kv[b], k1 = p.cu_kv[b + 1];
+    const int64_t pq0 = cqp[b], pq1 = cqp[b + 1], pk0 = ckp[b], pk1 = ckp[b + 1];
+    const int64_t lq = q1 - q0, lk = k1 - k0;
+    // real length within [0, slot]; slot within [0, total]: with every b
+    // checked this also makes the padded arrays non-decreasing, so slots are
+    // disjoint.
+    const bool bad = lq < 0 || lq > pq1 - pq0 || lk < 0 || lk > pk1 - pk0 || pq0 < 0 ||
+                     pq1 > p.total_q || pk0 < 0 || pk1 > p.total_kv;
+    if (bad) atomicOr(&s_bad, 1);
+    SeqInfo s;
+    s.oq = bad ? 0 : (int)pq0;
+    s.lq = bad ? 0 : (int)lq;
+    s.ok = bad ? 0 : (int)pk0;
+    s.lk = bad ? 0 : (int)lk;
+    p.seq[b] = s;
+  }
+  __syncthreads();
+  const int bad = s_bad;
+  int nq = 0, nk = 0;
+  if (!bad) {
+    __threadfence_block();
+    if (p.q_tile > 0) nq = build_list(p, false, p.q_tile, p.q_list, hist, part);
+    if (p.kv_tile > 0) nk = build_list(p, true, p.kv_tile, p.kv_list, hist, part);
+  }
+  if (tid == 0) {
+    p.hdr[kHdrStatus] = bad ? 1 : 0;
+    p.hdr[kHdrNQTiles] = nq;
+    p.hdr[kHdrNKVTiles] = nk;
+  }
+}
+
+// ----------------------------------------------------------------- zero fill
+// One workgroup per 64 rows.  A query row is covered when it lies inside the
+// real part of a sequence that has at least one real key; a key row when it
+// lies inside the real part of a sequence with at least one real query.
+// Uncovered rows get +0.0 (and lse = -inf).  With bad cu_seqlens data no row
+// is covered.
+constexpr int kZeroRows = 64;
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(ZeroParams p) {
+  __shared__ int s_uncov[kZeroRows];
+  __shared__ int s_n;
+  const int tid = threadIdx.x;
+  const int row0 = blockIdx.x * kZeroRows;
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  if (tid < kZeroRows && row0 + tid < p.rows) {
+    const int t = row0 + tid;
+    bool cov = false;
+    if (p.hdr[kHdrStatus] == 0 && p.batch > 0) {
+      // largest b with offset(b) <= t (offsets are non-decreasing when valid)
+      int lo = 0, hi = p.batch - 1, b = -1;
+      while (lo <= hi) {
+        int mid = (lo + hi) >> 1;
+        int off = p.kv_side ? p.seq[mid].ok : p.seq[mid].oq;
+        if (off <= t) { b = mid; lo = mid + 1; } else { hi = mid - 1; }
+      }
+      if (b >= 0) {
+        SeqInfo s = p.seq[b];
+        cov = p.kv_side ? (t - s.ok < s.lk && s.lq > 0) : (t - s.oq < s.lq && s.lk > 0);
+      }
+    }
+    if (!cov) {
+      int slot = atomicAdd(&s_n, 1);
+      s_uncov[slot] = t;
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  const int chunks = p.width >> 3;   // 16-byte chunks per row (width % 8 == 0)
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < n; ++i) {
+    const int64_t t = s_uncov[i];
+    for (int c = tid; c < chunks; c += 256) {
+      if (p.t0) reinterpret_cast<u32x4*>(p.t0)[t * chunks + c] = z;
+      if (p.t1) reinterpret_cast<u32x4*>(p.t1)[t * chunks + c] = z;
+    }
+    if (p.lse)
+      for (int h = tid; h < p.lse_heads; h += 256) p.lse[t * p.lse_heads + h] = -__builtin_inff();
+  }
+}
+
+// ----------------------------------------------------------------- Delta
+// Delta[t, h] = sum_c dO[t,h,c] * O[t,h,c] in fp32 for the real query rows
+// of every listed query tile.  CHP lanes (a power of two >= d/8) cooperate on
+// one row, 16 bytes each; the partial sums are combined with xor shuffles.
+template <int DT, int CHP>
+__global__ __launch_bounds__(256) void delta_kernel(AttnParams p) {
+  const int ntiles = p.hdr[kHdrNQTiles];
+  const int item = blockIdx.x / p.hq;
+  const int h = blockIdx.x - item * p.hq;
+  if (item >= ntiles) return;
+  const int2 e = p.list[item];
+  const SeqInfo s = p.seq[e.x];
+  const int i0 = e.y * kQTile;
+  const int rows = min(kQTile, s.lq - i0);
+  const int tid = threadIdx.x;
+  const int lane_c = tid & (CHP - 1);
+  const int chunks = p.d >> 3;
+  constexpr int kRowsPerPass = 256 / CHP;
+  const int64_t rs = (int64_t)p.hq * p.d;   // row stride in elements
+  for (int r = tid / CHP; r < rows; r += kRowsPerPass) {
+    const int64_t row = s.oq + i0 + r;
+    float acc = 0.f;
+    if (lane_c < chunks) {
+      const int64_t off = row * rs + (int64_t)h * p.d + lane_c * 8;
+      u32x4 a = ldg16(reinterpret_cast<const uint16_t*>(p.o) + off);
+      u32x4 b = ldg16(reinterpret_cast<const uint16_t*>(p.dout) + off);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float a0, a1, b0, b1;
+        // copy the lane word out first: bit-casting a vector element in place
+        // miscompiles (every w read element 0)
+        const uint32_t aw = a[w], bw = b[w];
+        if (DT == kBF16) {
+          a0 = __uint_as_float(aw << 16); a1 = __uint_as_float(aw & 0xffff0000u);
+          b0 = __uint_as_float(bw << 16); b1 = __uint_as_float(bw & 0xffff0000u);
+        } else {
+          f16x2 ha = __builtin_bit_cast(f16x2, aw);
+          f16x2 hb = __builtin_bit_cast(f16x2, bw);
+          a0 = (float)ha[0]; a1 = (float)ha[1]; b0 = (float)hb[0]; b1 = (float)hb[1];
+        }
+        acc = __builtin_fmaf(a0, b0, acc);
+        acc = __builtin_fmaf(a1, b1, acc);
+      }
+    }
+#pragma unroll
+    for (int off = CHP / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CHP);
+    if (lane_c == 0) p.delta[row * p.hq + h] = acc;
+  }
+}
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_sched(const SchedParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_fill(const ZeroParams& p, hipStream_t st) {
+  if (p.rows <= 0) return hipSuccess;
+  const int blocks = (p.rows + kZeroRows - 1) / kZeroRows;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_delta_dt(const AttnParams& p, int grid, hipStream_t st) {
+  const int ch = p.d >> 3;
+  if (ch <= 1) hipLaunchKernelGGL((delta_kernel<DT, 1>), dim3(grid), dim3(256), 0, st, p);
+  else if (ch <= 2) hipLaunchKernelGGL((delta_kernel<DT, 2>), dim3(grid), dim3(256), 0, st, p);
+  else if (ch <= 4) hipLaunchKernelGGL((delta_kernel<DT, 4>), dim3(grid), dim3(256), 0, st, p);
+  else if (ch <= 8) hipLaunchKernelGGL((delta_kernel<DT, 8>), dim3(grid), dim3(256), 0, st, p);
+  else if (ch <= 16) hipLaunchKernelGGL((delta_kernel<DT, 16>), dim3(grid), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((delta_kernel<DT, 32>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_delta(const AttnParams& p, int dtype, int max_q_tiles, hipStream_t st) {
+  const int grid = max_q_tiles * p.hq;
+  if (grid <= 0) return hipSuccess;
+  return dtype == kBF16 ? launch_delta_dt<kBF16>(p, grid, st) : launch_delta_dt<kFP16>(p, grid, st);
+}
+
+}  // namespace attn

@@ -1,0 +1,149 @@
+/*
+ * attn_thd.h -- C ABI of the MI355X (gfx950) THD varlen attention library.
+ *
+ * Fused scaled-dot-product attention, forward (O and the softmax statistic
+ * LSE) and backward (dQ, dK, dV), over packed variable-length sequences in
+ * THD layout, with grouped-query attention and the "padding" and
+ * "padding_causal" masks.
+ *
+ * Operation (TransformerEngine issue 3333 "FusedAttention (cuDNN) THD
+ * backward produces wrong gradients on sm_120", section "Reproduction": a
+ * per-sequence SDPA; issue 3216 "flash-attn-4 4.0.0b11: ... wrong dQ/dK/dV
+ * at head_dim=256", section "Reproduce": GQA by repeating KV heads, scale,
+ * causal triangle).  For every sequence b and query head h, with
+ * g = h / (hq / hkv):
+ *     S   = scale * Q_bh K_bg^T             (Lq_b x Lk_b)
+ *     P   = softmax over the allowed keys    (padding: all real keys;
+ *                                             padding_causal: key j <= query i)
+ *     O   = P V_bg,     LSE_i = ln sum_{j allowed} exp(S_ij)
+ *   backward, from dO:
+ *     dP = dO V^T, Delta_i = sum_c dO_ic O_ic, dS = P o (dP - Delta)
+ *     dQ = scale dS K,  dK_g = scale sum_{h in g} dS^T Q,  dV_g = sum_{h in g} P^T dO
+ *
+ * Boundaries (issue 2892 "SIGSEGV in fused_attn_fwd when cu_seqlens_q !=
+ * cu_seqlens_q_padded ...", section "Expected Behavior"): cu_seqlens_* give
+ * the REAL token counts and drive the mask; cu_seqlens_*_padded give the
+ * MEMORY layout and drive indexing; outputs keep the padded layout.  The
+ * real tokens of sequence b are rows [cu_padded[b], cu_padded[b] + L_b) of
+ * its slot; the rest of the slot is padding.  Issue 2448 "Inconsistent
+ * fused_attn_bwd results of dk, dv under THD layout + GQA on multiple
+ * calls", section "Expected behavior": KV rows of a sequence without valid
+ * queries get dK = dV = 0, and no result depends on earlier calls.
+ *
+ * Layouts (all row-major, contiguous, head_dim fastest):
+ *   q, out, dout, dq : [total_q,  hq,  d]  dtype (bf16 or fp16)
+ *   k, v, dk, dv     : [total_kv, hkv, d]  same dtype
+ *   lse              : [total_q,  hq]      float32, natural log
+ *   cu_seqlens_*     : int32 [batch + 1], device memory, non-decreasing
+ * A NULL cu_seqlens_*_padded pointer means "same as the real array".
+ *
+ * Every row the method does not reach is written explicitly on every call:
+ * out = dq = +0.0 and lse = -inf on query rows outside the real ranges (and
+ * on real query rows of a sequence with no real key); dk = dv = +0.0 on KV
+ * rows outside the real ranges and on every KV row of a sequence with no
+ * real query.  Outputs may therefore be uninitialised on entry.
+ *
+ * Ownership: every pointer is caller-owned device memory.  The library
+ * never allocates, frees or caches device memory and keeps no pointer after
+ * a call returns.  The workspace is scratch whose contents are undefined on
+ * entry (garbage or NaN is fine): each call initialises every byte it
+ * reads.  Calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ * default stream); no host<->device copy and no synchronisation happen
+ * inside.  Concurrent calls need distinct workspaces.
+ *
+ * Errors: host-checkable argument errors return a non-zero status before
+ * anything is enqueued (no partial writes).  Bad DEVICE data in the
+ * cu_seqlens arrays (decreasing entries, a real length above its padded
+ * slot, a slot beyond total_*) cannot be seen from the host: the call then
+ * treats every sequence as empty -- all outputs are written as for
+ * uncovered rows -- and sets a status word in the workspace, readable with
+ * attn_thd_read_device_status().  The library never reads or writes out of
+ * bounds on such data.
+ *
+ * Results are deterministic: repeated calls with the same inputs give
+ * bitwise identical outputs, whatever ran before (no atomics in any
+ * floating-point reduction).
+ */
+#ifndef ATTN_THD_H
+#define ATTN_THD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_THD_OK = 0,
+  ATTN_THD_EINVAL = 1,        /* bad argument: null pointer, negative size, hq % hkv != 0, ... */
+  ATTN_THD_EUNSUPPORTED = 2,  /* d not a multiple of 8 in [8, 256], or unknown dtype / mask */
+  ATTN_THD_EWORKSPACE = 3,    /* workspace NULL, too small or not 256-byte aligned */
+  ATTN_THD_ELAUNCH = 4        /* the HIP runtime rejected a kernel launch */
+} attn_thd_status;
+
+enum { ATTN_THD_BF16 = 0, ATTN_THD_FP16 = 1 };                        /* dtype     */
+enum { ATTN_THD_MASK_PADDING = 0, ATTN_THD_MASK_PADDING_CAUSAL = 1 }; /* mask_type */
+
+/* Device status bits (attn_thd_read_device_status). */
+enum {
+  ATTN_THD_DEV_OK = 0,
+  ATTN_THD_DEV_BAD_SEQLENS = 1  /* cu_seqlens data inconsistent; outputs written as all-uncovered */
+};
+
+/*
+ * Bytes of workspace attn_fwd_thd / attn_bwd_thd need for these sizes
+ * (the same figure serves both).  Returns 0 on invalid sizes.
+ */
+size_t attn_thd_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv,
+                               int32_t hq, int32_t hkv, int32_t d);
+
+/*
+ * Forward.  Writes out [total_q, hq, d] and lse [total_q, hq] (float32).
+ *   scale         softmax scale (no default at this level; 1/sqrt(d) is usual)
+ *   max_seqlen_*  an upper-bound hint only; correctness never depends on it
+ *   mask_type     ATTN_THD_MASK_PADDING or ATTN_THD_MASK_PADDING_CAUSAL
+ *                 (causal is top-left aligned: query i sees keys j <= i)
+ *   dtype         ATTN_THD_BF16 or ATTN_THD_FP16 (q, k, v, out)
+ */
+attn_thd_status attn_fwd_thd(
+    const void* q, const void* k, const void* v, void* out, float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward.  Reads q, k, v, out, dout and lse (as written by attn_fwd_thd
+ * for the same arguments) and writes dq [total_q, hq, d], dk and dv
+ * [total_kv, hkv, d].  dK/dV of a KV head are summed over the hq/hkv query
+ * heads of its group in a fixed order.  Other arguments as attn_fwd_thd.
+ */
+attn_thd_status attn_bwd_thd(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_thd_status_string(int32_t status);
+
+/*
+ * Test helper: waits for `stream`, then copies the device status word of
+ * the last call that used `workspace` into *status_out (ATTN_THD_DEV_* bits).
+ * This one synchronises; the compute entry points never do.
+ */
+attn_thd_status attn_thd_read_device_status(const void* workspace, void* stream,
+                                            int32_t* status_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_THD_H */

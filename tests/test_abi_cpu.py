@@ -1,0 +1,106 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function the
+header declares, sizes its workspace, and rejects bad host arguments before
+launching anything (no GPU is touched on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_thd.h")
+
+
+@pytest.fixture(scope="module")
+def A():
+    import bwd_thd_varlen_amd as A
+    A.lib()
+    return A
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd_thd", "attn_bwd_thd", "attn_thd_workspace_size", "attn_thd_status_string",
+              "attn_thd_read_device_status"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(A):
+    lib = A.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), f"missing export {n}"
+
+
+def test_status_strings(A):
+    for code in range(5):
+        assert A.status_string(code)
+    assert A.status_string(99) == "unknown status"
+
+
+def test_workspace_size(A):
+    ws = A.workspace_size(16, 65536, 65536, 64, 8, 128)
+    # Delta alone is total_q * hq * 4 bytes
+    assert ws >= 65536 * 64 * 4
+    assert ws % 256 == 0
+    assert A.workspace_size(-1, 10, 10, 1, 1, 8) == 0
+    assert A.workspace_size(0, 0, 0, 1, 1, 8) > 0
+
+
+FAKE = 1 << 20   # never dereferenced: every call below fails validation first
+
+
+def fwd_call(A, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cu_seqlens_q=FAKE,
+                cu_seqlens_kv=FAKE, cu_seqlens_q_padded=None, cu_seqlens_kv_padded=None, batch=2,
+                total_q=16, total_kv=16, max_seqlen_q=8, max_seqlen_kv=8, hq=4, hkv=2, d=64,
+                scale=0.125, mask_type=0, dtype=0, workspace=None, workspace_bytes=0, stream=None)
+    args.update(over)
+    return A.attn_fwd_thd(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(hq=4, hkv=3), 1),                 # hkv does not divide hq
+    (dict(hq=0), 1),
+    (dict(batch=-1), 1),
+    (dict(total_q=-5), 1),
+    (dict(d=12), 2),                        # not a multiple of 8
+    (dict(d=264), 2),                       # above 256
+    (dict(dtype=7), 2),
+    (dict(mask_type=3), 2),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(cu_seqlens_q=None), 1),
+    (dict(q=None), 1),
+    (dict(workspace=None), 3),              # every other argument fine
+    (dict(workspace=FAKE, workspace_bytes=16), 3),
+    (dict(workspace=FAKE + 8, workspace_bytes=1 << 30), 3),   # misaligned
+])
+def test_fwd_rejects_bad_host_arguments(A, over, code):
+    assert fwd_call(A, **over) == code
+
+
+def test_bwd_rejects_bad_host_arguments(A):
+    base = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                cu_seqlens_q=FAKE, cu_seqlens_kv=FAKE, cu_seqlens_q_padded=None,
+                cu_seqlens_kv_padded=None, batch=2, total_q=16, total_kv=16, max_seqlen_q=8,
+                max_seqlen_kv=8, hq=4, hkv=2, d=64, scale=0.125, mask_type=1, dtype=1,
+                workspace=None, workspace_bytes=0, stream=None)
+    assert A.attn_bwd_thd(**dict(base, hkv=3)) == 1
+    assert A.attn_bwd_thd(**dict(base, d=4)) == 2
+    assert A.attn_bwd_thd(**base) == 3
+    assert A.attn_bwd_thd(**dict(base, dk=None, workspace=FAKE, workspace_bytes=1 << 30)) == 1
+    assert A.attn_bwd_thd(**dict(base, dout=None, workspace=FAKE, workspace_bytes=1 << 30)) == 1
+
+
+def test_product_has_no_cpu_fallback():
+    """The binding loads only the HIP library; it never imports the oracle."""
+    src = open(os.path.join(ROOT, "bwd_thd_varlen_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("the CPU oracle", "")
+    for f in os.listdir(os.path.join(ROOT, "bwd_thd_varlen_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "bwd_thd_varlen_amd", "csrc", f)).read()
