@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of THD varlen attention forward + backward on one MI355X.
+
+Workload (the headline configuration): 65536 packed tokens, 16 sequences
+with lengths drawn uniform in [256, 8192] (seed 0) and padded to multiples of
+64, hq=64, hkv=8, d=128, bf16, padding_causal, deterministic backward.
+A step is one forward (scheduler, forward kernel, zero fill) plus one
+backward (scheduler, Delta, dQ, dK/dV, zero fills) over the whole batch,
+with inputs, outputs and workspace resident in HBM.
+
+FLOP model of the metric: F_fwd = 4*d*hq*sum(Lq*Lkv)/2 (causal) on real
+lengths, F_bwd = 2.5*F_fwd; value = (F_fwd + F_bwd) / time per step.
+
+Prints ONE JSON line.  Besides the metric it carries
+  roofline     -- the dominant kernel's algorithmic FLOP/s (from HIP events
+                  recorded around its launches in the timed region) against
+                  the dense bf16 MFMA peak, and its HBM traffic from the
+                  committed rocprofv3 counter summary when that summary was
+                  taken on the current kernel source (else null);
+  cpu_baseline -- the fp64 CPU oracle timed on a bounded sample of the same
+                  workload (rank 0, N=1 only).
+
+Options: --gpus N (only 1 is supported: this build runs on one GPU),
+--steps K, --warmup W, --no-cpu-baseline, --copy-calibration (adds a plain
+1 GiB device copy after the timed region, used to scale rocprofv3's
+FETCH_SIZE / WRITE_SIZE counters to bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
+METRIC = "fwd+bwd TFLOP/s (THD bf16 padding_causal, hq64/hkv8/d128) + % MFMA peak"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "fwd": ["bwd_thd_varlen_amd/csrc/fwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
+    "dq": ["bwd_thd_varlen_amd/csrc/bwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
+    "dkdv": ["bwd_thd_varlen_amd/csrc/bwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
+    "delta": ["bwd_thd_varlen_amd/csrc/sched.hip", "bwd_thd_varlen_amd/csrc/common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(stage: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(stage, []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(stage: str):
+    """HBM bytes per launch of `stage` from profiles/<stage>_throughput_65k_pmc.txt,
+    or None when absent or taken on other kernel source."""
+    path = os.path.join(PROFILES, f"{stage}_throughput_65k_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_0-9]+)\s*=\s*(\S+)\s*$", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256") != source_hash(stage):
+        log(f"[bench] {path}: taken on other kernel source -> traffic null")
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(case, budget_s: float = 10.0):
+    """The fp64 oracle, as it stands, on (sequence, KV group) units of the same
+    workload: the 2397-token sequence, groups 0, 1, ... until `budget_s` of
+    CPU work has been spent."""
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    real = np.diff(case.cu_seqlens_q)
+    b = int(np.argmin(np.abs(real - 2397)))
+    L, oq = int(real[b]), int(case.cu_seqlens_q_padded[b])
+    G = case.hq // case.hkv
+    f64 = lambda t: t.to(torch.float64).numpy()
+    flops, spent, groups = 0.0, 0.0, 0
+    for g in range(case.hkv):
+        q = f64(case.q[oq:oq + L, g * G:(g + 1) * G])
+        k = f64(case.k[oq:oq + L, g:g + 1])
+        v = f64(case.v[oq:oq + L, g:g + 1])
+        do = f64(case.dout[oq:oq + L, g * G:(g + 1) * G])
+        t0 = time.perf_counter()
+        oracle.attn_fwd_seq(q, k, v, case.scale, True)
+        oracle.attn_bwd_seq(q, k, v, do, case.scale, True)
+        spent += time.perf_counter() - t0
+        flops += 3.5 * 4.0 * case.d * G * L * L / 2.0
+        groups += 1
+        if spent >= budget_s:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle fwd+bwd of sequence {b} (L={L}) x {groups} KV group(s) "
+                       f"({G} query heads each) of the same workload, {spent:.1f} s; "
+                       f"FLOPs by the metric's causal model")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the per-GPU kernel is measured with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bwd_thd_varlen_amd as A
+    import workloads
+
+    A.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] generating the 65536-token workload")
+    case = workloads.throughput_65k()
+    f_fwd, f_bwd = workloads.causal_flops(case.cu_seqlens_q, case.cu_seqlens_kv, case.hq, case.d,
+                                          case.causal)
+    q, k, v, do = (t.to(dev) for t in (case.q, case.k, case.v, case.dout))
+    cu = lambda a: torch.as_tensor(a, dtype=torch.int32, device=dev)
+    cq, ck = cu(case.cu_seqlens_q), cu(case.cu_seqlens_kv)
+    cqp, ckp = cu(case.cu_seqlens_q_padded), cu(case.cu_seqlens_kv_padded)
+    out, lse = torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(A.workspace_size(case.batch, q.shape[0], k.shape[0], case.hq, case.hkv,
+                                      case.d), dtype=torch.uint8, device=dev)
+    kw = dict(cu_seqlens_q_padded=cqp, cu_seqlens_kv_padded=ckp,
+              max_seqlen_q=case.max_seqlen_q, max_seqlen_kv=case.max_seqlen_kv,
+              attn_mask_type="padding_causal", softmax_scale=case.scale, workspace=ws)
+
+    def step(ev_f=None, ev_b=None):
+        A.fwd(q, k, v, cq, ck, out=out, lse=lse, events=ev_f, **kw)
+        A.bwd(q, k, v, out, do, lse, cq, ck, dq=dq, dk=dk, dv=dv, events=ev_b, **kw)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(A.StageEvents(len(A.FWD_STAGES) + 1), A.StageEvents(len(A.BWD_STAGES) + 1))
+           for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ef, eb in evs:
+        step(ef, eb)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+
+    stage_ms = {}
+    for ef, eb in evs:
+        for name, ms in zip(("fwd." + s for s in A.FWD_STAGES), ef.stage_ms()):
+            stage_ms.setdefault(name, []).append(ms)
+        for name, ms in zip(("bwd." + s for s in A.BWD_STAGES), eb.stage_ms()):
+            stage_ms.setdefault(name, []).append(ms)
+    avg = {k_: sum(v_) / len(v_) for k_, v_ in stage_ms.items()}
+    log("[bench] per-stage average ms: " + ", ".join(f"{k_}={v_:.3f}" for k_, v_ in avg.items()))
+
+    # algorithmic work per launch of each compute kernel (GEMM FLOPs it must do)
+    work = {"fwd.fwd": ("fwd", f_fwd),            # S = QK^T, O = PV
+            "bwd.dkdv": ("dkdv", 2.0 * f_fwd),    # S, dP, dV = P^T dO, dK = dS^T Q
+            "bwd.dq": ("dq", 1.5 * f_fwd)}        # S, dP (recomputed), dQ = dS K
+    dom = max(work, key=lambda s: avg[s])
+    kname, flops = work[dom]
+    achieved = flops / (avg[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
+                "traffic": read_traffic(kname), "kernel": kname,
+                "avg_launch_ms": round(avg[dom], 4)}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(case)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "throughput_65k: 65536 packed tokens, 16 sequences, lengths "
+                               "U[256,8192] seed 0 padded to 64, hq=64 hkv=8 d=128, bf16, "
+                               "padding_causal, fwd+bwd",
+                   "tokens": int(q.shape[0]), "sequences": case.batch, "hq": case.hq,
+                   "hkv": case.hkv, "d": case.d, "max_seqlen": case.max_seqlen_q,
+                   "flops_per_step": f_fwd + f_bwd},
+        "pct_mfma_peak": round(100.0 * value / MFMA_PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {k_: round(v_, 4) for k_, v_ in avg.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,8 +20,10 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd", "fwd", "bwd",
-           "status_string", "read_device_status", "AttnError", "STATUS", "DEV_BAD_SEQLENS"]
+__all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
+           "attn_fwd_thd_timed", "attn_bwd_thd_timed", "fwd", "bwd", "status_string",
+           "read_device_status", "AttnError", "STATUS", "DEV_BAD_SEQLENS", "StageEvents",
+           "FWD_STAGES", "BWD_STAGES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
@@ -42,6 +44,8 @@ _FWD_ARGS = [_P, _P, _P, _P, _P,          # q k v out lse
              _I, _I, _I, _I, _I,          # batch total_q total_kv max_q max_kv
              _I, _I, _I, _F, _I, _I,      # hq hkv d scale mask dtype
              _P, _S, _P]                  # workspace bytes stream
+FWD_STAGES = ("sched", "fwd", "zero_fill_q")
+BWD_STAGES = ("sched", "delta", "dq", "dkdv", "zero_fill_q", "zero_fill_kv")
 _BWD_ARGS = [_P, _P, _P, _P, _P, _P,      # q k v out dout lse
              _P, _P, _P,                  # dq dk dv
              _P, _P, _P, _P,
@@ -71,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_thd.restype = ctypes.c_int
         L.attn_bwd_thd.argtypes = _BWD_ARGS
         L.attn_bwd_thd.restype = ctypes.c_int
+        L.attn_fwd_thd_timed.argtypes = _FWD_ARGS + [ctypes.POINTER(_P), _I]
+        L.attn_fwd_thd_timed.restype = ctypes.c_int
+        L.attn_bwd_thd_timed.argtypes = _BWD_ARGS + [ctypes.POINTER(_P), _I]
+        L.attn_bwd_thd_timed.restype = ctypes.c_int
         L.attn_thd_status_string.argtypes = [_I]
         L.attn_thd_status_string.restype = ctypes.c_char_p
         L.attn_thd_read_device_status.argtypes = [_P, _P, ctypes.POINTER(_I)]
@@ -112,6 +120,64 @@ def attn_bwd_thd(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k
                                   cu_seqlens_kv, cu_seqlens_q_padded, cu_seqlens_kv_padded, batch,
                                   total_q, total_kv, max_seqlen_q, max_seqlen_kv, hq, hkv, d,
                                   scale, mask_type, dtype, workspace, workspace_bytes, stream))
+
+
+def attn_fwd_thd_timed(*args, events, n_events) -> int:
+    """attn_fwd_thd plus per-stage HIP events (see StageEvents)."""
+    return int(lib().attn_fwd_thd_timed(*args, events, n_events))
+
+
+def attn_bwd_thd_timed(*args, events, n_events) -> int:
+    """attn_bwd_thd plus per-stage HIP events (see StageEvents)."""
+    return int(lib().attn_bwd_thd_timed(*args, events, n_events))
+
+
+class StageEvents:
+    """n HIP events (created with the HIP runtime torch loaded) to hand to the
+    instrumented entry points; ``stage_ms()`` reads the stage durations."""
+
+    def __init__(self, n: int):
+        self.n = n
+        self._hip = _hip_runtime()
+        self._arr = (_P * n)()
+        for i in range(n):
+            ev = _P()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise AttnError("hipEventCreate failed")
+            self._arr[i] = ev
+        self.ptr = ctypes.cast(self._arr, ctypes.POINTER(_P))
+
+    def stage_ms(self):
+        self._hip.hipEventSynchronize(self._arr[self.n - 1])
+        out = []
+        for i in range(self.n - 1):
+            ms = ctypes.c_float(0.0)
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), self._arr[i], self._arr[i + 1]) != 0:
+                raise AttnError("hipEventElapsedTime failed")
+            out.append(float(ms.value))
+        return out
+
+    def __del__(self):
+        try:
+            for i in range(self.n):
+                self._hip.hipEventDestroy(self._arr[i])
+        except Exception:
+            pass
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime already mapped into this process (the one torch loaded)."""
+    torch.cuda.init()
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1] if len(line.split()) >= 6 else ""
+        if os.path.basename(path).startswith("libamdhip64.so"):
+            h = ctypes.CDLL(path)
+            h.hipEventCreate.argtypes = [ctypes.POINTER(_P)]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _P, _P]
+            h.hipEventSynchronize.argtypes = [_P]
+            h.hipEventDestroy.argtypes = [_P]
+            return h
+    raise AttnError("HIP runtime not loaded")
 
 
 def read_device_status(workspace: torch.Tensor) -> int:
@@ -162,8 +228,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.T
         cu_seqlens_kv_padded: Optional[torch.Tensor] = None, max_seqlen_q: int = 0,
         max_seqlen_kv: int = 0, attn_mask_type: str = "padding",
         softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-        lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
-        ) -> Tuple[torch.Tensor, torch.Tensor]:
+        lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+        events: Optional["StageEvents"] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward: returns (out [Tq,hq,d] in q's dtype, lse [Tq,hq] float32)."""
     dev = q.device
     _need(q, "q", None, dev)
@@ -193,11 +259,14 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.T
     _need(lse, "lse", torch.float32, dev)
     ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = attn_fwd_thd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                      cq.data_ptr(), ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk,
-                      int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, d, scale,
-                      _MASK[attn_mask_type], _DTYPE[q.dtype], ws.data_ptr(),
-                      ws.numel() * ws.element_size(), stream)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            cq.data_ptr(), ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk,
+            int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, d, scale, _MASK[attn_mask_type],
+            _DTYPE[q.dtype], ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if events is None:
+        st = attn_fwd_thd(*args)
+    else:
+        st = attn_fwd_thd_timed(*args, events=events.ptr, n_events=events.n)
     _check(st, "attn_fwd_thd")
     return out, lse
 
@@ -209,7 +278,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         max_seqlen_kv: int = 0, attn_mask_type: str = "padding",
         softmax_scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
         dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None
+        workspace: Optional[torch.Tensor] = None, events: Optional["StageEvents"] = None
         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Backward: returns (dq, dk, dv) in q's dtype."""
     dev = q.device
@@ -243,10 +312,14 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     _need(dv, "dv", q.dtype, dev)
     ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = attn_bwd_thd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cq.data_ptr(),
-                      ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk, int(max_seqlen_q),
-                      int(max_seqlen_kv), hq, hkv, d, scale, _MASK[attn_mask_type],
-                      _DTYPE[q.dtype], ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cq.data_ptr(),
+            ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk, int(max_seqlen_q),
+            int(max_seqlen_kv), hq, hkv, d, scale, _MASK[attn_mask_type], _DTYPE[q.dtype],
+            ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+    if events is None:
+        st = attn_bwd_thd(*args)
+    else:
+        st = attn_bwd_thd_timed(*args, events=events.ptr, n_events=events.n)
     _check(st, "attn_bwd_thd")
     return dq, dk, dv

@@ -149,6 +149,105 @@ ZeroParams zero_params(const Common& c, int32_t batch, int rows, int width, bool
     if ((expr) != hipSuccess) return ATTN_THD_ELAUNCH;   \
   } while (0)
 
+// Optional per-stage event marks (benchmark instrumentation).
+struct Marks {
+  void* const* ev;
+  int n;
+  hipStream_t s;
+  hipError_t mark(int i) const {
+    return (ev && i < n) ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  }
+};
+
+constexpr int kFwdStages = 3;   // scheduler, forward, zero fill
+constexpr int kBwdStages = 6;   // scheduler, Delta, dQ, dK/dV, zero fill (q rows), zero fill (kv rows)
+
+attn_thd_status fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
+                         const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_qp,
+                         const int32_t* cu_kp, int32_t batch, int32_t total_q, int32_t total_kv,
+                         int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
+                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* events, int32_t n_events) {
+  Common c;
+  attn_thd_status st = check_common(q, k, v, cu_q, cu_kv, batch, total_q, total_kv, hq, hkv, d,
+                                    scale, mask_type, dtype, workspace, workspace_bytes, c);
+  if (st != ATTN_THD_OK) return st;
+  if (total_q > 0 && (!out || !lse)) return ATTN_THD_EINVAL;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_THD_EINVAL;
+  if (events && n_events != kFwdStages + 1) return ATTN_THD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Marks m{events, n_events, s};
+  const bool causal = mask_type == ATTN_THD_MASK_PADDING_CAUSAL;
+
+  ATTN_TRY(m.mark(0));
+  ATTN_TRY(launch_sched(sched_params(c, cu_q, cu_kv, cu_qp, cu_kp, batch, total_q, total_kv,
+                                     kQTile, 0, causal), s));
+  AttnParams a = attn_params(c, hq, hkv, d, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse_out = lse;
+  a.list = reinterpret_cast<const int2*>(c.ws + c.L.q_list);
+  ATTN_TRY(m.mark(1));
+  ATTN_TRY(launch_fwd(a, dtype, causal, (int)c.q_tiles_max, s));
+  ATTN_TRY(m.mark(2));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, out, nullptr, lse, hq), s));
+  ATTN_TRY(m.mark(3));
+  return ATTN_THD_OK;
+}
+
+attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_qp,
+                         const int32_t* cu_kp, int32_t batch, int32_t total_q, int32_t total_kv,
+                         int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
+                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* events, int32_t n_events) {
+  Common c;
+  attn_thd_status st = check_common(q, k, v, cu_q, cu_kv, batch, total_q, total_kv, hq, hkv, d,
+                                    scale, mask_type, dtype, workspace, workspace_bytes, c);
+  if (st != ATTN_THD_OK) return st;
+  if (total_q > 0 && (!out || !dout || !lse || !dq)) return ATTN_THD_EINVAL;
+  if (total_kv > 0 && (!dk || !dv)) return ATTN_THD_EINVAL;
+  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return ATTN_THD_EINVAL;
+  if (events && n_events != kBwdStages + 1) return ATTN_THD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Marks m{events, n_events, s};
+  const bool causal = mask_type == ATTN_THD_MASK_PADDING_CAUSAL;
+  const int kv_tile = dkdv_tile(d);
+
+  ATTN_TRY(m.mark(0));
+  ATTN_TRY(launch_sched(sched_params(c, cu_q, cu_kv, cu_qp, cu_kp, batch, total_q, total_kv,
+                                     kQTile, kv_tile, causal), s));
+  AttnParams a = attn_params(c, hq, hkv, d, scale);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.list = reinterpret_cast<const int2*>(c.ws + c.L.q_list);
+  ATTN_TRY(m.mark(1));
+  ATTN_TRY(launch_delta(a, dtype, (int)c.q_tiles_max, s));
+  ATTN_TRY(m.mark(2));
+  ATTN_TRY(launch_dq(a, dtype, causal, (int)c.q_tiles_max, s));
+  a.list = reinterpret_cast<const int2*>(c.ws + c.L.kv_list);
+  ATTN_TRY(m.mark(3));
+  ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
+  ATTN_TRY(m.mark(4));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0), s));
+  ATTN_TRY(m.mark(5));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0), s));
+  ATTN_TRY(m.mark(6));
+  return ATTN_THD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,29 +268,27 @@ attn_thd_status attn_fwd_thd(const void* q, const void* k, const void* v, void* 
                              void* stream) {
   (void)max_seqlen_q;
   (void)max_seqlen_kv;
-  Common c;
-  attn_thd_status st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv,
-                                    hq, hkv, d, scale, mask_type, dtype, workspace,
-                                    workspace_bytes, c);
-  if (st != ATTN_THD_OK) return st;
-  if (total_q > 0 && (!out || !lse)) return ATTN_THD_EINVAL;
-  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_THD_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool causal = mask_type == ATTN_THD_MASK_PADDING_CAUSAL;
+  return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                  cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d, scale, mask_type,
+                  dtype, workspace, workspace_bytes, stream, nullptr, 0);
+}
 
-  ATTN_TRY(launch_sched(sched_params(c, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
-                                     cu_seqlens_kv_padded, batch, total_q, total_kv, kQTile, 0,
-                                     causal), s));
-  AttnParams a = attn_params(c, hq, hkv, d, scale);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.lse_out = lse;
-  a.list = reinterpret_cast<const int2*>(c.ws + c.L.q_list);
-  ATTN_TRY(launch_fwd(a, dtype, causal, (int)c.q_tiles_max, s));
-  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, out, nullptr, lse, hq), s));
-  return ATTN_THD_OK;
+attn_thd_status attn_fwd_thd_timed(const void* q, const void* k, const void* v, void* out,
+                                   float* lse, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_kv,
+                                   const int32_t* cu_seqlens_q_padded,
+                                   const int32_t* cu_seqlens_kv_padded, int32_t batch,
+                                   int32_t total_q, int32_t total_kv, int32_t max_seqlen_q,
+                                   int32_t max_seqlen_kv, int32_t hq, int32_t hkv, int32_t d,
+                                   float scale, int32_t mask_type, int32_t dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* events,
+                                   int32_t n_events) {
+  (void)max_seqlen_q;
+  (void)max_seqlen_kv;
+  if (!events) return ATTN_THD_EINVAL;
+  return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                  cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d, scale, mask_type,
+                  dtype, workspace, workspace_bytes, stream, events, n_events);
 }
 
 attn_thd_status attn_bwd_thd(const void* q, const void* k, const void* v, const void* out,
@@ -205,41 +302,28 @@ attn_thd_status attn_bwd_thd(const void* q, const void* k, const void* v, const 
                              void* stream) {
   (void)max_seqlen_q;
   (void)max_seqlen_kv;
-  Common c;
-  attn_thd_status st = check_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv,
-                                    hq, hkv, d, scale, mask_type, dtype, workspace,
-                                    workspace_bytes, c);
-  if (st != ATTN_THD_OK) return st;
-  if (total_q > 0 && (!out || !dout || !lse || !dq)) return ATTN_THD_EINVAL;
-  if (total_kv > 0 && (!dk || !dv)) return ATTN_THD_EINVAL;
-  if (!aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
-      (reinterpret_cast<uintptr_t>(lse) & 3u))
-    return ATTN_THD_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool causal = mask_type == ATTN_THD_MASK_PADDING_CAUSAL;
-  const int kv_tile = dkdv_tile(d);
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
+                  cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
+                  scale, mask_type, dtype, workspace, workspace_bytes, stream, nullptr, 0);
+}
 
-  ATTN_TRY(launch_sched(sched_params(c, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
-                                     cu_seqlens_kv_padded, batch, total_q, total_kv, kQTile,
-                                     kv_tile, causal), s));
-  AttnParams a = attn_params(c, hq, hkv, d, scale);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = out;
-  a.dout = dout;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.list = reinterpret_cast<const int2*>(c.ws + c.L.q_list);
-  ATTN_TRY(launch_delta(a, dtype, (int)c.q_tiles_max, s));
-  ATTN_TRY(launch_dq(a, dtype, causal, (int)c.q_tiles_max, s));
-  a.list = reinterpret_cast<const int2*>(c.ws + c.L.kv_list);
-  ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
-  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0), s));
-  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0), s));
-  return ATTN_THD_OK;
+attn_thd_status attn_bwd_thd_timed(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, void* dq, void* dk,
+                                   void* dv, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_kv,
+                                   const int32_t* cu_seqlens_q_padded,
+                                   const int32_t* cu_seqlens_kv_padded, int32_t batch,
+                                   int32_t total_q, int32_t total_kv, int32_t max_seqlen_q,
+                                   int32_t max_seqlen_kv, int32_t hq, int32_t hkv, int32_t d,
+                                   float scale, int32_t mask_type, int32_t dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* events,
+                                   int32_t n_events) {
+  (void)max_seqlen_q;
+  (void)max_seqlen_kv;
+  if (!events) return ATTN_THD_EINVAL;
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
+                  cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
+                  scale, mask_type, dtype, workspace, workspace_bytes, stream, events, n_events);
 }
 
 const char* attn_thd_status_string(int32_t status) {

@@ -131,6 +131,39 @@ attn_thd_status attn_bwd_thd(
     int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Instrumented variants for benchmarks.  Same arguments and behaviour as
+ * attn_fwd_thd / attn_bwd_thd, plus an array of caller-created HIP events
+ * (hipEvent_t, passed as void*) that the call records on `stream`:
+ * events[i] just before stage i is launched and events[n_events-1] after the
+ * last stage, so hipEventElapsedTime(events[i], events[i+1]) is stage i.
+ *   forward  (n_events = 4): scheduler, forward kernel, zero fill
+ *   backward (n_events = 7): scheduler, Delta preprocess, dQ kernel,
+ *                            dK/dV kernel, zero fill (query rows),
+ *                            zero fill (key rows)
+ * A NULL `events` or another n_events returns ATTN_THD_EINVAL.
+ */
+attn_thd_status attn_fwd_thd_timed(
+    const void* q, const void* k, const void* v, void* out, float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
+attn_thd_status attn_bwd_thd_timed(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_thd_status_string(int32_t status);
 
