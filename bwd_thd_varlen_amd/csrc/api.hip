@@ -30,7 +30,7 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t hdr, seq, q_list, kv_list, delta, total;
+  size_t hdr, seq, q_list, kv_list, delta, lse2, total;
   int64_t q_cap, kv_cap;   // list capacities for the smallest tile
 };
 
@@ -52,6 +52,8 @@ Layout layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq) {
   L.kv_list = off;
   off += round_up((size_t)L.kv_cap * sizeof(int2));
   L.delta = off;
+  off += round_up((size_t)total_q * (size_t)hq * sizeof(float));
+  L.lse2 = off;
   off += round_up((size_t)total_q * (size_t)hq * sizeof(float));
   L.total = off;
   return L;
@@ -119,6 +121,7 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.hdr = reinterpret_cast<const int32_t*>(c.ws + c.L.hdr);
   a.seq = reinterpret_cast<const SeqInfo*>(c.ws + c.L.seq);
   a.delta = reinterpret_cast<float*>(c.ws + c.L.delta);
+  a.lse2 = reinterpret_cast<float*>(c.ws + c.L.lse2);
   a.hq = hq;
   a.hkv = hkv;
   a.group = hq / hkv;

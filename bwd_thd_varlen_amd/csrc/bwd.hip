@@ -16,43 +16,45 @@
 // through LDS; S and dP are recomputed here instead of accumulating dQ across
 // key-tile workgroups, which keeps every dQ element owned by one workgroup.
 //
+// Both kernels fill double-buffered LDS tiles by global->LDS DMA one step
+// ahead of the compute (see TileDma in common.h).
+//
 // Layout tricks are those of the forward kernel (common.h): score tiles are
 // computed so that the lane index runs over the dimension that survives the
-// next product, and the matching operand is read from a transposed LDS copy
-// stored in perm16 order.
+// next product, and the operand that contracts over a tile's rows is read
+// from the same row-major LDS tile with the transpose read.
 #include "common.h"
 
 namespace attn {
 
 // ----------------------------------------------------------------- dQ
 template <int DT, int DPAD, bool CAUSAL>
-__global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void dq_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void dq_kernel(AttnParams p) {
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
   constexpr int KS = kKVStep;
-  constexpr int SRS = DPAD + 8;        // row-major K / V stride
-  constexpr int STS = KS + 8;          // K^T stride
-  constexpr int CPR = DPAD / 8;
-  constexpr int UNITS = (KS / 4) * CPR;
-  constexpr int UPT = (UNITS + 255) / 256;
+  using Dma = TileDma<DPAD, KS, 4>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KS * SRS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[KS * SRS];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[DPAD * STS];
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[KS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[KS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[KS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[KS * DPAD];
 
-  const int ntiles = p.hdr[kHdrNQTiles];
+  const int ntiles = uniform(p.hdr[kHdrNQTiles]);
   int item, h;
   xcd_split(blockIdx.x, p.hq, item, h);
   if (item >= ntiles) return;
-  const int2 e = p.list[item];
-  const SeqInfo s = p.seq[e.x];
+  const WorkItem w = load_item(p.list, p.seq, item);
+  const SeqInfo s = w.s;
   const int g = h / p.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
-  const int m0 = e.y * kQTile;
+  const int m0 = w.tile * kQTile;
   const int qi = m0 + wave * 32 + li;
   const int wq_lo = m0 + wave * 32, wq_hi = wq_lo + 31;
   const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
+  const uint32_t kv_rs_bytes = (uint32_t)(kvrs * 2);
   const int64_t qoff = (int64_t)s.oq * qrs + (int64_t)h * p.d;
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + qoff;
   const uint16_t* dob = reinterpret_cast<const uint16_t*>(p.dout) + qoff;
@@ -60,6 +62,20 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void dq_kernel(AttnParams
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   const bool qvalid = qi < s.lq;
+
+  const int q_end = min(s.lq, m0 + kQTile);
+  const int kend = CAUSAL ? min(s.lk, q_end) : s.lk;
+  const int nsteps = (kend + KS - 1) / KS;
+  const float sl2e = p.scale_log2e;
+
+  Dma dma_kv;
+  dma_kv.init(wave, lane, p.d, kv_rs_bytes);
+  auto issue = [&](int step, uint16_t* tK, uint16_t* tV) {
+    const int n0 = step * KS;
+    dma_kv.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, wave);
+    dma_kv.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, wave);
+  };
+  if (nsteps > 0) issue(0, sK0, sV0);
 
   u32x4 qreg[NT], doreg[NT];
 #pragma unroll
@@ -70,101 +86,60 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void dq_kernel(AttnParams
     doreg[t] = ok ? ldg16(dob + (int64_t)qi * qrs + c) : z4;
   }
   const int64_t srow = (int64_t)(s.oq + qi) * p.hq + h;
-  const float lse2 = qvalid ? p.lse[srow] * kLog2e : __builtin_inff();
+  const float lse2 = qvalid ? p.lse2[srow] : __builtin_inff();
   const float dlt = qvalid ? p.delta[srow] : 0.f;
-
-  const int q_end = min(s.lq, m0 + kQTile);
-  const int kend = CAUSAL ? min(s.lk, q_end) : s.lk;
-  const int nsteps = (kend + KS - 1) / KS;
-  const float sl2e = p.scale_log2e;
+  wait_vm<0>();
 
   f32x16 acc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero16();
 
-  u32x4 pk[UPT][4], pv[UPT][4];
-  auto load_step = [&](int step) {
+  auto do_step = [&](int step, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
+    if (step + 1 < nsteps) {
+      issue(step + 1, nK, nV);
+      wait_vm<2 * Dma::PER_WAVE>();
+    } else {
+      wait_vm<0>();
+    }
+    barrier_lds_dma();
     const int n0 = step * KS;
+    if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi)) {
+      f32x16 sc[2], dp[2];
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + 256 * u;
-      const int rg = unit / CPR, cc = unit - rg * CPR;
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        sc[kb2] = zero16();
+        dp[kb2] = zero16();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = n0 + 4 * rg + r;
-        const bool ok = unit < UNITS && j < kend && 8 * cc < p.d;
-        const int64_t off = (int64_t)j * kvrs + 8 * cc;
-        pk[u][r] = ok ? ldg16(kb + off) : z4;
-        pv[u][r] = ok ? ldg16(vb + off) : z4;
-      }
-    }
-  };
-  auto store_step = [&]() {
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + 256 * u;
-      if (UNITS % 256 != 0 && unit >= UNITS) continue;
-      const int rg = unit / CPR, cc = unit - rg * CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<u32x4*>(&sK[(4 * rg + r) * SRS + 8 * cc]) = pk[u][r];
-        *reinterpret_cast<u32x4*>(&sV[(4 * rg + r) * SRS + 8 * cc]) = pv[u][r];
-      }
-      const int pos = perm16(4 * rg);
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const int w = e8 >> 1, sh = (e8 & 1) * 16;
-        const uint32_t x0 = (pk[u][0][w] >> sh) & 0xffffu, x1 = (pk[u][1][w] >> sh) & 0xffffu;
-        const uint32_t x2 = (pk[u][2][w] >> sh) & 0xffffu, x3 = (pk[u][3][w] >> sh) & 0xffffu;
-        u32x2 val = {x0 | (x1 << 16), x2 | (x3 << 16)};
-        *reinterpret_cast<u32x2*>(&sKt[(8 * cc + e8) * STS + pos]) = val;
-      }
-    }
-  };
-
-  if (nsteps > 0) load_step(0);
-  for (int step = 0; step < nsteps; ++step) {
-    __syncthreads();
-    store_step();
-    __syncthreads();
-    if (step + 1 < nsteps) load_step(step + 1);
-    const int n0 = step * KS;
-    if (wq_lo >= s.lq) continue;
-    if (CAUSAL && n0 > wq_hi) continue;
-
-    f32x16 sc[2], dp[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sc[kb2] = zero16();
-      dp[kb2] = zero16();
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int o = (32 * kb2 + li) * SRS + 16 * t + 8 * hh;
-        sc[kb2] = Mfma<DT>::mma(*reinterpret_cast<const u32x4*>(&sK[o]), qreg[t], sc[kb2]);
-        dp[kb2] = Mfma<DT>::mma(*reinterpret_cast<const u32x4*>(&sV[o]), doreg[t], dp[kb2]);
-      }
-    }
-    const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo);
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -lse2));
-        if (need_mask) {
-          const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j > qi) pr = 0.f;
+        for (int t = 0; t < NT; ++t) {
+          sc[kb2] = Mfma<DT>::mma(lds_row8<DPAD>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
+          dp[kb2] = Mfma<DT>::mma(lds_row8<DPAD>(tV, 32 * kb2 + li, 16 * t + 8 * hh), doreg[t], dp[kb2]);
         }
-        sc[kb2][r] = pr * (dp[kb2][r] - dlt);     // dS
       }
+      const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&sKt[(32 * cb + li) * STS + 16 * u + 8 * hh]);
-        acc[cb] = Mfma<DT>::mma(a, b, acc[cb]);
+        for (int r = 0; r < 16; ++r) {
+          float pr = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -lse2));
+          if (need_mask) {
+            const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (j > qi) pr = 0.f;
+          }
+          sc[kb2][r] = pr * (dp[kb2][r] - dlt);     // dS
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tK, cb, u, lane), b, acc[cb]);
       }
     }
+    barrier_lds_dma();
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    do_step(step, sK0, sV0, sK1, sV1);
+    if (step + 1 < nsteps) do_step(step + 1, sK1, sV1, sK0, sV0);
   }
 
   if (qvalid) {
@@ -186,68 +161,99 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void dq_kernel(AttnParams
 
 // ----------------------------------------------------------------- dK / dV
 // NW waves (32 keys each), BM queries per step, K/V operands in registers
-// (KV_LDS = false) or re-read from LDS (KV_LDS = true, for d = 256).
+// (KV_LDS = false) or re-read from LDS (KV_LDS = true, for d = 256).  Each
+// step DMAs the Q and dO tiles of one (query head, query tile) pair plus
+// their LSE*log2(e) and Delta vectors (one 4-byte DMA per wave: wave 0 LSE,
+// wave 1 Delta, other waves a dummy so that every wave issues the same
+// number of DMAs and can use the same wait count).  Query rows past the real
+// length arrive as zeros in Q, dO, LSE and Delta, so they add nothing.
 template <int DT, int DPAD, bool CAUSAL, int NW, int BM, bool KV_LDS>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(AttnParams p) {
-  constexpr int NTH = NW * 64;
   constexpr int BN = 32 * NW;
   constexpr int NIB = BM / 32;         // 32-query blocks per step
   constexpr int NU = BM / 16;          // 16-query chunks per step
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
-  constexpr int SRS = DPAD + 8;        // row-major stride
-  constexpr int STS = BM + 8;          // transposed stride
-  constexpr int CPR = DPAD / 8;
-  constexpr int UNITS = (BM / 4) * CPR;
-  constexpr int UPT = (UNITS + NTH - 1) / NTH;
   constexpr int KVROWS = KV_LDS ? BN : 1;
+  using Dma = TileDma<DPAD, BM, NW>;
+  using DmaKV = TileDma<DPAD, (KV_LDS ? BN : 64), NW>;
+  constexpr int DMA_PER_STEP = 2 * Dma::PER_WAVE + 1;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BM * SRS];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[BM * SRS];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[DPAD * STS];
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[DPAD * STS];
-  __shared__ __attribute__((aligned(16))) float sL[BM];
-  __shared__ __attribute__((aligned(16))) float sD[BM];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KVROWS * SRS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[KVROWS * SRS];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[BM * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[BM * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO0[BM * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO1[BM * DPAD];
+  __shared__ __attribute__((aligned(16))) float sV0ec[2 * 64];   // LSE2 | Delta, buffer 0
+  __shared__ __attribute__((aligned(16))) float sV1ec[2 * 64];   // LSE2 | Delta, buffer 1
+  __shared__ __attribute__((aligned(16))) float sDummy[64];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[KVROWS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[KVROWS * DPAD];
 
-  const int ntiles = p.hdr[kHdrNKVTiles];
+  const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
   int item, g;
   xcd_split(blockIdx.x, p.hkv, item, g);
   if (item >= ntiles) return;
-  const int2 e = p.list[item];
-  const SeqInfo s = p.seq[e.x];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const WorkItem w = load_item(p.list, p.seq, item);
+  const SeqInfo s = w.s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
-  const int n0 = e.y * BN;
+  const int n0 = w.tile * BN;
   const int kj = n0 + wave * 32 + li;          // this lane's key (B-operand column)
   const int wk_lo = n0 + wave * 32, wk_hi = wk_lo + 31;
   const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
+  const uint32_t q_rs_bytes = (uint32_t)(qrs * 2), kv_rs_bytes = (uint32_t)(kvrs * 2);
   const int64_t kvoff = (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + kvoff;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + kvoff;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   const float sl2e = p.scale_log2e;
 
+  // query tiles that reach this key tile, times the heads of the group
+  const int m_first = CAUSAL ? n0 / BM : 0;
+  const int m_last = (s.lq + BM - 1) / BM;
+  const int nm = m_last > m_first ? m_last - m_first : 0;
+  const int nsteps = nm * p.group;
+  const int h0 = g * p.group;
+
+  Dma dma_q;
+  dma_q.init(wave, lane, p.d, q_rs_bytes);
+  // 4-byte DMA of the vector (LSE2 or Delta) rows i0 .. i0+BM-1 of head h
+  const uint32_t vec_voff = lane < BM ? (uint32_t)lane * (uint32_t)p.hq * 4u : kOutOfRange;
+  auto issue = [&](int step, uint16_t* tQ, uint16_t* tdO, float* tvec) {
+    const int hg = step / nm;
+    const int m = m_first + (step - hg * nm);
+    const int h = h0 + hg;
+    const int i0 = m * BM;
+    const int nrow = s.lq - i0;
+    const int64_t base = (int64_t)(s.oq + i0) * qrs + (int64_t)h * p.d;
+    dma_q.issue(reinterpret_cast<const uint16_t*>(p.q) + base, nrow, q_rs_bytes, tQ, wave);
+    dma_q.issue(reinterpret_cast<const uint16_t*>(p.dout) + base, nrow, q_rs_bytes, tdO, wave);
+    const int nr = uniform(nrow < 0 ? 0 : (nrow > BM ? BM : nrow));
+    const int64_t vbase = (int64_t)(s.oq + i0) * p.hq + h;
+    const float* src = wave == 0 ? p.lse2 + vbase : p.delta + vbase;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, wave < 2 ? (uint32_t)nr * (uint32_t)p.hq * 4u : 0u);
+    dma<4>(rs, wave == 0 ? tvec : (wave == 1 ? tvec + 64 : sDummy), vec_voff);
+  };
+  if (nsteps > 0) issue(0, sQ0, sdO0, sV0ec);
+
   // K and V operands of this wave's 32 keys (zero beyond the real keys)
   u32x4 kreg[KV_LDS ? 1 : NT], vreg[KV_LDS ? 1 : NT];
-  if (!KV_LDS) {
+  if constexpr (!KV_LDS) {
 #pragma unroll
-    for (int t = 0; t < (KV_LDS ? 1 : NT); ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int c = 16 * t + 8 * hh;
       const bool ok = kj < s.lk && c < p.d;
       kreg[t] = ok ? ldg16(kb + (int64_t)kj * kvrs + c) : z4;
       vreg[t] = ok ? ldg16(vb + (int64_t)kj * kvrs + c) : z4;
     }
   } else {
-    for (int unit = tid; unit < BN * CPR; unit += NTH) {
-      const int r = unit / CPR, cc = unit - r * CPR;
-      const int j = n0 + r;
-      const bool ok = j < s.lk && 8 * cc < p.d;
-      *reinterpret_cast<u32x4*>(&sK[r * SRS + 8 * cc]) = ok ? ldg16(kb + (int64_t)j * kvrs + 8 * cc) : z4;
-      *reinterpret_cast<u32x4*>(&sV[r * SRS + 8 * cc]) = ok ? ldg16(vb + (int64_t)j * kvrs + 8 * cc) : z4;
-    }
+    DmaKV dkv;
+    dkv.init(wave, lane, p.d, kv_rs_bytes);
+    dkv.issue(kb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sK, wave);
+    dkv.issue(vb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sV, wave);
   }
+  wait_vm<0>();
 
   f32x16 adk[NCB], adv[NCB];
 #pragma unroll
@@ -256,137 +262,71 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(AttnParams p) {
     adv[cb] = zero16();
   }
 
-  // query tiles that reach this key tile
-  const int m_first = CAUSAL ? n0 / BM : 0;
-  const int m_last = (s.lq + BM - 1) / BM;
-  const int nm = m_last > m_first ? m_last - m_first : 0;
-  const int nsteps = nm * p.group;
-  const int h0 = g * p.group;
-
-  u32x4 pq[UPT][4], pdo[UPT][4];
-  float pl = 0.f;
-  auto load_step = [&](int step) {
-    const int hg = step / nm;
-    const int m = m_first + (step - hg * nm);
-    const int h = h0 + hg;
-    const int i0 = m * BM;
-    const int64_t base = (int64_t)s.oq * qrs + (int64_t)h * p.d;
-    const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + base;
-    const uint16_t* dob = reinterpret_cast<const uint16_t*>(p.dout) + base;
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + NTH * u;
-      const int rg = unit / CPR, cc = unit - rg * CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * rg + r;
-        const bool ok = unit < UNITS && i < s.lq && 8 * cc < p.d;
-        const int64_t off = (int64_t)i * qrs + 8 * cc;
-        pq[u][r] = ok ? ldg16(qb + off) : z4;
-        pdo[u][r] = ok ? ldg16(dob + off) : z4;
-      }
+  auto do_step = [&](int step, const uint16_t* tQ, const uint16_t* tdO, const float* tvec,
+                     uint16_t* nQ, uint16_t* ndO, float* nvec) {
+    if (step + 1 < nsteps) {
+      issue(step + 1, nQ, ndO, nvec);
+      wait_vm<DMA_PER_STEP>();
+    } else {
+      wait_vm<0>();
     }
-    // threads [0, BM) fetch LSE*log2(e), threads [BM, 2BM) fetch Delta
-    if (tid < 2 * BM) {
-      const int i = i0 + (tid % BM);
-      const int64_t srow = (int64_t)(s.oq + i) * p.hq + h;
-      if (tid < BM) pl = i < s.lq ? p.lse[srow] * kLog2e : __builtin_inff();
-      else pl = i < s.lq ? p.delta[srow] : 0.f;
-    }
-  };
-  auto store_step = [&]() {
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + NTH * u;
-      if (UNITS % NTH != 0 && unit >= UNITS) continue;
-      const int rg = unit / CPR, cc = unit - rg * CPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<u32x4*>(&sQ[(4 * rg + r) * SRS + 8 * cc]) = pq[u][r];
-        *reinterpret_cast<u32x4*>(&sdO[(4 * rg + r) * SRS + 8 * cc]) = pdo[u][r];
-      }
-      const int pos = perm16(4 * rg);
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const int w = e8 >> 1, sh = (e8 & 1) * 16;
-        {
-          const uint32_t x0 = (pq[u][0][w] >> sh) & 0xffffu, x1 = (pq[u][1][w] >> sh) & 0xffffu;
-          const uint32_t x2 = (pq[u][2][w] >> sh) & 0xffffu, x3 = (pq[u][3][w] >> sh) & 0xffffu;
-          u32x2 val = {x0 | (x1 << 16), x2 | (x3 << 16)};
-          *reinterpret_cast<u32x2*>(&sQt[(8 * cc + e8) * STS + pos]) = val;
-        }
-        {
-          const uint32_t x0 = (pdo[u][0][w] >> sh) & 0xffffu, x1 = (pdo[u][1][w] >> sh) & 0xffffu;
-          const uint32_t x2 = (pdo[u][2][w] >> sh) & 0xffffu, x3 = (pdo[u][3][w] >> sh) & 0xffffu;
-          u32x2 val = {x0 | (x1 << 16), x2 | (x3 << 16)};
-          *reinterpret_cast<u32x2*>(&sdOt[(8 * cc + e8) * STS + pos]) = val;
-        }
-      }
-    }
-    if (tid < BM) sL[tid] = pl;
-    else if (tid < 2 * BM) sD[tid - BM] = pl;
-  };
-
-  if (nsteps > 0) load_step(0);
-  for (int step = 0; step < nsteps; ++step) {
-    __syncthreads();
-    store_step();
-    __syncthreads();
-    if (step + 1 < nsteps) load_step(step + 1);
+    barrier_lds_dma();
     const int hg = step / nm;
     const int i0 = (m_first + (step - hg * nm)) * BM;
-    if (wk_lo >= s.lk) continue;                  // no real key in this wave
-    if (CAUSAL && i0 + BM - 1 < wk_lo) continue;  // every query precedes every key
-
-    f32x16 sc[NIB], dp[NIB];
+    // waves with no real key, or whose keys all follow every query, idle
+    if (wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo)) {
+      f32x16 sc[NIB], dp[NIB];
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-      sc[ib] = zero16();
-      dp[ib] = zero16();
+      for (int ib = 0; ib < NIB; ++ib) {
+        sc[ib] = zero16();
+        dp[ib] = zero16();
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int o = (32 * ib + li) * SRS + 16 * t + 8 * hh;
-        u32x4 kop, vop;
-        if (KV_LDS) {
-          const int ko = (32 * wave + li) * SRS + 16 * t + 8 * hh;
-          kop = *reinterpret_cast<const u32x4*>(&sK[ko]);
-          vop = *reinterpret_cast<const u32x4*>(&sV[ko]);
-        } else {
-          kop = kreg[KV_LDS ? 0 : t];
-          vop = vreg[KV_LDS ? 0 : t];
-        }
-        sc[ib] = Mfma<DT>::mma(*reinterpret_cast<const u32x4*>(&sQ[o]), kop, sc[ib]);
-        dp[ib] = Mfma<DT>::mma(*reinterpret_cast<const u32x4*>(&sdO[o]), vop, dp[ib]);
-      }
-    }
-    const bool need_mask = CAUSAL && (i0 < wk_hi);
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int ibase = 32 * ib + 8 * q4 + 4 * hh;   // first of 4 consecutive queries
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[ibase]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[ibase]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * q4 + c;
-          float pr = fast_exp2(__builtin_fmaf(sc[ib][r], sl2e, -l4[c]));
-          if (need_mask && kj > i0 + ibase + c) pr = 0.f;
-          sc[ib][r] = pr;
-          dp[ib][r] = pr * (dp[ib][r] - d4[c]);
+        for (int t = 0; t < NT; ++t) {
+          u32x4 kop, vop;
+          if constexpr (KV_LDS) {
+            kop = lds_row8<DPAD>(sK, 32 * wave + li, 16 * t + 8 * hh);
+            vop = lds_row8<DPAD>(sV, 32 * wave + li, 16 * t + 8 * hh);
+          } else {
+            kop = kreg[KV_LDS ? 0 : t];
+            vop = vreg[KV_LDS ? 0 : t];
+          }
+          sc[ib] = Mfma<DT>::mma(lds_row8<DPAD>(tQ, 32 * ib + li, 16 * t + 8 * hh), kop, sc[ib]);
+          dp[ib] = Mfma<DT>::mma(lds_row8<DPAD>(tdO, 32 * ib + li, 16 * t + 8 * hh), vop, dp[ib]);
         }
       }
+      const bool need_mask = CAUSAL && (i0 < wk_hi);
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const u32x4 bp = pack_operand<DT>(sc[u >> 1], u & 1);
-      const u32x4 bds = pack_operand<DT>(dp[u >> 1], u & 1);
+      for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int o = (32 * cb + li) * STS + 16 * u + 8 * hh;
-        adv[cb] = Mfma<DT>::mma(*reinterpret_cast<const u32x4*>(&sdOt[o]), bp, adv[cb]);
-        adk[cb] = Mfma<DT>::mma(*reinterpret_cast<const u32x4*>(&sQt[o]), bds, adk[cb]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ibase = 32 * ib + 8 * q4 + 4 * hh;   // first of 4 consecutive queries
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[ibase]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + ibase]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * q4 + c;
+            float pr = fast_exp2(__builtin_fmaf(sc[ib][r], sl2e, -l4[c]));
+            if (need_mask && kj > i0 + ibase + c) pr = 0.f;
+            sc[ib][r] = pr;
+            dp[ib][r] = pr * (dp[ib][r] - d4[c]);
+          }
+        }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const u32x4 bp = pack_operand<DT>(sc[u >> 1], u & 1);
+        const u32x4 bds = pack_operand<DT>(dp[u >> 1], u & 1);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          adv[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tdO, cb, u, lane), bp, adv[cb]);
+          adk[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tQ, cb, u, lane), bds, adk[cb]);
+        }
       }
     }
+    barrier_lds_dma();
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    do_step(step, sQ0, sdO0, sV0ec, sQ1, sdO1, sV1ec);
+    if (step + 1 < nsteps) do_step(step + 1, sQ1, sdO1, sV1ec, sQ0, sdO0, sV0ec);
   }
 
   if (kj < s.lk) {

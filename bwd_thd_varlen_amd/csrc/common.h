@@ -13,10 +13,9 @@
 //     8*(r/4) + 4*(l >> 5) + (r%4).
 // An accumulator tile C read column-by-lane therefore already has, for a
 // 16-row chunk u, the rows 16u + 8*(s/4) + 4*hh + (s%4) in registers
-// 8*(u%2) + s: exactly a B (or A) operand in P-order.  A second operand that
-// must match is stored in LDS transposed with the matching permutation of its
-// contraction index inside each 16-block (perm16), so one 16-byte LDS read
-// yields it.
+// 8*(u%2) + s: exactly a B (or A) operand in P-order.  The operand it meets
+// must be read transposed from a row-major LDS tile in the same order; the
+// gfx950 LDS transpose read does that (lds_tr_operand).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -93,11 +92,161 @@ __device__ __forceinline__ u32x4 pack_operand(const f32x16& c, int half8) {
   return r;
 }
 
-// Position of contraction index j inside its 16-block when stored for a
-// P-order operand: swaps bits 2 and 3 so that lane half hh finds its eight
-// values j = 8a + 4hh + p (a in {0,1}, p in 0..3) at 8hh + 4a + p.
-__device__ __forceinline__ int perm16(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+// ----------------------------------------------------------------- LDS tiles
+// Every LDS tile is row-major with DPAD 16-bit columns and no padding; the
+// 16-byte chunks of row r are permuted by x -> x ^ swz(r).  With this
+// swizzle three access patterns are free of bank conflicts (64 banks of 4
+// bytes; a 16-byte access is served 16 lanes per pass, an 8-byte one 32):
+//   * 16-byte row reads: lane l reads chunk x of row base + (l & 31);
+//   * transposed reads (ds_read_b64_tr_b16): 32 lanes cover 4 consecutive
+//     rows x 64 bytes;
+//   * 16-byte staging writes of whole rows.
+template <int DPAD>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (DPAD >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (DPAD == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return (r >> 2) & 3;
+}
+
+// element offset of (row r, column c) in a swizzled tile
+template <int DPAD>
+__device__ __forceinline__ int toff(int r, int c) {
+  return r * DPAD + ((((c >> 3) ^ swz<DPAD>(r))) << 3) + (c & 7);
+}
+
+// 16-byte row read: columns [c, c+8) of row r (c a multiple of 8)
+template <int DPAD>
+__device__ __forceinline__ u32x4 lds_row8(const uint16_t* tile, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(tile + toff<DPAD>(r, c));
+}
+
+__device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Transposed MFMA operand from a row-major tile, for a product that
+// contracts over the tile's rows: lane l receives column 32*cb + (l & 31) at
+// rows 16u + 8*(s/4) + 4*(l >> 5) + (s%4), s = 0..7 (the P-order of an
+// accumulator tile).  ds_read_b64_tr_b16 hands lane i of each 16-lane group
+// element (i & 3) of the 8-byte chunk addressed by lane 4k + (i >> 2), as its
+// k-th value; so lane J of the group addresses row j0 + (J >> 2), columns
+// c0 + 4*(J & 3) .. +3.
+template <int DPAD>
+__device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* tile, int cb, int u, int lane) {
+  const int J = lane & 15;
+  const int c = 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (J & 3);
+  const int r = 16 * u + 4 * (lane >> 5) + (J >> 2);
+  const u32x2 a = lds_tr4(tile + toff<DPAD>(r, c));
+  const u32x2 b = lds_tr4(tile + toff<DPAD>(r + 8, c));
+  u32x4 o = {a[0], a[1], b[0], b[1]};
+  return o;
+}
+
+// ----------------------------------------------------------------- LDS DMA
+// Raw buffer resource over `bytes` bytes at p (no stride; the hardware range
+// check returns zeros for any offset >= bytes and does not touch memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a lane offset the range check always rejects
+
+// Global -> LDS DMA of BYTES (4 or 16) per lane: lane l's bytes land at
+// lds_wave_base + BYTES * l (wave-uniform base); no VGPR is written.  Issued
+// from inline asm so that the compiler does not try to order LDS reads
+// against it (its alias tracking cannot tell the double buffers apart and
+// would wait for the DMA of the next step); the kernels wait for their own
+// DMA explicitly (wait_vm) and then barrier.  M0 is reserved by the
+// compiler, but nothing else in these kernels uses it.
+template <int BYTES>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, const void* lds_wave_base, uint32_t voff) {
+  static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte lanes");
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) const void*)lds_wave_base));
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory");
+}
+
+// s_waitcnt for vector-memory operations only: at most n (< 64) outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for loops whose LDS is written only by DMA: the caller
+// has already waited (wait_vm) for its own DMA, and every LDS read before the
+// barrier has been consumed, so no memory fence is needed.  (A fenced
+// __syncthreads would also wait for the DMA just issued for the next step.)
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_lds_dma() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Fills a ROWS x DPAD swizzled tile from global rows (row stride `rs_bytes`),
+// NWAVES waves sharing the work: each 64-lane DMA instruction covers 1 KB of
+// the tile, i.e. tile slots [64k, 64k + 64) of 16 bytes; slot s is row
+// s / (DPAD/8), position s % (DPAD/8), which holds logical chunk
+// position ^ swz(row).  Chunks at or beyond the head dim d and rows at or
+// beyond the valid count come back as zeros.
+template <int DPAD, int ROWS, int NWAVES>
+struct TileDma {
+  static constexpr int CPR = DPAD / 8;
+  static constexpr int INSTR = ROWS * CPR / 64;
+  static constexpr int PER_WAVE = INSTR / NWAVES;
+  static_assert(INSTR % NWAVES == 0 && PER_WAVE > 0, "tile must split evenly over the waves");
+  uint32_t voff[PER_WAVE];
+
+  __device__ __forceinline__ void init(int wave, int lane, int d, uint32_t rs_bytes) {
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+      const int slot = (wave * PER_WAVE + k) * 64 + lane;
+      const int r = slot / CPR;
+      const int x = (slot % CPR) ^ swz<DPAD>(r);
+      voff[k] = (8 * x < d) ? (uint32_t)r * rs_bytes + 16u * (uint32_t)x : kOutOfRange;
+    }
+  }
+  // rows [0, rows_valid) of the tile start at `row0`
+  __device__ __forceinline__ void issue(const uint16_t* row0, int rows_valid, uint32_t rs_bytes,
+                                        uint16_t* tile, int wave) const {
+    const int nr = __builtin_amdgcn_readfirstlane(rows_valid < 0 ? 0 : (rows_valid > ROWS ? ROWS : rows_valid));
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(row0, (uint32_t)nr * rs_bytes);
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) dma<16>(rsrc, tile + (wave * PER_WAVE + k) * 512, voff[k]);
+  }
+};
+
+// A value the compiler cannot prove wave-uniform (e.g. loaded by a vector
+// load) but that is: keep it in a scalar register.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Work item of a compute kernel: the (sequence, tile) pair and the
+// sequence's record, all wave-uniform.
+struct WorkItem {
+  int b, tile;
+  SeqInfo s;
+};
+__device__ __forceinline__ WorkItem load_item(const int2* list, const SeqInfo* seq, int item) {
+  WorkItem w;
+  const int2 e = list[item];
+  w.b = uniform(e.x);
+  w.tile = uniform(e.y);
+  const SeqInfo s = seq[w.b];
+  w.s.oq = uniform(s.oq);
+  w.s.lq = uniform(s.lq);
+  w.s.ok = uniform(s.ok);
+  w.s.lk = uniform(s.lk);
+  return w;
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -168,6 +317,7 @@ struct AttnParams {
   void* dk;
   void* dv;
   float* delta;
+  float* lse2;       // LSE * log2(e), written by the preprocess
   const int32_t* hdr;
   const SeqInfo* seq;
   const int2* list;

@@ -9,9 +9,9 @@
 // Work split: 4 waves x 32 queries.  Each lane owns one query (column of the
 // transposed score tile S^T = K Q^T), so the softmax statistics are per-lane
 // scalars and the probabilities, still in registers, are directly the B
-// operand of O^T = V^T P^T.  Q stays in registers for the whole tile; each
-// 64-key step stages K (row-major) and V^T (transposed, perm16 order) in LDS,
-// the next step's K/V being fetched into registers while this one computes.
+// operand of O^T = V^T P^T.  Q stays in registers for the whole tile; K and V
+// arrive by global->LDS DMA into two row-major (swizzled) buffers, one step
+// ahead of the compute, and V^T operands come from the LDS transpose read.
 // Online softmax in the log2 domain: m = running max of scale*log2(e)*S,
 // l = running sum of exp2(x - m), O rescaled by exp2(m_old - m_new) only when
 // some lane's maximum moved.
@@ -24,32 +24,48 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
   constexpr int NT = DPAD / 16;        // 16-wide k chunks over the head dim
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
   constexpr int KS = kKVStep;          // keys per step
-  constexpr int SKS = DPAD + 8;        // K row stride in LDS (elements)
-  constexpr int SVS = KS + 8;          // V^T row stride in LDS (elements)
-  constexpr int CPR = DPAD / 8;        // 16-byte chunks per row
-  constexpr int UNITS = (KS / 4) * CPR;
-  constexpr int UPT = (UNITS + 255) / 256;
+  using Dma = TileDma<DPAD, KS, 4>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KS * SKS];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[DPAD * SVS];
+  // two buffers of K and V (distinct arrays, so the compiler can see that
+  // reading one buffer does not depend on the DMA filling the other)
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[KS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[KS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[KS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[KS * DPAD];
 
-  const int ntiles = p.hdr[kHdrNQTiles];
+  const int ntiles = uniform(p.hdr[kHdrNQTiles]);
   int item, h;
   xcd_split(blockIdx.x, p.hq, item, h);
   if (item >= ntiles) return;
-  const int2 e = p.list[item];
-  const SeqInfo s = p.seq[e.x];
+  const WorkItem w = load_item(p.list, p.seq, item);
+  const SeqInfo s = w.s;
   const int g = h / p.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, hh = lane >> 5;
-  const int m0 = e.y * kQTile;
+  const int m0 = w.tile * kQTile;
   const int qi = m0 + wave * 32 + li;
   const int wq_lo = m0 + wave * 32, wq_hi = wq_lo + 31;
   const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
+  const uint32_t kv_rs_bytes = (uint32_t)(kvrs * 2);
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)s.oq * qrs + (int64_t)h * p.d;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+  const int q_end = min(s.lq, m0 + kQTile);
+  const int kend = CAUSAL ? min(s.lk, q_end) : s.lk;
+  const int nsteps = (kend + KS - 1) / KS;
+  const float sl2e = p.scale_log2e;
+
+  Dma dma_kv;
+  dma_kv.init(wave, lane, p.d, kv_rs_bytes);
+  auto issue = [&](int step, uint16_t* tK, uint16_t* tV) {
+    const int n0 = step * KS;
+    dma_kv.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, wave);
+    dma_kv.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, wave);
+  };
+  if (nsteps > 0) issue(0, sK0, sV0);
 
   u32x4 qreg[NT];
 #pragma unroll
@@ -57,120 +73,81 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
     const int c = 16 * t + 8 * hh;
     qreg[t] = (qi < s.lq && c < p.d) ? ldg16(qb + (int64_t)qi * qrs + c) : z4;
   }
-
-  const int q_end = min(s.lq, m0 + kQTile);
-  const int kend = CAUSAL ? min(s.lk, q_end) : s.lk;
-  const int nsteps = (kend + KS - 1) / KS;
-  const float sl2e = p.scale_log2e;
+  wait_vm<0>();   // Q and the first step's tiles; keeps the compiler from re-waiting in the loop
 
   f32x16 acc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero16();
   float m_run = -__builtin_inff(), l_run = 0.f;
 
-  u32x4 pk[UPT][4], pv[UPT][4];
-  auto load_step = [&](int step) {
+  auto do_step = [&](int step, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
+    if (step + 1 < nsteps) {
+      issue(step + 1, nK, nV);
+      wait_vm<2 * Dma::PER_WAVE>();            // this step's tiles have landed
+    } else {
+      wait_vm<0>();
+    }
+    barrier_lds_dma();
     const int n0 = step * KS;
+    // waves with no real query, or whose queries all precede the step, idle
+    if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi)) {
+      f32x16 sc[2];
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + 256 * u;
-      const int rg = unit / CPR, cc = unit - rg * CPR;
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        sc[kb2] = zero16();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = n0 + 4 * rg + r;
-        const bool ok = unit < UNITS && j < kend && 8 * cc < p.d;
-        const int64_t off = (int64_t)j * kvrs + 8 * cc;
-        pk[u][r] = ok ? ldg16(kb + off) : z4;
-        pv[u][r] = ok ? ldg16(vb + off) : z4;
+        for (int t = 0; t < NT; ++t)
+          sc[kb2] = Mfma<DT>::mma(lds_row8<DPAD>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
       }
-    }
-  };
-  auto store_step = [&]() {
+      const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo);
+      if (need_mask) {
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + 256 * u;
-      if (UNITS % 256 != 0 && unit >= UNITS) continue;
-      const int rg = unit / CPR, cc = unit - rg * CPR;
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<u32x4*>(&sK[(4 * rg + r) * SKS + 8 * cc]) = pk[u][r];
-      const int pos = perm16(4 * rg);
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const int w = e8 >> 1, sh = (e8 & 1) * 16;
-        const uint32_t x0 = (pv[u][0][w] >> sh) & 0xffffu, x1 = (pv[u][1][w] >> sh) & 0xffffu;
-        const uint32_t x2 = (pv[u][2][w] >> sh) & 0xffffu, x3 = (pv[u][3][w] >> sh) & 0xffffu;
-        u32x2 val = {x0 | (x1 << 16), x2 | (x3 << 16)};
-        *reinterpret_cast<u32x2*>(&sVt[(8 * cc + e8) * SVS + pos]) = val;
+          for (int r = 0; r < 16; ++r) {
+            const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (j >= kend || (CAUSAL && j > qi)) sc[kb2][r] = -__builtin_inff();
+          }
       }
-    }
-  };
-
-  if (nsteps > 0) load_step(0);
-  for (int step = 0; step < nsteps; ++step) {
-    __syncthreads();
-    store_step();
-    __syncthreads();
-    if (step + 1 < nsteps) load_step(step + 1);
-    const int n0 = step * KS;
-    if (wq_lo >= s.lq) continue;                 // no real query in this wave
-    if (CAUSAL && n0 > wq_hi) continue;          // whole step above this wave's diagonal
-
-    f32x16 sc[2];
+      float mx = -__builtin_inff();
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sc[kb2] = zero16();
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&sK[(32 * kb2 + li) * SKS + 16 * t + 8 * hh]);
-        sc[kb2] = Mfma<DT>::mma(a, qreg[t], sc[kb2]);
-      }
-    }
-    const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo);
-    if (need_mask) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * sl2e);
+      const float base = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - base);
+      float rsum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j >= kend || (CAUSAL && j > qi)) sc[kb2][r] = -__builtin_inff();
+          const float pr = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -base));
+          sc[kb2][r] = pr;
+          rsum += pr;
         }
-    }
-    float mx = -__builtin_inff();
+      l_run = l_run * alpha + rsum;
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2e);
-    const float base = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - base);
-    float rsum = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -base));
-        sc[kb2][r] = pr;
-        rsum += pr;
+          for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
       }
-    l_run = l_run * alpha + rsum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&sVt[(32 * cb + li) * SVS + 16 * u + 8 * hh]);
-        acc[cb] = Mfma<DT>::mma(a, b, acc[cb]);
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tV, cb, u, lane), b, acc[cb]);
       }
     }
+    barrier_lds_dma();                           // this buffer is refilled two steps on
+  };
+  for (int step = 0; step < nsteps; step += 2) {
+    do_step(step, sK0, sV0, sK1, sV1);
+    if (step + 1 < nsteps) do_step(step + 1, sK1, sV1, sK0, sV0);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);

@@ -193,7 +193,8 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(ZeroParams p) {
 
 // ----------------------------------------------------------------- Delta
 // Delta[t, h] = sum_c dO[t,h,c] * O[t,h,c] in fp32 for the real query rows
-// of every listed query tile.  CHP lanes (a power of two >= d/8) cooperate on
+// of every listed query tile; also LSE * log2(e) for the same rows, the form
+// the backward kernels exponentiate with exp2.  CHP lanes (a power of two >= d/8) cooperate on
 // one row, 16 bytes each; the partial sums are combined with xor shuffles.
 template <int DT, int CHP>
 __global__ __launch_bounds__(256) void delta_kernel(AttnParams p) {
@@ -237,7 +238,10 @@ __global__ __launch_bounds__(256) void delta_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int off = CHP / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CHP);
-    if (lane_c == 0) p.delta[row * p.hq + h] = acc;
+    if (lane_c == 0) {
+      p.delta[row * p.hq + h] = acc;
+      p.lse2[row * p.hq + h] = p.lse[row * p.hq + h] * kLog2e;
+    }
   }
 }
 
