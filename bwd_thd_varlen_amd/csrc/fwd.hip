@@ -12,12 +12,19 @@
 // operand of O^T = V^T P^T.  Q stays in registers for the whole tile; K and V
 // arrive by global->LDS DMA into two row-major (swizzled) buffers, one step
 // ahead of the compute, and V^T operands come from the LDS transpose read.
-// Online softmax in the log2 domain: m = running max of scale*log2(e)*S,
-// l = running sum of exp2(x - m), O rescaled by exp2(m_old - m_new) only when
-// some lane's maximum moved.
+// Online softmax in the log2 domain: m = reference maximum of
+// scale*log2(e)*S, l = running sum of exp2(x - m); the reference (and with it
+// O and l, by exp2(m_old - m_new)) moves only when a row's maximum passes it
+// by more than kRescaleSlack.
 #include "common.h"
 
 namespace attn {
+
+// The running maximum used as the exp2 reference only moves when a row's
+// maximum exceeds it by more than this (log2 units): probabilities stay
+// below 2^8 and the accumulator is rescaled rarely.  The result is the
+// same softmax, since the final normalisation uses the same reference.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int DT, int DPAD, bool CAUSAL>
 __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParams p) {
@@ -114,10 +121,23 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2e);
-      const float base = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - base);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2e;
+      // the exp2 reference moves only when a row's maximum exceeds it by
+      // more than kRescaleSlack, so O is rarely rescaled
+      const bool move = mx > m_run + kRescaleSlack;
+      if (__any(move)) {
+        const float m_new = move ? mx : m_run;
+        // 1 for lanes that keep their reference (also when it is still -inf),
+        // 0 for a lane whose first finite maximum arrives
+        const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+        m_run = m_new;
+      }
+      const float base = (m_run == -__builtin_inff()) ? 0.f : m_run;
       float rsum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -127,14 +147,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
           sc[kb2][r] = pr;
           rsum += pr;
         }
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
-      }
+      l_run += rsum;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
@@ -167,7 +180,8 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
       }
     if (hh == 0)
       p.lse_out[(int64_t)(s.oq + qi) * p.hq + h] =
-          l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+          l_tot > 0.f ? ((m_run == -__builtin_inff() ? 0.f : m_run) + __builtin_log2f(l_tot)) * kLn2
+                      : -__builtin_inff();
   }
 }
 

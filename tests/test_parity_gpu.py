@@ -159,3 +159,30 @@ def test_throughput_workload_sampled():
     for t in (o, dq, dk, dv):
         sel = t[torch.as_tensor(~qrows, device=t.device)]
         assert int(torch.count_nonzero(sel.view(torch.int16))) == 0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_reference_moves_every_step(d, causal):
+    """Scores grow along the sequence (k_j = 0.02*j on every channel, q = 1), so
+    the row maximum jumps by more than 8 (log2 units) from one key step to the
+    next and the online-softmax reference must move; values are random."""
+    rng = np.random.default_rng(21)
+    L = [300, 170]
+    T = sum(L)
+    hq, hkv = 2, 1
+    q = torch.ones((T, hq, d), dtype=torch.bfloat16)
+    pos = np.concatenate([np.arange(l) for l in L]).astype(np.float32)
+    k = torch.from_numpy(np.repeat((0.02 * pos)[:, None, None], d, axis=2)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((T, hkv, d), dtype=np.float32)).to(torch.bfloat16)
+    do = torch.from_numpy(rng.standard_normal((T, hq, d), dtype=np.float32)).to(torch.bfloat16)
+    cu = np.array([0, L[0], T], np.int32)
+    case = workloads.Case(name="growing_scores", q=q, k=k, v=v, dout=do, cu_seqlens_q=cu,
+                          cu_seqlens_kv=cu.copy(), cu_seqlens_q_padded=cu.copy(),
+                          cu_seqlens_kv_padded=cu.copy(), scale=1 / math.sqrt(d), causal=causal,
+                          dtype="bf16", max_seqlen_q=300, max_seqlen_kv=300)
+    res = gpu_run(case)
+    ref = oracle_run(case)
+    rows = np.ones(T, bool)
+    assert_close("out", res[0], ref[0], case.dtype)
+    assert_lse_close(res[1], ref[1], rows)
