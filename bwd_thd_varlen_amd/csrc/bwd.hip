@@ -160,23 +160,26 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 }
 
 // ----------------------------------------------------------------- dK / dV
-// NW waves (32 keys each), BM queries per step, K/V operands in registers
-// (KV_LDS = false) or re-read from LDS (KV_LDS = true, for d = 256).  Each
+// NW waves (32 keys each), BM queries per step; the K and V operands of the
+// wave's keys stay in registers or are re-read from LDS tiles loaded once
+// (KVM: 0 both in registers, 1 V in LDS, 2 both in LDS), trading registers
+// (occupancy) against LDS traffic.  Each
 // step DMAs the Q and dO tiles of one (query head, query tile) pair plus
 // their LSE*log2(e) and Delta vectors (one 4-byte DMA per wave: wave 0 LSE,
 // wave 1 Delta, other waves a dummy so that every wave issues the same
 // number of DMAs and can use the same wait count).  Query rows past the real
 // length arrive as zeros in Q, dO, LSE and Delta, so they add nothing.
-template <int DT, int DPAD, bool CAUSAL, int NW, int BM, bool KV_LDS>
-__global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(AttnParams p) {
+template <int DT, int DPAD, bool CAUSAL, int NW, int BM, int KVM, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
+  constexpr bool K_LDS = KVM == 2;     // K operand re-read from LDS
+  constexpr bool V_LDS = KVM >= 1;     // V operand re-read from LDS
   constexpr int BN = 32 * NW;
   constexpr int NIB = BM / 32;         // 32-query blocks per step
   constexpr int NU = BM / 16;          // 16-query chunks per step
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
-  constexpr int KVROWS = KV_LDS ? BN : 1;
   using Dma = TileDma<DPAD, BM, NW>;
-  using DmaKV = TileDma<DPAD, (KV_LDS ? BN : 64), NW>;
+  using DmaKV = TileDma<DPAD, BN, NW>;
   constexpr int DMA_PER_STEP = 2 * Dma::PER_WAVE + 1;
 
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[BM * DPAD];
@@ -186,8 +189,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float sV0ec[2 * 64];   // LSE2 | Delta, buffer 0
   __shared__ __attribute__((aligned(16))) float sV1ec[2 * 64];   // LSE2 | Delta, buffer 1
   __shared__ __attribute__((aligned(16))) float sDummy[64];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KVROWS * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[KVROWS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[(K_LDS ? BN : 1) * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[(V_LDS ? BN : 1) * DPAD];
 
   const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
   int item, g;
@@ -237,21 +240,21 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(AttnParams p) {
   };
   if (nsteps > 0) issue(0, sQ0, sdO0, sV0ec);
 
-  // K and V operands of this wave's 32 keys (zero beyond the real keys)
-  u32x4 kreg[KV_LDS ? 1 : NT], vreg[KV_LDS ? 1 : NT];
-  if constexpr (!KV_LDS) {
+  // K and V operands of this wave's 32 keys (zero beyond the real keys),
+  // held in registers or re-read from a resident LDS tile
+  u32x4 kreg[K_LDS ? 1 : NT], vreg[V_LDS ? 1 : NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = 16 * t + 8 * hh;
-      const bool ok = kj < s.lk && c < p.d;
-      kreg[t] = ok ? ldg16(kb + (int64_t)kj * kvrs + c) : z4;
-      vreg[t] = ok ? ldg16(vb + (int64_t)kj * kvrs + c) : z4;
-    }
-  } else {
+  for (int t = 0; t < NT; ++t) {
+    const int c = 16 * t + 8 * hh;
+    const bool ok = kj < s.lk && c < p.d;
+    if constexpr (!K_LDS) kreg[t] = ok ? ldg16(kb + (int64_t)kj * kvrs + c) : z4;
+    if constexpr (!V_LDS) vreg[t] = ok ? ldg16(vb + (int64_t)kj * kvrs + c) : z4;
+  }
+  if constexpr (K_LDS || V_LDS) {
     DmaKV dkv;
     dkv.init(wave, lane, p.d, kv_rs_bytes);
-    dkv.issue(kb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sK, wave);
-    dkv.issue(vb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sV, wave);
+    if constexpr (K_LDS) dkv.issue(kb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sK, wave);
+    if constexpr (V_LDS) dkv.issue(vb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sV, wave);
   }
   wait_vm<0>();
 
@@ -283,13 +286,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(AttnParams p) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           u32x4 kop, vop;
-          if constexpr (KV_LDS) {
-            kop = lds_row8<DPAD>(sK, 32 * wave + li, 16 * t + 8 * hh);
-            vop = lds_row8<DPAD>(sV, 32 * wave + li, 16 * t + 8 * hh);
-          } else {
-            kop = kreg[KV_LDS ? 0 : t];
-            vop = vreg[KV_LDS ? 0 : t];
-          }
+          if constexpr (K_LDS) kop = lds_row8<DPAD>(sK, 32 * wave + li, 16 * t + 8 * hh);
+          else kop = kreg[K_LDS ? 0 : t];
+          if constexpr (V_LDS) vop = lds_row8<DPAD>(sV, 32 * wave + li, 16 * t + 8 * hh);
+          else vop = vreg[V_LDS ? 0 : t];
           sc[ib] = Mfma<DT>::mma(lds_row8<DPAD>(tQ, 32 * ib + li, 16 * t + 8 * hh), kop, sc[ib]);
           dp[ib] = Mfma<DT>::mma(lds_row8<DPAD>(tdO, 32 * ib + li, 16 * t + 8 * hh), vop, dp[ib]);
         }
@@ -377,20 +377,20 @@ hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tile
 // keys per dK/dV work item for a head dim
 int dkdv_tile(int d) { return d <= 128 ? 128 : 64; }
 
-template <int DT, int DPAD, int NW, int BM, bool KVL>
+template <int DT, int DPAD, int NW, int BM, int KVM, int OCC>
 static void launch_dkdv_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
   if (causal)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, NW, BM, KVL>), dim3(grid), dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, NW, BM, KVM, OCC>), dim3(grid), dim3(NW * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, NW, BM, KVL>), dim3(grid), dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, NW, BM, KVM, OCC>), dim3(grid), dim3(NW * 64), 0, st, p);
 }
 
 template <int DT>
 static void launch_dkdv_dt(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (p.d <= 32) launch_dkdv_d<DT, 32, 4, 64, false>(p, causal, grid, st);
-  else if (p.d <= 64) launch_dkdv_d<DT, 64, 4, 64, false>(p, causal, grid, st);
-  else if (p.d <= 128) launch_dkdv_d<DT, 128, 4, 64, false>(p, causal, grid, st);
-  else launch_dkdv_d<DT, 256, 2, 32, true>(p, causal, grid, st);
+  if (p.d <= 32) launch_dkdv_d<DT, 32, 4, 64, 0, 1>(p, causal, grid, st);
+  else if (p.d <= 64) launch_dkdv_d<DT, 64, 4, 64, 0, 1>(p, causal, grid, st);
+  else if (p.d <= 128) launch_dkdv_d<DT, 128, 4, 32, 0, 2>(p, causal, grid, st);
+  else launch_dkdv_d<DT, 256, 2, 32, 2, 1>(p, causal, grid, st);
 }
 
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st) {
