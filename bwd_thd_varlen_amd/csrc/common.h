@@ -262,6 +262,81 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine lanes l and l ^ 32 (the two half-waves) with the gfx950 half-wave
+// swap, a VALU op, instead of an LDS permute.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum / sum of the N x 16 accumulator values of a lane as a balanced
+// tree, so the reduction costs log depth rather than a 16N-long chain of
+// dependent instructions.  The maximum goes three operands at a time (one
+// v_max3 each).
+template <int N>
+__device__ __forceinline__ float tree_max(const f32x16 (&c)[N]) {
+  constexpr int M = 16 * N;
+  float t[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) t[i] = c[i / 16][i % 16];
+  int n = M;
+#pragma unroll
+  for (int level = 0; level < 6; ++level) {
+    if (n == 1) break;
+    const int m = (n + 2) / 3;
+#pragma unroll
+    for (int i = 0; i < m; ++i) {
+      float v = t[3 * i];
+      if (3 * i + 1 < n) v = fmaxf(v, t[3 * i + 1]);
+      if (3 * i + 2 < n) v = fmaxf(v, t[3 * i + 2]);
+      t[i] = v;
+    }
+    n = m;
+  }
+  return t[0];
+}
+template <int N>
+__device__ __forceinline__ float tree_sum(const f32x16 (&c)[N]) {
+  float t[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    t[r] = c[0][r];
+#pragma unroll
+    for (int i = 1; i < N; ++i) t[r] += c[i][r];
+  }
+#pragma unroll
+  for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+    for (int r = 0; r < w; ++r) t[r] += t[r + w];
+  return t[0];
+}
+
+// ----------------------------------------------------------------- scheduling
+// Left to itself the backend issues each LDS operand read right before the
+// MFMA that consumes it and waits for it there, so the matrix core idles for
+// the LDS latency on every product.  These hints (the backend's scheduling
+// groups, instruction classes by mask) order the products of one basic block
+// as a software pipeline: the reads of the first AHEAD MFMAs go first, then
+// each MFMA is followed by the R reads of the MFMA AHEAD places later.
+// Other instructions of the block are placed freely around the pipeline.
+constexpr unsigned kSgMfma = 0x008, kSgDsRead = 0x100;
+
+template <int NMFMA, int R, int AHEAD = 4>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  constexpr int A = AHEAD < NMFMA ? AHEAD : NMFMA;
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, A * R, 0);
+#pragma unroll
+  for (int z = 0; z < NMFMA - A; ++z) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, A, 0);
+}
+
 // Maps a linear workgroup id onto (work item, head) so that the heads an
 // XCD receives are contiguous (they share K/V tiles in that XCD's L2).
 // Workgroups are dispatched round-robin over the 8 XCDs by id.  Falls back

@@ -31,6 +31,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
   constexpr int NT = DPAD / 16;        // 16-wide k chunks over the head dim
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
   constexpr int KS = kKVStep;          // keys per step
+  constexpr int NKB = KS / 32;         // 32-key blocks of S^T per step
   using Dma = TileDma<DPAD, KS, 4>;
 
   // two buffers of K and V (distinct arrays, so the compiler can see that
@@ -98,30 +99,26 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
     const int n0 = step * KS;
     // waves with no real query, or whose queries all precede the step, idle
     if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi)) {
-      f32x16 sc[2];
+      f32x16 sc[NKB];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
         sc[kb2] = zero16();
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           sc[kb2] = Mfma<DT>::mma(lds_row8<DPAD>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
       }
+      pipeline_lds_mfma<NKB * NT, 1>();
       const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo);
       if (need_mask) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
             if (j >= kend || (CAUSAL && j > qi)) sc[kb2][r] = -__builtin_inff();
           }
       }
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2e;
+      const float mx = max_halves(tree_max(sc)) * sl2e;
       // the exp2 reference moves only when a row's maximum exceeds it by
       // more than kRescaleSlack, so O is rarely rescaled
       const bool move = mx > m_run + kRescaleSlack;
@@ -138,23 +135,19 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
         m_run = m_new;
       }
       const float base = (m_run == -__builtin_inff()) ? 0.f : m_run;
-      float rsum = 0.f;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -base));
-          sc[kb2][r] = pr;
-          rsum += pr;
-        }
-      l_run += rsum;
+        for (int r = 0; r < 16; ++r) sc[kb2][r] = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -base));
+      l_run += tree_sum(sc);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 2 * NKB; ++u) {
         const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           acc[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tV, cb, u, lane), b, acc[cb]);
       }
+      pipeline_lds_mfma<2 * NKB * NCB, 2>();
     }
     barrier_lds_dma();                           // this buffer is refilled two steps on
   };
@@ -163,7 +156,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
     if (step + 1 < nsteps) do_step(step + 1, sK1, sV1, sK0, sV0);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (qi < s.lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(s.oq + qi) * qrs + (int64_t)h * p.d;
