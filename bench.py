@@ -28,7 +28,6 @@ FETCH_SIZE / WRITE_SIZE counters to bytes).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -42,24 +41,10 @@ MFMA_PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
 METRIC = "fwd+bwd TFLOP/s (THD bf16 padding_causal, hq64/hkv8/d128) + % MFMA peak"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {
-    "fwd": ["bwd_thd_varlen_amd/csrc/fwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
-    "dq": ["bwd_thd_varlen_amd/csrc/bwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
-    "dkdv": ["bwd_thd_varlen_amd/csrc/bwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
-    "delta": ["bwd_thd_varlen_amd/csrc/sched.hip", "bwd_thd_varlen_amd/csrc/common.h"],
-}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def source_hash(stage: str) -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES.get(stage, []):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def read_traffic(stage: str):
@@ -73,6 +58,7 @@ def read_traffic(stage: str):
         m = re.match(r"^\s*([a-z_0-9]+)\s*=\s*(\S+)\s*$", line)
         if m:
             kv[m.group(1)] = m.group(2)
+    from bwd_thd_varlen_amd.rocprof_summary import source_hash
     if kv.get("kernel_source_sha256") != source_hash(stage):
         log(f"[bench] {path}: taken on other kernel source -> traffic null")
         return None
@@ -82,10 +68,10 @@ def read_traffic(stage: str):
         return None
 
 
-def cpu_baseline(case, budget_s: float = 10.0):
+def cpu_baseline(case, budget_s: float = 12.0):
     """The fp64 oracle, as it stands, on (sequence, KV group) units of the same
-    workload: the 2397-token sequence, groups 0, 1, ... until `budget_s` of
-    CPU work has been spent."""
+    workload: the sequences closest to 2400 tokens first, KV groups 0, 1, ...
+    of each, until `budget_s` of CPU work has been spent."""
     import numpy as np
     import torch
 
@@ -96,29 +82,33 @@ def cpu_baseline(case, budget_s: float = 10.0):
     except Exception:
         cores = os.cpu_count()
     real = np.diff(case.cu_seqlens_q)
-    b = int(np.argmin(np.abs(real - 2397)))
-    L, oq = int(real[b]), int(case.cu_seqlens_q_padded[b])
     G = case.hq // case.hkv
     f64 = lambda t: t.to(torch.float64).numpy()
-    flops, spent, groups = 0.0, 0.0, 0
-    for g in range(case.hkv):
-        q = f64(case.q[oq:oq + L, g * G:(g + 1) * G])
-        k = f64(case.k[oq:oq + L, g:g + 1])
-        v = f64(case.v[oq:oq + L, g:g + 1])
-        do = f64(case.dout[oq:oq + L, g * G:(g + 1) * G])
-        t0 = time.perf_counter()
-        oracle.attn_fwd_seq(q, k, v, case.scale, True)
-        oracle.attn_bwd_seq(q, k, v, do, case.scale, True)
-        spent += time.perf_counter() - t0
-        flops += 3.5 * 4.0 * case.d * G * L * L / 2.0
-        groups += 1
+    flops, spent, units = 0.0, 0.0, []
+    for b in np.argsort(np.abs(real - 2400), kind="stable"):
+        L, oq = int(real[b]), int(case.cu_seqlens_q_padded[b])
+        for g in range(case.hkv):
+            q = f64(case.q[oq:oq + L, g * G:(g + 1) * G])
+            k = f64(case.k[oq:oq + L, g:g + 1])
+            v = f64(case.v[oq:oq + L, g:g + 1])
+            do = f64(case.dout[oq:oq + L, g * G:(g + 1) * G])
+            t0 = time.perf_counter()
+            oracle.attn_fwd_seq(q, k, v, case.scale, True)
+            oracle.attn_bwd_seq(q, k, v, do, case.scale, True)
+            spent += time.perf_counter() - t0
+            flops += 3.5 * 4.0 * case.d * G * L * L / 2.0
+            units.append((int(b), L))
+            if spent >= budget_s:
+                break
         if spent >= budget_s:
             break
+    seqs = sorted({u for u in units})
+    desc = ", ".join(f"sequence {b} (L={L}) x {sum(1 for u in units if u[0] == b)} KV group(s)"
+                     for b, L in seqs)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": (f"fp64 numpy oracle fwd+bwd of sequence {b} (L={L}) x {groups} KV group(s) "
-                       f"({G} query heads each) of the same workload, {spent:.1f} s; "
-                       f"FLOPs by the metric's causal model")}
+            "sample": (f"fp64 numpy oracle fwd+bwd of {desc} ({G} query heads per group) of the "
+                       f"same workload, {spent:.1f} s; FLOPs by the metric's causal model")}
 
 
 def main():

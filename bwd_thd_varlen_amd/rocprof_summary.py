@@ -1,0 +1,169 @@
+"""Text summaries of rocprofv3 result databases for ``profiles/``.
+
+Two modes, each run on the databases a GPU run left behind:
+
+  python -m bwd_thd_varlen_amd.rocprof_summary trace DB OUT.md --command CMD
+      kernel-trace summary (calls, average and total duration per kernel)
+      from the ``top_kernels`` view of a ``rocprofv3 --kernel-trace --stats``
+      database.
+
+  python -m bwd_thd_varlen_amd.rocprof_summary traffic FETCH_DB WRITE_DB \\
+          --command-fetch CMD --command-write CMD
+      HBM traffic per launch of each compute kernel from two counter runs
+      (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``) of ``bench.py
+      --copy-calibration``.  The counters (KiB per dispatch) are scaled by
+      what they read for the plain 1 GiB device copies that option adds, so
+      that a copy of N bytes counts N bytes read and N written.  Writes
+      ``profiles/<stage>_throughput_65k_pmc.txt`` for fwd, dq, dkdv and
+      delta, stamped with the hash of the kernel sources (``source_hash``);
+      bench.py reports the traffic only while that hash matches.
+
+Reads SQLite files only; nothing here touches the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import os
+import sqlite3
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+
+# kernel sources behind each timed stage (a change to any of them makes a
+# stored counter summary stale)
+KERNEL_SOURCES = {
+    "fwd": ["bwd_thd_varlen_amd/csrc/fwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
+    "dq": ["bwd_thd_varlen_amd/csrc/bwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
+    "dkdv": ["bwd_thd_varlen_amd/csrc/bwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
+    "delta": ["bwd_thd_varlen_amd/csrc/sched.hip", "bwd_thd_varlen_amd/csrc/common.h"],
+}
+
+# demangled-name prefixes of each stage's kernel for the bf16 d=128 causal workload
+STAGE_KERNELS = {
+    "fwd": "void attn::fwd_kernel<0, 128, true",
+    "dq": "void attn::dq_kernel<0, 128, true",
+    "dkdv": "void attn::dkdv_kernel<0, 128, true",
+    "delta": "void attn::delta_kernel<0,",
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30          # bench.py --copy-calibration: 1 GiB copies
+COPY_MIN_KIB = (COPY_BYTES >> 10) // 4   # smaller copies (argument uploads) are ignored
+
+
+def source_hash(stage: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(stage, []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(db: str, sql: str):
+    con = sqlite3.connect(db)
+    try:
+        return list(con.execute(sql))
+    finally:
+        con.close()
+
+
+def trace(db: str, out: str, command: str) -> None:
+    rows = _rows(db, "select * from top_kernels")
+    total = sum(r[2] for r in rows)
+    lines = [
+        "# Kernel trace: throughput_65k (65536 tokens, hq=64 hkv=8 d=128, bf16, padding_causal)",
+        "",
+        "Command (run from the repository root on one MI355X, `TMPDIR=/tmp`):",
+        "",
+        f"    {command}",
+        "",
+        "Durations in microseconds, from the `top_kernels` view of the rocprofv3",
+        "results database (every dispatch of the run: warm-up and timed steps).",
+        "",
+        "| kernel | calls | avg us | total us | share |",
+        "|---|---|---|---|---|",
+    ]
+    for name, calls, tot, avg, *_ in rows:
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| {short} | {calls} | {avg:.1f} | {tot:.1f} | {100.0 * tot / total:.2f}% |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
+def _counter(db: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter."""
+    out = defaultdict(list)
+    for name, value in _rows(db, "select kernel_name, value from counters_collection "
+                                 f"where counter_name = '{counter}' order by dispatch_id"):
+        out[name].append(float(value))
+    return out
+
+
+def _copy_scale(values: dict) -> tuple:
+    big = [v for name, vs in values.items() if name.startswith(COPY_KERNEL) for v in vs
+           if v >= COPY_MIN_KIB]
+    if not big:
+        raise SystemExit("no 1 GiB copy dispatch found: run bench.py with --copy-calibration")
+    mean = sum(big) / len(big)
+    return (COPY_BYTES / 1024.0) / mean, len(big), mean
+
+
+def traffic(fetch_db: str, write_db: str, cmd_fetch: str, cmd_write: str) -> None:
+    fetch, write = _counter(fetch_db, "FETCH_SIZE"), _counter(write_db, "WRITE_SIZE")
+    fscale, fn, fmean = _copy_scale(fetch)
+    wscale, wn, wmean = _copy_scale(write)
+    for stage, prefix in STAGE_KERNELS.items():
+        fv = [v for name, vs in fetch.items() if name.startswith(prefix) for v in vs]
+        wv = [v for name, vs in write.items() if name.startswith(prefix) for v in vs]
+        if not fv or not wv:
+            print(f"{stage}: kernel {prefix!r} not in both databases, skipped")
+            continue
+        kname = next(name for name in fetch if name.startswith(prefix))
+        f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
+        hbm = (f_kib * fscale + w_kib * wscale) * 1024.0
+        path = os.path.join(PROFILES, f"{stage}_throughput_65k_pmc.txt")
+        with open(path, "w") as f:
+            f.write(
+                f"# HBM traffic per launch: {kname.split('(')[0]}, throughput_65k workload\n"
+                "# Two counter runs, from the repository root on one MI355X (TMPDIR=/tmp):\n"
+                f"#   {cmd_fetch}\n"
+                f"#   {cmd_write}\n"
+                "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by\n"
+                "# 1 GiB / (its value for the 1 GiB device copies of --copy-calibration).\n"
+                f"kernel_source_sha256 = {source_hash(stage)}\n"
+                f"dispatches = {len(fv)}\n"
+                f"fetch_kib_per_launch = {f_kib:.1f}\n"
+                f"write_kib_per_launch = {w_kib:.1f}\n"
+                f"copy_fetch_kib = {fmean:.1f}\n"
+                f"copy_write_kib = {wmean:.1f}\n"
+                f"copy_dispatches = {min(fn, wn)}\n"
+                f"fetch_scale = {fscale:.4f}\n"
+                f"write_scale = {wscale:.4f}\n"
+                f"hbm_bytes_per_launch = {hbm:.0f}\n")
+        print(f"wrote {path}: {hbm / 2**30:.3f} GiB per launch")
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("out")
+    t.add_argument("--command", required=True)
+    c = sub.add_parser("traffic")
+    c.add_argument("fetch_db")
+    c.add_argument("write_db")
+    c.add_argument("--command-fetch", required=True)
+    c.add_argument("--command-write", required=True)
+    a = ap.parse_args(argv)
+    if a.mode == "trace":
+        trace(a.db, a.out, a.command)
+    else:
+        traffic(a.fetch_db, a.write_db, a.command_fetch, a.command_write)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
