@@ -33,12 +33,16 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
   constexpr int KS = kKVStep;
-  using Dma = TileDma<DPAD, KS, 4>;
+  using LK = Swz<DPAD>;          // K: row reads (S) and transposed reads (dQ)
+  using LV = Swz<DPAD>;          // V: row reads (dP)
+  using DmaK = TileDma<LK, KS, 4>;
+  using DmaV = TileDma<LV, KS, 4>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[KS * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[KS * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[KS * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[KS * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[LV::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[LV::template elems<KS>()];
+  static_assert(!DmaK::SINK && !DmaV::SINK, "these tiles split evenly over the waves");
 
   const int ntiles = uniform(p.hdr[kHdrNQTiles]);
   int item, h;
@@ -68,12 +72,14 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   const int nsteps = (kend + KS - 1) / KS;
   const float sl2e = p.scale_log2e;
 
-  Dma dma_kv;
-  dma_kv.init(wave, lane, p.d, kv_rs_bytes);
+  DmaK dma_k;
+  DmaV dma_v;
+  dma_k.init(wave, lane, p.d, kv_rs_bytes);
+  dma_v.init(wave, lane, p.d, kv_rs_bytes);
   auto issue = [&](int step, uint16_t* tK, uint16_t* tV) {
     const int n0 = step * KS;
-    dma_kv.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, wave);
-    dma_kv.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, wave);
+    dma_k.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, nullptr, wave);
+    dma_v.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, nullptr, wave);
   };
   if (nsteps > 0) issue(0, sK0, sV0);
 
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   auto do_step = [&](int step, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
     if (step + 1 < nsteps) {
       issue(step + 1, nK, nV);
-      wait_vm<2 * Dma::PER_WAVE>();
+      wait_vm<DmaK::PER_WAVE + DmaV::PER_WAVE>();
     } else {
       wait_vm<0>();
     }
@@ -111,8 +117,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
         dp[kb2] = zero16();
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          sc[kb2] = Mfma<DT>::mma(lds_row8<DPAD>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
-          dp[kb2] = Mfma<DT>::mma(lds_row8<DPAD>(tV, 32 * kb2 + li, 16 * t + 8 * hh), doreg[t], dp[kb2]);
+          sc[kb2] = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
+          dp[kb2] = Mfma<DT>::mma(lds_row8<LV>(tV, 32 * kb2 + li, 16 * t + 8 * hh), doreg[t], dp[kb2]);
         }
       }
       const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo);
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
         const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          acc[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tK, cb, u, lane), b, acc[cb]);
+          acc[cb] = Mfma<DT>::mma(lds_tr_operand<LK>(tK, cb, u, lane), b, acc[cb]);
       }
     }
     barrier_lds_dma();
@@ -178,19 +184,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   constexpr int NU = BM / 16;          // 16-query chunks per step
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
-  using Dma = TileDma<DPAD, BM, NW>;
-  using DmaKV = TileDma<DPAD, BN, NW>;
+  using LQ = Lay<DPAD, true>;          // Q, dO: row reads (S, dP) and transposed reads (dK, dV)
+  using LKV = Lay<DPAD, false>;        // K, V kept in LDS (KVM): row reads
+  using Dma = TileDma<LQ, BM, NW>;
+  using DmaKV = TileDma<LKV, BN, NW>;
   constexpr int DMA_PER_STEP = 2 * Dma::PER_WAVE + 1;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sQ0[BM * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ1[BM * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO0[BM * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO1[BM * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[LQ::template elems<BM>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[LQ::template elems<BM>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO0[LQ::template elems<BM>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO1[LQ::template elems<BM>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sSink[Dma::SINK || DmaKV::SINK ? 512 : 8];
   __shared__ __attribute__((aligned(16))) float sV0ec[2 * 64];   // LSE2 | Delta, buffer 0
   __shared__ __attribute__((aligned(16))) float sV1ec[2 * 64];   // LSE2 | Delta, buffer 1
   __shared__ __attribute__((aligned(16))) float sDummy[64];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[(K_LDS ? BN : 1) * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[(V_LDS ? BN : 1) * DPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[K_LDS ? LKV::template elems<BN>() : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[V_LDS ? LKV::template elems<BN>() : 8];
 
   const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
   int item, g;
@@ -230,8 +239,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     const int i0 = m * BM;
     const int nrow = s.lq - i0;
     const int64_t base = (int64_t)(s.oq + i0) * qrs + (int64_t)h * p.d;
-    dma_q.issue(reinterpret_cast<const uint16_t*>(p.q) + base, nrow, q_rs_bytes, tQ, wave);
-    dma_q.issue(reinterpret_cast<const uint16_t*>(p.dout) + base, nrow, q_rs_bytes, tdO, wave);
+    dma_q.issue(reinterpret_cast<const uint16_t*>(p.q) + base, nrow, q_rs_bytes, tQ, sSink, wave);
+    dma_q.issue(reinterpret_cast<const uint16_t*>(p.dout) + base, nrow, q_rs_bytes, tdO, sSink, wave);
     const int nr = uniform(nrow < 0 ? 0 : (nrow > BM ? BM : nrow));
     const int64_t vbase = (int64_t)(s.oq + i0) * p.hq + h;
     const float* src = wave == 0 ? p.lse2 + vbase : p.delta + vbase;
@@ -253,8 +262,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   if constexpr (K_LDS || V_LDS) {
     DmaKV dkv;
     dkv.init(wave, lane, p.d, kv_rs_bytes);
-    if constexpr (K_LDS) dkv.issue(kb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sK, wave);
-    if constexpr (V_LDS) dkv.issue(vb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sV, wave);
+    if constexpr (K_LDS) dkv.issue(kb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sK, sSink, wave);
+    if constexpr (V_LDS) dkv.issue(vb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sV, sSink, wave);
   }
   wait_vm<0>();
 
@@ -286,12 +295,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           u32x4 kop, vop;
-          if constexpr (K_LDS) kop = lds_row8<DPAD>(sK, 32 * wave + li, 16 * t + 8 * hh);
+          if constexpr (K_LDS) kop = lds_row8<LKV>(sK, 32 * wave + li, 16 * t + 8 * hh);
           else kop = kreg[K_LDS ? 0 : t];
-          if constexpr (V_LDS) vop = lds_row8<DPAD>(sV, 32 * wave + li, 16 * t + 8 * hh);
+          if constexpr (V_LDS) vop = lds_row8<LKV>(sV, 32 * wave + li, 16 * t + 8 * hh);
           else vop = vreg[V_LDS ? 0 : t];
-          sc[ib] = Mfma<DT>::mma(lds_row8<DPAD>(tQ, 32 * ib + li, 16 * t + 8 * hh), kop, sc[ib]);
-          dp[ib] = Mfma<DT>::mma(lds_row8<DPAD>(tdO, 32 * ib + li, 16 * t + 8 * hh), vop, dp[ib]);
+          sc[ib] = Mfma<DT>::mma(lds_row8<LQ>(tQ, 32 * ib + li, 16 * t + 8 * hh), kop, sc[ib]);
+          dp[ib] = Mfma<DT>::mma(lds_row8<LQ>(tdO, 32 * ib + li, 16 * t + 8 * hh), vop, dp[ib]);
         }
       }
       const bool need_mask = CAUSAL && (i0 < wk_hi);
@@ -317,8 +326,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
         const u32x4 bds = pack_operand<DT>(dp[u >> 1], u & 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          adv[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tdO, cb, u, lane), bp, adv[cb]);
-          adk[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tQ, cb, u, lane), bds, adk[cb]);
+          adv[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tdO, cb, u, lane), bp, adv[cb]);
+          adk[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tQ, cb, u, lane), bds, adk[cb]);
         }
       }
     }

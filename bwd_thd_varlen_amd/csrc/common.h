@@ -93,31 +93,66 @@ __device__ __forceinline__ u32x4 pack_operand(const f32x16& c, int half8) {
 }
 
 // ----------------------------------------------------------------- LDS tiles
-// Every LDS tile is row-major with DPAD 16-bit columns and no padding; the
-// 16-byte chunks of row r are permuted by x -> x ^ swz(r).  With this
-// swizzle three access patterns are free of bank conflicts (64 banks of 4
-// bytes; a 16-byte access is served 16 lanes per pass, an 8-byte one 32):
-//   * 16-byte row reads: lane l reads chunk x of row base + (l & 31);
-//   * transposed reads (ds_read_b64_tr_b16): 32 lanes cover 4 consecutive
-//     rows x 64 bytes;
-//   * 16-byte staging writes of whole rows.
-template <int DPAD>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (DPAD >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else if constexpr (DPAD == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  else return (r >> 2) & 3;
-}
+// LDS tiles are row-major.  A row of DPAD 16-bit columns is padded by P
+// 16-byte slots and stored shifted right by rot(r) slots, so element (r, c)
+// sits at r * RE + 8 * rot(r) + c: offsets are linear in the column and,
+// for rows 16 apart, in the row.  Every MFMA operand read is then a per-lane
+// base plus an immediate offset (an XOR swizzle would need one address
+// register per read; kept live across the loop, those spill).
+//   Lay<DPAD, false> -- tiles read only by 16-byte row reads (lane l reads a
+//     chunk of row base + (l & 31), 16 lanes per pass): P = 1, rot = 0; the
+//     odd row stride (in 16-byte slots) puts 16 consecutive rows on 16
+//     distinct bank groups.
+//   Lay<DPAD, true> -- tiles also read transposed (ds_read_b64_tr_b16: 32
+//     lanes per pass over 4 consecutive rows x 64 bytes): for DPAD >= 64,
+//     P = 4 and rot = (r >> 2) & 3, free of bank conflicts for both reads
+//     (64 banks of 4 bytes); DPAD = 32 keeps P = 1, rot = 0.
+template <int DPAD, bool TR>
+struct Lay {
+  static constexpr bool ROT = TR && DPAD >= 64;
+  static constexpr int P = ROT ? 4 : 1;
+  static constexpr int CPR = DPAD / 8;          // data slots per row
+  static constexpr int SPR = CPR + P;           // slots per row
+  static constexpr int RE = 8 * SPR;            // elements per row
+  static constexpr bool PADDED = true;
+  static __device__ __forceinline__ int rot(int r) { return ROT ? ((r >> 2) & 3) : 0; }
+  // logical chunk held by slot position `pos` of row r (-1: padding)
+  static __device__ __forceinline__ int chunk_at(int r, int pos) {
+    const int x = pos - rot(r);
+    return (x >= 0 && x < CPR) ? x : -1;
+  }
+  static __device__ __forceinline__ int off(int r, int c) { return r * RE + 8 * rot(r) + c; }
+  // 16-bit elements of a ROWS-row tile, rounded up to whole 1 KB DMA units
+  template <int ROWS>
+  static constexpr int elems() { return (ROWS * SPR + 63) / 64 * 512; }
+};
 
-// element offset of (row r, column c) in a swizzled tile
+// Unpadded alternative: the 16-byte chunks of row r are permuted by
+// x -> x ^ swz(r) (conflict-free for row reads, transposed reads and whole-
+// row staging); the smallest footprint and DMA count, but one address per
+// (row block, chunk) pair.  Used where those addresses fit in registers.
 template <int DPAD>
-__device__ __forceinline__ int toff(int r, int c) {
-  return r * DPAD + ((((c >> 3) ^ swz<DPAD>(r))) << 3) + (c & 7);
-}
+struct Swz {
+  static constexpr int CPR = DPAD / 8;
+  static constexpr int SPR = CPR;
+  static constexpr int RE = DPAD;
+  static constexpr bool PADDED = false;
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (DPAD >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else if constexpr (DPAD == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+  }
+  // logical chunk held by slot position `pos` of row r (-1: padding)
+  static __device__ __forceinline__ int chunk_at(int r, int pos) { return pos ^ swz(r); }
+  static __device__ __forceinline__ int off(int r, int c) { return r * DPAD + (((c >> 3) ^ swz(r)) << 3) + (c & 7); }
+  template <int ROWS>
+  static constexpr int elems() { return (ROWS * SPR + 63) / 64 * 512; }
+};
 
 // 16-byte row read: columns [c, c+8) of row r (c a multiple of 8)
-template <int DPAD>
+template <class L>
 __device__ __forceinline__ u32x4 lds_row8(const uint16_t* tile, int r, int c) {
-  return *reinterpret_cast<const u32x4*>(tile + toff<DPAD>(r, c));
+  return *reinterpret_cast<const u32x4*>(tile + L::off(r, c));
 }
 
 __device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
@@ -134,13 +169,13 @@ __device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
 // element (i & 3) of the 8-byte chunk addressed by lane 4k + (i >> 2), as its
 // k-th value; so lane J of the group addresses row j0 + (J >> 2), columns
 // c0 + 4*(J & 3) .. +3.
-template <int DPAD>
+template <class L>
 __device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* tile, int cb, int u, int lane) {
   const int J = lane & 15;
   const int c = 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (J & 3);
   const int r = 16 * u + 4 * (lane >> 5) + (J >> 2);
-  const u32x2 a = lds_tr4(tile + toff<DPAD>(r, c));
-  const u32x2 b = lds_tr4(tile + toff<DPAD>(r + 8, c));
+  const u32x2 a = lds_tr4(tile + L::off(r, c));
+  const u32x2 b = lds_tr4(tile + L::off(r + 8, c));
   u32x4 o = {a[0], a[1], b[0], b[1]};
   return o;
 }
@@ -193,36 +228,46 @@ __device__ __forceinline__ void barrier_lds_dma() {
   asm volatile("" ::: "memory");
 }
 
-// Fills a ROWS x DPAD swizzled tile from global rows (row stride `rs_bytes`),
-// NWAVES waves sharing the work: each 64-lane DMA instruction covers 1 KB of
-// the tile, i.e. tile slots [64k, 64k + 64) of 16 bytes; slot s is row
-// s / (DPAD/8), position s % (DPAD/8), which holds logical chunk
-// position ^ swz(row).  Chunks at or beyond the head dim d and rows at or
-// beyond the valid count come back as zeros.
-template <int DPAD, int ROWS, int NWAVES>
+// Fills a ROWS-row tile of layout L from global rows (row stride
+// `rs_bytes`), NWAVES waves sharing the work.  Each 64-lane DMA instruction
+// writes 1 KB of the tile, i.e. slots [64i, 64i + 64) of 16 bytes; slot s is
+// row s / SPR, position s % SPR, which holds the data chunk L::chunk_at
+// gives (none for a padding slot).  Padding slots, chunks at or beyond the head
+// dim d and rows at or beyond the valid count come back as zeros.  When the
+// instructions do not split evenly, a wave's extra instruction writes
+// (zeros) to the 1 KB `sink` instead, so that every wave issues the same
+// number of DMAs and can use the same wait count.
+template <class L, int ROWS, int NWAVES>
 struct TileDma {
-  static constexpr int CPR = DPAD / 8;
-  static constexpr int INSTR = ROWS * CPR / 64;
-  static constexpr int PER_WAVE = INSTR / NWAVES;
-  static_assert(INSTR % NWAVES == 0 && PER_WAVE > 0, "tile must split evenly over the waves");
+  static constexpr int INSTR = (ROWS * L::SPR + 63) / 64;
+  static constexpr int PER_WAVE = (INSTR + NWAVES - 1) / NWAVES;
+  static constexpr bool SINK = PER_WAVE * NWAVES != INSTR;   // some wave issues a sink DMA
   uint32_t voff[PER_WAVE];
 
   __device__ __forceinline__ void init(int wave, int lane, int d, uint32_t rs_bytes) {
 #pragma unroll
     for (int k = 0; k < PER_WAVE; ++k) {
-      const int slot = (wave * PER_WAVE + k) * 64 + lane;
-      const int r = slot / CPR;
-      const int x = (slot % CPR) ^ swz<DPAD>(r);
-      voff[k] = (8 * x < d) ? (uint32_t)r * rs_bytes + 16u * (uint32_t)x : kOutOfRange;
+      const int i = wave * PER_WAVE + k;
+      const int slot = i * 64 + lane;
+      const int r = slot / L::SPR;
+      const int x = L::chunk_at(r, slot % L::SPR);
+      // (all but the last test only matter for padded or unevenly split tiles)
+      const bool ok = (!SINK || i < INSTR) && (ROWS * L::SPR % 64 == 0 || r < ROWS) &&
+                      (!L::PADDED || x >= 0) && 8 * x < d;
+      voff[k] = ok ? (uint32_t)r * rs_bytes + 16u * (uint32_t)x : kOutOfRange;
     }
   }
-  // rows [0, rows_valid) of the tile start at `row0`
+  // rows [0, rows_valid) of the tile start at `row0`; `sink` (1 KB) is
+  // only used when SINK
   __device__ __forceinline__ void issue(const uint16_t* row0, int rows_valid, uint32_t rs_bytes,
-                                        uint16_t* tile, int wave) const {
+                                        uint16_t* tile, uint16_t* sink, int wave) const {
     const int nr = __builtin_amdgcn_readfirstlane(rows_valid < 0 ? 0 : (rows_valid > ROWS ? ROWS : rows_valid));
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(row0, (uint32_t)nr * rs_bytes);
 #pragma unroll
-    for (int k = 0; k < PER_WAVE; ++k) dma<16>(rsrc, tile + (wave * PER_WAVE + k) * 512, voff[k]);
+    for (int k = 0; k < PER_WAVE; ++k) {
+      const int i = wave * PER_WAVE + k;
+      dma<16>(rsrc, (!SINK || i < INSTR) ? tile + i * 512 : sink, voff[k]);
+    }
   }
 };
 

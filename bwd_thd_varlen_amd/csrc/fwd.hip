@@ -10,7 +10,7 @@
 // transposed score tile S^T = K Q^T), so the softmax statistics are per-lane
 // scalars and the probabilities, still in registers, are directly the B
 // operand of O^T = V^T P^T.  Q stays in registers for the whole tile; K and V
-// arrive by global->LDS DMA into two row-major (swizzled) buffers, one step
+// arrive by global->LDS DMA into two row-major (padded) buffers, one step
 // ahead of the compute, and V^T operands come from the LDS transpose read.
 // Online softmax in the log2 domain: m = reference maximum of
 // scale*log2(e)*S, l = running sum of exp2(x - m); the reference (and with it
@@ -32,14 +32,17 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
   constexpr int KS = kKVStep;          // keys per step
   constexpr int NKB = KS / 32;         // 32-key blocks of S^T per step
-  using Dma = TileDma<DPAD, KS, 4>;
+  using LK = Swz<DPAD>;          // K: row reads
+  using LV = Swz<DPAD>;          // V: transposed reads
+  using DmaK = TileDma<LK, KS, 4>;
+  using DmaV = TileDma<LV, KS, 4>;
 
-  // two buffers of K and V (distinct arrays, so the compiler can see that
-  // reading one buffer does not depend on the DMA filling the other)
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[KS * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[KS * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[KS * DPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[KS * DPAD];
+  // two buffers of K and V
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[LV::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[LV::template elems<KS>()];
+  static_assert(!DmaK::SINK && !DmaV::SINK, "these tiles split evenly over the waves");
 
   const int ntiles = uniform(p.hdr[kHdrNQTiles]);
   int item, h;
@@ -66,12 +69,14 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
   const int nsteps = (kend + KS - 1) / KS;
   const float sl2e = p.scale_log2e;
 
-  Dma dma_kv;
-  dma_kv.init(wave, lane, p.d, kv_rs_bytes);
+  DmaK dma_k;
+  DmaV dma_v;
+  dma_k.init(wave, lane, p.d, kv_rs_bytes);
+  dma_v.init(wave, lane, p.d, kv_rs_bytes);
   auto issue = [&](int step, uint16_t* tK, uint16_t* tV) {
     const int n0 = step * KS;
-    dma_kv.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, wave);
-    dma_kv.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, wave);
+    dma_k.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, nullptr, wave);
+    dma_v.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, nullptr, wave);
   };
   if (nsteps > 0) issue(0, sK0, sV0);
 
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
   auto do_step = [&](int step, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
     if (step + 1 < nsteps) {
       issue(step + 1, nK, nV);
-      wait_vm<2 * Dma::PER_WAVE>();            // this step's tiles have landed
+      wait_vm<DmaK::PER_WAVE + DmaV::PER_WAVE>();   // this step's tiles have landed
     } else {
       wait_vm<0>();
     }
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
         sc[kb2] = zero16();
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          sc[kb2] = Mfma<DT>::mma(lds_row8<DPAD>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
+          sc[kb2] = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
       }
       pipeline_lds_mfma<NKB * NT, 1>();
       const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo);
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParam
         const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          acc[cb] = Mfma<DT>::mma(lds_tr_operand<DPAD>(tV, cb, u, lane), b, acc[cb]);
+          acc[cb] = Mfma<DT>::mma(lds_tr_operand<LV>(tV, cb, u, lane), b, acc[cb]);
       }
       pipeline_lds_mfma<2 * NKB * NCB, 2>();
     }
