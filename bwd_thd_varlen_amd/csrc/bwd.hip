@@ -33,8 +33,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
   constexpr int KS = kKVStep;
-  using LK = Swz<DPAD>;          // K: row reads (S) and transposed reads (dQ)
-  using LV = Swz<DPAD>;          // V: row reads (dP)
+  using LK = Lay<DPAD, true>;          // K: row reads (S) and transposed reads (dQ)
+  using LV = Lay<DPAD, false>;         // V: row reads (dP)
   using DmaK = TileDma<LK, KS, 4>;
   using DmaV = TileDma<LV, KS, 4>;
 
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   __shared__ __attribute__((aligned(16))) uint16_t sK1[LK::template elems<KS>()];
   __shared__ __attribute__((aligned(16))) uint16_t sV0[LV::template elems<KS>()];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[LV::template elems<KS>()];
-  static_assert(!DmaK::SINK && !DmaV::SINK, "these tiles split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint16_t sSink[DmaK::SINK || DmaV::SINK ? 512 : 8];
 
   const int ntiles = uniform(p.hdr[kHdrNQTiles]);
   int item, h;
@@ -78,8 +78,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   dma_v.init(wave, lane, p.d, kv_rs_bytes);
   auto issue = [&](int step, uint16_t* tK, uint16_t* tV) {
     const int n0 = step * KS;
-    dma_k.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, nullptr, wave);
-    dma_v.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, nullptr, wave);
+    dma_k.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, sSink, wave);
+    dma_v.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, sSink, wave);
   };
   if (nsteps > 0) issue(0, sK0, sV0);
 
@@ -110,35 +110,33 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     barrier_lds_dma();
     const int n0 = step * KS;
     if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi)) {
-      f32x16 sc[2], dp[2];
+      const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo);
+      // the step's two 32-key halves one after the other (S, dP -> dS -> dQ
+      // part), so that only one half's score tiles are live at a time
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        sc[kb2] = zero16();
-        dp[kb2] = zero16();
+        f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          sc[kb2] = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
-          dp[kb2] = Mfma<DT>::mma(lds_row8<LV>(tV, 32 * kb2 + li, 16 * t + 8 * hh), doreg[t], dp[kb2]);
+          sc = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc);
+          dp = Mfma<DT>::mma(lds_row8<LV>(tV, 32 * kb2 + li, 16 * t + 8 * hh), doreg[t], dp);
         }
-      }
-      const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo);
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -lse2));
+          float pr = fast_exp2(__builtin_fmaf(sc[r], sl2e, -lse2));
           if (need_mask) {
             const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
             if (j > qi) pr = 0.f;
           }
-          sc[kb2][r] = pr * (dp[kb2][r] - dlt);     // dS
+          sc[r] = pr * (dp[r] - dlt);     // dS
         }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
+        const u32x4 b0 = pack_operand<DT>(sc, 0), b1 = pack_operand<DT>(sc, 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          acc[cb] = Mfma<DT>::mma(lds_tr_operand<LK>(tK, cb, u, lane), b, acc[cb]);
+          acc[cb] = Mfma<DT>::mma(lds_tr_operand<LK>(tK, cb, 2 * kb2, lane), b0, acc[cb]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[cb] = Mfma<DT>::mma(lds_tr_operand<LK>(tK, cb, 2 * kb2 + 1, lane), b1, acc[cb]);
       }
     }
     barrier_lds_dma();
@@ -320,16 +318,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
             dp[ib][r] = pr * (dp[ib][r] - d4[c]);
           }
         }
+      // P and dS as packed operands (the fp32 tiles die here)
+      u32x4 bp[NU], bds[NU];
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const u32x4 bp = pack_operand<DT>(sc[u >> 1], u & 1);
-        const u32x4 bds = pack_operand<DT>(dp[u >> 1], u & 1);
+        bp[u] = pack_operand<DT>(sc[u >> 1], u & 1);
+        bds[u] = pack_operand<DT>(dp[u >> 1], u & 1);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          adv[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tdO, cb, u, lane), bp, adv[cb]);
-          adk[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tQ, cb, u, lane), bds, adk[cb]);
+          adv[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tdO, cb, u, lane), bp[u], adv[cb]);
+          adk[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tQ, cb, u, lane), bds[u], adk[cb]);
         }
-      }
     }
     barrier_lds_dma();
   };
