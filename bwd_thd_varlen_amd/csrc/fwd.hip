@@ -10,7 +10,7 @@
 // transposed score tile S^T = K Q^T), so the softmax statistics are per-lane
 // scalars and the probabilities, still in registers, are directly the B
 // operand of O^T = V^T P^T.  Q stays in registers for the whole tile; K and V
-// arrive by global->LDS DMA into two row-major (padded) buffers, one step
+// arrive by global->LDS DMA into two row-major (swizzled) buffers, one step
 // ahead of the compute, and V^T operands come from the LDS transpose read.
 // Online softmax in the log2 domain: m = reference maximum of
 // scale*log2(e)*S, l = running sum of exp2(x - m); the reference (and with it
@@ -26,11 +26,16 @@ namespace attn {
 // same softmax, since the final normalisation uses the same reference.
 constexpr float kRescaleSlack = 8.0f;
 
+// Keys per step: 32 for head dims 64..128, so that the tiles (32 KB of LDS)
+// and registers (< 168) of three workgroups fit one CU; 64 otherwise.
+template <int DPAD>
+constexpr int fwd_step_keys() { return (DPAD >= 64 && DPAD <= 128) ? 32 : 64; }
+
 template <int DT, int DPAD, bool CAUSAL>
-__global__ __launch_bounds__(256, DPAD <= 128 ? 2 : 1) void fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParams p) {
   constexpr int NT = DPAD / 16;        // 16-wide k chunks over the head dim
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
-  constexpr int KS = kKVStep;          // keys per step
+  constexpr int KS = fwd_step_keys<DPAD>();   // keys per step
   constexpr int NKB = KS / 32;         // 32-key blocks of S^T per step
   using LK = Swz<DPAD>;          // K: row reads
   using LV = Swz<DPAD>;          // V: transposed reads
