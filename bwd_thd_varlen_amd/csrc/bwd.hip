@@ -16,8 +16,8 @@
 // through LDS; S and dP are recomputed here instead of accumulating dQ across
 // key-tile workgroups, which keeps every dQ element owned by one workgroup.
 //
-// Both kernels fill double-buffered LDS tiles by global->LDS DMA one step
-// ahead of the compute (see TileDma in common.h).
+// Both kernels fill LDS tiles by global->LDS DMA ahead of the compute (see
+// TileDma in common.h): dQ double-buffers one step ahead, dK/dV uses a ring.
 //
 // Layout tricks are those of the forward kernel (common.h): score tiles are
 // computed so that the lane index runs over the dimension that survives the
@@ -173,7 +173,9 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 // wave 1 Delta, other waves a dummy so that every wave issues the same
 // number of DMAs and can use the same wait count).  Query rows past the real
 // length arrive as zeros in Q, dO, LSE and Delta, so they add nothing.
-template <int DT, int DPAD, bool CAUSAL, int NW, int BM, int KVM, int OCC>
+// The tiles come through a ring of NBUF buffers filled NBUF-1 steps ahead,
+// with one barrier per step.
+template <int DT, int DPAD, bool CAUSAL, int NW, int BM, int KVM, int OCC, int NBUF>
 __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   constexpr bool K_LDS = KVM == 2;     // K operand re-read from LDS
   constexpr bool V_LDS = KVM >= 1;     // V operand re-read from LDS
@@ -188,13 +190,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   using DmaKV = TileDma<LKV, BN, NW>;
   constexpr int DMA_PER_STEP = 2 * Dma::PER_WAVE + 1;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sQ0[LQ::template elems<BM>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ1[LQ::template elems<BM>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO0[LQ::template elems<BM>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO1[LQ::template elems<BM>()];
+  static_assert(NBUF >= 2 && NBUF <= 6, "ring depth");
+  // ring of NBUF buffers of the Q and dO tiles and their LSE2 | Delta vectors
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[NBUF][LQ::template elems<BM>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[NBUF][LQ::template elems<BM>()];
+  __shared__ __attribute__((aligned(16))) float sVec[NBUF][2 * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sSink[Dma::SINK || DmaKV::SINK ? 512 : 8];
-  __shared__ __attribute__((aligned(16))) float sV0ec[2 * 64];   // LSE2 | Delta, buffer 0
-  __shared__ __attribute__((aligned(16))) float sV1ec[2 * 64];   // LSE2 | Delta, buffer 1
   __shared__ __attribute__((aligned(16))) float sDummy[64];
   __shared__ __attribute__((aligned(16))) uint16_t sK[K_LDS ? LKV::template elems<BN>() : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sV[V_LDS ? LKV::template elems<BN>() : 8];
@@ -230,7 +231,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   dma_q.init(wave, lane, p.d, q_rs_bytes);
   // 4-byte DMA of the vector (LSE2 or Delta) rows i0 .. i0+BM-1 of head h
   const uint32_t vec_voff = lane < BM ? (uint32_t)lane * (uint32_t)p.hq * 4u : kOutOfRange;
-  auto issue = [&](int step, uint16_t* tQ, uint16_t* tdO, float* tvec) {
+  auto issue = [&](int step) {
+    const int buf = step % NBUF;
+    uint16_t* tQ = sQ[buf];
+    uint16_t* tdO = sdO[buf];
+    float* tvec = sVec[buf];
     const int hg = step / nm;
     const int m = m_first + (step - hg * nm);
     const int h = h0 + hg;
@@ -245,7 +250,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, wave < 2 ? (uint32_t)nr * (uint32_t)p.hq * 4u : 0u);
     dma<4>(rs, wave == 0 ? tvec : (wave == 1 ? tvec + 64 : sDummy), vec_voff);
   };
-  if (nsteps > 0) issue(0, sQ0, sdO0, sV0ec);
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k)
+    if (k < nsteps) issue(k);
 
   // K and V operands of this wave's 32 keys (zero beyond the real keys),
   // held in registers or re-read from a resident LDS tile
@@ -272,15 +279,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     adv[cb] = zero16();
   }
 
-  auto do_step = [&](int step, const uint16_t* tQ, const uint16_t* tdO, const float* tvec,
-                     uint16_t* nQ, uint16_t* ndO, float* nvec) {
-    if (step + 1 < nsteps) {
-      issue(step + 1, nQ, ndO, nvec);
-      wait_vm<DMA_PER_STEP>();
-    } else {
-      wait_vm<0>();
-    }
+  // One barrier per step: the buffer refilled at step j (that of step j-1)
+  // has been read by every wave once the wave passes step j's barrier.
+  for (int step = 0; step < nsteps; ++step) {
+    // this step's tiles have landed (up to NBUF-2 later steps may not have)
+    wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1 - step));
     barrier_lds_dma();
+    if (step + NBUF - 1 < nsteps) issue(step + NBUF - 1);
+    const int buf = step % NBUF;
+    const uint16_t* tQ = sQ[buf];
+    const uint16_t* tdO = sdO[buf];
+    const float* tvec = sVec[buf];
     const int hg = step / nm;
     const int i0 = (m_first + (step - hg * nm)) * BM;
     // waves with no real key, or whose keys all follow every query, idle
@@ -333,11 +342,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           adk[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tQ, cb, u, lane), bds[u], adk[cb]);
         }
     }
-    barrier_lds_dma();
-  };
-  for (int step = 0; step < nsteps; step += 2) {
-    do_step(step, sQ0, sdO0, sV0ec, sQ1, sdO1, sV1ec);
-    if (step + 1 < nsteps) do_step(step + 1, sQ1, sdO1, sV1ec, sQ0, sdO0, sV0ec);
   }
 
   if (kj < s.lk) {
@@ -388,20 +392,20 @@ hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tile
 // keys per dK/dV work item for a head dim
 int dkdv_tile(int d) { return d <= 128 ? 128 : 64; }
 
-template <int DT, int DPAD, int NW, int BM, int KVM, int OCC>
+template <int DT, int DPAD, int NW, int BM, int KVM, int OCC, int NBUF>
 static void launch_dkdv_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
   if (causal)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, NW, BM, KVM, OCC>), dim3(grid), dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, NW, BM, KVM, OCC, NBUF>), dim3(grid), dim3(NW * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, NW, BM, KVM, OCC>), dim3(grid), dim3(NW * 64), 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, NW, BM, KVM, OCC, NBUF>), dim3(grid), dim3(NW * 64), 0, st, p);
 }
 
 template <int DT>
 static void launch_dkdv_dt(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (p.d <= 32) launch_dkdv_d<DT, 32, 4, 64, 0, 1>(p, causal, grid, st);
-  else if (p.d <= 64) launch_dkdv_d<DT, 64, 4, 64, 0, 1>(p, causal, grid, st);
-  else if (p.d <= 128) launch_dkdv_d<DT, 128, 4, 32, 0, 2>(p, causal, grid, st);
-  else launch_dkdv_d<DT, 256, 2, 32, 2, 1>(p, causal, grid, st);
+  if (p.d <= 32) launch_dkdv_d<DT, 32, 4, 64, 0, 1, 2>(p, causal, grid, st);
+  else if (p.d <= 64) launch_dkdv_d<DT, 64, 4, 64, 0, 1, 2>(p, causal, grid, st);
+  else if (p.d <= 128) launch_dkdv_d<DT, 128, 4, 32, 0, 2, 2>(p, causal, grid, st);
+  else launch_dkdv_d<DT, 256, 2, 32, 2, 1, 2>(p, causal, grid, st);
 }
 
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st) {

@@ -216,6 +216,18 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most k steps of STEP vector-memory operations each are
+// outstanding (k is wave-uniform; s_waitcnt takes an immediate).
+template <int STEP, int MAXK>
+__device__ __forceinline__ void wait_vm_steps(int k) {
+  static_assert(MAXK >= 0 && MAXK <= 4, "at most 4 steps in flight");
+  if constexpr (MAXK >= 4) { if (k >= 4) { wait_vm<4 * STEP>(); return; } }
+  if constexpr (MAXK >= 3) { if (k >= 3) { wait_vm<3 * STEP>(); return; } }
+  if constexpr (MAXK >= 2) { if (k >= 2) { wait_vm<2 * STEP>(); return; } }
+  if constexpr (MAXK >= 1) { if (k >= 1) { wait_vm<STEP>(); return; } }
+  wait_vm<0>();
+}
+
 // Workgroup barrier for loops whose LDS is written only by DMA: the caller
 // has already waited (wait_vm) for its own DMA, and every LDS read before the
 // barrier has been consumed, so no memory fence is needed.  (A fenced
