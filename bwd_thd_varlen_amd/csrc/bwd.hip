@@ -38,10 +38,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   using DmaK = TileDma<LK, KS, 4>;
   using DmaV = TileDma<LV, KS, 4>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[LK::template elems<KS>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[LK::template elems<KS>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[LV::template elems<KS>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[LV::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][LV::template elems<KS>()];
   __shared__ __attribute__((aligned(16))) uint16_t sSink[DmaK::SINK || DmaV::SINK ? 512 : 8];
 
   const int ntiles = uniform(p.hdr[kHdrNQTiles]);
@@ -76,12 +74,14 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   DmaV dma_v;
   dma_k.init(wave, lane, p.d, kv_rs_bytes);
   dma_v.init(wave, lane, p.d, kv_rs_bytes);
-  auto issue = [&](int step, uint16_t* tK, uint16_t* tV) {
+  auto issue = [&](int step) {
+    uint16_t* tK = sK[step & 1];
+    uint16_t* tV = sV[step & 1];
     const int n0 = step * KS;
     dma_k.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, sSink, wave);
     dma_v.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, sSink, wave);
   };
-  if (nsteps > 0) issue(0, sK0, sV0);
+  if (nsteps > 0) issue(0);
 
   u32x4 qreg[NT], doreg[NT];
 #pragma unroll
@@ -100,14 +100,13 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero16();
 
-  auto do_step = [&](int step, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
-    if (step + 1 < nsteps) {
-      issue(step + 1, nK, nV);
-      wait_vm<DmaK::PER_WAVE + DmaV::PER_WAVE>();
-    } else {
-      wait_vm<0>();
-    }
+  // one barrier per step, as in the forward kernel
+  for (int step = 0; step < nsteps; ++step) {
+    wait_vm<0>();
     barrier_lds_dma();
+    if (step + 1 < nsteps) issue(step + 1);
+    const uint16_t* tK = sK[step & 1];
+    const uint16_t* tV = sV[step & 1];
     const int n0 = step * KS;
     if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi)) {
       const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo);
@@ -139,11 +138,6 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
           acc[cb] = Mfma<DT>::mma(lds_tr_operand<LK>(tK, cb, 2 * kb2 + 1, lane), b1, acc[cb]);
       }
     }
-    barrier_lds_dma();
-  };
-  for (int step = 0; step < nsteps; step += 2) {
-    do_step(step, sK0, sV0, sK1, sV1);
-    if (step + 1 < nsteps) do_step(step + 1, sK1, sV1, sK0, sV0);
   }
 
   if (qvalid) {

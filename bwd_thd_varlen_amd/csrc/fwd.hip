@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   using DmaK = TileDma<LK, KS, 4>;
   using DmaV = TileDma<LV, KS, 4>;
 
-  // two buffers of K and V
+  // two buffers of K and V (distinct arrays: their addresses are constants)
   __shared__ __attribute__((aligned(16))) uint16_t sK0[LK::template elems<KS>()];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[LK::template elems<KS>()];
   __shared__ __attribute__((aligned(16))) uint16_t sV0[LV::template elems<KS>()];
@@ -98,14 +98,12 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero16();
   float m_run = -__builtin_inff(), l_run = 0.f;
 
+  // One barrier per step: after it, every wave has finished step - 1, so the
+  // DMA of step + 1 can refill that step's buffer.
   auto do_step = [&](int step, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
-    if (step + 1 < nsteps) {
-      issue(step + 1, nK, nV);
-      wait_vm<DmaK::PER_WAVE + DmaV::PER_WAVE>();   // this step's tiles have landed
-    } else {
-      wait_vm<0>();
-    }
+    wait_vm<0>();                                // this step's tiles have landed
     barrier_lds_dma();
+    if (step + 1 < nsteps) issue(step + 1, nK, nV);
     const int n0 = step * KS;
     // waves with no real query, or whose queries all precede the step, idle
     if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi)) {
@@ -159,7 +157,6 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
       }
       pipeline_lds_mfma<2 * NKB * NCB, 2>();
     }
-    barrier_lds_dma();                           // this buffer is refilled two steps on
   };
   for (int step = 0; step < nsteps; step += 2) {
     do_step(step, sK0, sV0, sK1, sV1);
