@@ -105,8 +105,9 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     wait_vm<0>();
     barrier_lds_dma();
     if (step + 1 < nsteps) issue(step + 1);
-    const uint16_t* tK = sK[step & 1];
-    const uint16_t* tV = sV[step & 1];
+    const RowReader<LK> rk(sK[step & 1], lane);
+    const RowReader<LV> rv(sV[step & 1], lane);
+    const TrReader<LK> trk(sK[step & 1], lane);
     const int n0 = step * KS;
     if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi)) {
       const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo);
@@ -117,8 +118,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
         f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          sc = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc);
-          dp = Mfma<DT>::mma(lds_row8<LV>(tV, 32 * kb2 + li, 16 * t + 8 * hh), doreg[t], dp);
+          sc = Mfma<DT>::mma(rk.read(kb2, t), qreg[t], sc);
+          dp = Mfma<DT>::mma(rv.read(kb2, t), doreg[t], dp);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -132,10 +133,10 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
         const u32x4 b0 = pack_operand<DT>(sc, 0), b1 = pack_operand<DT>(sc, 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          acc[cb] = Mfma<DT>::mma(lds_tr_operand<LK>(tK, cb, 2 * kb2, lane), b0, acc[cb]);
+          acc[cb] = Mfma<DT>::mma(trk.read(cb, 2 * kb2), b0, acc[cb]);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          acc[cb] = Mfma<DT>::mma(lds_tr_operand<LK>(tK, cb, 2 * kb2 + 1, lane), b1, acc[cb]);
+          acc[cb] = Mfma<DT>::mma(trk.read(cb, 2 * kb2 + 1), b1, acc[cb]);
       }
     }
   }
@@ -281,8 +282,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     barrier_lds_dma();
     if (step + NBUF - 1 < nsteps) issue(step + NBUF - 1);
     const int buf = step % NBUF;
-    const uint16_t* tQ = sQ[buf];
-    const uint16_t* tdO = sdO[buf];
+    const RowReader<LQ> rq(sQ[buf], lane), rdo(sdO[buf], lane);
+    const TrReader<LQ> trq(sQ[buf], lane), trdo(sdO[buf], lane);
     const float* tvec = sVec[buf];
     const int hg = step / nm;
     const int i0 = (m_first + (step - hg * nm)) * BM;
@@ -300,8 +301,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           else kop = kreg[K_LDS ? 0 : t];
           if constexpr (V_LDS) vop = lds_row8<LKV>(sV, 32 * wave + li, 16 * t + 8 * hh);
           else vop = vreg[V_LDS ? 0 : t];
-          sc[ib] = Mfma<DT>::mma(lds_row8<LQ>(tQ, 32 * ib + li, 16 * t + 8 * hh), kop, sc[ib]);
-          dp[ib] = Mfma<DT>::mma(lds_row8<LQ>(tdO, 32 * ib + li, 16 * t + 8 * hh), vop, dp[ib]);
+          sc[ib] = Mfma<DT>::mma(rq.read(ib, t), kop, sc[ib]);
+          dp[ib] = Mfma<DT>::mma(rdo.read(ib, t), vop, dp[ib]);
         }
       }
       const bool need_mask = CAUSAL && (i0 < wk_hi);
@@ -332,8 +333,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
       for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          adv[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tdO, cb, u, lane), bp[u], adv[cb]);
-          adk[cb] = Mfma<DT>::mma(lds_tr_operand<LQ>(tQ, cb, u, lane), bds[u], adk[cb]);
+          adv[cb] = Mfma<DT>::mma(trdo.read(cb, u), bp[u], adv[cb]);
+          adk[cb] = Mfma<DT>::mma(trq.read(cb, u), bds[u], adk[cb]);
         }
     }
   }

@@ -180,6 +180,39 @@ __device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* tile, int cb, in
   return o;
 }
 
+// Operand readers for padded tiles (Lay): the lane-dependent part of every
+// read's offset is formed once (one address per tile and step), and each
+// read adds a compile-time constant, which goes into the instruction's
+// offset field -- also when the tile is picked at run time from a ring.
+//   RowReader(tile, lane).read(rb, t): the 16-byte row read of lds_row8 at
+//     row 32*rb + (lane & 31), columns 16*t + 8*(lane >> 5) ...
+//   TrReader(tile, lane).read(cb, u): lds_tr_operand(tile, cb, u, lane).
+template <class L>
+struct RowReader {
+  static_assert(L::PADDED, "linear offsets need the padded layout");
+  const uint16_t* p;
+  __device__ __forceinline__ RowReader(const uint16_t* tile, int lane)
+      : p(tile + L::off(lane & 31, 8 * (lane >> 5))) {}
+  __device__ __forceinline__ u32x4 read(int rb, int t) const {
+    return *reinterpret_cast<const u32x4*>(p + 32 * rb * L::RE + 16 * t);
+  }
+};
+template <class L>
+struct TrReader {
+  static_assert(L::PADDED, "linear offsets need the padded layout");
+  const uint16_t* p;
+  __device__ __forceinline__ TrReader(const uint16_t* tile, int lane)
+      : p(tile + L::off(4 * (lane >> 5) + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3))) {}
+  __device__ __forceinline__ u32x4 read(int cb, int u) const {
+    // rows r and r + 8 of the same lane: rot(r + 8) = rot(r) + 2 (r & 15 < 8)
+    const uint16_t* q = p + 16 * u * L::RE + 32 * cb;
+    const u32x2 a = lds_tr4(q);
+    const u32x2 b = lds_tr4(q + 8 * L::RE + (L::ROT ? 16 : 0));
+    u32x4 o = {a[0], a[1], b[0], b[1]};
+    return o;
+  }
+};
+
 // ----------------------------------------------------------------- LDS DMA
 // Raw buffer resource over `bytes` bytes at p (no stride; the hardware range
 // check returns zeros for any offset >= bytes and does not touch memory).
