@@ -34,7 +34,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * real tokens of sequence b occupy rows ``[cu_pad[b], cu_pad[b] + L_b)``,
   the rest of the slot is padding;
 * causal is top-left aligned: query i may see key j iff j <= i (the pages
-  only use causal with Lq == Lk, where every alignment agrees);
+  only use causal with Lq == Lk, where every alignment agrees); the
+  bottom-right variant, which the pages do not name, aligns the ends:
+  j <= i + (Lk - Lq);
 * LSE is the natural-log log-sum-exp of the scaled scores, fp32 ``[T, hq]``;
 * a query row with no allowed key (and every padding row) has O = 0 and
   LSE = -inf; every gradient row outside the real ranges is +0.0;
@@ -67,18 +69,26 @@ def sequence_slots(cu_seqlens: np.ndarray, cu_seqlens_padded: Optional[np.ndarra
     return [(int(o), int(L)) for o, L in zip(offsets, lengths)]
 
 
-def allowed_mask(lq: int, lk: int, causal: bool) -> np.ndarray:
+def allowed_mask(lq: int, lk: int, causal) -> np.ndarray:
     """Boolean [lq, lk]: key j is visible to query i.
 
-    ``padding``: all real keys of the sequence ([TE-2448], attn_mask_type
-    "padding").  ``padding_causal``: additionally j <= i -- the complement of
-    the strict upper triangle masked in [TE-3216]'s fp32_reference.
+    ``padding`` (causal False): all real keys of the sequence ([TE-2448],
+    attn_mask_type "padding").  ``padding_causal`` (causal True or
+    "top_left"): additionally j <= i -- the complement of the strict upper
+    triangle masked in [TE-3216]'s fp32_reference.  "bottom_right": the same
+    triangle aligned to the last query and key, j <= i + (lk - lq); with
+    lq == lk both alignments agree (the pages use causal only there, and do
+    not name the bottom-right variant: its definition here is the plain
+    reading of aligning the two sequences at their ends).
     """
     m = np.ones((lq, lk), dtype=bool)
     if causal:
+        if causal not in (True, "top_left", "bottom_right"):
+            raise ValueError(f"causal must be False, True, 'top_left' or 'bottom_right', not {causal!r}")
+        shift = (lk - lq) if causal == "bottom_right" else 0
         i = np.arange(lq)[:, None]
         j = np.arange(lk)[None, :]
-        m &= j <= i
+        m &= j <= i + shift
     return m
 
 
@@ -100,7 +110,7 @@ def _softmax_rows(s: np.ndarray, allowed: np.ndarray):
     return p, lse
 
 
-def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool):
+def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal):
     """Forward of one sequence, all heads: O = softmax(scale * Q K^T + mask) V.
 
     q: [Lq, hq, d]; k, v: [Lk, hkv, d] (real rows only, float64).
@@ -123,7 +133,7 @@ def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
     return out, lse
 
 
-def attn_bwd_seq(q, k, v, dout, scale: float, causal: bool, out=None, lse=None,
+def attn_bwd_seq(q, k, v, dout, scale: float, causal, out=None, lse=None,
                  mode: str = "definition"):
     """Backward of one sequence, all heads: dQ, dK, dV of l = sum(dO * O).
 
@@ -173,7 +183,7 @@ def _f64(x) -> np.ndarray:
 
 
 def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
-             cu_seqlens_kv_padded=None, scale: float = None, causal: bool = False
+             cu_seqlens_kv_padded=None, scale: float = None, causal=False
              ) -> Tuple[np.ndarray, np.ndarray]:
     """Forward over the packed THD tensors.
 
@@ -203,7 +213,7 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
 
 
 def attn_bwd(q, k, v, dout, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
-             cu_seqlens_kv_padded=None, scale: float = None, causal: bool = False,
+             cu_seqlens_kv_padded=None, scale: float = None, causal=False,
              out=None, lse=None, mode: str = "definition"):
     """Backward over the packed THD tensors: (dq, dk, dv), float64, padded layout.
 

@@ -4,7 +4,8 @@ Each test checks the oracle against mathematics or the pages:
 
 * central finite differences of l = sum(dO * O) (backward vs forward),
 * an independent library routine (torch CPU scaled_dot_product_attention in
-  float64, the routine [TE-3333]'s and [TE-3216]'s references call),
+  float64, the routine [TE-3333]'s and [TE-3216]'s references call; for the
+  bottom-right causal triangle, with torch's own lower-right causal bias),
 * hand-derived closed forms (one key, two keys, identical keys, causal row 0),
 * invariants (softmax rows sum to one, GQA == summed MHA over repeated KV,
   padding rows inert and exactly zero),
@@ -18,6 +19,7 @@ import numpy as np
 import pytest
 import torch
 import torch.nn.functional as F
+from torch.nn.attention.bias import causal_lower_right
 
 import workloads
 from oracle import attn_bwd, attn_fwd, attn_fwd_seq
@@ -121,8 +123,11 @@ def _sdpa_ref(c):
         qi = q[oq:oq + lq].transpose(0, 1)[None]
         ki = k[ok:ok + lk].transpose(0, 1)[None]
         vi = v[ok:ok + lk].transpose(0, 1)[None]
-        o = F.scaled_dot_product_attention(qi, ki, vi, is_causal=c["causal"], scale=c["scale"],
-                                           enable_gqa=True)
+        if c["causal"] == "bottom_right":
+            kw = dict(attn_mask=causal_lower_right(lq, lk))
+        else:
+            kw = dict(is_causal=bool(c["causal"]))
+        o = F.scaled_dot_product_attention(qi, ki, vi, scale=c["scale"], enable_gqa=True, **kw)
         outs.append((oq, lq, o[0].transpose(0, 1)))
     for oq, lq, o in outs:
         out = out.index_put((torch.arange(oq, oq + lq),), o)
@@ -144,6 +149,92 @@ def test_matches_torch_sdpa_fp64(shape, causal):
     ro, rdq, rdk, rdv = _sdpa_ref(c)
     for a, b in [(o, ro), (dq, rdq), (dk, rdk), (dv, rdv)]:
         np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+BR_SHAPES = [
+    dict(lq=[5, 0, 3], lk=[6, 4, 7], pq=[8, 2, 3], pk=[8, 4, 9], hq=6, hkv=2, d=16),
+    dict(lq=[17, 1], lk=[17, 9], pq=[20, 1], pk=[20, 9], hq=4, hkv=4, d=32),
+]
+
+
+@pytest.mark.parametrize("shape", BR_SHAPES)
+def test_bottom_right_matches_torch_lower_right_bias(shape):
+    """Bottom-right causal (Lq <= Lk) against torch's lower-right causal bias."""
+    rng = np.random.default_rng(12)
+    c = small_case(rng, causal="bottom_right", **shape)
+    o, l = fwd_of(c)
+    dq, dk, dv = bwd_of(c)
+    ro, rdq, rdk, rdv = _sdpa_ref(c)
+    for a, b in [(o, ro), (dq, rdq), (dk, rdk), (dv, rdv)]:
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_bottom_right_equals_top_left_when_lengths_match():
+    rng = np.random.default_rng(13)
+    c = small_case(rng, lq=[6, 9, 1], lk=[6, 9, 1], pq=[7, 9, 2], pk=[7, 9, 2], hq=4, hkv=2,
+                   d=8, causal=True)
+    br = dict(c, causal="bottom_right")
+    for a, b in zip(fwd_of(c) + bwd_of(c), fwd_of(br) + bwd_of(br)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_bottom_right_short_queries_are_the_tail_of_a_square_problem():
+    """Lq < Lk: the Lq queries behave as the last Lq rows of a top-left causal
+    problem over all Lk keys (the earlier rows given dO = 0 add nothing to dK, dV)."""
+    rng = np.random.default_rng(14)
+    lq, lk, hq, hkv, d = 4, 11, 4, 2, 8
+    q, dout = rng.standard_normal((lq, hq, d)), rng.standard_normal((lq, hq, d))
+    k, v = rng.standard_normal((lk, hkv, d)), rng.standard_normal((lk, hkv, d))
+    qs = np.concatenate([rng.standard_normal((lk - lq, hq, d)), q])
+    dos = np.concatenate([np.zeros((lk - lq, hq, d)), dout])
+    cq, ck = np.array([0, lq], np.int32), np.array([0, lk], np.int32)
+    o, l = attn_fwd(q, k, v, cq, ck, scale=0.4, causal="bottom_right")
+    g = attn_bwd(q, k, v, dout, cq, ck, scale=0.4, causal="bottom_right")
+    o2, l2 = attn_fwd(qs, k, v, ck, ck, scale=0.4, causal=True)
+    g2 = attn_bwd(qs, k, v, dos, ck, ck, scale=0.4, causal=True)
+    np.testing.assert_allclose(o, o2[lk - lq:], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(l, l2[lk - lq:], rtol=1e-13)
+    np.testing.assert_allclose(g[0], g2[0][lk - lq:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g[1], g2[1], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g[2], g2[2], rtol=1e-12, atol=1e-14)
+
+
+def test_bottom_right_long_queries_lead_with_empty_rows():
+    """Lq > Lk: the first Lq - Lk queries see no key (O = 0, LSE = -inf, dQ = 0);
+    the last Lk queries form a top-left causal problem over the Lk keys."""
+    rng = np.random.default_rng(15)
+    lq, lk, hq, hkv, d = 10, 4, 2, 1, 8
+    q, dout = rng.standard_normal((lq, hq, d)), rng.standard_normal((lq, hq, d))
+    k, v = rng.standard_normal((lk, hkv, d)), rng.standard_normal((lk, hkv, d))
+    cq, ck = np.array([0, lq], np.int32), np.array([0, lk], np.int32)
+    o, l = attn_fwd(q, k, v, cq, ck, scale=0.4, causal="bottom_right")
+    dq, dk, dv = attn_bwd(q, k, v, dout, cq, ck, scale=0.4, causal="bottom_right")
+    e = lq - lk
+    assert np.all(o[:e] == 0) and np.all(np.isneginf(l[:e])) and np.all(dq[:e] == 0)
+    o2, l2 = attn_fwd(q[e:], k, v, ck, ck, scale=0.4, causal=True)
+    dq2, dk2, dv2 = attn_bwd(q[e:], k, v, dout[e:], ck, ck, scale=0.4, causal=True)
+    np.testing.assert_allclose(o[e:], o2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(l[e:], l2, rtol=1e-13)
+    for a, b in [(dq[e:], dq2), (dk, dk2), (dv, dv2)]:
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    # the formula mode (saved statistics with -inf rows) agrees with the definition
+    gf = attn_bwd(q, k, v, dout, cq, ck, scale=0.4, causal="bottom_right", out=o, lse=l,
+                  mode="formula")
+    for a, b in zip((dq, dk, dv), gf):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+
+
+def test_finite_differences_bottom_right_both_directions():
+    rng = np.random.default_rng(16)
+    c = small_case(rng, lq=[2, 5], lk=[5, 3], pq=[3, 5], pk=[6, 4], hq=2, hkv=1, d=8,
+                   causal="bottom_right")
+    _fd_check(c)
+
+
+def test_unknown_alignment_is_rejected():
+    with pytest.raises(ValueError):
+        attn_fwd_seq(np.zeros((2, 1, 4)), np.zeros((2, 1, 4)), np.zeros((2, 1, 4)), 1.0,
+                     "top_right")
 
 
 # ---------------------------------------------------------------- closed forms
