@@ -9,7 +9,9 @@ if the library is missing or fails to load, every call raises.
 Names follow TransformerEngine's ``DotProductAttention`` / ``fused_attn_bwd``
 arguments (``cu_seqlens_q``, ``cu_seqlens_kv``, ``cu_seqlens_q_padded``,
 ``cu_seqlens_kv_padded``, ``max_seqlen_q``, ``max_seqlen_kv``,
-``attn_mask_type`` in {"padding", "padding_causal"}).
+``attn_mask_type`` in {"padding", "padding_causal",
+"padding_causal_bottom_right"}: the causal triangle top-left aligned, key
+j <= query i, or aligned at the sequence ends, j <= i + Lk - Lq).
 """
 from __future__ import annotations
 
@@ -33,7 +35,7 @@ STATUS = {0: "ATTN_THD_OK", 1: "ATTN_THD_EINVAL", 2: "ATTN_THD_EUNSUPPORTED",
           3: "ATTN_THD_EWORKSPACE", 4: "ATTN_THD_ELAUNCH"}
 DEV_BAD_SEQLENS = 1
 _DTYPE = {torch.bfloat16: 0, torch.float16: 1}
-_MASK = {"padding": 0, "padding_causal": 1}
+_MASK = {"padding": 0, "padding_causal": 1, "padding_causal_bottom_right": 2}
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32

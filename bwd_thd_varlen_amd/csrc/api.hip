@@ -75,7 +75,8 @@ attn_thd_status check_common(const void* q, const void* k, const void* v,
   if (hq % hkv != 0) return ATTN_THD_EINVAL;
   if (d % 8 != 0 || d > 256) return ATTN_THD_EUNSUPPORTED;
   if (dtype != ATTN_THD_BF16 && dtype != ATTN_THD_FP16) return ATTN_THD_EUNSUPPORTED;
-  if (mask_type != ATTN_THD_MASK_PADDING && mask_type != ATTN_THD_MASK_PADDING_CAUSAL)
+  if (mask_type != ATTN_THD_MASK_PADDING && mask_type != ATTN_THD_MASK_PADDING_CAUSAL &&
+      mask_type != ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT)
     return ATTN_THD_EUNSUPPORTED;
   if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_THD_EINVAL;
   if (!cu_q || !cu_kv) return ATTN_THD_EINVAL;
@@ -97,7 +98,8 @@ attn_thd_status check_common(const void* q, const void* k, const void* v,
 
 SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu_kv,
                          const int32_t* cu_qp, const int32_t* cu_kp, int32_t batch,
-                         int32_t total_q, int32_t total_kv, int q_tile, int kv_tile, bool causal) {
+                         int32_t total_q, int32_t total_kv, int q_tile, int kv_tile,
+                         int32_t mask_type) {
   SchedParams s;
   s.cu_q = cu_q;
   s.cu_kv = cu_kv;
@@ -108,7 +110,8 @@ SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu
   s.total_kv = total_kv;
   s.q_tile = q_tile;
   s.kv_tile = kv_tile;
-  s.causal = causal ? 1 : 0;
+  s.causal = mask_type == ATTN_THD_MASK_PADDING ? 0
+             : (mask_type == ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT ? 2 : 1);
   s.hdr = reinterpret_cast<int32_t*>(c.ws + c.L.hdr);
   s.seq = reinterpret_cast<SeqInfo*>(c.ws + c.L.seq);
   s.q_list = reinterpret_cast<int2*>(c.ws + c.L.q_list);
@@ -116,7 +119,8 @@ SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu
   return s;
 }
 
-AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, float scale) {
+AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, float scale,
+                       int32_t mask_type) {
   AttnParams a = {};
   a.hdr = reinterpret_cast<const int32_t*>(c.ws + c.L.hdr);
   a.seq = reinterpret_cast<const SeqInfo*>(c.ws + c.L.seq);
@@ -128,6 +132,7 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.d = d;
   a.scale = scale;
   a.scale_log2e = scale * kLog2e;
+  a.causal_br = mask_type == ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT ? 1 : 0;
   return a;
 }
 
@@ -180,12 +185,12 @@ attn_thd_status fwd_impl(const void* q, const void* k, const void* v, void* out,
   if (events && n_events != kFwdStages + 1) return ATTN_THD_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Marks m{events, n_events, s};
-  const bool causal = mask_type == ATTN_THD_MASK_PADDING_CAUSAL;
+  const bool causal = mask_type != ATTN_THD_MASK_PADDING;
 
   ATTN_TRY(m.mark(0));
   ATTN_TRY(launch_sched(sched_params(c, cu_q, cu_kv, cu_qp, cu_kp, batch, total_q, total_kv,
-                                     kQTile, 0, causal), s));
-  AttnParams a = attn_params(c, hq, hkv, d, scale);
+                                     kQTile, 0, mask_type), s));
+  AttnParams a = attn_params(c, hq, hkv, d, scale, mask_type);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -219,13 +224,13 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
   if (events && n_events != kBwdStages + 1) return ATTN_THD_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Marks m{events, n_events, s};
-  const bool causal = mask_type == ATTN_THD_MASK_PADDING_CAUSAL;
+  const bool causal = mask_type != ATTN_THD_MASK_PADDING;
   const int kv_tile = dkdv_tile(d);
 
   ATTN_TRY(m.mark(0));
   ATTN_TRY(launch_sched(sched_params(c, cu_q, cu_kv, cu_qp, cu_kp, batch, total_q, total_kv,
-                                     kQTile, kv_tile, causal), s));
-  AttnParams a = attn_params(c, hq, hkv, d, scale);
+                                     kQTile, kv_tile, mask_type), s));
+  AttnParams a = attn_params(c, hq, hkv, d, scale, mask_type);
   a.q = q;
   a.k = k;
   a.v = v;

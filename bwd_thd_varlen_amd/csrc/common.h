@@ -451,7 +451,7 @@ struct SchedParams {
   const int32_t* cu_kp;
   int32_t batch, total_q, total_kv;
   int32_t q_tile, kv_tile;       // 0 = do not build that list
-  int32_t causal;
+  int32_t causal;                // 0 none, 1 top-left, 2 bottom-right triangle
   int32_t* hdr;
   SeqInfo* seq;
   int2* q_list;
@@ -488,6 +488,14 @@ struct AttnParams {
   const int2* list;
   int32_t hq, hkv, group, d;
   float scale, scale_log2e;
+  int32_t causal_br;   // causal triangle aligned at the sequence ends (bottom right)
 };
+
+// Offset of the causal diagonal of a sequence: key j is visible to query i
+// iff j <= i + diag.  Top-left alignment: 0; bottom-right: Lk - Lq, so that
+// the last query sees every key (the two agree when Lq == Lk).
+__device__ __forceinline__ int causal_diag(const SeqInfo& s, int32_t bottom_right) {
+  return bottom_right ? s.lk - s.lq : 0;
+}
 
 }  // namespace attn

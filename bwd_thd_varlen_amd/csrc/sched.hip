@@ -19,16 +19,18 @@ constexpr int kSchedThreads = 1024;
 // ceil(a / b) for a >= 0, b > 0
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Work key of a query tile: keys it visits, in 64-key units.
+// Work key of a query tile: keys it visits, in 64-key units.  causal: 0 no
+// triangle, 1 top-left, 2 bottom-right (query i sees key j iff
+// j <= i + causal_diag).
 __device__ __forceinline__ int q_tile_key(const SeqInfo& s, int m, int tile, int causal) {
   int hi = min(s.lq, (m + 1) * tile);
-  int keys = causal ? min(s.lk, hi) : s.lk;
+  int keys = causal ? max(0, min(s.lk, hi + causal_diag(s, causal == 2))) : s.lk;
   return min(cdiv(keys, 64), kSchedKeys - 1);
 }
 
 // Work key of a key tile: queries that reach it, in 64-query units.
 __device__ __forceinline__ int kv_tile_key(const SeqInfo& s, int n, int tile, int causal) {
-  int q = causal ? max(0, s.lq - n * tile) : s.lq;
+  int q = causal ? max(0, s.lq - max(0, n * tile - causal_diag(s, causal == 2))) : s.lq;
   return min(cdiv(q, 64), kSchedKeys - 1);
 }
 

@@ -4,7 +4,8 @@
  * Fused scaled-dot-product attention, forward (O and the softmax statistic
  * LSE) and backward (dQ, dK, dV), over packed variable-length sequences in
  * THD layout, with grouped-query attention and the "padding" and
- * "padding_causal" masks.
+ * "padding_causal" masks (the causal triangle aligned top-left or
+ * bottom-right).
  *
  * Operation (TransformerEngine issue 3333 "FusedAttention (cuDNN) THD
  * backward produces wrong gradients on sm_120", section "Reproduction": a
@@ -14,7 +15,8 @@
  * g = h / (hq / hkv):
  *     S   = scale * Q_bh K_bg^T             (Lq_b x Lk_b)
  *     P   = softmax over the allowed keys    (padding: all real keys;
- *                                             padding_causal: key j <= query i)
+ *                                             padding_causal: key j <= query i;
+ *                                             bottom-right: j <= i + Lk_b - Lq_b)
  *     O   = P V_bg,     LSE_i = ln sum_{j allowed} exp(S_ij)
  *   backward, from dO:
  *     dP = dO V^T, Delta_i = sum_c dO_ic O_ic, dS = P o (dP - Delta)
@@ -83,7 +85,11 @@ typedef enum {
 } attn_thd_status;
 
 enum { ATTN_THD_BF16 = 0, ATTN_THD_FP16 = 1 };                        /* dtype     */
-enum { ATTN_THD_MASK_PADDING = 0, ATTN_THD_MASK_PADDING_CAUSAL = 1 }; /* mask_type */
+enum {                                                                /* mask_type */
+  ATTN_THD_MASK_PADDING = 0,
+  ATTN_THD_MASK_PADDING_CAUSAL = 1,               /* top-left:     key j <= query i           */
+  ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT = 2   /* bottom-right: key j <= query i + Lk - Lq */
+};
 
 /* Device status bits (attn_thd_read_device_status). */
 enum {
@@ -102,8 +108,14 @@ size_t attn_thd_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv,
  * Forward.  Writes out [total_q, hq, d] and lse [total_q, hq] (float32).
  *   scale         softmax scale (no default at this level; 1/sqrt(d) is usual)
  *   max_seqlen_*  an upper-bound hint only; correctness never depends on it
- *   mask_type     ATTN_THD_MASK_PADDING or ATTN_THD_MASK_PADDING_CAUSAL
- *                 (causal is top-left aligned: query i sees keys j <= i)
+ *   mask_type     ATTN_THD_MASK_PADDING, ATTN_THD_MASK_PADDING_CAUSAL (the
+ *                 triangle aligned top-left: query i sees keys j <= i) or
+ *                 ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT (aligned at the
+ *                 sequence ends: j <= i + Lk - Lq, so the last query sees
+ *                 every key).  The pages use the causal mask only with
+ *                 Lq == Lk, where both alignments agree; a query row that
+ *                 sees no key (bottom-right with Lq > Lk) gets out = +0.0,
+ *                 lse = -inf and dq = +0.0.
  *   dtype         ATTN_THD_BF16 or ATTN_THD_FP16 (q, k, v, out)
  */
 attn_thd_status attn_fwd_thd(

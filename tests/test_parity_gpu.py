@@ -116,6 +116,39 @@ def test_lq_differs_from_lk(causal):
     check_case(_ragged_case(lq, lk, pq, pk, hq=6, hkv=3, d=64, causal=causal, dtype="bf16", seed=3))
 
 
+# bottom-right causal: query i sees key j iff j <= i + Lk - Lq.  Lengths
+# where Lq < Lk (every query sees a prefix plus the diagonal), Lq > Lk by
+# less and by more than a 128-query tile (leading queries see no key: out 0,
+# lse -inf, dq 0), equal lengths, and empty sides.
+BR_LQ = [5, 130, 64, 0, 300, 40, 257, 1, 200]
+BR_LK = [9, 70, 64, 12, 33, 300, 129, 77, 0]
+BR_PQ = [8, 130, 70, 4, 300, 48, 260, 1, 201]
+BR_PK = [9, 72, 64, 12, 40, 300, 129, 80, 3]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_bottom_right_causal(d):
+    check_case(_ragged_case(BR_LQ, BR_LK, BR_PQ, BR_PK, hq=6, hkv=3, d=d, causal="bottom_right",
+                            dtype="bf16", seed=20 + d))
+
+
+def test_bottom_right_causal_fp16():
+    check_case(_ragged_case(BR_LQ, BR_LK, BR_PQ, BR_PK, hq=4, hkv=1, d=128, causal="bottom_right",
+                            dtype="fp16", seed=30))
+
+
+def test_bottom_right_equals_top_left_bitwise_when_lengths_match():
+    """With Lq == Lk in every sequence the two alignments are the same mask:
+    the library must give bitwise identical results for both mask types."""
+    L = [1, 64, 129, 300, 0, 77]
+    P = [4, 64, 130, 300, 2, 80]
+    tl = _ragged_case(L, L, P, P, hq=4, hkv=2, d=128, causal=True, dtype="bf16", seed=31)
+    br = _ragged_case(L, L, P, P, hq=4, hkv=2, d=128, causal="bottom_right", dtype="bf16", seed=31)
+    a, b = gpu_run(tl), gpu_run(br)
+    for name, x, y in zip(("out", "lse", "dq", "dk", "dv"), a, b):
+        assert torch.equal(x, y), name
+
+
 @pytest.mark.parametrize("d", [32, 128])
 def test_fp16(d):
     L = [100, 257, 64, 3]

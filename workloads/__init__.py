@@ -40,7 +40,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Union
 
 import numpy as np
 import torch
@@ -65,7 +65,7 @@ class Case:
     cu_seqlens_q_padded: np.ndarray  # int32 [B+1], memory layout boundaries
     cu_seqlens_kv_padded: np.ndarray
     scale: float
-    causal: bool
+    causal: Union[bool, str]   # False, True (top-left triangle) or "bottom_right"
     dtype: str
     max_seqlen_q: int = 0
     max_seqlen_kv: int = 0
@@ -89,6 +89,8 @@ class Case:
 
     @property
     def mask_type(self) -> str:
+        if self.causal == "bottom_right":
+            return "padding_causal_bottom_right"
         return "padding_causal" if self.causal else "padding"
 
 
