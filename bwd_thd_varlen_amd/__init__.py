@@ -12,6 +12,8 @@ arguments (``cu_seqlens_q``, ``cu_seqlens_kv``, ``cu_seqlens_q_padded``,
 ``attn_mask_type`` in {"padding", "padding_causal",
 "padding_causal_bottom_right"}: the causal triangle top-left aligned, key
 j <= query i, or aligned at the sequence ends, j <= i + Lk - Lq).
+``fwd_batched`` / ``bwd_batched`` read bshd ``[b, s, h, d]`` and sbhd
+``[s, b, h, d]`` tensors in place through the same kernels.
 """
 from __future__ import annotations
 
@@ -25,7 +27,8 @@ import torch
 __all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
            "attn_fwd_thd_timed", "attn_bwd_thd_timed", "fwd", "bwd", "status_string",
            "read_device_status", "AttnError", "STATUS", "DEV_BAD_SEQLENS", "StageEvents",
-           "FWD_STAGES", "BWD_STAGES"]
+           "FWD_STAGES", "BWD_STAGES", "attn_fwd_batched", "attn_bwd_batched", "fwd_batched",
+           "bwd_batched", "LAYOUTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
@@ -36,6 +39,7 @@ STATUS = {0: "ATTN_THD_OK", 1: "ATTN_THD_EINVAL", 2: "ATTN_THD_EUNSUPPORTED",
 DEV_BAD_SEQLENS = 1
 _DTYPE = {torch.bfloat16: 0, torch.float16: 1}
 _MASK = {"padding": 0, "padding_causal": 1, "padding_causal_bottom_right": 2}
+LAYOUTS = {"bshd": 1, "sbhd": 2}
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -54,6 +58,19 @@ _BWD_ARGS = [_P, _P, _P, _P, _P, _P,      # q k v out dout lse
              _I, _I, _I, _I, _I,
              _I, _I, _I, _F, _I, _I,
              _P, _S, _P]
+
+
+_BFWD_ARGS = [_P, _P, _P, _P, _P,         # q k v out lse
+              _P, _P, _I,                 # cu_q cu_kv layout
+              _I, _I, _I,                 # batch seqlen_q seqlen_kv
+              _I, _I, _I, _F, _I, _I,     # hq hkv d scale mask dtype
+              _P, _S, _P]                 # workspace bytes stream
+_BBWD_ARGS = [_P, _P, _P, _P, _P, _P,     # q k v out dout lse
+              _P, _P, _P,                 # dq dk dv
+              _P, _P, _I,
+              _I, _I, _I,
+              _I, _I, _I, _F, _I, _I,
+              _P, _S, _P]
 
 
 class AttnError(RuntimeError):
@@ -81,6 +98,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_thd_timed.restype = ctypes.c_int
         L.attn_bwd_thd_timed.argtypes = _BWD_ARGS + [ctypes.POINTER(_P), _I]
         L.attn_bwd_thd_timed.restype = ctypes.c_int
+        L.attn_fwd_batched.argtypes = _BFWD_ARGS
+        L.attn_fwd_batched.restype = ctypes.c_int
+        L.attn_bwd_batched.argtypes = _BBWD_ARGS
+        L.attn_bwd_batched.restype = ctypes.c_int
         L.attn_thd_status_string.argtypes = [_I]
         L.attn_thd_status_string.restype = ctypes.c_char_p
         L.attn_thd_read_device_status.argtypes = [_P, _P, ctypes.POINTER(_I)]
@@ -122,6 +143,25 @@ def attn_bwd_thd(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_k
                                   cu_seqlens_kv, cu_seqlens_q_padded, cu_seqlens_kv_padded, batch,
                                   total_q, total_kv, max_seqlen_q, max_seqlen_kv, hq, hkv, d,
                                   scale, mask_type, dtype, workspace, workspace_bytes, stream))
+
+
+def attn_fwd_batched(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, layout, batch, seqlen_q,
+                     seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace, workspace_bytes,
+                     stream) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_fwd_batched(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, layout,
+                                      batch, seqlen_q, seqlen_kv, hq, hkv, d, scale, mask_type,
+                                      dtype, workspace, workspace_bytes, stream))
+
+
+def attn_bwd_batched(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv, layout,
+                     batch, seqlen_q, seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
+                     workspace_bytes, stream) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_bwd_batched(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q,
+                                      cu_seqlens_kv, layout, batch, seqlen_q, seqlen_kv, hq, hkv,
+                                      d, scale, mask_type, dtype, workspace, workspace_bytes,
+                                      stream))
 
 
 def attn_fwd_thd_timed(*args, events, n_events) -> int:
@@ -324,4 +364,112 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     else:
         st = attn_bwd_thd_timed(*args, events=events.ptr, n_events=events.n)
     _check(st, "attn_bwd_thd")
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------- batched layouts
+def _batched_dims(q, k, layout):
+    if layout not in LAYOUTS:
+        raise AttnError(f"layout must be one of {sorted(LAYOUTS)}")
+    if q.dim() != 4 or k.dim() != 4:
+        raise AttnError("batched q and k must be 4-d ([b,s,h,d] or [s,b,h,d])")
+    if layout == "bshd":
+        (b, sq, hq, d), (bk, skv, hkv, dk_) = q.shape, k.shape
+    else:
+        (sq, b, hq, d), (skv, bk, hkv, dk_) = q.shape, k.shape
+    if bk != b or dk_ != d:
+        raise AttnError("q and k disagree on batch or head dim")
+    return b, sq, skv, hq, hkv, d
+
+
+def _lse_shape(layout, b, sq, hq):
+    return (b, sq, hq) if layout == "bshd" else (sq, b, hq)
+
+
+def fwd_batched(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str = "sbhd",
+                cu_seqlens_q: Optional[torch.Tensor] = None,
+                cu_seqlens_kv: Optional[torch.Tensor] = None, attn_mask_type: str = "padding",
+                softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward on bshd ``[b, s, h, d]`` or sbhd ``[s, b, h, d]`` tensors, read in place.
+
+    cu_seqlens_* (int32 [b+1]) give real lengths within the slots (None: full).
+    Returns out (q's layout and dtype) and lse float32 ([b, s, hq] or [s, b, hq]).
+    """
+    dev = q.device
+    _need(q, "q", None, dev)
+    if q.dtype not in _DTYPE:
+        raise AttnError(f"q must be bf16 or fp16, got {q.dtype}")
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    if v.shape != k.shape:
+        raise AttnError("k and v must have the same shape")
+    b, sq, skv, hq, hkv, d = _batched_dims(q, k, layout)
+    cq = _cu(cu_seqlens_q, "cu_seqlens_q", dev)
+    ck = _cu(cu_seqlens_kv, "cu_seqlens_kv", dev)
+    if any(c is not None and c.numel() != b + 1 for c in (cq, ck)):
+        raise AttnError("cu_seqlens arrays need batch + 1 entries")
+    if attn_mask_type not in _MASK:
+        raise AttnError(f"attn_mask_type must be one of {sorted(_MASK)}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(_lse_shape(layout, b, sq, hq), dtype=torch.float32, device=dev) \
+        if lse is None else lse
+    _need(out, "out", q.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if out.shape != q.shape or tuple(lse.shape) != _lse_shape(layout, b, sq, hq):
+        raise AttnError("out or lse has the wrong shape")
+    ws = _workspace(workspace, b, b * sq, b * skv, hq, hkv, d, dev)
+    st = attn_fwd_batched(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), _ptr(cq), _ptr(ck), LAYOUTS[layout], b, sq, skv, hq,
+                          hkv, d, scale, _MASK[attn_mask_type], _DTYPE[q.dtype], ws.data_ptr(),
+                          ws.numel() * ws.element_size(),
+                          torch.cuda.current_stream(dev).cuda_stream)
+    _check(st, "attn_fwd_batched")
+    return out, lse
+
+
+def bwd_batched(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                dout: torch.Tensor, lse: torch.Tensor, layout: str = "sbhd",
+                cu_seqlens_q: Optional[torch.Tensor] = None,
+                cu_seqlens_kv: Optional[torch.Tensor] = None, attn_mask_type: str = "padding",
+                softmax_scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+                dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward on bshd / sbhd tensors (arguments as ``fwd_batched``); returns (dq, dk, dv)."""
+    dev = q.device
+    _need(q, "q", None, dev)
+    if q.dtype not in _DTYPE:
+        raise AttnError(f"q must be bf16 or fp16, got {q.dtype}")
+    for t, n in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, q.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    b, sq, skv, hq, hkv, d = _batched_dims(q, k, layout)
+    if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
+        raise AttnError("shape mismatch among q, k, v, out, dout")
+    if tuple(lse.shape) != _lse_shape(layout, b, sq, hq):
+        raise AttnError("lse has the wrong shape")
+    cq = _cu(cu_seqlens_q, "cu_seqlens_q", dev)
+    ck = _cu(cu_seqlens_kv, "cu_seqlens_kv", dev)
+    if any(c is not None and c.numel() != b + 1 for c in (cq, ck)):
+        raise AttnError("cu_seqlens arrays need batch + 1 entries")
+    if attn_mask_type not in _MASK:
+        raise AttnError(f"attn_mask_type must be one of {sorted(_MASK)}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q.dtype, dev)
+    _need(dk, "dk", q.dtype, dev)
+    _need(dv, "dv", q.dtype, dev)
+    ws = _workspace(workspace, b, b * sq, b * skv, hq, hkv, d, dev)
+    st = attn_bwd_batched(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), _ptr(cq), _ptr(ck), LAYOUTS[layout], b, sq, skv, hq,
+                          hkv, d, scale, _MASK[attn_mask_type], _DTYPE[q.dtype], ws.data_ptr(),
+                          ws.numel() * ws.element_size(),
+                          torch.cuda.current_stream(dev).cuda_stream)
+    _check(st, "attn_bwd_batched")
     return dq, dk, dv

@@ -65,12 +65,25 @@ struct Common {
   int64_t q_tiles_max, kv_tiles_max;
 };
 
+// Token layout of a call: THD (slots from cu_seqlens_*_padded) or a batched
+// layout with fixed slots of slot_q / slot_kv tokens per sequence.
+struct Geom {
+  int32_t layout;
+  int32_t slot_q, slot_kv;
+  int32_t tsq(int32_t batch) const { return layout == kLayoutSbhd ? batch : 1; }
+};
+constexpr Geom kThd = {kLayoutThd, 0, 0};
+
+// the largest tile any kernel moves by one buffer-range DMA, in rows
+constexpr int64_t kMaxDmaRows = 256;
+
 // Checks shared by both entry points.  Nothing is launched before they pass.
 attn_thd_status check_common(const void* q, const void* k, const void* v,
                              const int32_t* cu_q, const int32_t* cu_kv, int32_t batch,
                              int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv,
                              int32_t d, float scale, int32_t mask_type, int32_t dtype,
-                             void* workspace, size_t workspace_bytes, Common& c) {
+                             void* workspace, size_t workspace_bytes, const Geom& geo,
+                             Common& c) {
   if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return ATTN_THD_EINVAL;
   if (hq % hkv != 0) return ATTN_THD_EINVAL;
   if (d % 8 != 0 || d > 256) return ATTN_THD_EUNSUPPORTED;
@@ -79,7 +92,11 @@ attn_thd_status check_common(const void* q, const void* k, const void* v,
       mask_type != ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT)
     return ATTN_THD_EUNSUPPORTED;
   if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_THD_EINVAL;
-  if (!cu_q || !cu_kv) return ATTN_THD_EINVAL;
+  // THD needs the real boundaries; the batched layouts default to full slots
+  if (geo.layout == kLayoutThd && (!cu_q || !cu_kv)) return ATTN_THD_EINVAL;
+  // every DMA range (rows x token stride) must stay below 2 GiB
+  const int64_t ts = geo.tsq(batch);
+  if (kMaxDmaRows * ts * (int64_t)(hq > hkv ? hq : hkv) * d * 2 > INT32_MAX) return ATTN_THD_EINVAL;
   if ((total_q > 0 && !q) || (total_kv > 0 && (!k || !v))) return ATTN_THD_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_THD_EINVAL;
   // grid sizes and element offsets must fit the kernels' integer types
@@ -99,7 +116,7 @@ attn_thd_status check_common(const void* q, const void* k, const void* v,
 SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu_kv,
                          const int32_t* cu_qp, const int32_t* cu_kp, int32_t batch,
                          int32_t total_q, int32_t total_kv, int q_tile, int kv_tile,
-                         int32_t mask_type) {
+                         int32_t mask_type, const Geom& geo) {
   SchedParams s;
   s.cu_q = cu_q;
   s.cu_kv = cu_kv;
@@ -112,6 +129,9 @@ SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu
   s.kv_tile = kv_tile;
   s.causal = mask_type == ATTN_THD_MASK_PADDING ? 0
              : (mask_type == ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT ? 2 : 1);
+  s.layout = geo.layout;
+  s.slot_q = geo.slot_q;
+  s.slot_kv = geo.slot_kv;
   s.hdr = reinterpret_cast<int32_t*>(c.ws + c.L.hdr);
   s.seq = reinterpret_cast<SeqInfo*>(c.ws + c.L.seq);
   s.q_list = reinterpret_cast<int2*>(c.ws + c.L.q_list);
@@ -120,7 +140,7 @@ SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu
 }
 
 AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, float scale,
-                       int32_t mask_type) {
+                       int32_t mask_type, const Geom& geo, int32_t batch) {
   AttnParams a = {};
   a.hdr = reinterpret_cast<const int32_t*>(c.ws + c.L.hdr);
   a.seq = reinterpret_cast<const SeqInfo*>(c.ws + c.L.seq);
@@ -133,11 +153,13 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.scale = scale;
   a.scale_log2e = scale * kLog2e;
   a.causal_br = mask_type == ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT ? 1 : 0;
+  a.tsq = geo.tsq(batch);
+  a.tskv = geo.tsq(batch);
   return a;
 }
 
 ZeroParams zero_params(const Common& c, int32_t batch, int rows, int width, bool kv_side,
-                       void* t0, void* t1, float* lse, int lse_heads) {
+                       void* t0, void* t1, float* lse, int lse_heads, const Geom& geo) {
   ZeroParams z;
   z.hdr = reinterpret_cast<const int32_t*>(c.ws + c.L.hdr);
   z.seq = reinterpret_cast<const SeqInfo*>(c.ws + c.L.seq);
@@ -146,6 +168,8 @@ ZeroParams zero_params(const Common& c, int32_t batch, int rows, int width, bool
   z.width = width;
   z.kv_side = kv_side ? 1 : 0;
   z.lse_heads = lse_heads;
+  z.layout = geo.layout;
+  z.slot = kv_side ? geo.slot_kv : geo.slot_q;
   z.t0 = t0;
   z.t1 = t1;
   z.lse = lse;
@@ -175,10 +199,10 @@ attn_thd_status fwd_impl(const void* q, const void* k, const void* v, void* out,
                          const int32_t* cu_kp, int32_t batch, int32_t total_q, int32_t total_kv,
                          int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
                          int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                         void* const* events, int32_t n_events) {
+                         void* const* events, int32_t n_events, const Geom& geo) {
   Common c;
   attn_thd_status st = check_common(q, k, v, cu_q, cu_kv, batch, total_q, total_kv, hq, hkv, d,
-                                    scale, mask_type, dtype, workspace, workspace_bytes, c);
+                                    scale, mask_type, dtype, workspace, workspace_bytes, geo, c);
   if (st != ATTN_THD_OK) return st;
   if (total_q > 0 && (!out || !lse)) return ATTN_THD_EINVAL;
   if (!aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_THD_EINVAL;
@@ -189,8 +213,8 @@ attn_thd_status fwd_impl(const void* q, const void* k, const void* v, void* out,
 
   ATTN_TRY(m.mark(0));
   ATTN_TRY(launch_sched(sched_params(c, cu_q, cu_kv, cu_qp, cu_kp, batch, total_q, total_kv,
-                                     kQTile, 0, mask_type), s));
-  AttnParams a = attn_params(c, hq, hkv, d, scale, mask_type);
+                                     kQTile, 0, mask_type, geo), s));
+  AttnParams a = attn_params(c, hq, hkv, d, scale, mask_type, geo, batch);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -200,7 +224,7 @@ attn_thd_status fwd_impl(const void* q, const void* k, const void* v, void* out,
   ATTN_TRY(m.mark(1));
   ATTN_TRY(launch_fwd(a, dtype, causal, (int)c.q_tiles_max, s));
   ATTN_TRY(m.mark(2));
-  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, out, nullptr, lse, hq), s));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, out, nullptr, lse, hq, geo), s));
   ATTN_TRY(m.mark(3));
   return ATTN_THD_OK;
 }
@@ -211,10 +235,10 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
                          const int32_t* cu_kp, int32_t batch, int32_t total_q, int32_t total_kv,
                          int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
                          int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                         void* const* events, int32_t n_events) {
+                         void* const* events, int32_t n_events, const Geom& geo) {
   Common c;
   attn_thd_status st = check_common(q, k, v, cu_q, cu_kv, batch, total_q, total_kv, hq, hkv, d,
-                                    scale, mask_type, dtype, workspace, workspace_bytes, c);
+                                    scale, mask_type, dtype, workspace, workspace_bytes, geo, c);
   if (st != ATTN_THD_OK) return st;
   if (total_q > 0 && (!out || !dout || !lse || !dq)) return ATTN_THD_EINVAL;
   if (total_kv > 0 && (!dk || !dv)) return ATTN_THD_EINVAL;
@@ -229,8 +253,8 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
 
   ATTN_TRY(m.mark(0));
   ATTN_TRY(launch_sched(sched_params(c, cu_q, cu_kv, cu_qp, cu_kp, batch, total_q, total_kv,
-                                     kQTile, kv_tile, mask_type), s));
-  AttnParams a = attn_params(c, hq, hkv, d, scale, mask_type);
+                                     kQTile, kv_tile, mask_type, geo), s));
+  AttnParams a = attn_params(c, hq, hkv, d, scale, mask_type, geo, batch);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -249,9 +273,9 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
   ATTN_TRY(m.mark(3));
   ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
   ATTN_TRY(m.mark(4));
-  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0), s));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0, geo), s));
   ATTN_TRY(m.mark(5));
-  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0), s));
+  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0, geo), s));
   ATTN_TRY(m.mark(6));
   return ATTN_THD_OK;
 }
@@ -278,7 +302,7 @@ attn_thd_status attn_fwd_thd(const void* q, const void* k, const void* v, void* 
   (void)max_seqlen_kv;
   return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
                   cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d, scale, mask_type,
-                  dtype, workspace, workspace_bytes, stream, nullptr, 0);
+                  dtype, workspace, workspace_bytes, stream, nullptr, 0, kThd);
 }
 
 attn_thd_status attn_fwd_thd_timed(const void* q, const void* k, const void* v, void* out,
@@ -296,7 +320,7 @@ attn_thd_status attn_fwd_thd_timed(const void* q, const void* k, const void* v, 
   if (!events) return ATTN_THD_EINVAL;
   return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
                   cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d, scale, mask_type,
-                  dtype, workspace, workspace_bytes, stream, events, n_events);
+                  dtype, workspace, workspace_bytes, stream, events, n_events, kThd);
 }
 
 attn_thd_status attn_bwd_thd(const void* q, const void* k, const void* v, const void* out,
@@ -312,7 +336,7 @@ attn_thd_status attn_bwd_thd(const void* q, const void* k, const void* v, const 
   (void)max_seqlen_kv;
   return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
                   cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
-                  scale, mask_type, dtype, workspace, workspace_bytes, stream, nullptr, 0);
+                  scale, mask_type, dtype, workspace, workspace_bytes, stream, nullptr, 0, kThd);
 }
 
 attn_thd_status attn_bwd_thd_timed(const void* q, const void* k, const void* v, const void* out,
@@ -331,7 +355,54 @@ attn_thd_status attn_bwd_thd_timed(const void* q, const void* k, const void* v, 
   if (!events) return ATTN_THD_EINVAL;
   return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
                   cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
-                  scale, mask_type, dtype, workspace, workspace_bytes, stream, events, n_events);
+                  scale, mask_type, dtype, workspace, workspace_bytes, stream, events, n_events, kThd);
+}
+
+// Batched layouts: geometry checks, then the THD path with fixed slots.
+static attn_thd_status batched_geom(int32_t layout, int32_t batch, int32_t seqlen_q,
+                                    int32_t seqlen_kv, Geom& geo, int32_t& total_q,
+                                    int32_t& total_kv) {
+  if (layout != ATTN_THD_LAYOUT_BSHD && layout != ATTN_THD_LAYOUT_SBHD) return ATTN_THD_EUNSUPPORTED;
+  if (batch < 0 || seqlen_q < 0 || seqlen_kv < 0) return ATTN_THD_EINVAL;
+  const int64_t tq = (int64_t)batch * seqlen_q, tk = (int64_t)batch * seqlen_kv;
+  if (tq > INT32_MAX || tk > INT32_MAX) return ATTN_THD_EINVAL;
+  geo.layout = layout == ATTN_THD_LAYOUT_BSHD ? kLayoutBshd : kLayoutSbhd;
+  geo.slot_q = seqlen_q;
+  geo.slot_kv = seqlen_kv;
+  total_q = (int32_t)tq;
+  total_kv = (int32_t)tk;
+  return ATTN_THD_OK;
+}
+
+attn_thd_status attn_fwd_batched(const void* q, const void* k, const void* v, void* out,
+                                 float* lse, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_kv, int32_t layout, int32_t batch,
+                                 int32_t seqlen_q, int32_t seqlen_kv, int32_t hq, int32_t hkv,
+                                 int32_t d, float scale, int32_t mask_type, int32_t dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  Geom geo;
+  int32_t total_q, total_kv;
+  attn_thd_status st = batched_geom(layout, batch, seqlen_q, seqlen_kv, geo, total_q, total_kv);
+  if (st != ATTN_THD_OK) return st;
+  return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, nullptr, nullptr, batch,
+                  total_q, total_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
+                  workspace_bytes, stream, nullptr, 0, geo);
+}
+
+attn_thd_status attn_bwd_batched(const void* q, const void* k, const void* v, const void* out,
+                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                 int32_t layout, int32_t batch, int32_t seqlen_q,
+                                 int32_t seqlen_kv, int32_t hq, int32_t hkv, int32_t d,
+                                 float scale, int32_t mask_type, int32_t dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Geom geo;
+  int32_t total_q, total_kv;
+  attn_thd_status st = batched_geom(layout, batch, seqlen_q, seqlen_kv, geo, total_q, total_kv);
+  if (st != ATTN_THD_OK) return st;
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv, nullptr,
+                  nullptr, batch, total_q, total_kv, hq, hkv, d, scale, mask_type, dtype,
+                  workspace, workspace_bytes, stream, nullptr, 0, geo);
 }
 
 const char* attn_thd_status_string(int32_t status) {

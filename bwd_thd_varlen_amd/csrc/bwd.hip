@@ -55,8 +55,10 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   const int m0 = w.tile * kQTile;
   const int qi = m0 + wave * 32 + li;
   const int wq_lo = m0 + wave * 32, wq_hi = wq_lo + 31;
+  // elements per row, and between consecutive tokens of a sequence
   const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
-  const uint32_t kv_rs_bytes = (uint32_t)(kvrs * 2);
+  const int64_t qts = qrs * p.tsq, kvts = kvrs * p.tskv;
+  const uint32_t kv_rs_bytes = (uint32_t)(kvts * 2);
   const int64_t qoff = (int64_t)s.oq * qrs + (int64_t)h * p.d;
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + qoff;
   const uint16_t* dob = reinterpret_cast<const uint16_t*>(p.dout) + qoff;
@@ -80,8 +82,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     uint16_t* tK = sK[step & 1];
     uint16_t* tV = sV[step & 1];
     const int n0 = step * KS;
-    dma_k.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, sSink, wave);
-    dma_v.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, sSink, wave);
+    dma_k.issue(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tK, sSink, wave);
+    dma_v.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tV, sSink, wave);
   };
   if (nsteps > 0) issue(0);
 
@@ -90,10 +92,11 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   for (int t = 0; t < NT; ++t) {
     const int c = 16 * t + 8 * hh;
     const bool ok = qvalid && c < p.d;
-    qreg[t] = ok ? ldg16(qb + (int64_t)qi * qrs + c) : z4;
-    doreg[t] = ok ? ldg16(dob + (int64_t)qi * qrs + c) : z4;
+    qreg[t] = ok ? ldg16(qb + (int64_t)qi * qts + c) : z4;
+    doreg[t] = ok ? ldg16(dob + (int64_t)qi * qts + c) : z4;
   }
-  const int64_t srow = (int64_t)(s.oq + qi) * p.hq + h;
+  const int64_t qrow = (int64_t)s.oq + (int64_t)qi * p.tsq;
+  const int64_t srow = qrow * p.hq + h;
   const float lse2 = qvalid ? p.lse2[srow] : __builtin_inff();
   const float dlt = qvalid ? p.delta[srow] : 0.f;
   wait_vm<0>();
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   }
 
   if (qvalid) {
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.dq) + (int64_t)(s.oq + qi) * qrs + (int64_t)h * p.d;
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d;
     const float sc0 = p.scale;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -209,8 +212,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   const int n0 = w.tile * BN;
   const int kj = n0 + wave * 32 + li;          // this lane's key (B-operand column)
   const int wk_lo = n0 + wave * 32, wk_hi = wk_lo + 31;
+  // elements per row, and between consecutive tokens of a sequence
   const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
-  const uint32_t q_rs_bytes = (uint32_t)(qrs * 2), kv_rs_bytes = (uint32_t)(kvrs * 2);
+  const int64_t qts = qrs * p.tsq, kvts = kvrs * p.tskv;
+  const uint32_t q_rs_bytes = (uint32_t)(qts * 2), kv_rs_bytes = (uint32_t)(kvts * 2);
   const int64_t kvoff = (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + kvoff;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + kvoff;
@@ -229,7 +234,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   Dma dma_q;
   dma_q.init(wave, lane, p.d, q_rs_bytes);
   // 4-byte DMA of the vector (LSE2 or Delta) rows i0 .. i0+BM-1 of head h
-  const uint32_t vec_voff = lane < BM ? (uint32_t)lane * (uint32_t)p.hq * 4u : kOutOfRange;
+  const uint32_t vec_rs_bytes = (uint32_t)p.hq * (uint32_t)p.tsq * 4u;
+  const uint32_t vec_voff = lane < BM ? (uint32_t)lane * vec_rs_bytes : kOutOfRange;
   auto issue = [&](int step) {
     const int buf = step % NBUF;
     uint16_t* tQ = sQ[buf];
@@ -240,13 +246,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     const int h = h0 + hg;
     const int i0 = m * BM;
     const int nrow = s.lq - i0;
-    const int64_t base = (int64_t)(s.oq + i0) * qrs + (int64_t)h * p.d;
+    const int64_t row0 = (int64_t)s.oq + (int64_t)i0 * p.tsq;
+    const int64_t base = row0 * qrs + (int64_t)h * p.d;
     dma_q.issue(reinterpret_cast<const uint16_t*>(p.q) + base, nrow, q_rs_bytes, tQ, sSink, wave);
     dma_q.issue(reinterpret_cast<const uint16_t*>(p.dout) + base, nrow, q_rs_bytes, tdO, sSink, wave);
     const int nr = uniform(nrow < 0 ? 0 : (nrow > BM ? BM : nrow));
-    const int64_t vbase = (int64_t)(s.oq + i0) * p.hq + h;
+    const int64_t vbase = row0 * p.hq + h;
     const float* src = wave == 0 ? p.lse2 + vbase : p.delta + vbase;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, wave < 2 ? (uint32_t)nr * (uint32_t)p.hq * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, wave < 2 ? (uint32_t)nr * vec_rs_bytes : 0u);
     dma<4>(rs, wave == 0 ? tvec : (wave == 1 ? tvec + 64 : sDummy), vec_voff);
   };
 #pragma unroll
@@ -260,14 +267,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   for (int t = 0; t < NT; ++t) {
     const int c = 16 * t + 8 * hh;
     const bool ok = kj < s.lk && c < p.d;
-    if constexpr (!K_LDS) kreg[t] = ok ? ldg16(kb + (int64_t)kj * kvrs + c) : z4;
-    if constexpr (!V_LDS) vreg[t] = ok ? ldg16(vb + (int64_t)kj * kvrs + c) : z4;
+    if constexpr (!K_LDS) kreg[t] = ok ? ldg16(kb + (int64_t)kj * kvts + c) : z4;
+    if constexpr (!V_LDS) vreg[t] = ok ? ldg16(vb + (int64_t)kj * kvts + c) : z4;
   }
   if constexpr (K_LDS || V_LDS) {
     DmaKV dkv;
     dkv.init(wave, lane, p.d, kv_rs_bytes);
-    if constexpr (K_LDS) dkv.issue(kb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sK, sSink, wave);
-    if constexpr (V_LDS) dkv.issue(vb + (int64_t)n0 * kvrs, s.lk - n0, kv_rs_bytes, sV, sSink, wave);
+    if constexpr (K_LDS) dkv.issue(kb + (int64_t)n0 * kvts, s.lk - n0, kv_rs_bytes, sK, sSink, wave);
+    if constexpr (V_LDS) dkv.issue(vb + (int64_t)n0 * kvts, s.lk - n0, kv_rs_bytes, sV, sSink, wave);
   }
   wait_vm<0>();
 
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   }
 
   if (kj < s.lk) {
-    const int64_t row = (int64_t)kj * kvrs;
+    const int64_t row = (int64_t)kj * kvts;
     uint16_t* dkb = reinterpret_cast<uint16_t*>(p.dk) + kvoff + row;
     uint16_t* dvb = reinterpret_cast<uint16_t*>(p.dv) + kvoff + row;
     const float sc0 = p.scale;

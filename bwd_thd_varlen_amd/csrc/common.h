@@ -52,9 +52,16 @@ constexpr int kHdrNKVTiles = 2;
 constexpr int kHdrWords = 64;    // 256 bytes
 
 // Per-sequence record written by the scheduler.
+// Token rows: token i of sequence b is row oq + i * ts of the q-side
+// tensors (ok + i * ts on the kv side), with ts the layout's token stride:
+// 1 for THD and bshd, the batch size for sbhd.
 struct SeqInfo {
-  int32_t oq, lq, ok, lk;        // padded offsets and real lengths
+  int32_t oq, lq, ok, lk;        // first row of the slot and real lengths
 };
+
+// How token rows are laid out (the batched layouts have fixed slots of
+// seqlen_q / seqlen_kv rows per sequence).
+enum : int32_t { kLayoutThd = 0, kLayoutBshd = 1, kLayoutSbhd = 2 };
 
 template <int DT> struct Mfma;
 
@@ -452,6 +459,8 @@ struct SchedParams {
   int32_t batch, total_q, total_kv;
   int32_t q_tile, kv_tile;       // 0 = do not build that list
   int32_t causal;                // 0 none, 1 top-left, 2 bottom-right triangle
+  int32_t layout;                // kLayoutThd: slots from the padded arrays;
+  int32_t slot_q, slot_kv;       // batched layouts: fixed slot lengths
   int32_t* hdr;
   SeqInfo* seq;
   int2* q_list;
@@ -464,6 +473,7 @@ struct ZeroParams {
   int32_t batch, rows, width;    // width = heads * d elements per row
   int32_t kv_side;               // 0: query rows (out/dq, lse); 1: key rows (dk, dv)
   int32_t lse_heads;             // heads of lse (0 = no lse to write)
+  int32_t layout, slot;          // token layout and (batched) slot length of this side
   void* t0;
   void* t1;
   float* lse;
@@ -489,6 +499,7 @@ struct AttnParams {
   int32_t hq, hkv, group, d;
   float scale, scale_log2e;
   int32_t causal_br;   // causal triangle aligned at the sequence ends (bottom right)
+  int32_t tsq, tskv;   // token strides in rows (1 for THD and bshd, batch for sbhd)
 };
 
 // Offset of the causal diagonal of a sequence: key j is visible to query i

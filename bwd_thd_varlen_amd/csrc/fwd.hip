@@ -62,8 +62,10 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   const int m0 = w.tile * kQTile;
   const int qi = m0 + wave * 32 + li;
   const int wq_lo = m0 + wave * 32, wq_hi = wq_lo + 31;
+  // elements per row, and between consecutive tokens of a sequence
   const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
-  const uint32_t kv_rs_bytes = (uint32_t)(kvrs * 2);
+  const int64_t qts = qrs * p.tsq, kvts = kvrs * p.tskv;
+  const uint32_t kv_rs_bytes = (uint32_t)(kvts * 2);
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)s.oq * qrs + (int64_t)h * p.d;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
@@ -82,8 +84,8 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   dma_v.init(wave, lane, p.d, kv_rs_bytes);
   auto issue = [&](int step, uint16_t* tK, uint16_t* tV) {
     const int n0 = step * KS;
-    dma_k.issue(kb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tK, nullptr, wave);
-    dma_v.issue(vb + (int64_t)n0 * kvrs, kend - n0, kv_rs_bytes, tV, nullptr, wave);
+    dma_k.issue(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tK, nullptr, wave);
+    dma_v.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tV, nullptr, wave);
   };
   if (nsteps > 0) issue(0, sK0, sV0);
 
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int c = 16 * t + 8 * hh;
-    qreg[t] = (qi < s.lq && c < p.d) ? ldg16(qb + (int64_t)qi * qrs + c) : z4;
+    qreg[t] = (qi < s.lq && c < p.d) ? ldg16(qb + (int64_t)qi * qts + c) : z4;
   }
   wait_vm<0>();   // Q and the first step's tiles; keeps the compiler from re-waiting in the loop
 
@@ -168,7 +170,8 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   const float l_tot = sum_halves(l_run);
   if (qi < s.lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + (int64_t)(s.oq + qi) * qrs + (int64_t)h * p.d;
+    const int64_t row = (int64_t)s.oq + (int64_t)qi * p.tsq;
+    uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + row * qrs + (int64_t)h * p.d;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
         }
       }
     if (hh == 0)
-      p.lse_out[(int64_t)(s.oq + qi) * p.hq + h] =
+      p.lse_out[row * p.hq + h] =
           l_tot > 0.f ? ((m_run == -__builtin_inff() ? 0.f : m_run) + __builtin_log2f(l_tot)) * kLn2
                       : -__builtin_inff();
   }

@@ -108,22 +108,33 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
+  const bool thd = p.layout == kLayoutThd;
   const int32_t* cqp = p.cu_qp ? p.cu_qp : p.cu_q;
   const int32_t* ckp = p.cu_kp ? p.cu_kp : p.cu_kv;
   for (int b = tid; b < p.batch; b += kSchedThreads) {
-    const int64_t q0 = p.cu_q[b], q1 = p.cu_q[b + 1], k0 = p.cu_kv[b], k1 = p.cu_kv[b + 1];
-    const int64_t pq0 = cqp[b], pq1 = cqp[b + 1], pk0 = ckp[b], pk1 = ckp[b + 1];
-    const int64_t lq = q1 - q0, lk = k1 - k0;
+    // batched layouts: a missing real-length array means full slots
+    const int64_t lq = p.cu_q ? (int64_t)p.cu_q[b + 1] - p.cu_q[b] : p.slot_q;
+    const int64_t lk = p.cu_kv ? (int64_t)p.cu_kv[b + 1] - p.cu_kv[b] : p.slot_kv;
+    // slot [pq0, pq1) in token positions (rows for THD and bshd; sbhd
+    // slots are strided, their first row is b)
+    int64_t pq0, pq1, pk0, pk1;
+    if (thd) {
+      pq0 = cqp[b]; pq1 = cqp[b + 1]; pk0 = ckp[b]; pk1 = ckp[b + 1];
+    } else {
+      pq0 = (int64_t)b * p.slot_q; pq1 = pq0 + p.slot_q;
+      pk0 = (int64_t)b * p.slot_kv; pk1 = pk0 + p.slot_kv;
+    }
     // real length within [0, slot]; slot within [0, total]: with every b
     // checked this also makes the padded arrays non-decreasing, so slots are
     // disjoint.
     const bool bad = lq < 0 || lq > pq1 - pq0 || lk < 0 || lk > pk1 - pk0 || pq0 < 0 ||
                      pq1 > p.total_q || pk0 < 0 || pk1 > p.total_kv;
     if (bad) atomicOr(&s_bad, 1);
+    const bool sbhd = p.layout == kLayoutSbhd;
     SeqInfo s;
-    s.oq = bad ? 0 : (int)pq0;
+    s.oq = bad ? 0 : (sbhd ? b : (int)pq0);
     s.lq = bad ? 0 : (int)lq;
-    s.ok = bad ? 0 : (int)pk0;
+    s.ok = bad ? 0 : (sbhd ? b : (int)pk0);
     s.lk = bad ? 0 : (int)lk;
     p.seq[b] = s;
   }
@@ -160,7 +171,16 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(ZeroParams p) {
   if (tid < kZeroRows && row0 + tid < p.rows) {
     const int t = row0 + tid;
     bool cov = false;
-    if (p.hdr[kHdrStatus] == 0 && p.batch > 0) {
+    if (p.hdr[kHdrStatus] == 0 && p.batch > 0 && p.layout != kLayoutThd) {
+      // batched layouts: row t is token i of sequence b
+      const bool sbhd = p.layout == kLayoutSbhd;
+      const int b = sbhd ? t % p.batch : t / p.slot;
+      const int i = sbhd ? t / p.batch : t % p.slot;
+      if (b < p.batch) {
+        SeqInfo s = p.seq[b];
+        cov = p.kv_side ? (i < s.lk && s.lq > 0) : (i < s.lq && s.lk > 0);
+      }
+    } else if (p.hdr[kHdrStatus] == 0 && p.batch > 0) {
       // largest b with offset(b) <= t (offsets are non-decreasing when valid)
       int lo = 0, hi = p.batch - 1, b = -1;
       while (lo <= hi) {
@@ -214,7 +234,7 @@ __global__ __launch_bounds__(256) void delta_kernel(AttnParams p) {
   constexpr int kRowsPerPass = 256 / CHP;
   const int64_t rs = (int64_t)p.hq * p.d;   // row stride in elements
   for (int r = tid / CHP; r < rows; r += kRowsPerPass) {
-    const int64_t row = s.oq + i0 + r;
+    const int64_t row = s.oq + (int64_t)(i0 + r) * p.tsq;
     float acc = 0.f;
     if (lane_c < chunks) {
       const int64_t off = row * rs + (int64_t)h * p.d + lane_c * 8;

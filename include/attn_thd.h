@@ -144,6 +144,45 @@ attn_thd_status attn_bwd_thd(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Batched layouts read in place, as THD views (TransformerEngine issue 3216,
+ * section "Reproduce", runs its sbhd [seq, batch, heads, d] tensors through
+ * DotProductAttention; bshd is the same with batch first).  Every sequence
+ * has a slot of seqlen_q query tokens and seqlen_kv key tokens:
+ *   BSHD  q, out, dout, dq : [batch, seqlen_q,  hq,  d]   (token i of b is row b*seqlen_q + i)
+ *         k, v, dk, dv     : [batch, seqlen_kv, hkv, d]
+ *   SBHD  q, out, dout, dq : [seqlen_q,  batch, hq,  d]   (token i of b is row i*batch + b)
+ *         k, v, dk, dv     : [seqlen_kv, batch, hkv, d]
+ *   lse                    : float32, one value per (row, query head), rows in
+ *                            the same order as q: [batch, seqlen_q, hq] for
+ *                            BSHD, [seqlen_q, batch, hq] for SBHD
+ * cu_seqlens_q / cu_seqlens_kv (int32 [batch + 1], device) give the REAL
+ * lengths as in THD, each at most its slot; the real tokens are the first of
+ * the slot and the rest is padding (written as for THD).  NULL means every
+ * sequence fills its slot.  The operation, masks, outputs written, workspace
+ * (attn_thd_workspace_size(batch, batch*seqlen_q, batch*seqlen_kv, hq, hkv,
+ * d)), errors and stream semantics are those of attn_fwd_thd / attn_bwd_thd.
+ * Extra error: ATTN_THD_EINVAL when batch*seqlen exceeds INT32_MAX or a
+ * 256-token strided tile spans more than 2 GiB; ATTN_THD_EUNSUPPORTED for an
+ * unknown layout.
+ */
+enum { ATTN_THD_LAYOUT_BSHD = 1, ATTN_THD_LAYOUT_SBHD = 2 };   /* layout */
+
+attn_thd_status attn_fwd_batched(
+    const void* q, const void* k, const void* v, void* out, float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t layout,
+    int32_t batch, int32_t seqlen_q, int32_t seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+attn_thd_status attn_bwd_batched(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t layout,
+    int32_t batch, int32_t seqlen_q, int32_t seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Instrumented variants for benchmarks.  Same arguments and behaviour as
  * attn_fwd_thd / attn_bwd_thd, plus an array of caller-created HIP events
  * (hipEvent_t, passed as void*) that the call records on `stream`:

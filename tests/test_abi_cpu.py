@@ -104,3 +104,42 @@ def test_product_has_no_cpu_fallback():
     assert "oracle" not in src.replace("the CPU oracle", "")
     for f in os.listdir(os.path.join(ROOT, "bwd_thd_varlen_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "bwd_thd_varlen_amd", "csrc", f)).read()
+
+
+def test_bottom_right_mask_is_accepted(A):
+    # mask_type 2 passes validation: the call fails only at the missing workspace
+    assert fwd_call(A, mask_type=2) == 3
+
+
+def batched_fwd_call(A, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cu_seqlens_q=None,
+                cu_seqlens_kv=None, layout=2, batch=2, seqlen_q=8, seqlen_kv=8, hq=4, hkv=2,
+                d=64, scale=0.125, mask_type=1, dtype=0, workspace=None, workspace_bytes=0,
+                stream=None)
+    args.update(over)
+    return A.attn_fwd_batched(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(), 3),                                # NULL real lengths are fine (full slots)
+    (dict(layout=1), 3),
+    (dict(layout=0), 2),                        # THD goes through attn_fwd_thd
+    (dict(layout=3), 2),
+    (dict(seqlen_q=-1), 1),
+    (dict(batch=1 << 16, seqlen_q=1 << 16), 1),  # batch * seqlen above INT32_MAX
+    (dict(batch=1 << 15, hq=64, hkv=8, d=128), 1),  # a strided 256-token tile spans > 2 GiB
+    (dict(hq=4, hkv=3), 1),
+    (dict(d=12), 2),
+])
+def test_batched_rejects_bad_host_arguments(A, over, code):
+    assert batched_fwd_call(A, **over) == code
+
+
+def test_batched_bwd_rejects_bad_host_arguments(A):
+    base = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                cu_seqlens_q=None, cu_seqlens_kv=None, layout=1, batch=2, seqlen_q=8,
+                seqlen_kv=8, hq=4, hkv=2, d=64, scale=0.125, mask_type=0, dtype=1,
+                workspace=None, workspace_bytes=0, stream=None)
+    assert A.attn_bwd_batched(**base) == 3
+    assert A.attn_bwd_batched(**dict(base, layout=5)) == 2
+    assert A.attn_bwd_batched(**dict(base, dq=None, workspace=FAKE, workspace_bytes=1 << 30)) == 1
