@@ -23,7 +23,14 @@ Prints ONE JSON line.  Besides the metric it carries
 Options: --gpus N (only 1 is supported: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --copy-calibration (adds a plain
 1 GiB device copy after the timed region, used to scale rocprofv3's
-FETCH_SIZE / WRITE_SIZE counters to bytes).
+FETCH_SIZE / WRITE_SIZE counters to bytes), --workload NAME:
+  throughput_65k        the headline configuration above (default)
+  sbhd_65k              sbhd [4096, 16, 64, 128] bf16 padding_causal, read in
+                        place by the batched entry points (same FLOP model)
+  chunked_bottom_right  THD query chunks of 2048 tokens (the last tokens of
+                        each context) against contexts U[2048, 8192] (65536
+                        key tokens), bottom-right causal; FLOPs counted on
+                        the exact number of visible (query, key) pairs
 """
 from __future__ import annotations
 
@@ -41,6 +48,25 @@ MFMA_PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
 METRIC = "fwd+bwd TFLOP/s (THD bf16 padding_causal, hq64/hkv8/d128) + % MFMA peak"
 PROFILES = os.path.join(ROOT, "profiles")
+
+WORKLOADS = {
+    "throughput_65k": dict(
+        layout="thd", metric=METRIC,
+        desc="throughput_65k: 65536 packed tokens, 16 sequences, lengths U[256,8192] seed 0 "
+             "padded to 64, hq=64 hkv=8 d=128, bf16, padding_causal, fwd+bwd"),
+    "sbhd_65k": dict(
+        layout="sbhd",
+        metric="fwd+bwd TFLOP/s (sbhd bf16 padding_causal, hq64/hkv8/d128) + % MFMA peak",
+        desc="sbhd_65k: sbhd [4096, 16, 64, 128] read in place, 16 full sequences, hq=64 "
+             "hkv=8 d=128, bf16, padding_causal, fwd+bwd"),
+    "chunked_bottom_right": dict(
+        layout="thd",
+        metric="fwd+bwd TFLOP/s (THD bf16 padding_causal_bottom_right, query chunks, "
+               "hq64/hkv8/d128) + % MFMA peak",
+        desc="chunked_bottom_right: 14 contexts U[2048,8192] seed 0 padded to 64 (65536 key "
+             "tokens), queries = last 2048 tokens of each, hq=64 hkv=8 d=128, bf16, "
+             "bottom-right causal, fwd+bwd; FLOPs on exact visible pairs"),
+}
 
 
 def log(*a):
@@ -68,10 +94,19 @@ def read_traffic(stage: str):
         return None
 
 
+def visible_pairs(lq: int, lk: int, causal) -> float:
+    """(query, key) pairs a FLOP model counts for one sequence: Lq*Lk, halved
+    for the top-left causal triangle (the headline metric's model), and the
+    exact count of pairs with key <= query + Lk - Lq for bottom-right."""
+    if causal == "bottom_right":
+        return float(sum(max(0, min(lk, i + lk - lq + 1)) for i in range(lq)))
+    return lq * lk / 2.0 if causal else float(lq * lk)
+
+
 def cpu_baseline(case, budget_s: float = 12.0):
     """The fp64 oracle, as it stands, on (sequence, KV group) units of the same
-    workload: the sequences closest to 2400 tokens first, KV groups 0, 1, ...
-    of each, until `budget_s` of CPU work has been spent."""
+    workload: the sequences closest to 2400 query tokens first, KV groups 0,
+    1, ... of each, until `budget_s` of CPU work has been spent."""
     import numpy as np
     import torch
 
@@ -82,21 +117,23 @@ def cpu_baseline(case, budget_s: float = 12.0):
     except Exception:
         cores = os.cpu_count()
     real = np.diff(case.cu_seqlens_q)
+    real_k = np.diff(case.cu_seqlens_kv)
     G = case.hq // case.hkv
     f64 = lambda t: t.to(torch.float64).numpy()
     flops, spent, units = 0.0, 0.0, []
     for b in np.argsort(np.abs(real - 2400), kind="stable"):
         L, oq = int(real[b]), int(case.cu_seqlens_q_padded[b])
+        Lk, ok = int(real_k[b]), int(case.cu_seqlens_kv_padded[b])
         for g in range(case.hkv):
             q = f64(case.q[oq:oq + L, g * G:(g + 1) * G])
-            k = f64(case.k[oq:oq + L, g:g + 1])
-            v = f64(case.v[oq:oq + L, g:g + 1])
+            k = f64(case.k[ok:ok + Lk, g:g + 1])
+            v = f64(case.v[ok:ok + Lk, g:g + 1])
             do = f64(case.dout[oq:oq + L, g * G:(g + 1) * G])
             t0 = time.perf_counter()
-            oracle.attn_fwd_seq(q, k, v, case.scale, True)
-            oracle.attn_bwd_seq(q, k, v, do, case.scale, True)
+            oracle.attn_fwd_seq(q, k, v, case.scale, case.causal)
+            oracle.attn_bwd_seq(q, k, v, do, case.scale, case.causal)
             spent += time.perf_counter() - t0
-            flops += 3.5 * 4.0 * case.d * G * L * L / 2.0
+            flops += 3.5 * 4.0 * case.d * G * visible_pairs(L, Lk, case.causal)
             units.append((int(b), L))
             if spent >= budget_s:
                 break
@@ -108,7 +145,7 @@ def cpu_baseline(case, budget_s: float = 12.0):
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": (f"fp64 numpy oracle fwd+bwd of {desc} ({G} query heads per group) of the "
-                       f"same workload, {spent:.1f} s; FLOPs by the metric's causal model")}
+                       f"same workload, {spent:.1f} s; FLOPs by the workload's pair model")}
 
 
 def main():
@@ -118,6 +155,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--workload", default="throughput_65k", choices=sorted(WORKLOADS))
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -126,6 +164,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import bwd_thd_varlen_amd as A
@@ -134,25 +173,43 @@ def main():
     A.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log("[bench] generating the 65536-token workload")
-    case = workloads.throughput_65k()
-    f_fwd, f_bwd = workloads.causal_flops(case.cu_seqlens_q, case.cu_seqlens_kv, case.hq, case.d,
-                                          case.causal)
+    wl = WORKLOADS[args.workload]
+    log(f"[bench] generating the {args.workload} workload")
+    case = getattr(workloads, args.workload)()
+    pairs = sum(visible_pairs(int(a), int(b_), case.causal)
+                for a, b_ in zip(np.diff(case.cu_seqlens_q), np.diff(case.cu_seqlens_kv)))
+    f_fwd = 4.0 * case.d * case.hq * pairs
+    f_bwd = 2.5 * f_fwd
     q, k, v, do = (t.to(dev) for t in (case.q, case.k, case.v, case.dout))
     cu = lambda a: torch.as_tensor(a, dtype=torch.int32, device=dev)
     cq, ck = cu(case.cu_seqlens_q), cu(case.cu_seqlens_kv)
     cqp, ckp = cu(case.cu_seqlens_q_padded), cu(case.cu_seqlens_kv_padded)
-    out, lse = torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(A.workspace_size(case.batch, q.shape[0], k.shape[0], case.hq, case.hkv,
-                                      case.d), dtype=torch.uint8, device=dev)
-    kw = dict(cu_seqlens_q_padded=cqp, cu_seqlens_kv_padded=ckp,
-              max_seqlen_q=case.max_seqlen_q, max_seqlen_kv=case.max_seqlen_kv,
-              attn_mask_type="padding_causal", softmax_scale=case.scale, workspace=ws)
+    if wl["layout"] == "sbhd":
+        # the THD rows b*S + i laid out as sbhd [S, B, h, d] (outside the timed region)
+        S, B = case.max_seqlen_q, case.batch
+        sb = lambda t: t.view(B, S, *t.shape[1:]).transpose(0, 1).contiguous()
+        q, k, v, do = sb(q), sb(k), sb(v), sb(do)
+    out, dq, dk, dv = (torch.empty_like(t) for t in (q, q, k, v))
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    tq, tk = case.q.shape[0], case.k.shape[0]
+    ws = torch.empty(A.workspace_size(case.batch, tq, tk, case.hq, case.hkv, case.d),
+                     dtype=torch.uint8, device=dev)
 
-    def step(ev_f=None, ev_b=None):
-        A.fwd(q, k, v, cq, ck, out=out, lse=lse, events=ev_f, **kw)
-        A.bwd(q, k, v, out, do, lse, cq, ck, dq=dq, dk=dk, dv=dv, events=ev_b, **kw)
+    if wl["layout"] == "sbhd":
+        bkw = dict(layout="sbhd", cu_seqlens_q=cq, cu_seqlens_kv=ck,
+                   attn_mask_type=case.mask_type, softmax_scale=case.scale, workspace=ws)
+
+        def step(ev_f=None, ev_b=None):
+            A.fwd_batched(q, k, v, out=out, lse=lse, events=ev_f, **bkw)
+            A.bwd_batched(q, k, v, out, do, lse, dq=dq, dk=dk, dv=dv, events=ev_b, **bkw)
+    else:
+        kw = dict(cu_seqlens_q_padded=cqp, cu_seqlens_kv_padded=ckp,
+                  max_seqlen_q=case.max_seqlen_q, max_seqlen_kv=case.max_seqlen_kv,
+                  attn_mask_type=case.mask_type, softmax_scale=case.scale, workspace=ws)
+
+        def step(ev_f=None, ev_b=None):
+            A.fwd(q, k, v, cq, ck, out=out, lse=lse, events=ev_f, **kw)
+            A.bwd(q, k, v, out, do, lse, cq, ck, dq=dq, dk=dk, dv=dv, events=ev_b, **kw)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -188,7 +245,9 @@ def main():
     achieved = flops / (avg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
-                "traffic": read_traffic(kname), "kernel": kname,
+                # counter summaries are taken on the headline workload only
+                "traffic": read_traffic(kname) if args.workload == "throughput_65k" else None,
+                "kernel": kname,
                 "avg_launch_ms": round(avg[dom], 4)}
 
     if args.copy_calibration:
@@ -205,15 +264,14 @@ def main():
         cpu = cpu_baseline(case)
 
     rec = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": wl["metric"], "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "throughput_65k: 65536 packed tokens, 16 sequences, lengths "
-                               "U[256,8192] seed 0 padded to 64, hq=64 hkv=8 d=128, bf16, "
-                               "padding_causal, fwd+bwd",
-                   "tokens": int(q.shape[0]), "sequences": case.batch, "hq": case.hq,
-                   "hkv": case.hkv, "d": case.d, "max_seqlen": case.max_seqlen_q,
+        "config": {"workload": wl["desc"],
+                   "tokens_q": int(tq), "tokens_kv": int(tk), "sequences": case.batch,
+                   "hq": case.hq, "hkv": case.hkv, "d": case.d,
+                   "max_seqlen_q": case.max_seqlen_q, "max_seqlen_kv": case.max_seqlen_kv,
                    "flops_per_step": f_fwd + f_bwd},
         "pct_mfma_peak": round(100.0 * value / MFMA_PEAK_BF16_TFLOPS, 2),
         "stages_ms": {k_: round(v_, 4) for k_, v_ in avg.items()},

@@ -102,6 +102,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_batched.restype = ctypes.c_int
         L.attn_bwd_batched.argtypes = _BBWD_ARGS
         L.attn_bwd_batched.restype = ctypes.c_int
+        L.attn_fwd_batched_timed.argtypes = _BFWD_ARGS + [ctypes.POINTER(_P), _I]
+        L.attn_fwd_batched_timed.restype = ctypes.c_int
+        L.attn_bwd_batched_timed.argtypes = _BBWD_ARGS + [ctypes.POINTER(_P), _I]
+        L.attn_bwd_batched_timed.restype = ctypes.c_int
         L.attn_thd_status_string.argtypes = [_I]
         L.attn_thd_status_string.restype = ctypes.c_char_p
         L.attn_thd_read_device_status.argtypes = [_P, _P, ctypes.POINTER(_I)]
@@ -162,6 +166,16 @@ def attn_bwd_batched(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqle
                                       cu_seqlens_kv, layout, batch, seqlen_q, seqlen_kv, hq, hkv,
                                       d, scale, mask_type, dtype, workspace, workspace_bytes,
                                       stream))
+
+
+def attn_fwd_batched_timed(*args, events, n_events) -> int:
+    """attn_fwd_batched plus per-stage HIP events (see StageEvents)."""
+    return int(lib().attn_fwd_batched_timed(*args, events, n_events))
+
+
+def attn_bwd_batched_timed(*args, events, n_events) -> int:
+    """attn_bwd_batched plus per-stage HIP events (see StageEvents)."""
+    return int(lib().attn_bwd_batched_timed(*args, events, n_events))
 
 
 def attn_fwd_thd_timed(*args, events, n_events) -> int:
@@ -390,8 +404,8 @@ def fwd_batched(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str =
                 cu_seqlens_q: Optional[torch.Tensor] = None,
                 cu_seqlens_kv: Optional[torch.Tensor] = None, attn_mask_type: str = "padding",
                 softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
-                ) -> Tuple[torch.Tensor, torch.Tensor]:
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                events: Optional["StageEvents"] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward on bshd ``[b, s, h, d]`` or sbhd ``[s, b, h, d]`` tensors, read in place.
 
     cu_seqlens_* (int32 [b+1]) give real lengths within the slots (None: full).
@@ -421,11 +435,14 @@ def fwd_batched(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: str =
     if out.shape != q.shape or tuple(lse.shape) != _lse_shape(layout, b, sq, hq):
         raise AttnError("out or lse has the wrong shape")
     ws = _workspace(workspace, b, b * sq, b * skv, hq, hkv, d, dev)
-    st = attn_fwd_batched(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          lse.data_ptr(), _ptr(cq), _ptr(ck), LAYOUTS[layout], b, sq, skv, hq,
-                          hkv, d, scale, _MASK[attn_mask_type], _DTYPE[q.dtype], ws.data_ptr(),
-                          ws.numel() * ws.element_size(),
-                          torch.cuda.current_stream(dev).cuda_stream)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), _ptr(cq),
+            _ptr(ck), LAYOUTS[layout], b, sq, skv, hq, hkv, d, scale, _MASK[attn_mask_type],
+            _DTYPE[q.dtype], ws.data_ptr(), ws.numel() * ws.element_size(),
+            torch.cuda.current_stream(dev).cuda_stream)
+    if events is None:
+        st = attn_fwd_batched(*args)
+    else:
+        st = attn_fwd_batched_timed(*args, events=events.ptr, n_events=events.n)
     _check(st, "attn_fwd_batched")
     return out, lse
 
@@ -436,7 +453,7 @@ def bwd_batched(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
                 cu_seqlens_kv: Optional[torch.Tensor] = None, attn_mask_type: str = "padding",
                 softmax_scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
                 dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None
+                workspace: Optional[torch.Tensor] = None, events: Optional["StageEvents"] = None
                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Backward on bshd / sbhd tensors (arguments as ``fwd_batched``); returns (dq, dk, dv)."""
     dev = q.device
@@ -465,11 +482,14 @@ def bwd_batched(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
     _need(dk, "dk", q.dtype, dev)
     _need(dv, "dv", q.dtype, dev)
     ws = _workspace(workspace, b, b * sq, b * skv, hq, hkv, d, dev)
-    st = attn_bwd_batched(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                          dv.data_ptr(), _ptr(cq), _ptr(ck), LAYOUTS[layout], b, sq, skv, hq,
-                          hkv, d, scale, _MASK[attn_mask_type], _DTYPE[q.dtype], ws.data_ptr(),
-                          ws.numel() * ws.element_size(),
-                          torch.cuda.current_stream(dev).cuda_stream)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(cq), _ptr(ck),
+            LAYOUTS[layout], b, sq, skv, hq, hkv, d, scale, _MASK[attn_mask_type],
+            _DTYPE[q.dtype], ws.data_ptr(), ws.numel() * ws.element_size(),
+            torch.cuda.current_stream(dev).cuda_stream)
+    if events is None:
+        st = attn_bwd_batched(*args)
+    else:
+        st = attn_bwd_batched_timed(*args, events=events.ptr, n_events=events.n)
     _check(st, "attn_bwd_batched")
     return dq, dk, dv

@@ -374,19 +374,48 @@ static attn_thd_status batched_geom(int32_t layout, int32_t batch, int32_t seqle
   return ATTN_THD_OK;
 }
 
+static attn_thd_status fwd_batched(const void* q, const void* k, const void* v, void* out,
+                                   float* lse, const int32_t* cu_q, const int32_t* cu_kv,
+                                   int32_t layout, int32_t batch, int32_t seqlen_q,
+                                   int32_t seqlen_kv, int32_t hq, int32_t hkv, int32_t d,
+                                   float scale, int32_t mask_type, int32_t dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* events,
+                                   int32_t n_events) {
+  Geom geo;
+  int32_t total_q, total_kv;
+  attn_thd_status st = batched_geom(layout, batch, seqlen_q, seqlen_kv, geo, total_q, total_kv);
+  if (st != ATTN_THD_OK) return st;
+  return fwd_impl(q, k, v, out, lse, cu_q, cu_kv, nullptr, nullptr, batch, total_q, total_kv, hq,
+                  hkv, d, scale, mask_type, dtype, workspace, workspace_bytes, stream, events,
+                  n_events, geo);
+}
+
+static attn_thd_status bwd_batched(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, void* dq, void* dk,
+                                   void* dv, const int32_t* cu_q, const int32_t* cu_kv,
+                                   int32_t layout, int32_t batch, int32_t seqlen_q,
+                                   int32_t seqlen_kv, int32_t hq, int32_t hkv, int32_t d,
+                                   float scale, int32_t mask_type, int32_t dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* events,
+                                   int32_t n_events) {
+  Geom geo;
+  int32_t total_q, total_kv;
+  attn_thd_status st = batched_geom(layout, batch, seqlen_q, seqlen_kv, geo, total_q, total_kv);
+  if (st != ATTN_THD_OK) return st;
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_q, cu_kv, nullptr, nullptr, batch,
+                  total_q, total_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
+                  workspace_bytes, stream, events, n_events, geo);
+}
+
 attn_thd_status attn_fwd_batched(const void* q, const void* k, const void* v, void* out,
                                  float* lse, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_kv, int32_t layout, int32_t batch,
                                  int32_t seqlen_q, int32_t seqlen_kv, int32_t hq, int32_t hkv,
                                  int32_t d, float scale, int32_t mask_type, int32_t dtype,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  Geom geo;
-  int32_t total_q, total_kv;
-  attn_thd_status st = batched_geom(layout, batch, seqlen_q, seqlen_kv, geo, total_q, total_kv);
-  if (st != ATTN_THD_OK) return st;
-  return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, nullptr, nullptr, batch,
-                  total_q, total_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
-                  workspace_bytes, stream, nullptr, 0, geo);
+  return fwd_batched(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, layout, batch, seqlen_q,
+                     seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace, workspace_bytes,
+                     stream, nullptr, 0);
 }
 
 attn_thd_status attn_bwd_batched(const void* q, const void* k, const void* v, const void* out,
@@ -396,13 +425,38 @@ attn_thd_status attn_bwd_batched(const void* q, const void* k, const void* v, co
                                  int32_t seqlen_kv, int32_t hq, int32_t hkv, int32_t d,
                                  float scale, int32_t mask_type, int32_t dtype, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  Geom geo;
-  int32_t total_q, total_kv;
-  attn_thd_status st = batched_geom(layout, batch, seqlen_q, seqlen_kv, geo, total_q, total_kv);
-  if (st != ATTN_THD_OK) return st;
-  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv, nullptr,
-                  nullptr, batch, total_q, total_kv, hq, hkv, d, scale, mask_type, dtype,
-                  workspace, workspace_bytes, stream, nullptr, 0, geo);
+  return bwd_batched(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv, layout,
+                     batch, seqlen_q, seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
+                     workspace_bytes, stream, nullptr, 0);
+}
+
+attn_thd_status attn_fwd_batched_timed(const void* q, const void* k, const void* v, void* out,
+                                       float* lse, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_kv, int32_t layout,
+                                       int32_t batch, int32_t seqlen_q, int32_t seqlen_kv,
+                                       int32_t hq, int32_t hkv, int32_t d, float scale,
+                                       int32_t mask_type, int32_t dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream, void* const* events,
+                                       int32_t n_events) {
+  if (!events) return ATTN_THD_EINVAL;
+  return fwd_batched(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, layout, batch, seqlen_q,
+                     seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace, workspace_bytes,
+                     stream, events, n_events);
+}
+
+attn_thd_status attn_bwd_batched_timed(const void* q, const void* k, const void* v,
+                                       const void* out, const void* dout, const float* lse,
+                                       void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_kv, int32_t layout,
+                                       int32_t batch, int32_t seqlen_q, int32_t seqlen_kv,
+                                       int32_t hq, int32_t hkv, int32_t d, float scale,
+                                       int32_t mask_type, int32_t dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream, void* const* events,
+                                       int32_t n_events) {
+  if (!events) return ATTN_THD_EINVAL;
+  return bwd_batched(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv, layout,
+                     batch, seqlen_q, seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
+                     workspace_bytes, stream, events, n_events);
 }
 
 const char* attn_thd_status_string(int32_t status) {

@@ -73,6 +73,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   const int kend = CAUSAL ? max(0, min(s.lk, q_end + diag)) : s.lk;
   const int nsteps = (kend + KS - 1) / KS;
   const float sl2e = p.scale_log2e;
+  // the wave's queries and this lane's query shifted onto the key axis
+  const int wq_lo_k = wq_lo + diag, wq_hi_k = wq_hi + diag, qi_k = qi + diag;
 
   DmaK dma_k;
   DmaV dma_v;
@@ -114,8 +116,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     const RowReader<LV> rv(sV[step & 1], lane);
     const TrReader<LK> trk(sK[step & 1], lane);
     const int n0 = step * KS;
-    if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi + diag)) {
-      const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo + diag);
+    if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi_k)) {
+      const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo_k);
       // the step's two 32-key halves one after the other (S, dP -> dS -> dQ
       // part), so that only one half's score tiles are live at a time
 #pragma unroll
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
           float pr = fast_exp2(__builtin_fmaf(sc[r], sl2e, -lse2));
           if (need_mask) {
             const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (j > qi + diag) pr = 0.f;
+            if (j > qi_k) pr = 0.f;
           }
           sc[r] = pr * (dp[r] - dlt);     // dS
         }
@@ -226,6 +228,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   // j <= i + diag), times the heads of the group
   const int diag = CAUSAL ? uniform(causal_diag(s, p.causal_br)) : 0;
   const int m_first = CAUSAL ? max(0, n0 - diag) / BM : 0;
+  // the wave's keys and this lane's key shifted onto the query axis
+  // (query i sees key j iff i >= j - diag)
+  const int wk_lo_q = wk_lo - diag, wk_hi_q = wk_hi - diag, kj_q = kj - diag;
   const int m_last = (s.lq + BM - 1) / BM;
   const int nm = m_last > m_first ? m_last - m_first : 0;
   const int nsteps = nm * p.group;
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     const int hg = step / nm;
     const int i0 = (m_first + (step - hg * nm)) * BM;
     // waves with no real key, or whose keys all follow every query, idle
-    if (wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 + diag < wk_lo)) {
+    if (wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q)) {
       f32x16 sc[NIB], dp[NIB];
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           dp[ib] = Mfma<DT>::mma(rdo.read(ib, t), vop, dp[ib]);
         }
       }
-      const bool need_mask = CAUSAL && (i0 + diag < wk_hi);
+      const bool need_mask = CAUSAL && (i0 < wk_hi_q);
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * q4 + c;
             float pr = fast_exp2(__builtin_fmaf(sc[ib][r], sl2e, -l4[c]));
-            if (need_mask && kj > i0 + ibase + c + diag) pr = 0.f;
+            if (need_mask && kj_q > i0 + ibase + c) pr = 0.f;
             sc[ib][r] = pr;
             dp[ib][r] = pr * (dp[ib][r] - d4[c]);
           }

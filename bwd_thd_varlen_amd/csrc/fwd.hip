@@ -77,6 +77,8 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   const int kend = CAUSAL ? max(0, min(s.lk, q_end + diag)) : s.lk;
   const int nsteps = (kend + KS - 1) / KS;
   const float sl2e = p.scale_log2e;
+  // the wave's queries and this lane's query shifted onto the key axis
+  const int wq_lo_k = wq_lo + diag, wq_hi_k = wq_hi + diag, qi_k = qi + diag;
 
   DmaK dma_k;
   DmaV dma_v;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
     if (step + 1 < nsteps) issue(step + 1, nK, nV);
     const int n0 = step * KS;
     // waves with no real query, or whose queries all precede the step, idle
-    if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi + diag)) {
+    if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi_k)) {
       f32x16 sc[NKB];
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2) {
@@ -120,14 +122,14 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
           sc[kb2] = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
       }
       pipeline_lds_mfma<NKB * NT, 1>();
-      const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo + diag);
+      const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo_k);
       if (need_mask) {
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (j >= kend || (CAUSAL && j > qi + diag)) sc[kb2][r] = -__builtin_inff();
+            if (j >= kend || (CAUSAL && j > qi_k)) sc[kb2][r] = -__builtin_inff();
           }
       }
       const float mx = max_halves(tree_max(sc)) * sl2e;

@@ -184,7 +184,8 @@ attn_thd_status attn_bwd_batched(
 
 /*
  * Instrumented variants for benchmarks.  Same arguments and behaviour as
- * attn_fwd_thd / attn_bwd_thd, plus an array of caller-created HIP events
+ * attn_fwd_thd / attn_bwd_thd (attn_fwd_batched / attn_bwd_batched for the
+ * *_batched_timed pair), plus an array of caller-created HIP events
  * (hipEvent_t, passed as void*) that the call records on `stream`:
  * events[i] just before stage i is launched and events[n_events-1] after the
  * last stage, so hipEventElapsedTime(events[i], events[i+1]) is stage i.
@@ -211,6 +212,23 @@ attn_thd_status attn_bwd_thd_timed(
     const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
     int32_t batch, int32_t total_q, int32_t total_kv,
     int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
+attn_thd_status attn_fwd_batched_timed(
+    const void* q, const void* k, const void* v, void* out, float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t layout,
+    int32_t batch, int32_t seqlen_q, int32_t seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
+attn_thd_status attn_bwd_batched_timed(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t layout,
+    int32_t batch, int32_t seqlen_q, int32_t seqlen_kv,
     int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int32_t n_events);

@@ -249,6 +249,46 @@ def throughput_65k(seed: int = 0, hq: int = 64, hkv: int = 8, d: int = 128,
                 max_seqlen_kv=max(real))
 
 
+def sbhd_65k(seed: int = 0, S: int = 4096, B: int = 16, hq: int = 64, hkv: int = 8,
+             d: int = 128) -> Case:
+    """16 full sequences of 4096 tokens (65536 tokens), hq=64 hkv=8 d=128, bf16,
+    padding_causal, in THD form (token i of sequence b is row b*S + i); the
+    benchmark lays it out as sbhd [S, B, h, d] on the device."""
+    rng = np.random.default_rng(seed)
+    T = S * B
+    q = _normal(rng, (T, hq, d), BF16)
+    k = _normal(rng, (T, hkv, d), BF16)
+    v = _normal(rng, (T, hkv, d), BF16)
+    dout = _normal(rng, (T, hq, d), BF16)
+    cu = _cu([S] * B)
+    return Case(name="sbhd_65k", q=q, k=k, v=v, dout=dout, cu_seqlens_q=cu,
+                cu_seqlens_kv=cu.copy(), cu_seqlens_q_padded=cu.copy(),
+                cu_seqlens_kv_padded=cu.copy(), scale=1.0 / math.sqrt(d), causal=True,
+                dtype=BF16, max_seqlen_q=S, max_seqlen_kv=S)
+
+
+def chunked_bottom_right(seed: int = 0, chunk: int = 2048, total_kv: int = 65536,
+                         lo: int = 2048, hi: int = 8192, hq: int = 64, hkv: int = 8,
+                         d: int = 128) -> Case:
+    """Query chunks against longer contexts, bottom-right causal: context
+    lengths U[lo, hi] (seed) padded to 64 until total_kv tokens; each
+    sequence's queries are its last min(chunk, Lk) tokens.  bf16, hq=64 hkv=8
+    d=128."""
+    real_k, pad_k, rng = throughput_lengths(seed, total=total_kv, lo=lo, hi=hi)
+    real_q = [min(chunk, L) for L in real_k]
+    pad_q = [int(math.ceil(L / 64) * 64) for L in real_q]
+    Tq, Tk = sum(pad_q), sum(pad_k)
+    q = _normal(rng, (Tq, hq, d), BF16)
+    k = _normal(rng, (Tk, hkv, d), BF16)
+    v = _normal(rng, (Tk, hkv, d), BF16)
+    dout = _normal(rng, (Tq, hq, d), BF16)
+    return Case(name="chunked_bottom_right", q=q, k=k, v=v, dout=dout,
+                cu_seqlens_q=_cu(real_q), cu_seqlens_kv=_cu(real_k),
+                cu_seqlens_q_padded=_cu(pad_q), cu_seqlens_kv_padded=_cu(pad_k),
+                scale=1.0 / math.sqrt(d), causal="bottom_right", dtype=BF16,
+                max_seqlen_q=max(real_q), max_seqlen_kv=max(real_k))
+
+
 def causal_flops(cu_q: np.ndarray, cu_kv: np.ndarray, hq: int, d: int, causal: bool):
     """FLOP model of the headline metric: 4*d*hq*sum(Lq*Lkv), halved when causal.
 
