@@ -5,7 +5,7 @@ backward.  Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
 CPU-baseline leg may import it; the GPU library never does.
 """
 from .attention import (allowed_mask, attn_bwd, attn_bwd_seq, attn_fwd, attn_fwd_seq,
-                        sequence_slots)
+                        merge_partials, sequence_slots)
 
 __all__ = ["allowed_mask", "attn_bwd", "attn_bwd_seq", "attn_fwd", "attn_fwd_seq",
-           "sequence_slots"]
+           "merge_partials", "sequence_slots"]

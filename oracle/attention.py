@@ -49,7 +49,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["sequence_slots", "attn_fwd", "attn_bwd", "attn_fwd_seq", "attn_bwd_seq",
-           "allowed_mask"]
+           "allowed_mask", "merge_partials"]
 
 
 def sequence_slots(cu_seqlens: np.ndarray, cu_seqlens_padded: Optional[np.ndarray]):
@@ -69,7 +69,7 @@ def sequence_slots(cu_seqlens: np.ndarray, cu_seqlens_padded: Optional[np.ndarra
     return [(int(o), int(L)) for o, L in zip(offsets, lengths)]
 
 
-def allowed_mask(lq: int, lk: int, causal) -> np.ndarray:
+def allowed_mask(lq: int, lk: int, causal, shift: Optional[int] = None) -> np.ndarray:
     """Boolean [lq, lk]: key j is visible to query i.
 
     ``padding`` (causal False): all real keys of the sequence ([TE-2448],
@@ -80,12 +80,20 @@ def allowed_mask(lq: int, lk: int, causal) -> np.ndarray:
     lq == lk both alignments agree (the pages use causal only there, and do
     not name the bottom-right variant: its definition here is the plain
     reading of aligning the two sequences at their ends).
+
+    ``shift`` (causal True only) gives the diagonal directly: j <= i + shift.
+    A chunk of queries at sequence positions q0 + i and a chunk of keys at
+    k0 + j see each other iff k0 + j <= q0 + i, i.e. shift = q0 - k0 (the
+    causal rule of the whole sequence restricted to the two chunks).
     """
     m = np.ones((lq, lk), dtype=bool)
     if causal:
         if causal not in (True, "top_left", "bottom_right"):
             raise ValueError(f"causal must be False, True, 'top_left' or 'bottom_right', not {causal!r}")
-        shift = (lk - lq) if causal == "bottom_right" else 0
+        if shift is None:
+            shift = (lk - lq) if causal == "bottom_right" else 0
+        elif causal == "bottom_right":
+            raise ValueError("an explicit shift goes with causal=True")
         i = np.arange(lq)[:, None]
         j = np.arange(lk)[None, :]
         m &= j <= i + shift
@@ -110,7 +118,8 @@ def _softmax_rows(s: np.ndarray, allowed: np.ndarray):
     return p, lse
 
 
-def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal):
+def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal,
+                 shift: Optional[int] = None):
     """Forward of one sequence, all heads: O = softmax(scale * Q K^T + mask) V.
 
     q: [Lq, hq, d]; k, v: [Lk, hkv, d] (real rows only, float64).
@@ -123,7 +132,7 @@ def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
     G = hq // hkv
     out = np.zeros((lq, hq, d))
     lse = np.full((lq, hq), -np.inf)
-    allowed = allowed_mask(lq, lk, causal)
+    allowed = allowed_mask(lq, lk, causal, shift)
     for h in range(hq):
         g = h // G
         s = scale * (q[:, h, :] @ k[:, g, :].T)
@@ -134,7 +143,7 @@ def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
 
 
 def attn_bwd_seq(q, k, v, dout, scale: float, causal, out=None, lse=None,
-                 mode: str = "definition"):
+                 mode: str = "definition", shift: Optional[int] = None):
     """Backward of one sequence, all heads: dQ, dK, dV of l = sum(dO * O).
 
     ``definition`` (default): the exact gradient, with P recomputed from q,k
@@ -153,7 +162,7 @@ def attn_bwd_seq(q, k, v, dout, scale: float, causal, out=None, lse=None,
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    allowed = allowed_mask(lq, lk, causal)
+    allowed = allowed_mask(lq, lk, causal, shift)
     for h in range(hq):
         g = h // G
         Q, K, V, dO = q[:, h, :], k[:, g, :], v[:, g, :], dout[:, h, :]
@@ -182,9 +191,18 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def _shifts(q_pos0, kv_pos0, n):
+    """Per-sequence diagonal shift q_pos0[b] - kv_pos0[b] (None: derived from the mask)."""
+    if q_pos0 is None and kv_pos0 is None:
+        return [None] * n
+    qp = np.zeros(n, np.int64) if q_pos0 is None else np.asarray(q_pos0, np.int64)
+    kp = np.zeros(n, np.int64) if kv_pos0 is None else np.asarray(kv_pos0, np.int64)
+    return [int(a - b) for a, b in zip(qp, kp)]
+
+
 def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
-             cu_seqlens_kv_padded=None, scale: float = None, causal=False
-             ) -> Tuple[np.ndarray, np.ndarray]:
+             cu_seqlens_kv_padded=None, scale: float = None, causal=False,
+             q_pos0=None, kv_pos0=None) -> Tuple[np.ndarray, np.ndarray]:
     """Forward over the packed THD tensors.
 
     q: [Tq, hq, d], k, v: [Tkv, hkv, d].  Returns out [Tq, hq, d] (float64)
@@ -192,6 +210,10 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
     out = 0 and lse = -inf; the output keeps the padded layout ([TE-2892]
     "Expected Behavior", item 3).  ``scale`` defaults to 1/sqrt(d)
     ([TE-3216] fp32_reference, [TE-2448] comment's softmax_scale).
+
+    ``q_pos0`` / ``kv_pos0`` (per sequence, with causal True): the slots hold
+    chunks of longer sequences whose first real tokens sit at these positions;
+    the causal rule is applied to the positions (see ``allowed_mask``).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     Tq, hq, d = q.shape
@@ -203,10 +225,11 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
     lse = np.full((Tq, hq), -np.inf)
     qs = sequence_slots(cu_seqlens_q, cu_seqlens_q_padded)
     ks = sequence_slots(cu_seqlens_kv, cu_seqlens_kv_padded)
-    for (oq, lq), (ok, lk) in zip(qs, ks):
+    shifts = _shifts(q_pos0, kv_pos0, len(qs))
+    for (oq, lq), (ok, lk), sh in zip(qs, ks, shifts):
         if lq == 0:
             continue
-        o_b, l_b = attn_fwd_seq(q[oq:oq + lq], k[ok:ok + lk], v[ok:ok + lk], scale, causal)
+        o_b, l_b = attn_fwd_seq(q[oq:oq + lq], k[ok:ok + lk], v[ok:ok + lk], scale, causal, sh)
         out[oq:oq + lq] = o_b
         lse[oq:oq + lq] = l_b
     return out, lse
@@ -214,7 +237,7 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
 
 def attn_bwd(q, k, v, dout, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
              cu_seqlens_kv_padded=None, scale: float = None, causal=False,
-             out=None, lse=None, mode: str = "definition"):
+             out=None, lse=None, mode: str = "definition", q_pos0=None, kv_pos0=None):
     """Backward over the packed THD tensors: (dq, dk, dv), float64, padded layout.
 
     Rows outside the real ranges are exactly 0; so is every KV row of a
@@ -230,11 +253,33 @@ def attn_bwd(q, k, v, dout, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=Non
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     qs = sequence_slots(cu_seqlens_q, cu_seqlens_q_padded)
     ks = sequence_slots(cu_seqlens_kv, cu_seqlens_kv_padded)
-    for (oq, lq), (ok, lk) in zip(qs, ks):
+    shifts = _shifts(q_pos0, kv_pos0, len(qs))
+    for (oq, lq), (ok, lk), sh in zip(qs, ks, shifts):
         if lq == 0 or lk == 0:
             continue
         sq, sk = slice(oq, oq + lq), slice(ok, ok + lk)
         r = attn_bwd_seq(q[sq], k[sk], v[sk], dout[sq], scale, causal,
-                         None if out is None else out[sq], None if lse is None else lse[sq], mode)
+                         None if out is None else out[sq], None if lse is None else lse[sq], mode,
+                         sh)
         dq[sq], dk[sk], dv[sk] = r
     return dq, dk, dv
+
+
+def merge_partials(out_a, lse_a, out_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax over the union of two disjoint key sets from the two partial results.
+
+    With P_a = exp(S - LSE_a) over set A (so that O_a = P_a V_A) and likewise
+    for B, the softmax over A u B has LSE = ln(exp(LSE_a) + exp(LSE_b)) and
+    O = exp(LSE_a - LSE) O_a + exp(LSE_b - LSE) O_b.  A side with LSE = -inf
+    (no key) has weight 0; if both do, O = 0 and LSE = -inf.
+    out_*: [T, h, d], lse_*: [T, h] (float64).
+    """
+    la, lb = _f64(lse_a), _f64(lse_b)
+    oa, ob = _f64(out_a), _f64(out_b)
+    lse = np.logaddexp(la, lb)                 # -inf when both are -inf
+    fin = np.isfinite(lse)
+    safe = np.where(fin, lse, 0.0)
+    wa = np.where(fin, np.exp(la - safe), 0.0)  # exp(-inf) = 0 for an empty side
+    wb = np.where(fin, np.exp(lb - safe), 0.0)
+    out = wa[..., None] * oa + wb[..., None] * ob
+    return out, lse

@@ -417,3 +417,104 @@ def test_te2448_comment_dk_max_magnitude():
     m = float(np.abs(dk).max())
     lo, hi = gold["range"]
     assert lo <= m <= hi, m
+
+
+# ---------------------------------------------------------------- chunked (context-parallel) form
+from oracle import merge_partials  # noqa: E402
+
+
+def _chunk_rows(lengths, cuts):
+    """Per sequence, the [start, end) of each chunk given interior cut points."""
+    return [list(zip([0] + c, c + [L])) for L, c in zip(lengths, cuts)]
+
+
+def _gather(x, offs, ranges):
+    """Rows of chunk `ranges[b]` of every sequence b, packed (THD, no padding)."""
+    return np.concatenate([x[o + a:o + b] for o, (a, b) in zip(offs, ranges)], axis=0)
+
+
+def _cu_of(ranges):
+    return np.concatenate([[0], np.cumsum([b - a for a, b in ranges])]).astype(np.int32)
+
+
+def test_chunked_causal_forward_merge_and_backward_equal_the_whole():
+    """Queries and keys of every sequence cut into uneven chunks at sequence
+    positions q0/k0: the causal rule on positions per chunk pair, partial (O, LSE)
+    merged over key chunks, equals attention over the whole sequences; the
+    backward of every chunk pair with the whole O and LSE sums to the whole
+    gradients (dQ over key chunks, dK/dV over query chunks)."""
+    rng = np.random.default_rng(17)
+    L = [13, 7, 20]
+    hq, hkv, d, sc = 4, 2, 8, 0.35
+    T = sum(L)
+    offs = np.concatenate([[0], np.cumsum(L)])[:-1]
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    q, dout = rng.standard_normal((T, hq, d)), rng.standard_normal((T, hq, d))
+    k, v = rng.standard_normal((T, hkv, d)), rng.standard_normal((T, hkv, d))
+    o_full, l_full = attn_fwd(q, k, v, cu, cu, scale=sc, causal=True)
+    g_full = attn_bwd(q, k, v, dout, cu, cu, scale=sc, causal=True)
+    qch = _chunk_rows(L, [[5], [3], [8, 9]])            # 2, 2, 3 query chunks
+    kch = _chunk_rows(L, [[4, 11], [6], [2, 15]])        # 3, 2, 3 key chunks
+    nq = max(len(c) for c in qch)
+    nk = max(len(c) for c in kch)
+    pick = lambda ch, i: [c[i] if i < len(c) else (c[-1][1], c[-1][1]) for c in ch]
+    dq = np.zeros_like(q)
+    dk, dv = np.zeros_like(k), np.zeros_like(v)
+    for iq in range(nq):
+        qr = pick(qch, iq)
+        qq, qdo = _gather(q, offs, qr), _gather(dout, offs, qr)
+        cq = _cu_of(qr)
+        o_glob, l_glob = _gather(o_full, offs, qr), _gather(l_full, offs, qr)
+        acc_o, acc_l = None, None
+        for ik in range(nk):
+            kr = pick(kch, ik)
+            kk, vv, ck = _gather(k, offs, kr), _gather(v, offs, kr), _cu_of(kr)
+            pos = dict(q_pos0=[a for a, _ in qr], kv_pos0=[a for a, _ in kr])
+            o_p, l_p = attn_fwd(qq, kk, vv, cq, ck, scale=sc, causal=True, **pos)
+            acc_o, acc_l = (o_p, l_p) if acc_o is None else merge_partials(acc_o, acc_l, o_p, l_p)
+            gq, gk, gv = attn_bwd(qq, kk, vv, qdo, cq, ck, scale=sc, causal=True, out=o_glob,
+                                  lse=l_glob, mode="formula", **pos)
+            for b, ((qa, qb), (ka, kb)) in enumerate(zip(qr, kr)):
+                dq[offs[b] + qa:offs[b] + qb] += gq[cq[b]:cq[b + 1]]
+                dk[offs[b] + ka:offs[b] + kb] += gk[ck[b]:ck[b + 1]]
+                dv[offs[b] + ka:offs[b] + kb] += gv[ck[b]:ck[b + 1]]
+        np.testing.assert_allclose(acc_o, o_glob, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(acc_l, l_glob, rtol=1e-13)
+    for a, b in zip((dq, dk, dv), g_full):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+
+
+def test_position_shift_reproduces_both_alignments():
+    rng = np.random.default_rng(18)
+    q, k, v = rng.standard_normal((5, 2, 8)), rng.standard_normal((9, 1, 8)), rng.standard_normal((9, 1, 8))
+    np.testing.assert_array_equal(attn_fwd_seq(q, k, v, 0.5, True, shift=0)[0],
+                                  attn_fwd_seq(q, k, v, 0.5, True)[0])
+    np.testing.assert_array_equal(attn_fwd_seq(q, k, v, 0.5, True, shift=4)[0],
+                                  attn_fwd_seq(q, k, v, 0.5, "bottom_right")[0])
+    # a key chunk entirely after every query: nothing visible
+    o, l = attn_fwd_seq(q, k, v, 0.5, True, shift=-5)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+def test_merge_partials_closed_forms():
+    rng = np.random.default_rng(19)
+    oa, ob = rng.standard_normal((6, 3, 4)), rng.standard_normal((6, 3, 4))
+    la, lb = rng.standard_normal((6, 3)), rng.standard_normal((6, 3))
+    ninf = np.full((6, 3), -np.inf)
+    # an empty side leaves the other unchanged, exactly
+    o, l = merge_partials(oa, la, ob, ninf)
+    np.testing.assert_array_equal(o, oa)
+    np.testing.assert_array_equal(l, la)
+    # both empty: zero output, -inf statistic
+    o, l = merge_partials(oa, ninf, ob, ninf)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+    # two equal halves: same output, statistic + ln 2
+    o, l = merge_partials(oa, la, oa, la)
+    np.testing.assert_allclose(o, oa, rtol=1e-15)
+    np.testing.assert_allclose(l, la + math.log(2), rtol=1e-15)
+    # symmetric, and the weights are the two softmax masses
+    o1, l1 = merge_partials(oa, la, ob, lb)
+    o2, l2 = merge_partials(ob, lb, oa, la)
+    np.testing.assert_allclose(o1, o2, rtol=1e-14)
+    w = 1.0 / (1.0 + np.exp(lb - la))
+    np.testing.assert_allclose(o1, w[..., None] * oa + (1 - w)[..., None] * ob, rtol=1e-12)
