@@ -28,7 +28,8 @@ __all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
            "attn_fwd_thd_timed", "attn_bwd_thd_timed", "fwd", "bwd", "status_string",
            "read_device_status", "AttnError", "STATUS", "DEV_BAD_SEQLENS", "StageEvents",
            "FWD_STAGES", "BWD_STAGES", "attn_fwd_batched", "attn_bwd_batched", "fwd_batched",
-           "bwd_batched", "LAYOUTS"]
+           "bwd_batched", "LAYOUTS", "attn_fwd_thd_chunk", "attn_bwd_thd_chunk",
+           "attn_merge_thd", "fwd_chunk", "bwd_chunk", "merge"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
@@ -73,6 +74,19 @@ _BBWD_ARGS = [_P, _P, _P, _P, _P, _P,     # q k v out dout lse
               _P, _S, _P]
 
 
+_CFWD_ARGS = [_P, _P, _P, _P, _P,         # q k v out lse
+              _P, _P, _P, _P, _P, _P,     # cu_q cu_kv cu_q_pad cu_kv_pad q_pos0 kv_pos0
+              _I, _I, _I,                 # batch total_q total_kv
+              _I, _I, _I, _F, _I, _I,     # hq hkv d scale mask dtype
+              _P, _S, _P]
+_CBWD_ARGS = [_P, _P, _P, _P, _P, _P,     # q k v out dout lse
+              _P, _P, _P,                 # dq dk dv
+              _P, _P, _P, _P, _P, _P,
+              _I, _I, _I,
+              _I, _I, _I, _F, _I, _I, _I,  # hq hkv d scale mask accumulate dtype
+              _P, _S, _P]
+
+
 class AttnError(RuntimeError):
     pass
 
@@ -106,6 +120,12 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_batched_timed.restype = ctypes.c_int
         L.attn_bwd_batched_timed.argtypes = _BBWD_ARGS + [ctypes.POINTER(_P), _I]
         L.attn_bwd_batched_timed.restype = ctypes.c_int
+        L.attn_fwd_thd_chunk.argtypes = _CFWD_ARGS
+        L.attn_fwd_thd_chunk.restype = ctypes.c_int
+        L.attn_bwd_thd_chunk.argtypes = _CBWD_ARGS
+        L.attn_bwd_thd_chunk.restype = ctypes.c_int
+        L.attn_merge_thd.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P]
+        L.attn_merge_thd.restype = ctypes.c_int
         L.attn_thd_status_string.argtypes = [_I]
         L.attn_thd_status_string.restype = ctypes.c_char_p
         L.attn_thd_read_device_status.argtypes = [_P, _P, ctypes.POINTER(_I)]
@@ -176,6 +196,21 @@ def attn_fwd_batched_timed(*args, events, n_events) -> int:
 def attn_bwd_batched_timed(*args, events, n_events) -> int:
     """attn_bwd_batched plus per-stage HIP events (see StageEvents)."""
     return int(lib().attn_bwd_batched_timed(*args, events, n_events))
+
+
+def attn_fwd_thd_chunk(*args) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_fwd_thd_chunk(*args))
+
+
+def attn_bwd_thd_chunk(*args) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_bwd_thd_chunk(*args))
+
+
+def attn_merge_thd(out, lse, out_part, lse_part, total_q, hq, d, dtype, stream) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_merge_thd(out, lse, out_part, lse_part, total_q, hq, d, dtype, stream))
 
 
 def attn_fwd_thd_timed(*args, events, n_events) -> int:
@@ -493,3 +528,108 @@ def bwd_batched(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
         st = attn_bwd_batched_timed(*args, events=events.ptr, n_events=events.n)
     _check(st, "attn_bwd_batched")
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------- chunked form
+def _thd_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded, cu_seqlens_kv_padded,
+                q_pos0, kv_pos0, attn_mask_type):
+    dev = q.device
+    _need(q, "q", None, dev)
+    if q.dtype not in _DTYPE:
+        raise AttnError(f"q must be bf16 or fp16, got {q.dtype}")
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    if v.shape != k.shape or k.shape[2] != q.shape[2]:
+        raise AttnError("k and v must be [total_kv, hkv, d] with q's d")
+    cs = [_cu(t, n, dev) for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_kv, "cu_seqlens_kv"),
+                                      (cu_seqlens_q_padded, "cu_seqlens_q_padded"),
+                                      (cu_seqlens_kv_padded, "cu_seqlens_kv_padded"))]
+    batch = cs[0].numel() - 1
+    if any(c is not None and c.numel() != batch + 1 for c in cs):
+        raise AttnError("all cu_seqlens arrays need batch + 1 entries")
+    ps = [_cu(t, n, dev) for t, n in ((q_pos0, "q_pos0"), (kv_pos0, "kv_pos0"))]
+    if any(t is not None and t.numel() != batch for t in ps):
+        raise AttnError("q_pos0 / kv_pos0 need batch entries")
+    if attn_mask_type not in _MASK:
+        raise AttnError(f"attn_mask_type must be one of {sorted(_MASK)}")
+    return dev, cs, ps, batch
+
+
+def fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
+              cu_seqlens_kv_padded=None, q_pos0=None, kv_pos0=None,
+              attn_mask_type: str = "padding_causal", softmax_scale: Optional[float] = None,
+              out=None, lse=None, workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Partial forward over a key chunk: (out, lse) of the chunk's visible keys,
+    the causal rule applied to positions q_pos0[b] + i and kv_pos0[b] + j."""
+    dev, cs, ps, batch = _thd_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                                     cu_seqlens_kv_padded, q_pos0, kv_pos0, attn_mask_type)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((tq, hq), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", q.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
+    st = attn_fwd_thd_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), *[_ptr(c) for c in cs], *[_ptr(t) for t in ps], batch,
+                            tq, tk, hq, hkv, d, scale, _MASK[attn_mask_type], _DTYPE[q.dtype],
+                            ws.data_ptr(), ws.numel() * ws.element_size(),
+                            torch.cuda.current_stream(dev).cuda_stream)
+    _check(st, "attn_fwd_thd_chunk")
+    return out, lse
+
+
+def bwd_chunk(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
+              cu_seqlens_kv_padded=None, q_pos0=None, kv_pos0=None,
+              attn_mask_type: str = "padding_causal", softmax_scale: Optional[float] = None,
+              dq=None, dk=None, dv=None, accumulate: bool = False, workspace=None
+              ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of one (query chunk, key chunk) pair from the whole out / lse;
+    with accumulate=True the shares are added into dq, dk, dv (which must be given)."""
+    dev, cs, ps, batch = _thd_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                                     cu_seqlens_kv_padded, q_pos0, kv_pos0, attn_mask_type)
+    for t, n in ((out, "out"), (dout, "dout")):
+        _need(t, n, q.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    if out.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (tq, hq):
+        raise AttnError("shape mismatch among q, out, dout, lse")
+    if accumulate and (dq is None or dk is None or dv is None):
+        raise AttnError("accumulate=True adds into given dq, dk, dv")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q.dtype, dev)
+    _need(dk, "dk", q.dtype, dev)
+    _need(dv, "dv", q.dtype, dev)
+    ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
+    st = attn_bwd_thd_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), *[_ptr(c) for c in cs], *[_ptr(t) for t in ps], batch,
+                            tq, tk, hq, hkv, d, scale, _MASK[attn_mask_type], int(accumulate),
+                            _DTYPE[q.dtype], ws.data_ptr(), ws.numel() * ws.element_size(),
+                            torch.cuda.current_stream(dev).cuda_stream)
+    _check(st, "attn_bwd_thd_chunk")
+    return dq, dk, dv
+
+
+def merge(out: torch.Tensor, lse: torch.Tensor, out_part: torch.Tensor,
+          lse_part: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Combines two partials over disjoint key sets, in place on (out, lse)."""
+    dev = out.device
+    _need(out, "out", None, dev)
+    if out.dtype not in _DTYPE:
+        raise AttnError(f"out must be bf16 or fp16, got {out.dtype}")
+    _need(out_part, "out_part", out.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    _need(lse_part, "lse_part", torch.float32, dev)
+    tq, hq, d = out.shape
+    if out_part.shape != out.shape or lse.shape != (tq, hq) or lse_part.shape != (tq, hq):
+        raise AttnError("merge: shape mismatch")
+    _check(attn_merge_thd(out.data_ptr(), lse.data_ptr(), out_part.data_ptr(), lse_part.data_ptr(),
+                          tq, hq, d, _DTYPE[out.dtype], torch.cuda.current_stream(dev).cuda_stream),
+           "attn_merge_thd")
+    return out, lse

@@ -15,6 +15,8 @@ hipError_t launch_delta(const AttnParams& p, int dtype, int max_q_tiles, hipStre
 hipError_t launch_fwd(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st);
 hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st);
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st);
+hipError_t launch_merge(void* out, float* lse, const void* out_part, const float* lse_part,
+                        int64_t rows, int d, int dtype, hipStream_t st);
 int dkdv_tile(int d);
 }  // namespace attn
 
@@ -65,14 +67,19 @@ struct Common {
   int64_t q_tiles_max, kv_tiles_max;
 };
 
-// Token layout of a call: THD (slots from cu_seqlens_*_padded) or a batched
-// layout with fixed slots of slot_q / slot_kv tokens per sequence.
-struct Geom {
-  int32_t layout;
-  int32_t slot_q, slot_kv;
+// What varies between the entry points: the token layout (THD, with slots
+// from cu_seqlens_*_padded, or a batched layout with fixed slots of slot_q /
+// slot_kv tokens), the chunk positions of the causal rule, and whether the
+// backward adds into its outputs.
+struct CallOpts {
+  int32_t layout = kLayoutThd;
+  int32_t slot_q = 0, slot_kv = 0;
+  const int32_t* q_pos0 = nullptr;
+  const int32_t* kv_pos0 = nullptr;
+  int32_t accumulate = 0;
   int32_t tsq(int32_t batch) const { return layout == kLayoutSbhd ? batch : 1; }
 };
-constexpr Geom kThd = {kLayoutThd, 0, 0};
+constexpr CallOpts kThd = {kLayoutThd, 0, 0, nullptr, nullptr, 0};
 
 // the largest tile any kernel moves by one buffer-range DMA, in rows
 constexpr int64_t kMaxDmaRows = 256;
@@ -82,7 +89,7 @@ attn_thd_status check_common(const void* q, const void* k, const void* v,
                              const int32_t* cu_q, const int32_t* cu_kv, int32_t batch,
                              int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv,
                              int32_t d, float scale, int32_t mask_type, int32_t dtype,
-                             void* workspace, size_t workspace_bytes, const Geom& geo,
+                             void* workspace, size_t workspace_bytes, const CallOpts& geo,
                              Common& c) {
   if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return ATTN_THD_EINVAL;
   if (hq % hkv != 0) return ATTN_THD_EINVAL;
@@ -116,8 +123,8 @@ attn_thd_status check_common(const void* q, const void* k, const void* v,
 SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu_kv,
                          const int32_t* cu_qp, const int32_t* cu_kp, int32_t batch,
                          int32_t total_q, int32_t total_kv, int q_tile, int kv_tile,
-                         int32_t mask_type, const Geom& geo) {
-  SchedParams s;
+                         int32_t mask_type, const CallOpts& geo) {
+  SchedParams s = {};
   s.cu_q = cu_q;
   s.cu_kv = cu_kv;
   s.cu_qp = cu_qp;
@@ -132,6 +139,8 @@ SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu
   s.layout = geo.layout;
   s.slot_q = geo.slot_q;
   s.slot_kv = geo.slot_kv;
+  s.q_pos0 = geo.q_pos0;
+  s.kv_pos0 = geo.kv_pos0;
   s.hdr = reinterpret_cast<int32_t*>(c.ws + c.L.hdr);
   s.seq = reinterpret_cast<SeqInfo*>(c.ws + c.L.seq);
   s.q_list = reinterpret_cast<int2*>(c.ws + c.L.q_list);
@@ -140,7 +149,7 @@ SchedParams sched_params(const Common& c, const int32_t* cu_q, const int32_t* cu
 }
 
 AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, float scale,
-                       int32_t mask_type, const Geom& geo, int32_t batch) {
+                       int32_t mask_type, const CallOpts& geo, int32_t batch) {
   AttnParams a = {};
   a.hdr = reinterpret_cast<const int32_t*>(c.ws + c.L.hdr);
   a.seq = reinterpret_cast<const SeqInfo*>(c.ws + c.L.seq);
@@ -152,15 +161,16 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.d = d;
   a.scale = scale;
   a.scale_log2e = scale * kLog2e;
-  a.causal_br = mask_type == ATTN_THD_MASK_PADDING_CAUSAL_BOTTOM_RIGHT ? 1 : 0;
+  (void)mask_type;   // the causal diagonal reaches the kernels in the sequence table
   a.tsq = geo.tsq(batch);
   a.tskv = geo.tsq(batch);
+  a.accumulate = geo.accumulate;
   return a;
 }
 
 ZeroParams zero_params(const Common& c, int32_t batch, int rows, int width, bool kv_side,
-                       void* t0, void* t1, float* lse, int lse_heads, const Geom& geo) {
-  ZeroParams z;
+                       void* t0, void* t1, float* lse, int lse_heads, const CallOpts& geo) {
+  ZeroParams z = {};
   z.hdr = reinterpret_cast<const int32_t*>(c.ws + c.L.hdr);
   z.seq = reinterpret_cast<const SeqInfo*>(c.ws + c.L.seq);
   z.batch = batch;
@@ -199,7 +209,7 @@ attn_thd_status fwd_impl(const void* q, const void* k, const void* v, void* out,
                          const int32_t* cu_kp, int32_t batch, int32_t total_q, int32_t total_kv,
                          int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
                          int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                         void* const* events, int32_t n_events, const Geom& geo) {
+                         void* const* events, int32_t n_events, const CallOpts& geo) {
   Common c;
   attn_thd_status st = check_common(q, k, v, cu_q, cu_kv, batch, total_q, total_kv, hq, hkv, d,
                                     scale, mask_type, dtype, workspace, workspace_bytes, geo, c);
@@ -235,7 +245,7 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
                          const int32_t* cu_kp, int32_t batch, int32_t total_q, int32_t total_kv,
                          int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
                          int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                         void* const* events, int32_t n_events, const Geom& geo) {
+                         void* const* events, int32_t n_events, const CallOpts& geo) {
   Common c;
   attn_thd_status st = check_common(q, k, v, cu_q, cu_kv, batch, total_q, total_kv, hq, hkv, d,
                                     scale, mask_type, dtype, workspace, workspace_bytes, geo, c);
@@ -273,9 +283,12 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
   ATTN_TRY(m.mark(3));
   ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
   ATTN_TRY(m.mark(4));
-  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0, geo), s));
+  // an accumulating call leaves every row it does not reach as it was
+  if (!geo.accumulate)
+    ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0, geo), s));
   ATTN_TRY(m.mark(5));
-  ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0, geo), s));
+  if (!geo.accumulate)
+    ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0, geo), s));
   ATTN_TRY(m.mark(6));
   return ATTN_THD_OK;
 }
@@ -360,7 +373,7 @@ attn_thd_status attn_bwd_thd_timed(const void* q, const void* k, const void* v, 
 
 // Batched layouts: geometry checks, then the THD path with fixed slots.
 static attn_thd_status batched_geom(int32_t layout, int32_t batch, int32_t seqlen_q,
-                                    int32_t seqlen_kv, Geom& geo, int32_t& total_q,
+                                    int32_t seqlen_kv, CallOpts& geo, int32_t& total_q,
                                     int32_t& total_kv) {
   if (layout != ATTN_THD_LAYOUT_BSHD && layout != ATTN_THD_LAYOUT_SBHD) return ATTN_THD_EUNSUPPORTED;
   if (batch < 0 || seqlen_q < 0 || seqlen_kv < 0) return ATTN_THD_EINVAL;
@@ -381,7 +394,7 @@ static attn_thd_status fwd_batched(const void* q, const void* k, const void* v, 
                                    float scale, int32_t mask_type, int32_t dtype, void* workspace,
                                    size_t workspace_bytes, void* stream, void* const* events,
                                    int32_t n_events) {
-  Geom geo;
+  CallOpts geo = kThd;   // batched_geom sets the layout fields only
   int32_t total_q, total_kv;
   attn_thd_status st = batched_geom(layout, batch, seqlen_q, seqlen_kv, geo, total_q, total_kv);
   if (st != ATTN_THD_OK) return st;
@@ -398,7 +411,7 @@ static attn_thd_status bwd_batched(const void* q, const void* k, const void* v, 
                                    float scale, int32_t mask_type, int32_t dtype, void* workspace,
                                    size_t workspace_bytes, void* stream, void* const* events,
                                    int32_t n_events) {
-  Geom geo;
+  CallOpts geo = kThd;   // batched_geom sets the layout fields only
   int32_t total_q, total_kv;
   attn_thd_status st = batched_geom(layout, batch, seqlen_q, seqlen_kv, geo, total_q, total_kv);
   if (st != ATTN_THD_OK) return st;
@@ -457,6 +470,64 @@ attn_thd_status attn_bwd_batched_timed(const void* q, const void* k, const void*
   return bwd_batched(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv, layout,
                      batch, seqlen_q, seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
                      workspace_bytes, stream, events, n_events);
+}
+
+// ----------------------------------------------------------------- chunked form
+attn_thd_status attn_fwd_thd_chunk(const void* q, const void* k, const void* v, void* out,
+                                   float* lse, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_kv,
+                                   const int32_t* cu_seqlens_q_padded,
+                                   const int32_t* cu_seqlens_kv_padded, const int32_t* q_pos0,
+                                   const int32_t* kv_pos0, int32_t batch, int32_t total_q,
+                                   int32_t total_kv, int32_t hq, int32_t hkv, int32_t d,
+                                   float scale, int32_t mask_type, int32_t dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if ((q_pos0 || kv_pos0) && mask_type != ATTN_THD_MASK_PADDING_CAUSAL) return ATTN_THD_EINVAL;
+  CallOpts o = kThd;
+  o.q_pos0 = q_pos0;
+  o.kv_pos0 = kv_pos0;
+  return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                  cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d, scale, mask_type,
+                  dtype, workspace, workspace_bytes, stream, nullptr, 0, o);
+}
+
+attn_thd_status attn_bwd_thd_chunk(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, void* dq, void* dk,
+                                   void* dv, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_kv,
+                                   const int32_t* cu_seqlens_q_padded,
+                                   const int32_t* cu_seqlens_kv_padded, const int32_t* q_pos0,
+                                   const int32_t* kv_pos0, int32_t batch, int32_t total_q,
+                                   int32_t total_kv, int32_t hq, int32_t hkv, int32_t d,
+                                   float scale, int32_t mask_type, int32_t accumulate,
+                                   int32_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if ((q_pos0 || kv_pos0) && mask_type != ATTN_THD_MASK_PADDING_CAUSAL) return ATTN_THD_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return ATTN_THD_EINVAL;
+  CallOpts o = kThd;
+  o.q_pos0 = q_pos0;
+  o.kv_pos0 = kv_pos0;
+  o.accumulate = accumulate;
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
+                  cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
+                  scale, mask_type, dtype, workspace, workspace_bytes, stream, nullptr, 0, o);
+}
+
+attn_thd_status attn_merge_thd(void* out, float* lse, const void* out_part,
+                               const float* lse_part, int32_t total_q, int32_t hq, int32_t d,
+                               int32_t dtype, void* stream) {
+  if (total_q < 0 || hq < 1 || d < 1) return ATTN_THD_EINVAL;
+  if (d % 8 != 0 || d > 256) return ATTN_THD_EUNSUPPORTED;
+  if (dtype != ATTN_THD_BF16 && dtype != ATTN_THD_FP16) return ATTN_THD_EUNSUPPORTED;
+  if ((int64_t)total_q * hq > INT32_MAX) return ATTN_THD_EINVAL;
+  if (total_q > 0 && (!out || !lse || !out_part || !lse_part)) return ATTN_THD_EINVAL;
+  if (!aligned16(out) || !aligned16(out_part) || (reinterpret_cast<uintptr_t>(lse) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse_part) & 3u))
+    return ATTN_THD_EINVAL;
+  if (launch_merge(out, lse, out_part, lse_part, (int64_t)total_q * hq, d, dtype,
+                   static_cast<hipStream_t>(stream)) != hipSuccess)
+    return ATTN_THD_ELAUNCH;
+  return ATTN_THD_OK;
 }
 
 const char* attn_thd_status_string(int32_t status) {

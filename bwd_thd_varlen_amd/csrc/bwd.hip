@@ -27,8 +27,20 @@
 
 namespace attn {
 
+// x[0..3] += the four values stored at w (accumulating backward): the sum is
+// formed in fp32 and rounded once.
+template <int DT>
+__device__ __forceinline__ void add_stored(float* x, u32x2 w) {
+  const f32x2 a = Mfma<DT>::unpack2(w[0]), b = Mfma<DT>::unpack2(w[1]);
+  x[0] += a[0];
+  x[1] += a[1];
+  x[2] += b[0];
+  x[3] += b[1];
+}
+
 // ----------------------------------------------------------------- dQ
-template <int DT, int DPAD, bool CAUSAL>
+// ACC: add into dq (the chunked, accumulating backward) instead of writing it
+template <int DT, int DPAD, bool CAUSAL, bool ACC>
 __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void dq_kernel(AttnParams p) {
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
@@ -68,7 +80,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   const bool qvalid = qi < s.lq;
 
   // key j is visible to query i iff j <= i + diag (causal)
-  const int diag = CAUSAL ? uniform(causal_diag(s, p.causal_br)) : 0;
+  const int diag = CAUSAL ? s.diag : 0;
   const int q_end = min(s.lq, m0 + kQTile);
   const int kend = CAUSAL ? max(0, min(s.lk, q_end + diag)) : s.lk;
   const int nsteps = (kend + KS - 1) / KS;
@@ -157,8 +169,11 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
       for (int q4 = 0; q4 < 4; ++q4) {
         const int c0 = 32 * cb + 8 * q4 + 4 * hh;
         if (c0 < p.d) {
-          u32x2 val = {Mfma<DT>::pack2(acc[cb][4 * q4 + 0] * sc0, acc[cb][4 * q4 + 1] * sc0),
-                       Mfma<DT>::pack2(acc[cb][4 * q4 + 2] * sc0, acc[cb][4 * q4 + 3] * sc0)};
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = acc[cb][4 * q4 + e] * sc0;
+          if constexpr (ACC) add_stored<DT>(x, *reinterpret_cast<const u32x2*>(out + c0));
+          u32x2 val = {Mfma<DT>::pack2(x[0], x[1]), Mfma<DT>::pack2(x[2], x[3])};
           *reinterpret_cast<u32x2*>(out + c0) = val;
         }
       }
@@ -177,7 +192,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 // length arrive as zeros in Q, dO, LSE and Delta, so they add nothing.
 // The tiles come through a ring of NBUF buffers filled NBUF-1 steps ahead,
 // with one barrier per step.
-template <int DT, int DPAD, bool CAUSAL, int NW, int BM, int KVM, int OCC, int NBUF>
+// ACC: add into dk / dv instead of writing them
+template <int DT, int DPAD, bool CAUSAL, bool ACC, int NW, int BM, int KVM, int OCC, int NBUF>
 __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   constexpr bool K_LDS = KVM == 2;     // K operand re-read from LDS
   constexpr bool V_LDS = KVM >= 1;     // V operand re-read from LDS
@@ -226,7 +242,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 
   // query tiles that reach this key tile (query i sees key j iff
   // j <= i + diag), times the heads of the group
-  const int diag = CAUSAL ? uniform(causal_diag(s, p.causal_br)) : 0;
+  const int diag = CAUSAL ? s.diag : 0;
   const int m_first = CAUSAL ? max(0, n0 - diag) / BM : 0;
   // the wave's keys and this lane's key shifted onto the query axis
   // (query i sees key j iff i >= j - diag)
@@ -366,10 +382,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const int c0 = 32 * cb + 8 * q4 + 4 * hh;
         if (c0 < p.d) {
-          u32x2 vk = {Mfma<DT>::pack2(adk[cb][4 * q4 + 0] * sc0, adk[cb][4 * q4 + 1] * sc0),
-                      Mfma<DT>::pack2(adk[cb][4 * q4 + 2] * sc0, adk[cb][4 * q4 + 3] * sc0)};
-          u32x2 vv = {Mfma<DT>::pack2(adv[cb][4 * q4 + 0], adv[cb][4 * q4 + 1]),
-                      Mfma<DT>::pack2(adv[cb][4 * q4 + 2], adv[cb][4 * q4 + 3])};
+          float xk[4], xv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xk[e] = adk[cb][4 * q4 + e] * sc0;
+            xv[e] = adv[cb][4 * q4 + e];
+          }
+          if constexpr (ACC) {
+            add_stored<DT>(xk, *reinterpret_cast<const u32x2*>(dkb + c0));
+            add_stored<DT>(xv, *reinterpret_cast<const u32x2*>(dvb + c0));
+          }
+          u32x2 vk = {Mfma<DT>::pack2(xk[0], xk[1]), Mfma<DT>::pack2(xk[2], xk[3])};
+          u32x2 vv = {Mfma<DT>::pack2(xv[0], xv[1]), Mfma<DT>::pack2(xv[2], xv[3])};
           *reinterpret_cast<u32x2*>(dkb + c0) = vk;
           *reinterpret_cast<u32x2*>(dvb + c0) = vv;
         }
@@ -380,8 +404,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 // ----------------------------------------------------------------- launchers
 template <int DT, int DPAD>
 static void launch_dq_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (causal) hipLaunchKernelGGL((dq_kernel<DT, DPAD, true>), dim3(grid), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((dq_kernel<DT, DPAD, false>), dim3(grid), dim3(256), 0, st, p);
+  const bool acc = p.accumulate != 0;
+  if (causal && acc) hipLaunchKernelGGL((dq_kernel<DT, DPAD, true, true>), dim3(grid), dim3(256), 0, st, p);
+  else if (causal) hipLaunchKernelGGL((dq_kernel<DT, DPAD, true, false>), dim3(grid), dim3(256), 0, st, p);
+  else if (acc) hipLaunchKernelGGL((dq_kernel<DT, DPAD, false, true>), dim3(grid), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((dq_kernel<DT, DPAD, false, false>), dim3(grid), dim3(256), 0, st, p);
 }
 
 template <int DT>
@@ -405,10 +432,12 @@ int dkdv_tile(int d) { return d <= 128 ? 128 : 64; }
 
 template <int DT, int DPAD, int NW, int BM, int KVM, int OCC, int NBUF>
 static void launch_dkdv_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (causal)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, NW, BM, KVM, OCC, NBUF>), dim3(grid), dim3(NW * 64), 0, st, p);
-  else
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, NW, BM, KVM, OCC, NBUF>), dim3(grid), dim3(NW * 64), 0, st, p);
+  const dim3 g(grid), blk(NW * 64);
+  const bool acc = p.accumulate != 0;
+  if (causal && acc) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, true, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
+  else if (causal) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
+  else if (acc) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, true, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
+  else hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
 }
 
 template <int DT>

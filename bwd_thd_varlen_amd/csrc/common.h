@@ -57,6 +57,7 @@ constexpr int kHdrWords = 64;    // 256 bytes
 // 1 for THD and bshd, the batch size for sbhd.
 struct SeqInfo {
   int32_t oq, lq, ok, lk;        // first row of the slot and real lengths
+  int32_t diag;                  // causal: key j is visible to query i iff j <= i + diag
 };
 
 // How token rows are laid out (the batched layouts have fixed slots of
@@ -74,6 +75,10 @@ template <> struct Mfma<kBF16> {
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
   }
+  // two stored values (low half first) widened to fp32, exactly
+  static __device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+    return (f32x2){__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  }
 };
 
 template <> struct Mfma<kFP16> {
@@ -83,6 +88,9 @@ template <> struct Mfma<kFP16> {
   }
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+  }
+  static __device__ __forceinline__ f32x2 unpack2(uint32_t w) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
   }
 };
 
@@ -343,6 +351,7 @@ __device__ __forceinline__ WorkItem load_item(const int2* list, const SeqInfo* s
   w.s.lq = uniform(s.lq);
   w.s.ok = uniform(s.ok);
   w.s.lk = uniform(s.lk);
+  w.s.diag = uniform(s.diag);
   return w;
 }
 
@@ -459,6 +468,8 @@ struct SchedParams {
   int32_t batch, total_q, total_kv;
   int32_t q_tile, kv_tile;       // 0 = do not build that list
   int32_t causal;                // 0 none, 1 top-left, 2 bottom-right triangle
+  const int32_t* q_pos0;         // top-left with chunk positions: diag = q_pos0 - kv_pos0
+  const int32_t* kv_pos0;        // (either may be NULL = 0)
   int32_t layout;                // kLayoutThd: slots from the padded arrays;
   int32_t slot_q, slot_kv;       // batched layouts: fixed slot lengths
   int32_t* hdr;
@@ -498,15 +509,8 @@ struct AttnParams {
   const int2* list;
   int32_t hq, hkv, group, d;
   float scale, scale_log2e;
-  int32_t causal_br;   // causal triangle aligned at the sequence ends (bottom right)
   int32_t tsq, tskv;   // token strides in rows (1 for THD and bshd, batch for sbhd)
+  int32_t accumulate;  // backward: add into dq / dk / dv instead of writing them
 };
-
-// Offset of the causal diagonal of a sequence: key j is visible to query i
-// iff j <= i + diag.  Top-left alignment: 0; bottom-right: Lk - Lq, so that
-// the last query sees every key (the two agree when Lq == Lk).
-__device__ __forceinline__ int causal_diag(const SeqInfo& s, int32_t bottom_right) {
-  return bottom_right ? s.lk - s.lq : 0;
-}
 
 }  // namespace attn

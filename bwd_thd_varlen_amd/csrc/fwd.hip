@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   const u32x4 z4 = {0u, 0u, 0u, 0u};
 
   // key j is visible to query i iff j <= i + diag (causal)
-  const int diag = CAUSAL ? uniform(causal_diag(s, p.causal_br)) : 0;
+  const int diag = CAUSAL ? s.diag : 0;
   const int q_end = min(s.lq, m0 + kQTile);
   const int kend = CAUSAL ? max(0, min(s.lk, q_end + diag)) : s.lk;
   const int nsteps = (kend + KS - 1) / KS;

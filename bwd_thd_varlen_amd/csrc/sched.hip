@@ -24,13 +24,13 @@ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 // j <= i + causal_diag).
 __device__ __forceinline__ int q_tile_key(const SeqInfo& s, int m, int tile, int causal) {
   int hi = min(s.lq, (m + 1) * tile);
-  int keys = causal ? max(0, min(s.lk, hi + causal_diag(s, causal == 2))) : s.lk;
+  int keys = causal ? max(0, min(s.lk, hi + s.diag)) : s.lk;
   return min(cdiv(keys, 64), kSchedKeys - 1);
 }
 
 // Work key of a key tile: queries that reach it, in 64-query units.
 __device__ __forceinline__ int kv_tile_key(const SeqInfo& s, int n, int tile, int causal) {
-  int q = causal ? max(0, s.lq - max(0, n * tile - causal_diag(s, causal == 2))) : s.lq;
+  int q = causal ? max(0, s.lq - max(0, n * tile - s.diag)) : s.lq;
   return min(cdiv(q, 64), kSchedKeys - 1);
 }
 
@@ -136,6 +136,14 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
     s.lq = bad ? 0 : (int)lq;
     s.ok = bad ? 0 : (sbhd ? b : (int)pk0);
     s.lk = bad ? 0 : (int)lk;
+    // causal diagonal: top-left 0 (or the chunk positions' difference),
+    // bottom-right Lk - Lq; clamped to [-Lq, Lk], which leaves the mask as
+    // it is (beyond those bounds every key, or no key, is visible)
+    int64_t diag = 0;
+    if (p.causal == 2) diag = lk - lq;
+    else if (p.causal == 1)
+      diag = (int64_t)(p.q_pos0 ? p.q_pos0[b] : 0) - (int64_t)(p.kv_pos0 ? p.kv_pos0[b] : 0);
+    s.diag = bad ? 0 : (int)(diag < -lq ? -lq : (diag > lk ? lk : diag));
     p.seq[b] = s;
   }
   __syncthreads();

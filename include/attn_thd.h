@@ -183,6 +183,68 @@ attn_thd_status attn_bwd_batched(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked form (the building block of context parallelism, where each GPU
+ * holds chunks of a long sequence; the pages mention it only in passing:
+ * issue 3333, section "What we ruled out").  The slots of a THD call hold
+ * chunks of longer sequences: q_pos0[b] / kv_pos0[b] (int32 [batch], device;
+ * either may be NULL = all 0) are the positions in its whole sequence of the
+ * first real query / key of chunk b.  With mask_type
+ * ATTN_THD_MASK_PADDING_CAUSAL, key j is visible to query i iff
+ * kv_pos0[b] + j <= q_pos0[b] + i: the causal rule of the whole sequence
+ * restricted to the two chunks (positions with another mask: EINVAL).
+ *
+ * attn_fwd_thd_chunk writes the PARTIAL result of the chunk's keys: out and
+ * lse as attn_fwd_thd over the visible keys of the chunk (a query that sees
+ * none: out = +0.0, lse = -inf).  attn_merge_thd combines two partials of
+ * the same queries over disjoint key sets, in place on (out, lse):
+ *     LSE = ln(e^lse + e^lse_part),
+ *     O   = e^(lse - LSE) out + e^(lse_part - LSE) out_part,
+ * elementwise over [total_q, hq] rows (both -inf: out = +0.0, lse = -inf),
+ * in fp32, rounded once to dtype.  Merging the partials of every key chunk
+ * gives the attention over the whole keys.
+ *
+ * attn_bwd_thd_chunk is attn_bwd_thd for one (query chunk, key chunk) pair,
+ * reading out and lse of the WHOLE attention (merged) for these queries, so
+ * that P and Delta = rowsum(dO o O) are the whole sequence's: its dq is the
+ * chunk pair's share of dQ, its dk / dv the pair's share of dK / dV.  With
+ * accumulate = 1 the call adds its shares into dq, dk, dv (fp32 sum, one
+ * rounding) and leaves every row it does not reach untouched (no zero
+ * fill); with 0 it writes them as attn_bwd_thd does.  Summing over key
+ * chunks gives dQ, over query chunks dK and dV.
+ *
+ * Other arguments, layouts, workspace, errors and stream semantics as
+ * attn_fwd_thd / attn_bwd_thd (max_seqlen hints are not taken).
+ */
+attn_thd_status attn_fwd_thd_chunk(
+    const void* q, const void* k, const void* v, void* out, float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    const int32_t* q_pos0, const int32_t* kv_pos0,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+attn_thd_status attn_bwd_thd_chunk(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    const int32_t* q_pos0, const int32_t* kv_pos0,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t accumulate,
+    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * out [total_q, hq, d] (dtype), lse [total_q, hq] fp32: updated in place;
+ * out_part, lse_part: the other partial, same shapes, read only.  No
+ * workspace.  Errors: EINVAL (sizes, NULL or misaligned pointers),
+ * EUNSUPPORTED (d or dtype).
+ */
+attn_thd_status attn_merge_thd(void* out, float* lse, const void* out_part, const float* lse_part,
+                               int32_t total_q, int32_t hq, int32_t d, int32_t dtype,
+                               void* stream);
+
+/*
  * Instrumented variants for benchmarks.  Same arguments and behaviour as
  * attn_fwd_thd / attn_bwd_thd (attn_fwd_batched / attn_bwd_batched for the
  * *_batched_timed pair), plus an array of caller-created HIP events

@@ -143,3 +143,34 @@ def test_batched_bwd_rejects_bad_host_arguments(A):
     assert A.attn_bwd_batched(**base) == 3
     assert A.attn_bwd_batched(**dict(base, layout=5)) == 2
     assert A.attn_bwd_batched(**dict(base, dq=None, workspace=FAKE, workspace_bytes=1 << 30)) == 1
+
+
+def test_chunk_entry_points_reject_bad_host_arguments(A):
+    base = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cu_q=FAKE, cu_kv=FAKE, cu_qp=None,
+                cu_kp=None, q_pos0=FAKE, kv_pos0=None, batch=2, total_q=16, total_kv=16, hq=4,
+                hkv=2, d=64, scale=0.125, mask=1, dtype=0, ws=None, wsb=0, stream=None)
+    call = lambda **o: A.attn_fwd_thd_chunk(*dict(base, **o).values())
+    assert call() == 3                        # positions with the causal mask: fine
+    assert call(mask=0) == 1                  # positions need the causal mask
+    assert call(mask=2) == 1
+    assert call(q_pos0=None, mask=2) == 3     # no positions: any mask
+    bb = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+              cu_q=FAKE, cu_kv=FAKE, cu_qp=None, cu_kp=None, q_pos0=None, kv_pos0=FAKE, batch=2,
+              total_q=16, total_kv=16, hq=4, hkv=2, d=64, scale=0.125, mask=1, acc=1, dtype=0,
+              ws=None, wsb=0, stream=None)
+    bcall = lambda **o: A.attn_bwd_thd_chunk(*dict(bb, **o).values())
+    assert bcall() == 3
+    assert bcall(acc=2) == 1
+    assert bcall(mask=0) == 1
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(total_q=-1), 1), (dict(hq=0), 1), (dict(d=12), 2), (dict(d=512), 2),
+    (dict(dtype=5), 2), (dict(out=None), 1), (dict(lse_part=FAKE + 2), 1),
+    (dict(out_part=FAKE + 8), 1), (dict(total_q=1 << 20, hq=4096), 1),
+])
+def test_merge_rejects_bad_host_arguments(A, over, code):
+    args = dict(out=FAKE, lse=FAKE, out_part=FAKE, lse_part=FAKE, total_q=16, hq=4, d=64, dtype=0,
+                stream=None)
+    args.update(over)
+    assert A.attn_merge_thd(**args) == code
