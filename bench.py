@@ -27,6 +27,10 @@ FETCH_SIZE / WRITE_SIZE counters to bytes), --workload NAME:
   throughput_65k        the headline configuration above (default)
   sbhd_65k              sbhd [4096, 16, 64, 128] bf16 padding_causal, read in
                         place by the batched entry points (same FLOP model)
+  chunks4_65k           the headline sequences with every sequence's keys in 4
+                        chunks of consecutive positions, run through the
+                        chunked entry points (partial forwards merged, chunk
+                        backwards from the merged O/LSE, dQ accumulated)
   chunked_bottom_right  THD query chunks of 2048 tokens (the last tokens of
                         each context) against contexts U[2048, 8192] (65536
                         key tokens), bottom-right causal; FLOPs counted on
@@ -59,6 +63,13 @@ WORKLOADS = {
         metric="fwd+bwd TFLOP/s (sbhd bf16 padding_causal, hq64/hkv8/d128) + % MFMA peak",
         desc="sbhd_65k: sbhd [4096, 16, 64, 128] read in place, 16 full sequences, hq=64 "
              "hkv=8 d=128, bf16, padding_causal, fwd+bwd"),
+    "chunks4_65k": dict(
+        layout="chunks", chunks=4, case="throughput_65k",
+        metric="fwd+bwd TFLOP/s (THD bf16 padding_causal over 4 key chunks + merge, "
+               "hq64/hkv8/d128) + % MFMA peak",
+        desc="chunks4_65k: the throughput_65k sequences with every sequence's keys in 4 chunks "
+             "of consecutive positions; per step 4 chunk forwards + 3 (O, LSE) merges, then 4 "
+             "chunk backwards from the merged O/LSE with dQ accumulated; same FLOP model"),
     "chunked_bottom_right": dict(
         layout="thd",
         metric="fwd+bwd TFLOP/s (THD bf16 padding_causal_bottom_right, query chunks, "
@@ -175,7 +186,7 @@ def main():
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
     log(f"[bench] generating the {args.workload} workload")
-    case = getattr(workloads, args.workload)()
+    case = getattr(workloads, wl.get("case", args.workload))()
     pairs = sum(visible_pairs(int(a), int(b_), case.causal)
                 for a, b_ in zip(np.diff(case.cu_seqlens_q), np.diff(case.cu_seqlens_kv)))
     f_fwd = 4.0 * case.d * case.hq * pairs
@@ -195,48 +206,98 @@ def main():
     ws = torch.empty(A.workspace_size(case.batch, tq, tk, case.hq, case.hkv, case.d),
                      dtype=torch.uint8, device=dev)
 
+    # a step is n_fwd forward calls and n_bwd backward calls, each with its
+    # own stage events (the chunked workload also times its merges)
+    n_fwd = n_bwd = 1
+    merge_ev = None
     if wl["layout"] == "sbhd":
         bkw = dict(layout="sbhd", cu_seqlens_q=cq, cu_seqlens_kv=ck,
                    attn_mask_type=case.mask_type, softmax_scale=case.scale, workspace=ws)
 
-        def step(ev_f=None, ev_b=None):
-            A.fwd_batched(q, k, v, out=out, lse=lse, events=ev_f, **bkw)
-            A.bwd_batched(q, k, v, out, do, lse, dq=dq, dk=dk, dv=dv, events=ev_b, **bkw)
+        def step(ev_f=(None,), ev_b=(None,), ev_m=None):
+            A.fwd_batched(q, k, v, out=out, lse=lse, events=ev_f[0], **bkw)
+            A.bwd_batched(q, k, v, out, do, lse, dq=dq, dk=dk, dv=dv, events=ev_b[0], **bkw)
+    elif wl["layout"] == "chunks":
+        # every sequence's keys in C chunks of consecutive positions (outside
+        # the timed region: gathered into THD chunk tensors)
+        C = wl["chunks"]
+        real, offs = np.diff(case.cu_seqlens_kv), case.cu_seqlens_kv_padded[:-1]
+        chunks = []
+        for c in range(C):
+            a, e = real * c // C, real * (c + 1) // C
+            rows = np.concatenate([np.arange(o + x, o + y) for o, x, y in zip(offs, a, e)])
+            idx = torch.as_tensor(rows, dtype=torch.long, device=dev)
+            kc, vc = k.index_select(0, idx).contiguous(), v.index_select(0, idx).contiguous()
+            chunks.append(dict(k=kc, v=vc, cu=cu(np.concatenate([[0], np.cumsum(e - a)])),
+                               pos=cu(a), dk=torch.empty_like(kc), dv=torch.empty_like(vc)))
+        o_part, l_part = torch.empty_like(out), torch.empty_like(lse)
+        n_fwd = n_bwd = C
+        merge_ev = True
+        ckw = dict(cu_seqlens_q_padded=cqp, attn_mask_type=case.mask_type,
+                   softmax_scale=case.scale, workspace=ws)
+
+        def step(ev_f=(None,) * C, ev_b=(None,) * C, ev_m=None):
+            for c, ch in enumerate(chunks):
+                o_c, l_c = (out, lse) if c == 0 else (o_part, l_part)
+                A.fwd_chunk(q, ch["k"], ch["v"], cq, ch["cu"], kv_pos0=ch["pos"], out=o_c,
+                            lse=l_c, events=ev_f[c], **ckw)
+                if c > 0:
+                    if ev_m is not None:
+                        ev_m[c - 1][0].record()
+                    A.merge(out, lse, o_part, l_part)
+                    if ev_m is not None:
+                        ev_m[c - 1][1].record()
+            for c, ch in enumerate(chunks):
+                A.bwd_chunk(q, ch["k"], ch["v"], out, do, lse, cq, ch["cu"], kv_pos0=ch["pos"],
+                            dq=dq, dk=ch["dk"], dv=ch["dv"],
+                            accumulate={"dq"} if c > 0 else False, events=ev_b[c], **ckw)
     else:
         kw = dict(cu_seqlens_q_padded=cqp, cu_seqlens_kv_padded=ckp,
                   max_seqlen_q=case.max_seqlen_q, max_seqlen_kv=case.max_seqlen_kv,
                   attn_mask_type=case.mask_type, softmax_scale=case.scale, workspace=ws)
 
-        def step(ev_f=None, ev_b=None):
-            A.fwd(q, k, v, cq, ck, out=out, lse=lse, events=ev_f, **kw)
-            A.bwd(q, k, v, out, do, lse, cq, ck, dq=dq, dk=dk, dv=dv, events=ev_b, **kw)
+        def step(ev_f=(None,), ev_b=(None,), ev_m=None):
+            A.fwd(q, k, v, cq, ck, out=out, lse=lse, events=ev_f[0], **kw)
+            A.bwd(q, k, v, out, do, lse, cq, ck, dq=dq, dk=dk, dv=dv, events=ev_b[0], **kw)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(A.StageEvents(len(A.FWD_STAGES) + 1), A.StageEvents(len(A.BWD_STAGES) + 1))
+    evs = [([A.StageEvents(len(A.FWD_STAGES) + 1) for _ in range(n_fwd)],
+            [A.StageEvents(len(A.BWD_STAGES) + 1) for _ in range(n_bwd)],
+            [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_fwd - 1)] if merge_ev else None)
            for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for ef, eb in evs:
-        step(ef, eb)
+    for ef, eb, em in evs:
+        step(ef, eb, em)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
 
+    # per step, each stage summed over the step's calls; then averaged over steps
     stage_ms = {}
-    for ef, eb in evs:
-        for name, ms in zip(("fwd." + s for s in A.FWD_STAGES), ef.stage_ms()):
-            stage_ms.setdefault(name, []).append(ms)
-        for name, ms in zip(("bwd." + s for s in A.BWD_STAGES), eb.stage_ms()):
+    for ef, eb, em in evs:
+        tot = {}
+        for e in ef:
+            for name, ms in zip(("fwd." + s for s in A.FWD_STAGES), e.stage_ms()):
+                tot[name] = tot.get(name, 0.0) + ms
+        for e in eb:
+            for name, ms in zip(("bwd." + s for s in A.BWD_STAGES), e.stage_ms()):
+                tot[name] = tot.get(name, 0.0) + ms
+        if em:
+            tot["fwd.merge"] = sum(a.elapsed_time(b_) for a, b_ in em)
+        for name, ms in tot.items():
             stage_ms.setdefault(name, []).append(ms)
     avg = {k_: sum(v_) / len(v_) for k_, v_ in stage_ms.items()}
     log("[bench] per-stage average ms: " + ", ".join(f"{k_}={v_:.3f}" for k_, v_ in avg.items()))
 
-    # algorithmic work per launch of each compute kernel (GEMM FLOPs it must do)
+    # algorithmic work per step of each compute kernel (GEMM FLOPs it must
+    # do), over its time per step (one launch, or the sum of a step's launches)
     work = {"fwd.fwd": ("fwd", f_fwd),            # S = QK^T, O = PV
             "bwd.dkdv": ("dkdv", 2.0 * f_fwd),    # S, dP, dV = P^T dO, dK = dS^T Q
             "bwd.dq": ("dq", 1.5 * f_fwd)}        # S, dP (recomputed), dQ = dS K
@@ -248,7 +309,8 @@ def main():
                 # counter summaries are taken on the headline workload only
                 "traffic": read_traffic(kname) if args.workload == "throughput_65k" else None,
                 "kernel": kname,
-                "avg_launch_ms": round(avg[dom], 4)}
+                "avg_launch_ms": round(avg[dom] / (n_bwd if dom.startswith("bwd") else n_fwd), 4),
+                "launches_per_step": n_bwd if dom.startswith("bwd") else n_fwd}
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -41,6 +41,7 @@ DEV_BAD_SEQLENS = 1
 _DTYPE = {torch.bfloat16: 0, torch.float16: 1}
 _MASK = {"padding": 0, "padding_causal": 1, "padding_causal_bottom_right": 2}
 LAYOUTS = {"bshd": 1, "sbhd": 2}
+ACC_DQ, ACC_DKDV = 1, 2     # accumulate bits of attn_bwd_thd_chunk
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -78,13 +79,13 @@ _CFWD_ARGS = [_P, _P, _P, _P, _P,         # q k v out lse
               _P, _P, _P, _P, _P, _P,     # cu_q cu_kv cu_q_pad cu_kv_pad q_pos0 kv_pos0
               _I, _I, _I,                 # batch total_q total_kv
               _I, _I, _I, _F, _I, _I,     # hq hkv d scale mask dtype
-              _P, _S, _P]
+              _P, _S, _P, ctypes.POINTER(_P), _I]   # workspace bytes stream events n_events
 _CBWD_ARGS = [_P, _P, _P, _P, _P, _P,     # q k v out dout lse
               _P, _P, _P,                 # dq dk dv
               _P, _P, _P, _P, _P, _P,
               _I, _I, _I,
               _I, _I, _I, _F, _I, _I, _I,  # hq hkv d scale mask accumulate dtype
-              _P, _S, _P]
+              _P, _S, _P, ctypes.POINTER(_P), _I]
 
 
 class AttnError(RuntimeError):
@@ -558,7 +559,8 @@ def _thd_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded, cu_se
 def fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
               cu_seqlens_kv_padded=None, q_pos0=None, kv_pos0=None,
               attn_mask_type: str = "padding_causal", softmax_scale: Optional[float] = None,
-              out=None, lse=None, workspace=None) -> Tuple[torch.Tensor, torch.Tensor]:
+              out=None, lse=None, workspace=None, events: Optional["StageEvents"] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Partial forward over a key chunk: (out, lse) of the chunk's visible keys,
     the causal rule applied to positions q_pos0[b] + i and kv_pos0[b] + j."""
     dev, cs, ps, batch = _thd_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
@@ -575,7 +577,9 @@ def fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
                             lse.data_ptr(), *[_ptr(c) for c in cs], *[_ptr(t) for t in ps], batch,
                             tq, tk, hq, hkv, d, scale, _MASK[attn_mask_type], _DTYPE[q.dtype],
                             ws.data_ptr(), ws.numel() * ws.element_size(),
-                            torch.cuda.current_stream(dev).cuda_stream)
+                            torch.cuda.current_stream(dev).cuda_stream,
+                            None if events is None else events.ptr,
+                            0 if events is None else events.n)
     _check(st, "attn_fwd_thd_chunk")
     return out, lse
 
@@ -583,10 +587,13 @@ def fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
 def bwd_chunk(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
               cu_seqlens_kv_padded=None, q_pos0=None, kv_pos0=None,
               attn_mask_type: str = "padding_causal", softmax_scale: Optional[float] = None,
-              dq=None, dk=None, dv=None, accumulate: bool = False, workspace=None
+              dq=None, dk=None, dv=None, accumulate=False, workspace=None,
+              events: Optional["StageEvents"] = None
               ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Backward of one (query chunk, key chunk) pair from the whole out / lse;
-    with accumulate=True the shares are added into dq, dk, dv (which must be given)."""
+    """Backward of one (query chunk, key chunk) pair from the whole out / lse.
+
+    accumulate: False, True (add into dq, dk and dv), or a set of names among
+    {"dq", "dkdv"}; the accumulated outputs must be given."""
     dev, cs, ps, batch = _thd_common(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
                                      cu_seqlens_kv_padded, q_pos0, kv_pos0, attn_mask_type)
     for t, n in ((out, "out"), (dout, "dout")):
@@ -596,8 +603,14 @@ def bwd_chunk(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q
     tk, hkv, _ = k.shape
     if out.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (tq, hq):
         raise AttnError("shape mismatch among q, out, dout, lse")
-    if accumulate and (dq is None or dk is None or dv is None):
-        raise AttnError("accumulate=True adds into given dq, dk, dv")
+    if isinstance(accumulate, bool):
+        acc = ACC_DQ | ACC_DKDV if accumulate else 0
+    else:
+        if not set(accumulate) <= {"dq", "dkdv"}:
+            raise AttnError("accumulate names are 'dq' and 'dkdv'")
+        acc = (ACC_DQ if "dq" in accumulate else 0) | (ACC_DKDV if "dkdv" in accumulate else 0)
+    if (acc & ACC_DQ and dq is None) or (acc & ACC_DKDV and (dk is None or dv is None)):
+        raise AttnError("an accumulated output must be given")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -609,9 +622,11 @@ def bwd_chunk(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q
     st = attn_bwd_thd_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                             dv.data_ptr(), *[_ptr(c) for c in cs], *[_ptr(t) for t in ps], batch,
-                            tq, tk, hq, hkv, d, scale, _MASK[attn_mask_type], int(accumulate),
+                            tq, tk, hq, hkv, d, scale, _MASK[attn_mask_type], acc,
                             _DTYPE[q.dtype], ws.data_ptr(), ws.numel() * ws.element_size(),
-                            torch.cuda.current_stream(dev).cuda_stream)
+                            torch.cuda.current_stream(dev).cuda_stream,
+                            None if events is None else events.ptr,
+                            0 if events is None else events.n)
     _check(st, "attn_bwd_thd_chunk")
     return dq, dk, dv
 

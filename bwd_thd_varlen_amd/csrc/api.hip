@@ -8,6 +8,9 @@
 #include "../../include/attn_thd.h"
 #include "common.h"
 
+static_assert(ATTN_THD_ACC_DQ == attn::kAccDq && ATTN_THD_ACC_DKDV == attn::kAccDkDv,
+              "accumulate bits of the header and the kernels agree");
+
 namespace attn {
 hipError_t launch_sched(const SchedParams& p, hipStream_t st);
 hipError_t launch_zero_fill(const ZeroParams& p, hipStream_t st);
@@ -283,11 +286,11 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
   ATTN_TRY(m.mark(3));
   ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
   ATTN_TRY(m.mark(4));
-  // an accumulating call leaves every row it does not reach as it was
-  if (!geo.accumulate)
+  // an accumulated output keeps every row the call does not reach
+  if (!(geo.accumulate & kAccDq))
     ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0, geo), s));
   ATTN_TRY(m.mark(5));
-  if (!geo.accumulate)
+  if (!(geo.accumulate & kAccDkDv))
     ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0, geo), s));
   ATTN_TRY(m.mark(6));
   return ATTN_THD_OK;
@@ -481,14 +484,15 @@ attn_thd_status attn_fwd_thd_chunk(const void* q, const void* k, const void* v, 
                                    const int32_t* kv_pos0, int32_t batch, int32_t total_q,
                                    int32_t total_kv, int32_t hq, int32_t hkv, int32_t d,
                                    float scale, int32_t mask_type, int32_t dtype, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+                                   size_t workspace_bytes, void* stream, void* const* events,
+                                   int32_t n_events) {
   if ((q_pos0 || kv_pos0) && mask_type != ATTN_THD_MASK_PADDING_CAUSAL) return ATTN_THD_EINVAL;
   CallOpts o = kThd;
   o.q_pos0 = q_pos0;
   o.kv_pos0 = kv_pos0;
   return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
                   cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d, scale, mask_type,
-                  dtype, workspace, workspace_bytes, stream, nullptr, 0, o);
+                  dtype, workspace, workspace_bytes, stream, events, n_events, o);
 }
 
 attn_thd_status attn_bwd_thd_chunk(const void* q, const void* k, const void* v, const void* out,
@@ -501,16 +505,16 @@ attn_thd_status attn_bwd_thd_chunk(const void* q, const void* k, const void* v, 
                                    int32_t total_kv, int32_t hq, int32_t hkv, int32_t d,
                                    float scale, int32_t mask_type, int32_t accumulate,
                                    int32_t dtype, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
+                                   void* stream, void* const* events, int32_t n_events) {
   if ((q_pos0 || kv_pos0) && mask_type != ATTN_THD_MASK_PADDING_CAUSAL) return ATTN_THD_EINVAL;
-  if (accumulate != 0 && accumulate != 1) return ATTN_THD_EINVAL;
+  if (accumulate & ~(ATTN_THD_ACC_DQ | ATTN_THD_ACC_DKDV)) return ATTN_THD_EINVAL;
   CallOpts o = kThd;
   o.q_pos0 = q_pos0;
   o.kv_pos0 = kv_pos0;
   o.accumulate = accumulate;
   return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
                   cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
-                  scale, mask_type, dtype, workspace, workspace_bytes, stream, nullptr, 0, o);
+                  scale, mask_type, dtype, workspace, workspace_bytes, stream, events, n_events, o);
 }
 
 attn_thd_status attn_merge_thd(void* out, float* lse, const void* out_part,

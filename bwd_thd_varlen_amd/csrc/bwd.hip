@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 // ----------------------------------------------------------------- launchers
 template <int DT, int DPAD>
 static void launch_dq_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  const bool acc = p.accumulate != 0;
+  const bool acc = (p.accumulate & kAccDq) != 0;
   if (causal && acc) hipLaunchKernelGGL((dq_kernel<DT, DPAD, true, true>), dim3(grid), dim3(256), 0, st, p);
   else if (causal) hipLaunchKernelGGL((dq_kernel<DT, DPAD, true, false>), dim3(grid), dim3(256), 0, st, p);
   else if (acc) hipLaunchKernelGGL((dq_kernel<DT, DPAD, false, true>), dim3(grid), dim3(256), 0, st, p);
@@ -433,7 +433,7 @@ int dkdv_tile(int d) { return d <= 128 ? 128 : 64; }
 template <int DT, int DPAD, int NW, int BM, int KVM, int OCC, int NBUF>
 static void launch_dkdv_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
   const dim3 g(grid), blk(NW * 64);
-  const bool acc = p.accumulate != 0;
+  const bool acc = (p.accumulate & kAccDkDv) != 0;
   if (causal && acc) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, true, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
   else if (causal) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
   else if (acc) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, true, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);

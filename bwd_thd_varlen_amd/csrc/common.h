@@ -510,7 +510,8 @@ struct AttnParams {
   int32_t hq, hkv, group, d;
   float scale, scale_log2e;
   int32_t tsq, tskv;   // token strides in rows (1 for THD and bshd, batch for sbhd)
-  int32_t accumulate;  // backward: add into dq / dk / dv instead of writing them
+  int32_t accumulate;  // backward: bit kAccDq adds into dq, bit kAccDkDv into dk and dv
 };
+constexpr int32_t kAccDq = 1, kAccDkDv = 2;
 
 }  // namespace attn

@@ -206,15 +206,19 @@ attn_thd_status attn_bwd_batched(
  * attn_bwd_thd_chunk is attn_bwd_thd for one (query chunk, key chunk) pair,
  * reading out and lse of the WHOLE attention (merged) for these queries, so
  * that P and Delta = rowsum(dO o O) are the whole sequence's: its dq is the
- * chunk pair's share of dQ, its dk / dv the pair's share of dK / dV.  With
- * accumulate = 1 the call adds its shares into dq, dk, dv (fp32 sum, one
- * rounding) and leaves every row it does not reach untouched (no zero
- * fill); with 0 it writes them as attn_bwd_thd does.  Summing over key
- * chunks gives dQ, over query chunks dK and dV.
+ * chunk pair's share of dQ, its dk / dv the pair's share of dK / dV.
+ * accumulate is a bit mask: with ATTN_THD_ACC_DQ the call adds its share
+ * into dq, with ATTN_THD_ACC_DKDV into dk and dv (fp32 sum, one rounding),
+ * and an accumulated output keeps every row the call does not reach (no zero
+ * fill); outputs without their bit are written as attn_bwd_thd writes them.
+ * Summing over key chunks gives dQ, over query chunks dK and dV.
  *
  * Other arguments, layouts, workspace, errors and stream semantics as
- * attn_fwd_thd / attn_bwd_thd (max_seqlen hints are not taken).
+ * attn_fwd_thd / attn_bwd_thd (max_seqlen hints are not taken).  events /
+ * n_events: NULL / 0, or stage events as for the *_timed entry points.
  */
+enum { ATTN_THD_ACC_DQ = 1, ATTN_THD_ACC_DKDV = 2 };   /* accumulate bits */
+
 attn_thd_status attn_fwd_thd_chunk(
     const void* q, const void* k, const void* v, void* out, float* lse,
     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
@@ -222,7 +226,8 @@ attn_thd_status attn_fwd_thd_chunk(
     const int32_t* q_pos0, const int32_t* kv_pos0,
     int32_t batch, int32_t total_q, int32_t total_kv,
     int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
-    void* workspace, size_t workspace_bytes, void* stream);
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
 
 attn_thd_status attn_bwd_thd_chunk(
     const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -232,7 +237,8 @@ attn_thd_status attn_bwd_thd_chunk(
     const int32_t* q_pos0, const int32_t* kv_pos0,
     int32_t batch, int32_t total_q, int32_t total_kv,
     int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t accumulate,
-    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
 
 /*
  * out [total_q, hq, d] (dtype), lse [total_q, hq] fp32: updated in place;

@@ -148,7 +148,8 @@ def test_batched_bwd_rejects_bad_host_arguments(A):
 def test_chunk_entry_points_reject_bad_host_arguments(A):
     base = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cu_q=FAKE, cu_kv=FAKE, cu_qp=None,
                 cu_kp=None, q_pos0=FAKE, kv_pos0=None, batch=2, total_q=16, total_kv=16, hq=4,
-                hkv=2, d=64, scale=0.125, mask=1, dtype=0, ws=None, wsb=0, stream=None)
+                hkv=2, d=64, scale=0.125, mask=1, dtype=0, ws=None, wsb=0, stream=None,
+                events=None, n_events=0)
     call = lambda **o: A.attn_fwd_thd_chunk(*dict(base, **o).values())
     assert call() == 3                        # positions with the causal mask: fine
     assert call(mask=0) == 1                  # positions need the causal mask
@@ -157,10 +158,12 @@ def test_chunk_entry_points_reject_bad_host_arguments(A):
     bb = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
               cu_q=FAKE, cu_kv=FAKE, cu_qp=None, cu_kp=None, q_pos0=None, kv_pos0=FAKE, batch=2,
               total_q=16, total_kv=16, hq=4, hkv=2, d=64, scale=0.125, mask=1, acc=1, dtype=0,
-              ws=None, wsb=0, stream=None)
+              ws=None, wsb=0, stream=None, events=None, n_events=0)
     bcall = lambda **o: A.attn_bwd_thd_chunk(*dict(bb, **o).values())
     assert bcall() == 3
-    assert bcall(acc=2) == 1
+    assert bcall(acc=2) == 3
+    assert bcall(acc=3) == 3
+    assert bcall(acc=4) == 1
     assert bcall(mask=0) == 1
 
 

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import (COS_MIN, TOL, assert_close, assert_lse_close, cu_dev, f64, gpu_run,
+from helpers import (assert_close, assert_lse_close, cu_dev, f64,
                      oracle_run)
 import workloads
 
@@ -45,11 +45,6 @@ class ChunkCall:
         # (chunk row, whole row) pairs of the real tokens
         for b, (o, (a, e)) in enumerate(zip(offs, ranges)):
             self.rows += [(int(self.cu_pad[b]) + i, o + a + i) for i in range(e - a)]
-
-
-def _take(t, pairs, col):
-    idx = torch.as_tensor([p[col] for p in pairs], dtype=torch.long, device=t.device)
-    return t.index_select(0, idx)
 
 
 def _run_chunked(L, qcuts, kcuts, hq, hkv, d, dtype, seed):
@@ -216,3 +211,29 @@ def test_merge_kernel_against_oracle(dtype):
     # a side with lse = -inf leaves the other exactly
     only_a = np.isneginf(f64(lb)) & np.isfinite(f64(la))
     assert np.array_equal(og[only_a], f64(oa)[only_a])
+
+
+def test_accumulate_bits_select_the_outputs():
+    """accumulate={"dq"}: dq is added into, dk / dv are written as by the plain call."""
+    import bwd_thd_varlen_amd as A
+    L = [100, 37]
+    rng = np.random.default_rng(63)
+    mk = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32)).to(torch.bfloat16).cuda()
+    T = sum(L)
+    q, k, v, do = mk(T, 4, 64), mk(T, 2, 64), mk(T, 2, 64), mk(T, 4, 64)
+    cu = cu_dev(np.concatenate([[0], np.cumsum(L)]))
+    o, l = A.fwd(q, k, v, cu, cu, attn_mask_type="padding_causal")
+    g = A.bwd(q, k, v, o, do, l, cu, cu, attn_mask_type="padding_causal")
+    base = mk(T, 4, 64)
+    dq = base.clone()
+    dk, dv = torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    A.bwd_chunk(q, k, v, o, do, l, cu, cu, dq=dq, dk=dk, dv=dv, accumulate={"dq"})
+    assert torch.equal(dk, g[1]) and torch.equal(dv, g[2])
+    want = (base.float() + g[0].float()).to(torch.bfloat16)
+    assert (dq.float() - want.float()).abs().max().item() <= \
+        want.float().abs().max().item() * 2.0 ** -7
+    dq2 = torch.full_like(q, float("nan"))
+    dk2, dv2 = torch.zeros_like(k), torch.zeros_like(v)
+    A.bwd_chunk(q, k, v, o, do, l, cu, cu, dq=dq2, dk=dk2, dv=dv2, accumulate={"dkdv"})
+    assert torch.equal(dq2, g[0])
+    assert torch.equal(dk2, g[1]) and torch.equal(dv2, g[2])   # 0 + x rounds to x
