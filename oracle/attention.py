@@ -40,7 +40,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * LSE is the natural-log log-sum-exp of the scaled scores, fp32 ``[T, hq]``;
 * a query row with no allowed key (and every padding row) has O = 0 and
   LSE = -inf; every gradient row outside the real ranges is +0.0;
-* query head h reads KV head ``h // (hq // hkv)``.
+* query head h reads KV head ``h // (hq // hkv)``;
+* dropout (absent from the pages, which set ``dropout=0.0``): inverted
+  dropout on the softmax probabilities with the counter-based keep mask of
+  ``oracle.philox``; LSE is that of the softmax before dropout.
 """
 from __future__ import annotations
 
@@ -119,13 +122,17 @@ def _softmax_rows(s: np.ndarray, allowed: np.ndarray):
 
 
 def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal,
-                 shift: Optional[int] = None):
+                 shift: Optional[int] = None, keep=None, keep_scale: float = 1.0):
     """Forward of one sequence, all heads: O = softmax(scale * Q K^T + mask) V.
 
     q: [Lq, hq, d]; k, v: [Lk, hkv, d] (real rows only, float64).
     Returns O [Lq, hq, d] and LSE [Lq, hq].
     [TE-3333] "Reproduction" (per-sequence SDPA); [TE-3216] "Reproduce" (GQA
     by repeating KV heads over contiguous groups, explicit scale).
+
+    Dropout (``keep``: bool [hq, Lq, Lk]): the probabilities are multiplied by
+    keep * keep_scale before the product with V; LSE stays that of the
+    softmax itself.
     """
     lq, hq, d = q.shape
     lk, hkv, _ = k.shape
@@ -137,13 +144,16 @@ def attn_fwd_seq(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, caus
         g = h // G
         s = scale * (q[:, h, :] @ k[:, g, :].T)
         p, l = _softmax_rows(s, allowed)
+        if keep is not None:
+            p = p * keep[h] * keep_scale
         out[:, h, :] = p @ v[:, g, :]
         lse[:, h] = l
     return out, lse
 
 
 def attn_bwd_seq(q, k, v, dout, scale: float, causal, out=None, lse=None,
-                 mode: str = "definition", shift: Optional[int] = None):
+                 mode: str = "definition", shift: Optional[int] = None, keep=None,
+                 keep_scale: float = 1.0):
     """Backward of one sequence, all heads: dQ, dK, dV of l = sum(dO * O).
 
     ``definition`` (default): the exact gradient, with P recomputed from q,k
@@ -155,6 +165,11 @@ def attn_bwd_seq(q, k, v, dout, scale: float, causal, out=None, lse=None,
 
     dK and dV of a KV head sum the contributions of every query head in its
     group ([TE-3216] repeat_interleave; its transpose is a sum).
+
+    With dropout (``keep``, as in ``attn_fwd_seq``) the output is
+    O = (P o D) V with D = keep * keep_scale, so dV = (P o D)^T dO and the
+    gradient reaching P is dP = D o (dO V^T); Delta = sum_j P_ij dP_ij, which
+    equals rowsum(dO o O) (the formula mode's form).
     """
     lq, hq, d = q.shape
     lk, hkv, _ = k.shape
@@ -167,28 +182,40 @@ def attn_bwd_seq(q, k, v, dout, scale: float, causal, out=None, lse=None,
         g = h // G
         Q, K, V, dO = q[:, h, :], k[:, g, :], v[:, g, :], dout[:, h, :]
         s = scale * (Q @ K.T)
+        D = 1.0 if keep is None else keep[h] * keep_scale
         if mode == "definition":
             p, _ = _softmax_rows(s, allowed)
-            dp = dO @ V.T
+            dp = D * (dO @ V.T)
             delta = np.sum(p * dp, axis=1)
         elif mode == "formula":
             L = lse[:, h]
             use = allowed & np.isfinite(L)[:, None]
             p = np.zeros_like(s)
             p[use] = np.exp((s - L[:, None])[use])
-            dp = dO @ V.T
+            dp = D * (dO @ V.T)
             delta = np.sum(dO * out[:, h, :], axis=1)
         else:
             raise ValueError(mode)
         ds = p * (dp - delta[:, None])
         dq[:, h, :] = scale * (ds @ K)
         dk[:, g, :] += scale * (ds.T @ Q)
-        dv[:, g, :] += p.T @ dO
+        dv[:, g, :] += (p * D).T @ dO
     return dq, dk, dv
 
 
 def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
+
+
+def _dropout_masks(dropout, b, lq, lk, hq):
+    """(keep [hq, lq, lk], keep_scale) of sequence b for dropout = (p, seed, offset)."""
+    if dropout is None or dropout[0] == 0.0:
+        return None, 1.0
+    from .philox import dropout_threshold, keep_mask
+    p, seed, offset = dropout
+    t = dropout_threshold(p)
+    keep = np.stack([keep_mask(lq, lk, b, h, hq, seed, offset, t) for h in range(hq)])
+    return keep, 256.0 / (256.0 - t)
 
 
 def _shifts(q_pos0, kv_pos0, n):
@@ -202,7 +229,7 @@ def _shifts(q_pos0, kv_pos0, n):
 
 def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
              cu_seqlens_kv_padded=None, scale: float = None, causal=False,
-             q_pos0=None, kv_pos0=None) -> Tuple[np.ndarray, np.ndarray]:
+             q_pos0=None, kv_pos0=None, dropout=None) -> Tuple[np.ndarray, np.ndarray]:
     """Forward over the packed THD tensors.
 
     q: [Tq, hq, d], k, v: [Tkv, hkv, d].  Returns out [Tq, hq, d] (float64)
@@ -214,6 +241,9 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
     ``q_pos0`` / ``kv_pos0`` (per sequence, with causal True): the slots hold
     chunks of longer sequences whose first real tokens sit at these positions;
     the causal rule is applied to the positions (see ``allowed_mask``).
+
+    ``dropout`` = (p, seed, offset): the keep mask of ``oracle.philox`` for
+    every sequence b (its index in the batch) and query head.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     Tq, hq, d = q.shape
@@ -226,10 +256,12 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
     qs = sequence_slots(cu_seqlens_q, cu_seqlens_q_padded)
     ks = sequence_slots(cu_seqlens_kv, cu_seqlens_kv_padded)
     shifts = _shifts(q_pos0, kv_pos0, len(qs))
-    for (oq, lq), (ok, lk), sh in zip(qs, ks, shifts):
+    for b, ((oq, lq), (ok, lk), sh) in enumerate(zip(qs, ks, shifts)):
         if lq == 0:
             continue
-        o_b, l_b = attn_fwd_seq(q[oq:oq + lq], k[ok:ok + lk], v[ok:ok + lk], scale, causal, sh)
+        keep, ks_ = _dropout_masks(dropout, b, lq, lk, hq)
+        o_b, l_b = attn_fwd_seq(q[oq:oq + lq], k[ok:ok + lk], v[ok:ok + lk], scale, causal, sh,
+                                keep, ks_)
         out[oq:oq + lq] = o_b
         lse[oq:oq + lq] = l_b
     return out, lse
@@ -237,7 +269,8 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
 
 def attn_bwd(q, k, v, dout, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
              cu_seqlens_kv_padded=None, scale: float = None, causal=False,
-             out=None, lse=None, mode: str = "definition", q_pos0=None, kv_pos0=None):
+             out=None, lse=None, mode: str = "definition", q_pos0=None, kv_pos0=None,
+             dropout=None):
     """Backward over the packed THD tensors: (dq, dk, dv), float64, padded layout.
 
     Rows outside the real ranges are exactly 0; so is every KV row of a
@@ -254,13 +287,14 @@ def attn_bwd(q, k, v, dout, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=Non
     qs = sequence_slots(cu_seqlens_q, cu_seqlens_q_padded)
     ks = sequence_slots(cu_seqlens_kv, cu_seqlens_kv_padded)
     shifts = _shifts(q_pos0, kv_pos0, len(qs))
-    for (oq, lq), (ok, lk), sh in zip(qs, ks, shifts):
+    for b, ((oq, lq), (ok, lk), sh) in enumerate(zip(qs, ks, shifts)):
         if lq == 0 or lk == 0:
             continue
         sq, sk = slice(oq, oq + lq), slice(ok, ok + lk)
+        keep, ks_ = _dropout_masks(dropout, b, lq, lk, hq)
         r = attn_bwd_seq(q[sq], k[sk], v[sk], dout[sq], scale, causal,
                          None if out is None else out[sq], None if lse is None else lse[sq], mode,
-                         sh)
+                         sh, keep, ks_)
         dq[sq], dk[sk], dv[sk] = r
     return dq, dk, dv
 

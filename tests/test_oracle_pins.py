@@ -518,3 +518,115 @@ def test_merge_partials_closed_forms():
     np.testing.assert_allclose(o1, o2, rtol=1e-14)
     w = 1.0 / (1.0 + np.exp(lb - la))
     np.testing.assert_allclose(o1, w[..., None] * oa + (1 - w)[..., None] * ob, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- dropout (counter-based mask)
+from oracle.philox import dropout_threshold, keep_mask, philox4x32_10  # noqa: E402
+
+
+@pytest.mark.parametrize("ctr,key,want", [
+    # known-answer vectors published with the Philox generator (Salmon et al.,
+    # "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11; Random123's
+    # philox4x32, 10 rounds): zero, all-ones, and digits-of-pi inputs
+    ([0, 0, 0, 0], [0, 0], [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]),
+    ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2, [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]),
+    ([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344], [0xA4093822, 0x299F31D0],
+     [0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1]),
+])
+def test_philox_known_answers(ctr, key, want):
+    got = philox4x32_10(np.array(ctr, np.uint32), np.array(key, np.uint32))
+    assert [int(x) for x in got] == want
+
+
+def test_keep_mask_rate_and_determinism():
+    t = dropout_threshold(0.1)
+    assert t == 26
+    m = keep_mask(700, 900, 3, 5, 8, seed=2024, offset=7, t=t)
+    rate, want = m.mean(), 1 - t / 256
+    assert abs(rate - want) <= 5 * math.sqrt(want * (1 - want) / m.size)
+    assert np.array_equal(m, keep_mask(700, 900, 3, 5, 8, seed=2024, offset=7, t=t))
+    # other sequence, head, offset or seed: another mask (about p(1-p)*2 of entries differ)
+    for other in (dict(b=4, h=5, offset=7, seed=2024), dict(b=3, h=6, offset=7, seed=2024),
+                  dict(b=3, h=5, offset=8, seed=2024), dict(b=3, h=5, offset=7, seed=2025)):
+        o = keep_mask(700, 900, other["b"], other["h"], 8, seed=other["seed"],
+                      offset=other["offset"], t=t)
+        assert 0.12 < np.mean(o != m) < 0.24
+    assert keep_mask(5, 7, 0, 0, 1, seed=1, offset=0, t=0).all()
+
+
+def _dropout_case(seed=21, causal=True):
+    rng = np.random.default_rng(seed)
+    return small_case(rng, lq=[5, 9], lk=[7, 9], pq=[6, 10], pk=[8, 9], hq=4, hkv=2, d=8,
+                      causal=causal)
+
+
+def test_dropout_zero_is_no_dropout():
+    c = _dropout_case()
+    args = (c["q"], c["k"], c["v"], c["cu_q"], c["cu_kv"], c["cu_qp"], c["cu_kp"])
+    a = attn_fwd(*args, scale=c["scale"], causal=True)
+    b = attn_fwd(*args, scale=c["scale"], causal=True, dropout=(0.0, 5, 0))
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_dropout_finite_differences():
+    """Gradients with a fixed keep mask (same seed) against central differences."""
+    c = _dropout_case(seed=22)
+    drop = (0.3, 99, 3)
+    args = lambda q, k, v: (q, k, v, c["cu_q"], c["cu_kv"], c["cu_qp"], c["cu_kp"])
+    grads = attn_bwd(c["q"], c["k"], c["v"], c["dout"], c["cu_q"], c["cu_kv"], c["cu_qp"],
+                     c["cu_kp"], scale=c["scale"], causal=True, dropout=drop)
+    eps = 1e-6
+    for gi, name in enumerate("qkv"):
+        x = c[name]
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xs = []
+            for sgn in (1, -1):
+                xp = x.copy()
+                xp[idx] += sgn * eps
+                kw = dict(q=c["q"], k=c["k"], v=c["v"])
+                kw[name] = xp
+                o, _ = attn_fwd(*args(kw["q"], kw["k"], kw["v"]), scale=c["scale"], causal=True,
+                                dropout=drop)
+                xs.append(np.sum(c["dout"] * o))
+            num[idx] = (xs[0] - xs[1]) / (2 * eps)
+        err = np.linalg.norm(grads[gi] - num) / np.linalg.norm(num)
+        assert err <= 1e-7, (name, err)
+
+
+def test_dropout_formula_mode_matches_definition():
+    c = _dropout_case(seed=23)
+    drop = (0.25, 11, 0)
+    a = (c["q"], c["k"], c["v"], c["cu_q"], c["cu_kv"], c["cu_qp"], c["cu_kp"])
+    o, l = attn_fwd(*a, scale=c["scale"], causal=True, dropout=drop)
+    g1 = attn_bwd(c["q"], c["k"], c["v"], c["dout"], *a[3:], scale=c["scale"], causal=True,
+                  dropout=drop)
+    g2 = attn_bwd(c["q"], c["k"], c["v"], c["dout"], *a[3:], scale=c["scale"], causal=True,
+                  dropout=drop, out=o, lse=l, mode="formula")
+    for x, y in zip(g1, g2):
+        np.testing.assert_allclose(x, y, rtol=1e-11, atol=1e-13)
+    # LSE is the softmax's own: unchanged by dropout
+    _, l0 = attn_fwd(*a, scale=c["scale"], causal=True)
+    np.testing.assert_array_equal(l, l0)
+
+
+def test_dropout_is_unbiased_over_seeds():
+    """E over masks of O equals the output without dropout (inverted dropout)."""
+    c = _dropout_case(seed=24, causal=False)
+    a = (c["q"], c["k"], c["v"], c["cu_q"], c["cu_kv"], c["cu_qp"], c["cu_kp"])
+    o0, _ = attn_fwd(*a, scale=c["scale"])
+    n = 600
+    acc = np.zeros_like(o0)
+    sq = np.zeros_like(o0)
+    for s in range(n):
+        o, _ = attn_fwd(*a, scale=c["scale"], dropout=(0.5, 1000 + s, 0))
+        acc += o
+        sq += o * o
+    mean = acc / n
+    sd = np.sqrt(np.maximum(sq / n - mean ** 2, 0) / n)
+    rows = np.abs(o0).sum(axis=(1, 2)) > 0
+    z = np.abs(mean - o0)[rows] / (sd[rows] + 1e-12)
+    assert np.max(z) < 6.0
