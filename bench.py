@@ -31,6 +31,8 @@ FETCH_SIZE / WRITE_SIZE counters to bytes), --workload NAME:
                         chunks of consecutive positions, run through the
                         chunked entry points (partial forwards merged, chunk
                         backwards from the merged O/LSE, dQ accumulated)
+  dropout_65k           the headline workload with dropout p = 0.1 (Philox keep
+                        mask) in the forward and the backward
   chunked_bottom_right  THD query chunks of 2048 tokens (the last tokens of
                         each context) against contexts U[2048, 8192] (65536
                         key tokens), bottom-right causal; FLOPs counted on
@@ -70,6 +72,12 @@ WORKLOADS = {
         desc="chunks4_65k: the throughput_65k sequences with every sequence's keys in 4 chunks "
              "of consecutive positions; per step 4 chunk forwards + 3 (O, LSE) merges, then 4 "
              "chunk backwards from the merged O/LSE with dQ accumulated; same FLOP model"),
+    "dropout_65k": dict(
+        layout="thd", case="throughput_65k", dropout=(0.1, 0x5EED, 0),
+        metric="fwd+bwd TFLOP/s (THD bf16 padding_causal, dropout 0.1, hq64/hkv8/d128) "
+               "+ % MFMA peak",
+        desc="dropout_65k: the throughput_65k workload with dropout p = 0.1 (Philox keep mask, "
+             "seed 0x5EED, offset 0) in the forward and the backward; same FLOP model"),
     "chunked_bottom_right": dict(
         layout="thd",
         metric="fwd+bwd TFLOP/s (THD bf16 padding_causal_bottom_right, query chunks, "
@@ -114,7 +122,7 @@ def visible_pairs(lq: int, lk: int, causal) -> float:
     return lq * lk / 2.0 if causal else float(lq * lk)
 
 
-def cpu_baseline(case, budget_s: float = 12.0):
+def cpu_baseline(case, budget_s: float = 12.0, dropout=None):
     """The fp64 oracle, as it stands, on (sequence, KV group) units of the same
     workload: the sequences closest to 2400 query tokens first, KV groups 0,
     1, ... of each, until `budget_s` of CPU work has been spent."""
@@ -141,8 +149,16 @@ def cpu_baseline(case, budget_s: float = 12.0):
             v = f64(case.v[ok:ok + Lk, g:g + 1])
             do = f64(case.dout[oq:oq + L, g * G:(g + 1) * G])
             t0 = time.perf_counter()
-            oracle.attn_fwd_seq(q, k, v, case.scale, case.causal)
-            oracle.attn_bwd_seq(q, k, v, do, case.scale, case.causal)
+            keep, kscale = None, 1.0
+            if dropout is not None:
+                from oracle.philox import dropout_threshold, keep_mask
+                t = dropout_threshold(dropout[0])
+                keep = np.stack([keep_mask(L, Lk, int(b), h, case.hq, dropout[1], dropout[2], t)
+                                 for h in range(g * G, (g + 1) * G)])
+                kscale = 256.0 / (256.0 - t)
+            oracle.attn_fwd_seq(q, k, v, case.scale, case.causal, keep=keep, keep_scale=kscale)
+            oracle.attn_bwd_seq(q, k, v, do, case.scale, case.causal, keep=keep,
+                                keep_scale=kscale)
             spent += time.perf_counter() - t0
             flops += 3.5 * 4.0 * case.d * G * visible_pairs(L, Lk, case.causal)
             units.append((int(b), L))
@@ -255,6 +271,9 @@ def main():
         kw = dict(cu_seqlens_q_padded=cqp, cu_seqlens_kv_padded=ckp,
                   max_seqlen_q=case.max_seqlen_q, max_seqlen_kv=case.max_seqlen_kv,
                   attn_mask_type=case.mask_type, softmax_scale=case.scale, workspace=ws)
+        if "dropout" in wl:
+            p_, seed_, off_ = wl["dropout"]
+            kw.update(dropout_p=p_, rng_seed=seed_, rng_offset=off_)
 
         def step(ev_f=(None,), ev_b=(None,), ev_m=None):
             A.fwd(q, k, v, cq, ck, out=out, lse=lse, events=ev_f[0], **kw)
@@ -323,7 +342,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(case)
+        cpu = cpu_baseline(case, dropout=wl.get("dropout"))
 
     rec = {
         "metric": wl["metric"], "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,

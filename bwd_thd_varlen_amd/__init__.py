@@ -29,7 +29,8 @@ __all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
            "read_device_status", "AttnError", "STATUS", "DEV_BAD_SEQLENS", "StageEvents",
            "FWD_STAGES", "BWD_STAGES", "attn_fwd_batched", "attn_bwd_batched", "fwd_batched",
            "bwd_batched", "LAYOUTS", "attn_fwd_thd_chunk", "attn_bwd_thd_chunk",
-           "attn_merge_thd", "fwd_chunk", "bwd_chunk", "merge"]
+           "attn_merge_thd", "fwd_chunk", "bwd_chunk", "merge", "attn_fwd_thd_dropout",
+           "attn_bwd_thd_dropout"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
@@ -88,6 +89,23 @@ _CBWD_ARGS = [_P, _P, _P, _P, _P, _P,     # q k v out dout lse
               _P, _S, _P, ctypes.POINTER(_P), _I]
 
 
+_U64 = ctypes.c_uint64
+_U32 = ctypes.c_uint32
+_DFWD_ARGS = [_P, _P, _P, _P, _P,         # q k v out lse
+              _P, _P, _P, _P,             # cu_q cu_kv cu_q_pad cu_kv_pad
+              _I, _I, _I,                 # batch total_q total_kv
+              _I, _I, _I, _F, _I,         # hq hkv d scale mask
+              _F, _U64, _U32, _I,         # dropout_p seed offset dtype
+              _P, _S, _P, ctypes.POINTER(_P), _I]
+_DBWD_ARGS = [_P, _P, _P, _P, _P, _P,     # q k v out dout lse
+              _P, _P, _P,                 # dq dk dv
+              _P, _P, _P, _P,
+              _I, _I, _I,
+              _I, _I, _I, _F, _I,
+              _F, _U64, _U32, _I,
+              _P, _S, _P, ctypes.POINTER(_P), _I]
+
+
 class AttnError(RuntimeError):
     pass
 
@@ -127,6 +145,10 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_thd_chunk.restype = ctypes.c_int
         L.attn_merge_thd.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P]
         L.attn_merge_thd.restype = ctypes.c_int
+        L.attn_fwd_thd_dropout.argtypes = _DFWD_ARGS
+        L.attn_fwd_thd_dropout.restype = ctypes.c_int
+        L.attn_bwd_thd_dropout.argtypes = _DBWD_ARGS
+        L.attn_bwd_thd_dropout.restype = ctypes.c_int
         L.attn_thd_status_string.argtypes = [_I]
         L.attn_thd_status_string.restype = ctypes.c_char_p
         L.attn_thd_read_device_status.argtypes = [_P, _P, ctypes.POINTER(_I)]
@@ -197,6 +219,16 @@ def attn_fwd_batched_timed(*args, events, n_events) -> int:
 def attn_bwd_batched_timed(*args, events, n_events) -> int:
     """attn_bwd_batched plus per-stage HIP events (see StageEvents)."""
     return int(lib().attn_bwd_batched_timed(*args, events, n_events))
+
+
+def attn_fwd_thd_dropout(*args) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_fwd_thd_dropout(*args))
+
+
+def attn_bwd_thd_dropout(*args) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_bwd_thd_dropout(*args))
 
 
 def attn_fwd_thd_chunk(*args) -> int:
@@ -321,8 +353,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.T
         max_seqlen_kv: int = 0, attn_mask_type: str = "padding",
         softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-        events: Optional["StageEvents"] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Forward: returns (out [Tq,hq,d] in q's dtype, lse [Tq,hq] float32)."""
+        events: Optional["StageEvents"] = None, dropout_p: float = 0.0, rng_seed: int = 0,
+        rng_offset: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward: returns (out [Tq,hq,d] in q's dtype, lse [Tq,hq] float32).
+
+    dropout_p > 0: dropout on the probabilities with the Philox keep mask of
+    (rng_seed, rng_offset); the backward must get the same three values."""
     dev = q.device
     _need(q, "q", None, dev)
     if q.dtype not in _DTYPE:
@@ -351,6 +387,16 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.T
     _need(lse, "lse", torch.float32, dev)
     ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if dropout_p:
+        st = attn_fwd_thd_dropout(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            cq.data_ptr(), ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk, hq, hkv, d, scale,
+            _MASK[attn_mask_type], float(dropout_p), int(rng_seed) & (2 ** 64 - 1),
+            int(rng_offset) & 0xFFFFFFFF, _DTYPE[q.dtype], ws.data_ptr(),
+            ws.numel() * ws.element_size(), stream, None if events is None else events.ptr,
+            0 if events is None else events.n)
+        _check(st, "attn_fwd_thd_dropout")
+        return out, lse
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             cq.data_ptr(), ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk,
             int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, d, scale, _MASK[attn_mask_type],
@@ -370,9 +416,10 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         max_seqlen_kv: int = 0, attn_mask_type: str = "padding",
         softmax_scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
         dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None, events: Optional["StageEvents"] = None
+        workspace: Optional[torch.Tensor] = None, events: Optional["StageEvents"] = None,
+        dropout_p: float = 0.0, rng_seed: int = 0, rng_offset: int = 0
         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Backward: returns (dq, dk, dv) in q's dtype."""
+    """Backward: returns (dq, dk, dv) in q's dtype (dropout arguments as ``fwd``)."""
     dev = q.device
     _need(q, "q", None, dev)
     if q.dtype not in _DTYPE:
@@ -404,6 +451,17 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     _need(dv, "dv", q.dtype, dev)
     ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if dropout_p:
+        st = attn_bwd_thd_dropout(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cq.data_ptr(),
+            ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk, hq, hkv, d, scale,
+            _MASK[attn_mask_type], float(dropout_p), int(rng_seed) & (2 ** 64 - 1),
+            int(rng_offset) & 0xFFFFFFFF, _DTYPE[q.dtype], ws.data_ptr(),
+            ws.numel() * ws.element_size(), stream, None if events is None else events.ptr,
+            0 if events is None else events.n)
+        _check(st, "attn_bwd_thd_dropout")
+        return dq, dk, dv
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cq.data_ptr(),
             ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk, int(max_seqlen_q),

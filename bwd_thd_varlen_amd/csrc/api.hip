@@ -80,9 +80,12 @@ struct CallOpts {
   const int32_t* q_pos0 = nullptr;
   const int32_t* kv_pos0 = nullptr;
   int32_t accumulate = 0;
+  uint32_t drop_t = 0;        // dropout byte threshold round(256 p), 0 = none
+  uint64_t seed = 0;
+  uint32_t offset = 0;
   int32_t tsq(int32_t batch) const { return layout == kLayoutSbhd ? batch : 1; }
 };
-constexpr CallOpts kThd = {kLayoutThd, 0, 0, nullptr, nullptr, 0};
+constexpr CallOpts kThd = {};
 
 // the largest tile any kernel moves by one buffer-range DMA, in rows
 constexpr int64_t kMaxDmaRows = 256;
@@ -168,6 +171,11 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.tsq = geo.tsq(batch);
   a.tskv = geo.tsq(batch);
   a.accumulate = geo.accumulate;
+  a.drop_t = geo.drop_t;
+  a.seed_lo = (uint32_t)geo.seed;
+  a.seed_hi = (uint32_t)(geo.seed >> 32);
+  a.drop_c3 = geo.offset * (uint32_t)hq;
+  a.drop_scale = 256.f / (float)(256u - geo.drop_t);
   return a;
 }
 
@@ -473,6 +481,53 @@ attn_thd_status attn_bwd_batched_timed(const void* q, const void* k, const void*
   return bwd_batched(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv, layout,
                      batch, seqlen_q, seqlen_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
                      workspace_bytes, stream, events, n_events);
+}
+
+// ----------------------------------------------------------------- dropout
+// Byte threshold of a dropout probability: round(256 p) for p in [0, 255.5/256).
+static bool dropout_threshold(float p, uint32_t& t) {
+  if (!(p >= 0.f) || !(p < 255.5f / 256.f)) return false;
+  t = (uint32_t)std::floor(256.0 * (double)p + 0.5);
+  return true;
+}
+
+attn_thd_status attn_fwd_thd_dropout(const void* q, const void* k, const void* v, void* out,
+                                     float* lse, const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_kv,
+                                     const int32_t* cu_seqlens_q_padded,
+                                     const int32_t* cu_seqlens_kv_padded, int32_t batch,
+                                     int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv,
+                                     int32_t d, float scale, int32_t mask_type, float dropout_p,
+                                     uint64_t seed, uint32_t offset, int32_t dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events, int32_t n_events) {
+  CallOpts o = kThd;
+  if (!dropout_threshold(dropout_p, o.drop_t)) return ATTN_THD_EINVAL;
+  o.seed = seed;
+  o.offset = offset;
+  return fwd_impl(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                  cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d, scale, mask_type,
+                  dtype, workspace, workspace_bytes, stream, events, n_events, o);
+}
+
+attn_thd_status attn_bwd_thd_dropout(const void* q, const void* k, const void* v, const void* out,
+                                     const void* dout, const float* lse, void* dq, void* dk,
+                                     void* dv, const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_kv,
+                                     const int32_t* cu_seqlens_q_padded,
+                                     const int32_t* cu_seqlens_kv_padded, int32_t batch,
+                                     int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv,
+                                     int32_t d, float scale, int32_t mask_type, float dropout_p,
+                                     uint64_t seed, uint32_t offset, int32_t dtype,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events, int32_t n_events) {
+  CallOpts o = kThd;
+  if (!dropout_threshold(dropout_p, o.drop_t)) return ATTN_THD_EINVAL;
+  o.seed = seed;
+  o.offset = offset;
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
+                  cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
+                  scale, mask_type, dtype, workspace, workspace_bytes, stream, events, n_events, o);
 }
 
 // ----------------------------------------------------------------- chunked form

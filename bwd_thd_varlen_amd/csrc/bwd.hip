@@ -39,8 +39,9 @@ __device__ __forceinline__ void add_stored(float* x, u32x2 w) {
 }
 
 // ----------------------------------------------------------------- dQ
-// ACC: add into dq (the chunked, accumulating backward) instead of writing it
-template <int DT, int DPAD, bool CAUSAL, bool ACC>
+// ACC: add into dq (the chunked, accumulating backward) instead of writing it;
+// DROP: dropout on the probabilities (the keep mask of dropout_block)
+template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP>
 __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void dq_kernel(AttnParams p) {
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
@@ -140,6 +141,17 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
           sc = Mfma<DT>::mma(rk.read(kb2, t), qreg[t], sc);
           dp = Mfma<DT>::mma(rv.read(kb2, t), doreg[t], dp);
         }
+        if constexpr (DROP) {
+          // dP = D o (dO V^T): dropped elements 0, kept ones scaled
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x4 x = dropout_block(p, w.b, h, qi >> 2, (n0 + 32 * kb2 + 8 * g + 4 * hh) >> 2);
+            const uint32_t wq = (li & 3) == 0 ? x[0] : (li & 3) == 1 ? x[1] : (li & 3) == 2 ? x[2] : x[3];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              dp[4 * g + c] = keep_byte(wq, c, p.drop_t) ? dp[4 * g + c] * p.drop_scale : 0.f;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = fast_exp2(__builtin_fmaf(sc[r], sl2e, -lse2));
@@ -192,8 +204,9 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 // length arrive as zeros in Q, dO, LSE and Delta, so they add nothing.
 // The tiles come through a ring of NBUF buffers filled NBUF-1 steps ahead,
 // with one barrier per step.
-// ACC: add into dk / dv instead of writing them
-template <int DT, int DPAD, bool CAUSAL, bool ACC, int NW, int BM, int KVM, int OCC, int NBUF>
+// ACC: add into dk / dv instead of writing them; DROP: dropout on the
+// probabilities (the keep mask of dropout_block)
+template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, int NW, int BM, int KVM, int OCC, int NBUF>
 __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   constexpr bool K_LDS = KVM == 2;     // K operand re-read from LDS
   constexpr bool V_LDS = KVM >= 1;     // V operand re-read from LDS
@@ -319,6 +332,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     const float* tvec = sVec[buf];
     const int hg = step / nm;
     const int i0 = (m_first + (step - hg * nm)) * BM;
+    const int h_step = h0 + hg;   // query head of this step
     // waves with no real key, or whose keys all follow every query, idle
     if (wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q)) {
       f32x16 sc[NIB], dp[NIB];
@@ -345,13 +359,22 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           const int ibase = 32 * ib + 8 * q4 + 4 * hh;   // first of 4 consecutive queries
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[ibase]);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + ibase]);
+          u32x4 x;
+          if constexpr (DROP) x = dropout_block(p, w.b, h_step, (i0 + ibase) >> 2, kj >> 2);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * q4 + c;
             float pr = fast_exp2(__builtin_fmaf(sc[ib][r], sl2e, -l4[c]));
             if (need_mask && kj_q > i0 + ibase + c) pr = 0.f;
-            sc[ib][r] = pr;
-            dp[ib][r] = pr * (dp[ib][r] - d4[c]);
+            if constexpr (DROP) {
+              // P o D for dV, and dS = P o (D o dP - Delta)
+              const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;
+              sc[ib][r] = pr * dsc;
+              dp[ib][r] = pr * (dp[ib][r] * dsc - d4[c]);
+            } else {
+              sc[ib][r] = pr;
+              dp[ib][r] = pr * (dp[ib][r] - d4[c]);
+            }
           }
         }
       // P and dS as packed operands (the fp32 tiles die here)
@@ -402,13 +425,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 }
 
 // ----------------------------------------------------------------- launchers
+// dropout is not combined with accumulation (the chunked entry points take none)
+template <int DT, int DPAD, bool CAUSAL>
+static void launch_dq_c(const AttnParams& p, int grid, hipStream_t st) {
+  const dim3 g(grid), blk(256);
+  if (p.accumulate & kAccDq) hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, true, false>), g, blk, 0, st, p);
+  else if (p.drop_t) hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, false, true>), g, blk, 0, st, p);
+  else hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, false, false>), g, blk, 0, st, p);
+}
+
 template <int DT, int DPAD>
 static void launch_dq_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  const bool acc = (p.accumulate & kAccDq) != 0;
-  if (causal && acc) hipLaunchKernelGGL((dq_kernel<DT, DPAD, true, true>), dim3(grid), dim3(256), 0, st, p);
-  else if (causal) hipLaunchKernelGGL((dq_kernel<DT, DPAD, true, false>), dim3(grid), dim3(256), 0, st, p);
-  else if (acc) hipLaunchKernelGGL((dq_kernel<DT, DPAD, false, true>), dim3(grid), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((dq_kernel<DT, DPAD, false, false>), dim3(grid), dim3(256), 0, st, p);
+  if (causal) launch_dq_c<DT, DPAD, true>(p, grid, st);
+  else launch_dq_c<DT, DPAD, false>(p, grid, st);
 }
 
 template <int DT>
@@ -430,14 +459,21 @@ hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tile
 // keys per dK/dV work item for a head dim
 int dkdv_tile(int d) { return d <= 128 ? 128 : 64; }
 
+template <int DT, int DPAD, bool CAUSAL, int NW, int BM, int KVM, int OCC, int NBUF>
+static void launch_dkdv_c(const AttnParams& p, int grid, hipStream_t st) {
+  const dim3 g(grid), blk(NW * 64);
+  if (p.accumulate & kAccDkDv)
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, true, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
+  else if (p.drop_t)
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
+}
+
 template <int DT, int DPAD, int NW, int BM, int KVM, int OCC, int NBUF>
 static void launch_dkdv_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  const dim3 g(grid), blk(NW * 64);
-  const bool acc = (p.accumulate & kAccDkDv) != 0;
-  if (causal && acc) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, true, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
-  else if (causal) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, true, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
-  else if (acc) hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, true, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
-  else hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, false, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
+  if (causal) launch_dkdv_c<DT, DPAD, true, NW, BM, KVM, OCC, NBUF>(p, grid, st);
+  else launch_dkdv_c<DT, DPAD, false, NW, BM, KVM, OCC, NBUF>(p, grid, st);
 }
 
 template <int DT>

@@ -511,7 +511,48 @@ struct AttnParams {
   float scale, scale_log2e;
   int32_t tsq, tskv;   // token strides in rows (1 for THD and bshd, batch for sbhd)
   int32_t accumulate;  // backward: bit kAccDq adds into dq, bit kAccDkDv into dk and dv
+  // dropout: keep iff the element's random byte >= drop_t; kept values are
+  // scaled by drop_scale = 256 / (256 - drop_t)
+  uint32_t drop_t, seed_lo, seed_hi, drop_c3;   // drop_c3 = offset * hq
+  float drop_scale;
 };
 constexpr int32_t kAccDq = 1, kAccDkDv = 2;
+
+// ----------------------------------------------------------------- dropout
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds over a 4-word counter; each round
+// forms the 64-bit products of words 0 and 2 with two constants and
+// recombines their halves with words 1 and 3 and the key, which is bumped by
+// two Weyl constants between rounds.  The key is wave-uniform (scalar adds).
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  return (u32x4){c0, c1, c2, c3};
+}
+
+// Keep mask of one 4 x 4 block of (query, key) positions of sequence b and
+// query head h: one generator call with counter (key >> 2, query >> 2, b,
+// offset * hq + h) and key (seed_lo, seed_hi); element (i, j) uses byte
+// (j & 3) of word (i & 3).  Returns the four words.
+__device__ __forceinline__ u32x4 dropout_block(const AttnParams& p, int b, int h, int i4, int j4) {
+  return philox4x32_10((uint32_t)j4, (uint32_t)i4, (uint32_t)b, p.drop_c3 + (uint32_t)h,
+                       p.seed_lo, p.seed_hi);
+}
+__device__ __forceinline__ bool keep_byte(uint32_t word, int byte, uint32_t t) {
+  return ((word >> (8 * byte)) & 0xFFu) >= t;
+}
 
 }  // namespace attn

@@ -31,7 +31,8 @@ constexpr float kRescaleSlack = 8.0f;
 template <int DPAD>
 constexpr int fwd_step_keys() { return (DPAD >= 64 && DPAD <= 128) ? 32 : 64; }
 
-template <int DT, int DPAD, bool CAUSAL>
+// DROP: dropout on the probabilities (the keep mask of dropout_block)
+template <int DT, int DPAD, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParams p) {
   constexpr int NT = DPAD / 16;        // 16-wide k chunks over the head dim
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
@@ -153,7 +154,20 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
       for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[kb2][r] = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -base));
-      l_run += tree_sum(sc);
+      l_run += tree_sum(sc);   // the softmax's own sum: before dropout
+      if constexpr (DROP) {
+        // this lane's query row of each 4 x 4 block: keys 4 (r >> 2 block) + c
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x4 x = dropout_block(p, w.b, h, qi >> 2, (n0 + 32 * kb2 + 8 * g + 4 * hh) >> 2);
+            const uint32_t wq = (li & 3) == 0 ? x[0] : (li & 3) == 1 ? x[1] : (li & 3) == 2 ? x[2] : x[3];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (!keep_byte(wq, c, p.drop_t)) sc[kb2][4 * g + c] = 0.f;
+          }
+      }
 #pragma unroll
       for (int u = 0; u < 2 * NKB; ++u) {
         const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
@@ -171,7 +185,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 
   const float l_tot = sum_halves(l_run);
   if (qi < s.lq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;
     const int64_t row = (int64_t)s.oq + (int64_t)qi * p.tsq;
     uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + row * qrs + (int64_t)h * p.d;
 #pragma unroll
@@ -194,8 +208,11 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 
 template <int DT, int DPAD>
 static void launch_fwd_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true>), dim3(grid), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false>), dim3(grid), dim3(256), 0, st, p);
+  const bool drop = p.drop_t != 0;
+  if (causal && drop) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, true>), dim3(grid), dim3(256), 0, st, p);
+  else if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, false>), dim3(grid), dim3(256), 0, st, p);
+  else if (drop) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, true>), dim3(grid), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, false>), dim3(grid), dim3(256), 0, st, p);
 }
 
 template <int DT>

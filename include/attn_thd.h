@@ -217,6 +217,45 @@ attn_thd_status attn_bwd_batched(
  * attn_fwd_thd / attn_bwd_thd (max_seqlen hints are not taken).  events /
  * n_events: NULL / 0, or stage events as for the *_timed entry points.
  */
+/*
+ * Dropout on the attention probabilities (the pages only run with dropout
+ * 0.0, TE issue 2448 "Steps/Code to reproduce bug"; this is the library's
+ * own specification).  attn_fwd_thd / attn_bwd_thd with dropout_p in
+ * [0, 255.5/256), a 64-bit seed and a 32-bit call offset (advance it between
+ * calls that need different masks; the forward and its backward take the
+ * same values):
+ *   O = (P o D) V,  D_ij = keep_ij * 256 / (256 - t),  t = round(256 p),
+ * LSE that of the softmax itself; the backward is the exact gradient of
+ * that O (dV = (P o D)^T dO, dS = P o (D o dO V^T - Delta)).  keep_ij for
+ * sequence b (its index in the batch), query head h, query i and key j
+ * (positions in the sequence): the Philox4x32-10 generator (Salmon et al.,
+ * SC'11) with key (seed low word, seed high word) and counter
+ * (j >> 2, i >> 2, b, offset * hq + h) gives four words x0..x3; keep iff
+ * byte (j & 3) of x[i & 3] is >= t.  dropout_p = 0 is the plain call.
+ * Extra error: EINVAL for dropout_p outside its range or NaN.  events /
+ * n_events as for the *_timed entry points (NULL / 0: none).
+ */
+attn_thd_status attn_fwd_thd_dropout(
+    const void* q, const void* k, const void* v, void* out, float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
+    float dropout_p, uint64_t seed, uint32_t offset, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
+attn_thd_status attn_bwd_thd_dropout(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
+    float dropout_p, uint64_t seed, uint32_t offset, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
 enum { ATTN_THD_ACC_DQ = 1, ATTN_THD_ACC_DKDV = 2 };   /* accumulate bits */
 
 attn_thd_status attn_fwd_thd_chunk(

@@ -177,3 +177,14 @@ def test_merge_rejects_bad_host_arguments(A, over, code):
                 stream=None)
     args.update(over)
     assert A.attn_merge_thd(**args) == code
+
+
+@pytest.mark.parametrize("p,code", [(0.1, 3), (0.0, 3), (0.99, 3), (-0.1, 1), (1.0, 1),
+                                    (float("nan"), 1), (0.999, 1)])
+def test_dropout_probability_range(A, p, code):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 2, 16, 16, 4, 2, 64, 0.125, 1,
+            p, 1234, 0, 0, None, 0, None, None, 0]
+    assert A.attn_fwd_thd_dropout(*args) == code
+    bargs = [FAKE] * 9 + [FAKE, FAKE, None, None, 2, 16, 16, 4, 2, 64, 0.125, 1, p, 1234, 0, 0,
+                          None, 0, None, None, 0]
+    assert A.attn_bwd_thd_dropout(*bargs) == code
