@@ -143,14 +143,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
         }
         if constexpr (DROP) {
           // dP = D o (dO V^T): dropped elements 0, kept ones scaled
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x4 x = dropout_block(p, w.b, h, qi >> 2, (n0 + 32 * kb2 + 8 * g + 4 * hh) >> 2);
-            const uint32_t wq = (li & 3) == 0 ? x[0] : (li & 3) == 1 ? x[1] : (li & 3) == 2 ? x[2] : x[3];
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              dp[4 * g + c] = keep_byte(wq, c, p.drop_t) ? dp[4 * g + c] * p.drop_scale : 0.f;
-          }
+          dropout_row16(p, w.b, h, qi >> 2, (n0 + 32 * kb2 + 4 * hh) >> 2, li & 3, p.drop_scale, dp);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -353,14 +346,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
       }
       const bool need_mask = CAUSAL && (i0 < wk_hi_q);
 #pragma unroll
-      for (int ib = 0; ib < NIB; ++ib)
+      for (int ib = 0; ib < NIB; ++ib) {
+        // the key column of the 4 x 4 blocks at queries 32 ib + 8 q4 + 4 hh (+0..3)
+        uint32_t xcol[4][4];
+        if constexpr (DROP) dropout_cols(p, w.b, h_step, (i0 + 32 * ib + 4 * hh) >> 2, kj >> 2, li & 3, xcol);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int ibase = 32 * ib + 8 * q4 + 4 * hh;   // first of 4 consecutive queries
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[ibase]);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + ibase]);
           u32x4 x;
-          if constexpr (DROP) x = dropout_block(p, w.b, h_step, (i0 + ibase) >> 2, kj >> 2);
+          if constexpr (DROP) x = (u32x4){xcol[q4][0], xcol[q4][1], xcol[q4][2], xcol[q4][3]};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * q4 + c;
@@ -377,6 +373,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
             }
           }
         }
+      }
       // P and dS as packed operands (the fp32 tiles die here)
       u32x4 bp[NU], bds[NU];
 #pragma unroll

@@ -555,4 +555,56 @@ __device__ __forceinline__ bool keep_byte(uint32_t word, int byte, uint32_t t) {
   return ((word >> (8 * byte)) & 0xFFu) >= t;
 }
 
+// x as held by lane G of this lane's quad (lanes 4k .. 4k+3; DPP quad_perm
+// broadcast).  The four lanes of a quad share their query quad in the
+// forward and dQ kernels and their key quad in dK/dV, so each computes one
+// of the four generator calls they all need and the words are exchanged.
+template <int G>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, G * 0x55, 0xF, 0xF, false);
+}
+
+// Word (i & 3) of block g (computed by lane g of the quad) for this lane's
+// query i, c = i & 3.
+template <int G>
+__device__ __forceinline__ uint32_t row_word(const u32x4& mine, int c) {
+  const uint32_t x0 = quad_bcast<G>(mine[0]), x1 = quad_bcast<G>(mine[1]);
+  const uint32_t x2 = quad_bcast<G>(mine[2]), x3 = quad_bcast<G>(mine[3]);
+  return c == 0 ? x0 : c == 1 ? x1 : c == 2 ? x2 : x3;
+}
+
+// Applies the keep mask to the 16 values of this lane's query row in the four
+// 4 x 4 blocks at key quads j4_0 + 2g (value 4g + e is key 4 (j4_0 + 2g) + e):
+// dropped values become 0, kept ones are multiplied by `kept` (1, or the
+// dropout scale).  Lane c of the quad computes block g = c.
+__device__ __forceinline__ void dropout_row16(const AttnParams& p, int b, int h, int i4, int j4_0,
+                                              int c, float kept, f32x16& v) {
+  const u32x4 mine = dropout_block(p, b, h, i4, j4_0 + 2 * c);
+  uint32_t w;
+#define ATTN_DROP_APPLY(G)                                                   \
+  w = row_word<G>(mine, c);                                                  \
+  _Pragma("unroll") for (int e = 0; e < 4; ++e)                              \
+      v[4 * G + e] = keep_byte(w, e, p.drop_t) ? v[4 * G + e] * kept : 0.f;
+  ATTN_DROP_APPLY(0)
+  ATTN_DROP_APPLY(1)
+  ATTN_DROP_APPLY(2)
+  ATTN_DROP_APPLY(3)
+#undef ATTN_DROP_APPLY
+}
+
+// Key-column words of the four 4 x 4 blocks at query quads i4_0 + 2g: all four
+// words of block g (element (i, j) is byte (j & 3) of word (i & 3)); lane c of
+// the quad computes block g = c.
+__device__ __forceinline__ void dropout_cols(const AttnParams& p, int b, int h, int i4_0, int j4,
+                                             int c, uint32_t (&x)[4][4]) {
+  const u32x4 mine = dropout_block(p, b, h, i4_0 + 2 * c, j4);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[0][r] = quad_bcast<0>(mine[r]);
+    x[1][r] = quad_bcast<1>(mine[r]);
+    x[2][r] = quad_bcast<2>(mine[r]);
+    x[3][r] = quad_bcast<3>(mine[r]);
+  }
+}
+
 }  // namespace attn

@@ -156,17 +156,10 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
         for (int r = 0; r < 16; ++r) sc[kb2][r] = fast_exp2(__builtin_fmaf(sc[kb2][r], sl2e, -base));
       l_run += tree_sum(sc);   // the softmax's own sum: before dropout
       if constexpr (DROP) {
-        // this lane's query row of each 4 x 4 block: keys 4 (r >> 2 block) + c
+        // this lane's query row of the 4 x 4 blocks at keys 8g + 4hh (+0..3)
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x4 x = dropout_block(p, w.b, h, qi >> 2, (n0 + 32 * kb2 + 8 * g + 4 * hh) >> 2);
-            const uint32_t wq = (li & 3) == 0 ? x[0] : (li & 3) == 1 ? x[1] : (li & 3) == 2 ? x[2] : x[3];
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (!keep_byte(wq, c, p.drop_t)) sc[kb2][4 * g + c] = 0.f;
-          }
+          dropout_row16(p, w.b, h, qi >> 2, (n0 + 32 * kb2 + 4 * hh) >> 2, li & 3, 1.f, sc[kb2]);
       }
 #pragma unroll
       for (int u = 0; u < 2 * NKB; ++u) {
