@@ -54,7 +54,7 @@ _FWD_ARGS = [_P, _P, _P, _P, _P,          # q k v out lse
              _I, _I, _I, _F, _I, _I,      # hq hkv d scale mask dtype
              _P, _S, _P]                  # workspace bytes stream
 FWD_STAGES = ("sched", "fwd", "zero_fill_q")
-BWD_STAGES = ("sched", "delta", "dq", "dkdv", "zero_fill_q", "zero_fill_kv")
+BWD_STAGES = ("sched", "dq", "dkdv", "zero_fill_q", "zero_fill_kv")
 _BWD_ARGS = [_P, _P, _P, _P, _P, _P,      # q k v out dout lse
              _P, _P, _P,                  # dq dk dv
              _P, _P, _P, _P,

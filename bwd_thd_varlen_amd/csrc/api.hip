@@ -14,7 +14,6 @@ static_assert(ATTN_THD_ACC_DQ == attn::kAccDq && ATTN_THD_ACC_DKDV == attn::kAcc
 namespace attn {
 hipError_t launch_sched(const SchedParams& p, hipStream_t st);
 hipError_t launch_zero_fill(const ZeroParams& p, hipStream_t st);
-hipError_t launch_delta(const AttnParams& p, int dtype, int max_q_tiles, hipStream_t st);
 hipError_t launch_fwd(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st);
 hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st);
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st);
@@ -213,7 +212,7 @@ struct Marks {
 };
 
 constexpr int kFwdStages = 3;   // scheduler, forward, zero fill
-constexpr int kBwdStages = 6;   // scheduler, Delta, dQ, dK/dV, zero fill (q rows), zero fill (kv rows)
+constexpr int kBwdStages = 5;   // scheduler, dQ (+ Delta), dK/dV, zero fill (q rows), zero fill (kv rows)
 
 attn_thd_status fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse,
                          const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_qp,
@@ -287,20 +286,20 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
   a.dv = dv;
   a.list = reinterpret_cast<const int2*>(c.ws + c.L.q_list);
   ATTN_TRY(m.mark(1));
-  ATTN_TRY(launch_delta(a, dtype, (int)c.q_tiles_max, s));
-  ATTN_TRY(m.mark(2));
+  // dQ also forms Delta and LSE * log2(e) for every row it owns and writes
+  // them to the workspace for dK/dV
   ATTN_TRY(launch_dq(a, dtype, causal, (int)c.q_tiles_max, s));
   a.list = reinterpret_cast<const int2*>(c.ws + c.L.kv_list);
-  ATTN_TRY(m.mark(3));
+  ATTN_TRY(m.mark(2));
   ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
-  ATTN_TRY(m.mark(4));
+  ATTN_TRY(m.mark(3));
   // an accumulated output keeps every row the call does not reach
   if (!(geo.accumulate & kAccDq))
     ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_q, hq * d, false, dq, nullptr, nullptr, 0, geo), s));
-  ATTN_TRY(m.mark(5));
+  ATTN_TRY(m.mark(4));
   if (!(geo.accumulate & kAccDkDv))
     ATTN_TRY(launch_zero_fill(zero_params(c, batch, total_kv, hkv * d, true, dk, dv, nullptr, 0, geo), s));
-  ATTN_TRY(m.mark(6));
+  ATTN_TRY(m.mark(5));
   return ATTN_THD_OK;
 }
 

@@ -102,18 +102,38 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   };
   if (nsteps > 0) issue(0);
 
+  // Q and dO of this lane's query (half hh of the head dim) stay in
+  // registers; O is read once for the backward's preprocess:
+  // Delta = sum_c dO_c O_c, in fp32, over the two halves of the wave
+  const uint16_t* obase = reinterpret_cast<const uint16_t*>(p.o) + qoff;
   u32x4 qreg[NT], doreg[NT];
+  float dpart = 0.f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int c = 16 * t + 8 * hh;
     const bool ok = qvalid && c < p.d;
     qreg[t] = ok ? ldg16(qb + (int64_t)qi * qts + c) : z4;
     doreg[t] = ok ? ldg16(dob + (int64_t)qi * qts + c) : z4;
+    const u32x4 o4 = ok ? ldg16(obase + (int64_t)qi * qts + c) : z4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t dw = doreg[t][e], ow = o4[e];
+      const f32x2 x = Mfma<DT>::unpack2(dw), y = Mfma<DT>::unpack2(ow);
+      dpart = __builtin_fmaf(x[0], y[0], dpart);
+      dpart = __builtin_fmaf(x[1], y[1], dpart);
+    }
   }
   const int64_t qrow = (int64_t)s.oq + (int64_t)qi * p.tsq;
   const int64_t srow = qrow * p.hq + h;
-  const float lse2 = qvalid ? p.lse2[srow] : __builtin_inff();
-  const float dlt = qvalid ? p.delta[srow] : 0.f;
+  const float delta = sum_halves(dpart);
+  const float lse2 = qvalid ? p.lse[srow] * kLog2e : __builtin_inff();
+  const float dlt = qvalid ? delta : 0.f;
+  // the dK/dV kernel (launched next) reads both per (row, head); each is
+  // written by the one work item that owns the row
+  if (qvalid && hh == 0) {
+    p.delta[srow] = delta;
+    p.lse2[srow] = lse2;
+  }
   wait_vm<0>();
 
   f32x16 acc[NCB];

@@ -1,5 +1,4 @@
-// Varlen tile scheduler, uncovered-row zero fill and the backward
-// preprocess (Delta = rowsum(dO o O)).
+// Varlen tile scheduler and uncovered-row zero fill.
 //
 // The scheduler turns the four cu_seqlens arrays into (a) a per-sequence
 // table of padded offsets and real lengths and (b) work lists of
@@ -221,60 +220,6 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(ZeroParams p) {
   }
 }
 
-// ----------------------------------------------------------------- Delta
-// Delta[t, h] = sum_c dO[t,h,c] * O[t,h,c] in fp32 for the real query rows
-// of every listed query tile; also LSE * log2(e) for the same rows, the form
-// the backward kernels exponentiate with exp2.  CHP lanes (a power of two >= d/8) cooperate on
-// one row, 16 bytes each; the partial sums are combined with xor shuffles.
-template <int DT, int CHP>
-__global__ __launch_bounds__(256) void delta_kernel(AttnParams p) {
-  const int ntiles = p.hdr[kHdrNQTiles];
-  const int item = blockIdx.x / p.hq;
-  const int h = blockIdx.x - item * p.hq;
-  if (item >= ntiles) return;
-  const int2 e = p.list[item];
-  const SeqInfo s = p.seq[e.x];
-  const int i0 = e.y * kQTile;
-  const int rows = min(kQTile, s.lq - i0);
-  const int tid = threadIdx.x;
-  const int lane_c = tid & (CHP - 1);
-  const int chunks = p.d >> 3;
-  constexpr int kRowsPerPass = 256 / CHP;
-  const int64_t rs = (int64_t)p.hq * p.d;   // row stride in elements
-  for (int r = tid / CHP; r < rows; r += kRowsPerPass) {
-    const int64_t row = s.oq + (int64_t)(i0 + r) * p.tsq;
-    float acc = 0.f;
-    if (lane_c < chunks) {
-      const int64_t off = row * rs + (int64_t)h * p.d + lane_c * 8;
-      u32x4 a = ldg16(reinterpret_cast<const uint16_t*>(p.o) + off);
-      u32x4 b = ldg16(reinterpret_cast<const uint16_t*>(p.dout) + off);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float a0, a1, b0, b1;
-        // copy the lane word out first: bit-casting a vector element in place
-        // miscompiles (every w read element 0)
-        const uint32_t aw = a[w], bw = b[w];
-        if (DT == kBF16) {
-          a0 = __uint_as_float(aw << 16); a1 = __uint_as_float(aw & 0xffff0000u);
-          b0 = __uint_as_float(bw << 16); b1 = __uint_as_float(bw & 0xffff0000u);
-        } else {
-          f16x2 ha = __builtin_bit_cast(f16x2, aw);
-          f16x2 hb = __builtin_bit_cast(f16x2, bw);
-          a0 = (float)ha[0]; a1 = (float)ha[1]; b0 = (float)hb[0]; b1 = (float)hb[1];
-        }
-        acc = __builtin_fmaf(a0, b0, acc);
-        acc = __builtin_fmaf(a1, b1, acc);
-      }
-    }
-#pragma unroll
-    for (int off = CHP / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CHP);
-    if (lane_c == 0) {
-      p.delta[row * p.hq + h] = acc;
-      p.lse2[row * p.hq + h] = p.lse[row * p.hq + h] * kLog2e;
-    }
-  }
-}
-
 // ----------------------------------------------------------------- launchers
 hipError_t launch_sched(const SchedParams& p, hipStream_t st) {
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, st, p);
@@ -286,24 +231,6 @@ hipError_t launch_zero_fill(const ZeroParams& p, hipStream_t st) {
   const int blocks = (p.rows + kZeroRows - 1) / kZeroRows;
   hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, st, p);
   return hipGetLastError();
-}
-
-template <int DT>
-static hipError_t launch_delta_dt(const AttnParams& p, int grid, hipStream_t st) {
-  const int ch = p.d >> 3;
-  if (ch <= 1) hipLaunchKernelGGL((delta_kernel<DT, 1>), dim3(grid), dim3(256), 0, st, p);
-  else if (ch <= 2) hipLaunchKernelGGL((delta_kernel<DT, 2>), dim3(grid), dim3(256), 0, st, p);
-  else if (ch <= 4) hipLaunchKernelGGL((delta_kernel<DT, 4>), dim3(grid), dim3(256), 0, st, p);
-  else if (ch <= 8) hipLaunchKernelGGL((delta_kernel<DT, 8>), dim3(grid), dim3(256), 0, st, p);
-  else if (ch <= 16) hipLaunchKernelGGL((delta_kernel<DT, 16>), dim3(grid), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((delta_kernel<DT, 32>), dim3(grid), dim3(256), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_delta(const AttnParams& p, int dtype, int max_q_tiles, hipStream_t st) {
-  const int grid = max_q_tiles * p.hq;
-  if (grid <= 0) return hipSuccess;
-  return dtype == kBF16 ? launch_delta_dt<kBF16>(p, grid, st) : launch_delta_dt<kFP16>(p, grid, st);
 }
 
 }  // namespace attn

@@ -14,8 +14,8 @@ Two modes, each run on the databases a GPU run left behind:
       --copy-calibration``.  The counters (KiB per dispatch) are scaled by
       what they read for the plain 1 GiB device copies that option adds, so
       that a copy of N bytes counts N bytes read and N written.  Writes
-      ``profiles/<stage>_throughput_65k_pmc.txt`` for fwd, dq, dkdv and
-      delta, stamped with the hash of the kernel sources (``source_hash``);
+      ``profiles/<stage>_throughput_65k_pmc.txt`` for fwd, dq and dkdv,
+      stamped with the hash of the kernel sources (``source_hash``);
       bench.py reports the traffic only while that hash matches.
 
 Reads SQLite files only; nothing here touches the GPU.
@@ -38,7 +38,6 @@ KERNEL_SOURCES = {
     "fwd": ["bwd_thd_varlen_amd/csrc/fwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
     "dq": ["bwd_thd_varlen_amd/csrc/bwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
     "dkdv": ["bwd_thd_varlen_amd/csrc/bwd.hip", "bwd_thd_varlen_amd/csrc/common.h"],
-    "delta": ["bwd_thd_varlen_amd/csrc/sched.hip", "bwd_thd_varlen_amd/csrc/common.h"],
 }
 
 # demangled-name prefixes of each stage's kernel for the bf16 d=128 causal workload
@@ -46,7 +45,6 @@ STAGE_KERNELS = {
     "fwd": "void attn::fwd_kernel<0, 128, true",
     "dq": "void attn::dq_kernel<0, 128, true",
     "dkdv": "void attn::dkdv_kernel<0, 128, true",
-    "delta": "void attn::delta_kernel<0,",
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30          # bench.py --copy-calibration: 1 GiB copies

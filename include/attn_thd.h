@@ -297,9 +297,9 @@ attn_thd_status attn_merge_thd(void* out, float* lse, const void* out_part, cons
  * events[i] just before stage i is launched and events[n_events-1] after the
  * last stage, so hipEventElapsedTime(events[i], events[i+1]) is stage i.
  *   forward  (n_events = 4): scheduler, forward kernel, zero fill
- *   backward (n_events = 7): scheduler, Delta preprocess, dQ kernel,
- *                            dK/dV kernel, zero fill (query rows),
- *                            zero fill (key rows)
+ *   backward (n_events = 6): scheduler, dQ kernel (which also forms
+ *                            Delta = rowsum(dO o O)), dK/dV kernel,
+ *                            zero fill (query rows), zero fill (key rows)
  * A NULL `events` or another n_events returns ATTN_THD_EINVAL.
  */
 attn_thd_status attn_fwd_thd_timed(
