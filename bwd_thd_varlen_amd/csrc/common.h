@@ -421,28 +421,6 @@ __device__ __forceinline__ float tree_sum(const f32x16 (&c)[N]) {
   return t[0];
 }
 
-// ----------------------------------------------------------------- scheduling
-// Left to itself the backend issues each LDS operand read right before the
-// MFMA that consumes it and waits for it there, so the matrix core idles for
-// the LDS latency on every product.  These hints (the backend's scheduling
-// groups, instruction classes by mask) order the products of one basic block
-// as a software pipeline: the reads of the first AHEAD MFMAs go first, then
-// each MFMA is followed by the R reads of the MFMA AHEAD places later.
-// Other instructions of the block are placed freely around the pipeline.
-constexpr unsigned kSgMfma = 0x008, kSgDsRead = 0x100;
-
-template <int NMFMA, int R, int AHEAD = 4>
-__device__ __forceinline__ void pipeline_lds_mfma() {
-  constexpr int A = AHEAD < NMFMA ? AHEAD : NMFMA;
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, A * R, 0);
-#pragma unroll
-  for (int z = 0; z < NMFMA - A; ++z) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, R, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(kSgMfma, A, 0);
-}
-
 // Maps a linear workgroup id onto (work item, head) so that the heads an
 // XCD receives are contiguous (they share K/V tiles in that XCD's L2).
 // Workgroups are dispatched round-robin over the 8 XCDs by id.  Falls back

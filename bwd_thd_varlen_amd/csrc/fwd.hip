@@ -122,7 +122,6 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
         for (int t = 0; t < NT; ++t)
           sc[kb2] = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
       }
-      pipeline_lds_mfma<NKB * NT, 1>();
       const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo_k);
       if (need_mask) {
 #pragma unroll
@@ -168,7 +167,6 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
         for (int cb = 0; cb < NCB; ++cb)
           acc[cb] = Mfma<DT>::mma(lds_tr_operand<LV>(tV, cb, u, lane), b, acc[cb]);
       }
-      pipeline_lds_mfma<2 * NKB * NCB, 2>();
     }
   };
   for (int step = 0; step < nsteps; step += 2) {
