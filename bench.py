@@ -20,7 +20,7 @@ Prints ONE JSON line.  Besides the metric it carries
   cpu_baseline -- the fp64 CPU oracle timed on a bounded sample of the same
                   workload (rank 0, N=1 only).
 
-Options: --gpus N (only 1 is supported: this build runs on one GPU),
+Options: --gpus N (only 1 is supported: the library runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --copy-calibration (adds a plain
 1 GiB device copy after the timed region, used to scale rocprofv3's
 FETCH_SIZE / WRITE_SIZE counters to bytes), --workload NAME:
@@ -186,7 +186,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}, "
+        print(f"bench.py: the library runs on one GPU only (got --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the per-GPU kernel is measured with --gpus 1",
               file=sys.stderr)
         sys.exit(2)

@@ -1,7 +1,7 @@
 // Merge of two partial attention results over disjoint key sets: the step
 // that combines attention computed chunk by chunk over the keys (context
-// parallelism keeps a sequence's keys in chunks; the pages mention it only in
-// passing, TransformerEngine issue 3333, section "What we ruled out").
+// parallelism keeps a sequence's keys in chunks; TransformerEngine issue
+// 3333, section "What we ruled out", mentions it only in passing).
 //
 // With P_a = exp(S - LSE_a) on key set A (O_a = P_a V_A) and likewise for B,
 // the softmax over A u B has LSE = ln(e^LSE_a + e^LSE_b) and

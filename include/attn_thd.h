@@ -184,8 +184,8 @@ attn_thd_status attn_bwd_batched(
 
 /*
  * Chunked form (the building block of context parallelism, where each GPU
- * holds chunks of a long sequence; the pages mention it only in passing:
- * issue 3333, section "What we ruled out").  The slots of a THD call hold
+ * holds chunks of a long sequence; issue 3333, section "What we ruled out",
+ * mentions it only in passing).  The slots of a THD call hold
  * chunks of longer sequences: q_pos0[b] / kv_pos0[b] (int32 [batch], device;
  * either may be NULL = all 0) are the positions in its whole sequence of the
  * first real query / key of chunk b.  With mask_type
@@ -218,9 +218,9 @@ attn_thd_status attn_bwd_batched(
  * n_events: NULL / 0, or stage events as for the *_timed entry points.
  */
 /*
- * Dropout on the attention probabilities (the pages only run with dropout
- * 0.0, TE issue 2448 "Steps/Code to reproduce bug"; this is the library's
- * own specification).  attn_fwd_thd / attn_bwd_thd with dropout_p in
+ * Dropout on the attention probabilities (issue 2448, "Steps/Code to
+ * reproduce bug", runs with dropout 0.0; the mask below is the library's own
+ * specification).  attn_fwd_thd / attn_bwd_thd with dropout_p in
  * [0, 255.5/256), a 64-bit seed and a 32-bit call offset (advance it between
  * calls that need different masks; the forward and its backward take the
  * same values):

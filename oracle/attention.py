@@ -29,7 +29,7 @@ Sources (web pages, cited by title and section):
   cu_seqlens_q_padded": real boundaries mask, padded boundaries index, the
   output keeps the padded layout ("Expected Behavior").
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * real tokens of sequence b occupy rows ``[cu_pad[b], cu_pad[b] + L_b)``,
   the rest of the slot is padding;
