@@ -13,7 +13,8 @@ arguments (``cu_seqlens_q``, ``cu_seqlens_kv``, ``cu_seqlens_q_padded``,
 "padding_causal_bottom_right"}: the causal triangle top-left aligned, key
 j <= query i, or aligned at the sequence ends, j <= i + Lk - Lq).
 ``fwd_batched`` / ``bwd_batched`` read bshd ``[b, s, h, d]`` and sbhd
-``[s, b, h, d]`` tensors in place through the same kernels.
+``[s, b, h, d]`` tensors in place through the same kernels; ``attention_thd``
+is the forward and backward as one ``torch.autograd`` op.
 """
 from __future__ import annotations
 
@@ -30,7 +31,7 @@ __all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
            "FWD_STAGES", "BWD_STAGES", "attn_fwd_batched", "attn_bwd_batched", "fwd_batched",
            "bwd_batched", "LAYOUTS", "attn_fwd_thd_chunk", "attn_bwd_thd_chunk",
            "attn_merge_thd", "fwd_chunk", "bwd_chunk", "merge", "attn_fwd_thd_dropout",
-           "attn_bwd_thd_dropout"]
+           "attn_bwd_thd_dropout", "attention_thd"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
@@ -706,3 +707,43 @@ def merge(out: torch.Tensor, lse: torch.Tensor, out_part: torch.Tensor,
                           tq, hq, d, _DTYPE[out.dtype], torch.cuda.current_stream(dev).cuda_stream),
            "attn_merge_thd")
     return out, lse
+
+
+# ----------------------------------------------------------------- autograd
+class _AttentionTHD(torch.autograd.Function):
+    """The forward and backward entry points as one differentiable op (the
+    backward gets the forward's own out and lse, as TE-style callers pass them)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                cu_seqlens_kv_padded, attn_mask_type, softmax_scale, dropout_p, rng_seed,
+                rng_offset):
+        kw = dict(cu_seqlens_q_padded=cu_seqlens_q_padded,
+                  cu_seqlens_kv_padded=cu_seqlens_kv_padded, attn_mask_type=attn_mask_type,
+                  softmax_scale=softmax_scale, dropout_p=dropout_p, rng_seed=rng_seed,
+                  rng_offset=rng_offset)
+        out, lse = fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, **kw)
+        ctx.save_for_backward(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_kv)
+        ctx.kw = kw
+        ctx.mark_non_differentiable(lse)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, k, v, out, lse, cq, ck = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, out, dout.contiguous(), lse, cq, ck, **ctx.kw)
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None
+
+
+def attention_thd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  cu_seqlens_q: torch.Tensor, cu_seqlens_kv: torch.Tensor,
+                  cu_seqlens_q_padded: Optional[torch.Tensor] = None,
+                  cu_seqlens_kv_padded: Optional[torch.Tensor] = None,
+                  attn_mask_type: str = "padding_causal", softmax_scale: Optional[float] = None,
+                  dropout_p: float = 0.0, rng_seed: int = 0, rng_offset: int = 0,
+                  return_lse: bool = False):
+    """Differentiable THD attention: out (and lse if asked); gradients flow to q, k, v."""
+    out, lse = _AttentionTHD.apply(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                                   cu_seqlens_kv_padded, attn_mask_type, softmax_scale,
+                                   dropout_p, rng_seed, rng_offset)
+    return (out, lse) if return_lse else out
