@@ -630,3 +630,39 @@ def test_dropout_is_unbiased_over_seeds():
     rows = np.abs(o0).sum(axis=(1, 2)) > 0
     z = np.abs(mean - o0)[rows] / (sd[rows] + 1e-12)
     assert np.max(z) < 6.0
+
+
+# ---------------------------------------------------------------- FP8 inputs
+from oracle.fp8 import attn_fwd_fp8, decode_e4m3  # noqa: E402
+
+
+def test_e4m3_decoder_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.nanmax(got) == 448.0 and np.nanmin(got[got > 0]) == 2.0 ** -9
+
+
+def test_fp8_forward_folds_descales_into_the_bf16_definition():
+    """FP8 codes with descales equal the plain forward on the scaled values; scaling
+    q by 2 and its descale by 1/2 (exact in E4M3 away from the range ends) changes nothing."""
+    rng = np.random.default_rng(30)
+    T, hq, hkv, d = 20, 4, 2, 16
+    qn = rng.standard_normal((T, hq, d), dtype=np.float32) * 2
+    qn = np.sign(qn) * np.maximum(np.abs(qn), 0.1)    # normal E4M3 values: doubling is exact
+    q = torch.from_numpy(qn.astype(np.float32))
+    k = torch.from_numpy(rng.standard_normal((T, hkv, d), dtype=np.float32))
+    v = torch.from_numpy(rng.standard_normal((T, hkv, d), dtype=np.float32))
+    f8 = lambda t: t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    cu = np.array([0, 7, 20], np.int32)
+    o, l = attn_fwd_fp8(f8(q), f8(k), f8(v), 0.5, 0.25, 3.0, cu, cu, causal=True)
+    back = lambda t: t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    o2, l2 = attn_fwd(back(q) * 0.5, back(k) * 0.25, back(v) * 3.0, cu, cu, causal=True)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+    o3, l3 = attn_fwd_fp8(f8(q * 2), f8(k), f8(v), 0.25, 0.25, 3.0, cu, cu, causal=True)
+    np.testing.assert_allclose(o3, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l3, l, rtol=1e-12)
