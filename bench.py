@@ -31,6 +31,8 @@ FETCH_SIZE / WRITE_SIZE counters to bytes), --workload NAME:
                         chunks of consecutive positions, run through the
                         chunked entry points (partial forwards merged, chunk
                         backwards from the merged O/LSE, dQ accumulated)
+  fp8_65k               the headline sequences with q, k, v as E4M3 codes and
+                        per-tensor descales; the step is the FP8-input forward
   dropout_65k           the headline workload with dropout p = 0.1 (Philox keep
                         mask) in the forward and the backward
   chunked_bottom_right  THD query chunks of 2048 tokens (the last tokens of
@@ -78,6 +80,13 @@ WORKLOADS = {
                "+ % MFMA peak",
         desc="dropout_65k: the throughput_65k workload with dropout p = 0.1 (Philox keep mask, "
              "seed 0x5EED, offset 0) in the forward and the backward; same FLOP model"),
+    "fp8_65k": dict(
+        layout="fp8", case="throughput_65k", fwd_only=True,
+        metric="fwd TFLOP/s (THD FP8 E4M3 inputs, bf16 out, padding_causal, hq64/hkv8/d128) "
+               "+ % MFMA peak",
+        desc="fp8_65k: the throughput_65k sequences with q, k, v quantised to E4M3 (per-tensor "
+             "descale = amax / 448); one step = the FP8-input forward (decode + forward); "
+             "FLOPs = F_fwd"),
     "chunked_bottom_right": dict(
         layout="thd",
         metric="fwd+bwd TFLOP/s (THD bf16 padding_causal_bottom_right, query chunks, "
@@ -122,7 +131,7 @@ def visible_pairs(lq: int, lk: int, causal) -> float:
     return lq * lk / 2.0 if causal else float(lq * lk)
 
 
-def cpu_baseline(case, budget_s: float = 12.0, dropout=None):
+def cpu_baseline(case, budget_s: float = 12.0, dropout=None, fwd_only=False):
     """The fp64 oracle, as it stands, on (sequence, KV group) units of the same
     workload: the sequences closest to 2400 query tokens first, KV groups 0,
     1, ... of each, until `budget_s` of CPU work has been spent."""
@@ -157,10 +166,11 @@ def cpu_baseline(case, budget_s: float = 12.0, dropout=None):
                                  for h in range(g * G, (g + 1) * G)])
                 kscale = 256.0 / (256.0 - t)
             oracle.attn_fwd_seq(q, k, v, case.scale, case.causal, keep=keep, keep_scale=kscale)
-            oracle.attn_bwd_seq(q, k, v, do, case.scale, case.causal, keep=keep,
-                                keep_scale=kscale)
+            if not fwd_only:
+                oracle.attn_bwd_seq(q, k, v, do, case.scale, case.causal, keep=keep,
+                                    keep_scale=kscale)
             spent += time.perf_counter() - t0
-            flops += 3.5 * 4.0 * case.d * G * visible_pairs(L, Lk, case.causal)
+            flops += (1.0 if fwd_only else 3.5) * 4.0 * case.d * G * visible_pairs(L, Lk, case.causal)
             units.append((int(b), L))
             if spent >= budget_s:
                 break
@@ -171,7 +181,8 @@ def cpu_baseline(case, budget_s: float = 12.0, dropout=None):
                      for b, L in seqs)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": (f"fp64 numpy oracle fwd+bwd of {desc} ({G} query heads per group) of the "
+            "sample": (f"fp64 numpy oracle {'fwd' if fwd_only else 'fwd+bwd'} of {desc} ({G} query "
+                       f"heads per group) of the "
                        f"same workload, {spent:.1f} s; FLOPs by the workload's pair model")}
 
 
@@ -206,7 +217,7 @@ def main():
     pairs = sum(visible_pairs(int(a), int(b_), case.causal)
                 for a, b_ in zip(np.diff(case.cu_seqlens_q), np.diff(case.cu_seqlens_kv)))
     f_fwd = 4.0 * case.d * case.hq * pairs
-    f_bwd = 2.5 * f_fwd
+    f_bwd = 0.0 if wl.get("fwd_only") else 2.5 * f_fwd
     q, k, v, do = (t.to(dev) for t in (case.q, case.k, case.v, case.dout))
     cu = lambda a: torch.as_tensor(a, dtype=torch.int32, device=dev)
     cq, ck = cu(case.cu_seqlens_q), cu(case.cu_seqlens_kv)
@@ -233,6 +244,19 @@ def main():
         def step(ev_f=(None,), ev_b=(None,), ev_m=None):
             A.fwd_batched(q, k, v, out=out, lse=lse, events=ev_f[0], **bkw)
             A.bwd_batched(q, k, v, out, do, lse, dq=dq, dk=dk, dv=dv, events=ev_b[0], **bkw)
+    elif wl["layout"] == "fp8":
+        def quant(t):
+            s_ = float(t.float().abs().max()) / 448.0
+            return (t.float() / s_).to(torch.float8_e4m3fn), s_
+        (q8, sq), (k8, sk), (v8, sv) = quant(q), quant(k), quant(v)
+        ws8 = torch.empty(A.fp8_workspace_size(case.batch, q.shape[0], k.shape[0], case.hq,
+                                               case.hkv, case.d), dtype=torch.uint8, device=dev)
+        n_fwd, n_bwd = 1, 0
+        fkw = dict(cu_seqlens_q_padded=cqp, cu_seqlens_kv_padded=ckp,
+                   attn_mask_type=case.mask_type, softmax_scale=case.scale, workspace=ws8)
+
+        def step(ev_f=(None,), ev_b=(), ev_m=None):
+            A.fwd_fp8(q8, k8, v8, sq, sk, sv, cq, ck, out=out, lse=lse, events=ev_f[0], **fkw)
     elif wl["layout"] == "chunks":
         # every sequence's keys in C chunks of consecutive positions (outside
         # the timed region: gathered into THD chunk tensors)
@@ -283,7 +307,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [([A.StageEvents(len(A.FWD_STAGES) + 1) for _ in range(n_fwd)],
+    fwd_stage_names = A.FP8_FWD_STAGES if wl["layout"] == "fp8" else A.FWD_STAGES
+    evs = [([A.StageEvents(len(fwd_stage_names) + 1) for _ in range(n_fwd)],
             [A.StageEvents(len(A.BWD_STAGES) + 1) for _ in range(n_bwd)],
             [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(n_fwd - 1)] if merge_ev else None)
@@ -303,7 +328,7 @@ def main():
     for ef, eb, em in evs:
         tot = {}
         for e in ef:
-            for name, ms in zip(("fwd." + s for s in A.FWD_STAGES), e.stage_ms()):
+            for name, ms in zip(("fwd." + s for s in fwd_stage_names), e.stage_ms()):
                 tot[name] = tot.get(name, 0.0) + ms
         for e in eb:
             for name, ms in zip(("bwd." + s for s in A.BWD_STAGES), e.stage_ms()):
@@ -320,6 +345,7 @@ def main():
     work = {"fwd.fwd": ("fwd", f_fwd),            # S = QK^T, O = PV
             "bwd.dkdv": ("dkdv", 2.0 * f_fwd),    # S, dP, dV = P^T dO, dK = dS^T Q
             "bwd.dq": ("dq", 1.5 * f_fwd)}        # S, dP (recomputed), dQ = dS K
+    work = {k_: w_ for k_, w_ in work.items() if k_ in avg}
     dom = max(work, key=lambda s: avg[s])
     kname, flops = work[dom]
     achieved = flops / (avg[dom] * 1e-3) / 1e12
@@ -342,7 +368,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(case, dropout=wl.get("dropout"))
+        cpu = cpu_baseline(case, dropout=wl.get("dropout"), fwd_only=bool(wl.get("fwd_only")))
 
     rec = {
         "metric": wl["metric"], "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -31,7 +31,8 @@ __all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
            "FWD_STAGES", "BWD_STAGES", "attn_fwd_batched", "attn_bwd_batched", "fwd_batched",
            "bwd_batched", "LAYOUTS", "attn_fwd_thd_chunk", "attn_bwd_thd_chunk",
            "attn_merge_thd", "fwd_chunk", "bwd_chunk", "merge", "attn_fwd_thd_dropout",
-           "attn_bwd_thd_dropout", "attention_thd"]
+           "attn_bwd_thd_dropout", "attention_thd", "attn_fwd_thd_fp8", "fwd_fp8",
+           "fp8_workspace_size"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
@@ -56,6 +57,7 @@ _FWD_ARGS = [_P, _P, _P, _P, _P,          # q k v out lse
              _P, _S, _P]                  # workspace bytes stream
 FWD_STAGES = ("sched", "fwd", "zero_fill_q")
 BWD_STAGES = ("sched", "dq", "dkdv", "zero_fill_q", "zero_fill_kv")
+FP8_FWD_STAGES = ("decode",) + FWD_STAGES
 _BWD_ARGS = [_P, _P, _P, _P, _P, _P,      # q k v out dout lse
              _P, _P, _P,                  # dq dk dv
              _P, _P, _P, _P,
@@ -146,6 +148,12 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_thd_chunk.restype = ctypes.c_int
         L.attn_merge_thd.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P]
         L.attn_merge_thd.restype = ctypes.c_int
+        L.attn_thd_fp8_workspace_size.argtypes = [_I] * 6
+        L.attn_thd_fp8_workspace_size.restype = _S
+        L.attn_fwd_thd_fp8.argtypes = [_P, _P, _P, _F, _F, _F, _P, _P, _P, _P, _P, _P,
+                                       _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P,
+                                       ctypes.POINTER(_P), _I]
+        L.attn_fwd_thd_fp8.restype = ctypes.c_int
         L.attn_fwd_thd_dropout.argtypes = _DFWD_ARGS
         L.attn_fwd_thd_dropout.restype = ctypes.c_int
         L.attn_bwd_thd_dropout.argtypes = _DBWD_ARGS
@@ -220,6 +228,16 @@ def attn_fwd_batched_timed(*args, events, n_events) -> int:
 def attn_bwd_batched_timed(*args, events, n_events) -> int:
     """attn_bwd_batched plus per-stage HIP events (see StageEvents)."""
     return int(lib().attn_bwd_batched_timed(*args, events, n_events))
+
+
+def attn_fwd_thd_fp8(*args) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_fwd_thd_fp8(*args))
+
+
+def fp8_workspace_size(batch: int, total_q: int, total_kv: int, hq: int, hkv: int,
+                       d: int) -> int:
+    return int(lib().attn_thd_fp8_workspace_size(batch, total_q, total_kv, hq, hkv, d))
 
 
 def attn_fwd_thd_dropout(*args) -> int:
@@ -747,3 +765,59 @@ def attention_thd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                    cu_seqlens_kv_padded, attn_mask_type, softmax_scale,
                                    dropout_p, rng_seed, rng_offset)
     return (out, lse) if return_lse else out
+
+
+# ----------------------------------------------------------------- FP8 inputs
+def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: float,
+            descale_k: float, descale_v: float, cu_seqlens_q: torch.Tensor,
+            cu_seqlens_kv: torch.Tensor, cu_seqlens_q_padded: Optional[torch.Tensor] = None,
+            cu_seqlens_kv_padded: Optional[torch.Tensor] = None,
+            attn_mask_type: str = "padding", softmax_scale: Optional[float] = None,
+            out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            events: Optional["StageEvents"] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward from E4M3 inputs (torch.float8_e4m3fn or uint8 codes) with per-tensor
+    descales: (out [Tq,hq,d] in out_dtype, lse [Tq,hq] float32)."""
+    dev = q8.device
+    codes = lambda t, n: _fp8_codes(t, n, dev)
+    q8, k8, v8 = codes(q8, "q8"), codes(k8, "k8"), codes(v8, "v8")
+    tq, hq, d = q8.shape
+    tk, hkv, dk_ = k8.shape
+    if v8.shape != k8.shape or dk_ != d:
+        raise AttnError("k8 and v8 must be [total_kv, hkv, d] with q8's d")
+    if out_dtype not in _DTYPE:
+        raise AttnError("out_dtype must be bf16 or fp16")
+    cq = _cu(cu_seqlens_q, "cu_seqlens_q", dev)
+    ck = _cu(cu_seqlens_kv, "cu_seqlens_kv", dev)
+    cqp = _cu(cu_seqlens_q_padded, "cu_seqlens_q_padded", dev)
+    ckp = _cu(cu_seqlens_kv_padded, "cu_seqlens_kv_padded", dev)
+    batch = cq.numel() - 1
+    if ck.numel() != batch + 1 or any(c is not None and c.numel() != batch + 1 for c in (cqp, ckp)):
+        raise AttnError("all cu_seqlens arrays need batch + 1 entries")
+    if attn_mask_type not in _MASK:
+        raise AttnError(f"attn_mask_type must be one of {sorted(_MASK)}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty((tq, hq, d), dtype=out_dtype, device=dev) if out is None else out
+    lse = torch.empty((tq, hq), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", out_dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    need = fp8_workspace_size(batch, tq, tk, hq, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = attn_fwd_thd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), float(descale_q),
+                          float(descale_k), float(descale_v), out.data_ptr(), lse.data_ptr(),
+                          cq.data_ptr(), ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk, hq,
+                          hkv, d, scale, _MASK[attn_mask_type], _DTYPE[out_dtype],
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          torch.cuda.current_stream(dev).cuda_stream,
+                          None if events is None else events.ptr,
+                          0 if events is None else events.n)
+    _check(st, "attn_fwd_thd_fp8")
+    return out, lse
+
+
+def _fp8_codes(t: torch.Tensor, name: str, dev) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _need(t, name, torch.uint8, dev)
+    return t

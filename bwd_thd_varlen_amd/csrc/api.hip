@@ -19,6 +19,7 @@ hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tile
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st);
 hipError_t launch_merge(void* out, float* lse, const void* out_part, const float* lse_part,
                         int64_t rows, int d, int dtype, hipStream_t st);
+hipError_t launch_decode_e4m3(const void* src, void* dst, int64_t n, int dtype, hipStream_t st);
 int dkdv_tile(int d);
 }  // namespace attn
 
@@ -82,6 +83,7 @@ struct CallOpts {
   uint32_t drop_t = 0;        // dropout byte threshold round(256 p), 0 = none
   uint64_t seed = 0;
   uint32_t offset = 0;
+  float out_scale = 1.f;      // forward output multiplier
   int32_t tsq(int32_t batch) const { return layout == kLayoutSbhd ? batch : 1; }
 };
 constexpr CallOpts kThd = {};
@@ -175,6 +177,7 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.seed_hi = (uint32_t)(geo.seed >> 32);
   a.drop_c3 = geo.offset * (uint32_t)hq;
   a.drop_scale = 256.f / (float)(256u - geo.drop_t);
+  a.out_scale = geo.out_scale;
   return a;
 }
 
@@ -527,6 +530,81 @@ attn_thd_status attn_bwd_thd_dropout(const void* q, const void* k, const void* v
   return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
                   cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
                   scale, mask_type, dtype, workspace, workspace_bytes, stream, events, n_events, o);
+}
+
+// ----------------------------------------------------------------- FP8 inputs
+// Workspace of the FP8 forward: the plain layout, then 16-bit copies of q, k
+// and v (each 256-byte aligned).
+struct Fp8Layout {
+  size_t base, q, k, v, total;
+};
+static Fp8Layout fp8_layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq,
+                            int32_t hkv, int32_t d) {
+  Fp8Layout f;
+  f.base = layout(batch, total_q, total_kv, hq).total;
+  f.q = f.base;
+  f.k = f.q + round_up((size_t)total_q * hq * d * 2);
+  f.v = f.k + round_up((size_t)total_kv * hkv * d * 2);
+  f.total = f.v + round_up((size_t)total_kv * hkv * d * 2);
+  return f;
+}
+
+size_t attn_thd_fp8_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq,
+                                   int32_t hkv, int32_t d) {
+  if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return 0;
+  return fp8_layout(batch, total_q, total_kv, hq, hkv, d).total;
+}
+
+attn_thd_status attn_fwd_thd_fp8(const void* q8, const void* k8, const void* v8, float descale_q,
+                                 float descale_k, float descale_v, void* out, float* lse,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                 const int32_t* cu_seqlens_q_padded,
+                                 const int32_t* cu_seqlens_kv_padded, int32_t batch,
+                                 int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv,
+                                 int32_t d, float scale, int32_t mask_type, int32_t out_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events, int32_t n_events) {
+  if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return ATTN_THD_EINVAL;
+  if (events && n_events != kFwdStages + 2) return ATTN_THD_EINVAL;
+  for (float s : {descale_q, descale_k, descale_v})
+    if (!(s > 0.f) || !std::isfinite(s)) return ATTN_THD_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale) || !std::isfinite(scale * descale_q * descale_k) ||
+      !(scale * descale_q * descale_k > 0.f))
+    return ATTN_THD_EINVAL;
+  if ((total_q > 0 && !q8) || (total_kv > 0 && (!k8 || !v8))) return ATTN_THD_EINVAL;
+  // 8 codes per load: rows of d (a multiple of 8) bytes need 8-byte alignment
+  auto al8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; };
+  if (!al8(q8) || !al8(k8) || !al8(v8)) return ATTN_THD_EINVAL;
+  if (d % 8 != 0 || d > 256) return ATTN_THD_EUNSUPPORTED;
+  if (out_dtype != ATTN_THD_BF16 && out_dtype != ATTN_THD_FP16) return ATTN_THD_EUNSUPPORTED;
+  const Fp8Layout f = fp8_layout(batch, total_q, total_kv, hq, hkv, d);
+  char* ws = static_cast<char*>(workspace);
+  void* q16 = ws + f.q;
+  void* k16 = ws + f.k;
+  void* v16 = ws + f.v;
+  // the forward's own checks first (in its order), so that nothing is
+  // launched on bad arguments; then room for the decoded copies
+  Common c;
+  attn_thd_status st = check_common(q16, k16, v16, cu_seqlens_q, cu_seqlens_kv, batch, total_q,
+                                    total_kv, hq, hkv, d, scale * descale_q * descale_k,
+                                    mask_type, out_dtype, workspace, f.base, kThd, c);
+  if (st != ATTN_THD_OK) return st;
+  if (workspace_bytes < f.total) return ATTN_THD_EWORKSPACE;
+  if (total_q > 0 && (!out || !lse)) return ATTN_THD_EINVAL;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_THD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Marks m{events, n_events, s};
+  ATTN_TRY(m.mark(0));
+  ATTN_TRY(launch_decode_e4m3(q8, q16, (int64_t)total_q * hq * d, out_dtype, s));
+  ATTN_TRY(launch_decode_e4m3(k8, k16, (int64_t)total_kv * hkv * d, out_dtype, s));
+  ATTN_TRY(launch_decode_e4m3(v8, v16, (int64_t)total_kv * hkv * d, out_dtype, s));
+  CallOpts o = kThd;
+  o.out_scale = descale_v;
+  // the forward marks events[1..4]
+  return fwd_impl(q16, k16, v16, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
+                  cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
+                  scale * descale_q * descale_k, mask_type, out_dtype, workspace, f.base, stream,
+                  events ? events + 1 : nullptr, events ? n_events - 1 : 0, o);
 }
 
 // ----------------------------------------------------------------- chunked form

@@ -493,6 +493,7 @@ struct AttnParams {
   // scaled by drop_scale = 256 / (256 - drop_t)
   uint32_t drop_t, seed_lo, seed_hi, drop_c3;   // drop_c3 = offset * hq
   float drop_scale;
+  float out_scale;     // forward output multiplier (the V descale of FP8 inputs; else 1)
 };
 constexpr int32_t kAccDq = 1, kAccDkDv = 2;
 

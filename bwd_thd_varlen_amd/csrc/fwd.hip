@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 
   const float l_tot = sum_halves(l_run);
   if (qi < s.lq) {
-    const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (DROP ? p.drop_scale : 1.f) * p.out_scale / l_tot : 0.f;
     const int64_t row = (int64_t)s.oq + (int64_t)qi * p.tsq;
     uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + row * qrs + (int64_t)h * p.d;
 #pragma unroll

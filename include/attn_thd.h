@@ -256,6 +256,36 @@ attn_thd_status attn_bwd_thd_dropout(
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int32_t n_events);
 
+/*
+ * Forward from FP8 inputs (issue 2892, "SIGSEGV in fused_attn_fwd when
+ * cu_seqlens_q != cu_seqlens_q_padded with FP8 blockwise", runs this forward
+ * on THD inputs with real != padded boundaries; the arithmetic below is the
+ * library's own specification of it):
+ *   q8, k8, v8  E4M3 codes (OCP 8-bit floating point, torch.float8_e4m3fn),
+ *               same shapes and layouts as q, k, v of attn_fwd_thd, 8-byte
+ *               aligned; descale_* > 0 their per-tensor float factors:
+ *   O   = softmax(scale * descale_q * descale_k * Q8 K8^T + mask) (descale_v * V8)
+ *   LSE = natural log-sum-exp of those scaled scores (float32 [total_q, hq])
+ * out is written in out_dtype (ATTN_THD_BF16 or ATTN_THD_FP16).  The codes
+ * are decoded exactly into 16-bit copies in the workspace, whose size is
+ * attn_thd_fp8_workspace_size(...) (larger than attn_thd_workspace_size).
+ * Boundaries, masks, written rows, errors and stream semantics as
+ * attn_fwd_thd; NaN codes propagate.  events / n_events: NULL / 0, or 5
+ * events around the stages decode, scheduler, forward kernel, zero fill.
+ */
+size_t attn_thd_fp8_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv,
+                                   int32_t hq, int32_t hkv, int32_t d);
+
+attn_thd_status attn_fwd_thd_fp8(
+    const void* q8, const void* k8, const void* v8,
+    float descale_q, float descale_k, float descale_v, void* out, float* lse,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t out_dtype,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
 enum { ATTN_THD_ACC_DQ = 1, ATTN_THD_ACC_DKDV = 2 };   /* accumulate bits */
 
 attn_thd_status attn_fwd_thd_chunk(

@@ -188,3 +188,22 @@ def test_dropout_probability_range(A, p, code):
     bargs = [FAKE] * 9 + [FAKE, FAKE, None, None, 2, 16, 16, 4, 2, 64, 0.125, 1, p, 1234, 0, 0,
                           None, 0, None, None, 0]
     assert A.attn_bwd_thd_dropout(*bargs) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(), 3), (dict(sq=0.0), 1), (dict(sv=float("inf")), 1), (dict(sk=-1.0), 1),
+    (dict(q8=FAKE + 4), 1), (dict(d=12), 2), (dict(out_dtype=9), 2), (dict(mask=4), 2),
+    (dict(hq=4, hkv=3), 1),
+])
+def test_fp8_forward_rejects_bad_host_arguments(A, over, code):
+    args = dict(q8=FAKE, k8=FAKE, v8=FAKE, sq=0.5, sk=0.5, sv=2.0, out=FAKE, lse=FAKE,
+                cu_q=FAKE, cu_kv=FAKE, cu_qp=None, cu_kp=None, batch=2, total_q=16, total_kv=16,
+                hq=4, hkv=2, d=64, scale=0.125, mask=1, out_dtype=0, ws=None, wsb=0, stream=None,
+                events=None, n_events=0)
+    args.update(over)
+    assert A.attn_fwd_thd_fp8(*args.values()) == code
+
+
+def test_fp8_workspace_is_larger(A):
+    assert A.fp8_workspace_size(2, 100, 80, 8, 2, 64) >= \
+        A.workspace_size(2, 100, 80, 8, 2, 64) + (100 * 8 + 2 * 80 * 2) * 64 * 2

@@ -1,0 +1,84 @@
+"""GPU parity of the FP8-input forward (attn_fwd_thd_fp8).
+
+The E4M3 decode is exact (every code is a bf16 / fp16 value): with one query
+and one key the output is the value row itself, so O must equal the decoded
+codes bit for bit for all 256 of them.  The forward on the FP8 page's THD
+shape (TE-2892 "Reproduction": real [100,150,120,130] in padded
+[112,160,128,144], 32 heads, d = 48, real != padded) and on a GQA d = 128 case
+is compared with the oracle at the bar of the 16-bit output dtype.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import assert_close, assert_lse_close, cu_dev, f64, real_rows
+from oracle.fp8 import attn_fwd_fp8, decode_e4m3
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_decode_exact_for_every_code(out_dtype):
+    import bwd_thd_varlen_amd as A
+    d = 256
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(1, 1, d)
+    q8 = torch.full((1, 1, d), 0x38, dtype=torch.uint8)     # 1.0
+    cu = cu_dev([0, 1])
+    o, l = A.fwd_fp8(q8.cuda(), q8.cuda(), codes.cuda(), 1.0, 1.0, 1.0, cu, cu,
+                     out_dtype=out_dtype)
+    want = decode_e4m3(codes.numpy())[0, 0]
+    got = o.float().cpu().numpy()[0, 0]
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # one key: LSE = its scaled score
+    assert abs(float(l[0, 0]) - float(np.dot(np.ones(d), np.ones(d))) / np.sqrt(d)) < 1e-3
+
+
+def _quantize(x: torch.Tensor):
+    """Per-tensor E4M3 codes and descale (amax maps to 448)."""
+    s = float(x.abs().max()) / 448.0
+    return (x / s).to(torch.float8_e4m3fn).view(torch.uint8), s
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_fp8_real_vs_padded_te2892_shape(causal, out_dtype):
+    import bwd_thd_varlen_amd as A
+    rng = np.random.default_rng(90)
+    real, padded = [100, 150, 120, 130], [112, 160, 128, 144]
+    T, H, d = sum(padded) + 32, 32, 48                     # 32 rows past every slot
+    x = lambda: torch.from_numpy(rng.standard_normal((T, H, d), dtype=np.float32))
+    (q8, sq), (k8, sk), (v8, sv) = _quantize(x()), _quantize(x()), _quantize(x())
+    cu = np.concatenate([[0], np.cumsum(real)]).astype(np.int32)
+    cp = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    mask = "padding_causal" if causal else "padding"
+    o, l = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, cu_dev(cu), cu_dev(cu),
+                     cu_dev(cp), cu_dev(cp), attn_mask_type=mask, out_dtype=out_dtype)
+    ro, rl = attn_fwd_fp8(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv, cu, cu, cp, cp,
+                          causal=causal)
+    rows = real_rows(cu, cp, T)
+    dt = "bf16" if out_dtype == torch.bfloat16 else "fp16"
+    assert_close("out", o, ro, dt, rows)
+    assert_lse_close(l, rl, rows)
+    assert int(torch.count_nonzero(o[torch.as_tensor(~rows, device="cuda")].float())) == 0
+    assert bool(torch.all(torch.isneginf(l[torch.as_tensor(~rows, device="cuda")])))
+
+
+def test_fp8_gqa_d128_bottom_right():
+    import bwd_thd_varlen_amd as A
+    rng = np.random.default_rng(91)
+    lq, lk = [64, 200, 33], [130, 200, 9]
+    pq, pk = [64, 208, 40], [136, 200, 16]
+    Tq, Tk = sum(pq), sum(pk)
+    g = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32))
+    (q8, sq), (k8, sk), (v8, sv) = _quantize(g(Tq, 8, 128)), _quantize(g(Tk, 2, 128)), \
+        _quantize(g(Tk, 2, 128))
+    cu = lambda a: np.concatenate([[0], np.cumsum(a)]).astype(np.int32)
+    o, l = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, cu_dev(cu(lq)), cu_dev(cu(lk)),
+                     cu_dev(cu(pq)), cu_dev(cu(pk)), attn_mask_type="padding_causal_bottom_right")
+    ro, rl = attn_fwd_fp8(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv, cu(lq), cu(lk),
+                          cu(pq), cu(pk), causal="bottom_right")
+    rows = real_rows(cu(lq), cu(pq), Tq, cu(lk))
+    assert_close("out", o, ro, "bf16", rows)
+    assert_lse_close(l, rl, rows)
