@@ -84,6 +84,8 @@ struct CallOpts {
   uint64_t seed = 0;
   uint32_t offset = 0;
   float out_scale = 1.f;      // forward output multiplier
+  const void* q8 = nullptr;   // E4M3 q and k for the forward's 8-bit scores
+  const void* k8 = nullptr;
   int32_t tsq(int32_t batch) const { return layout == kLayoutSbhd ? batch : 1; }
 };
 constexpr CallOpts kThd = {};
@@ -178,6 +180,8 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.drop_c3 = geo.offset * (uint32_t)hq;
   a.drop_scale = 256.f / (float)(256u - geo.drop_t);
   a.out_scale = geo.out_scale;
+  a.q8 = geo.q8;
+  a.k8 = geo.k8;
   return a;
 }
 
@@ -582,12 +586,17 @@ attn_thd_status attn_fwd_thd_fp8(const void* q8, const void* k8, const void* v8,
   void* q16 = ws + f.q;
   void* k16 = ws + f.k;
   void* v16 = ws + f.v;
+  // head dims 80..128 (multiples of 16) with 16-byte aligned codes take the
+  // scores on the 8-bit products straight from q8 / k8; other shapes decode
+  // q and k too and run the 16-bit forward
+  const bool s8 = d % 16 == 0 && d > 64 && d <= 128 && aligned16(q8) && aligned16(k8);
   // the forward's own checks first (in its order), so that nothing is
   // launched on bad arguments; then room for the decoded copies
   Common c;
-  attn_thd_status st = check_common(q16, k16, v16, cu_seqlens_q, cu_seqlens_kv, batch, total_q,
-                                    total_kv, hq, hkv, d, scale * descale_q * descale_k,
-                                    mask_type, out_dtype, workspace, f.base, kThd, c);
+  attn_thd_status st = check_common(s8 ? q8 : q16, s8 ? k8 : k16, v16, cu_seqlens_q, cu_seqlens_kv,
+                                    batch, total_q, total_kv, hq, hkv, d,
+                                    scale * descale_q * descale_k, mask_type, out_dtype, workspace,
+                                    f.base, kThd, c);
   if (st != ATTN_THD_OK) return st;
   if (workspace_bytes < f.total) return ATTN_THD_EWORKSPACE;
   if (total_q > 0 && (!out || !lse)) return ATTN_THD_EINVAL;
@@ -595,11 +604,17 @@ attn_thd_status attn_fwd_thd_fp8(const void* q8, const void* k8, const void* v8,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Marks m{events, n_events, s};
   ATTN_TRY(m.mark(0));
-  ATTN_TRY(launch_decode_e4m3(q8, q16, (int64_t)total_q * hq * d, out_dtype, s));
-  ATTN_TRY(launch_decode_e4m3(k8, k16, (int64_t)total_kv * hkv * d, out_dtype, s));
+  if (!s8) {
+    ATTN_TRY(launch_decode_e4m3(q8, q16, (int64_t)total_q * hq * d, out_dtype, s));
+    ATTN_TRY(launch_decode_e4m3(k8, k16, (int64_t)total_kv * hkv * d, out_dtype, s));
+  }
   ATTN_TRY(launch_decode_e4m3(v8, v16, (int64_t)total_kv * hkv * d, out_dtype, s));
   CallOpts o = kThd;
   o.out_scale = descale_v;
+  if (s8) {
+    o.q8 = q8;
+    o.k8 = k8;
+  }
   // the forward marks events[1..4]
   return fwd_impl(q16, k16, v16, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
                   cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,

@@ -81,6 +81,18 @@ template <> struct Mfma<kBF16> {
   }
 };
 
+// C += A B with E4M3 operands (OCP 8-bit floating point): the 32 x 32 x 64
+// product; each operand is 32 codes per lane (row / column lane & 31, k range
+// 32 (lane >> 5) .. +32) passed as two 16-byte halves; block scales 1.
+__device__ __forceinline__ f32x16 mma_e4m3(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  const v8i a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const v8i b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                 (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 template <> struct Mfma<kFP16> {
   static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -494,6 +506,8 @@ struct AttnParams {
   uint32_t drop_t, seed_lo, seed_hi, drop_c3;   // drop_c3 = offset * hq
   float drop_scale;
   float out_scale;     // forward output multiplier (the V descale of FP8 inputs; else 1)
+  const void* q8;      // forward with E4M3 q and k (the scores on the 8-bit products)
+  const void* k8;
 };
 constexpr int32_t kAccDq = 1, kAccDkDv = 2;
 

@@ -16,6 +16,8 @@
 // scale*log2(e)*S, l = running sum of exp2(x - m); the reference (and with it
 // O and l, by exp2(m_old - m_new)) moves only when a row's maximum passes it
 // by more than kRescaleSlack.
+#include <type_traits>
+
 #include "common.h"
 
 namespace attn {
@@ -31,14 +33,20 @@ constexpr float kRescaleSlack = 8.0f;
 template <int DPAD>
 constexpr int fwd_step_keys() { return (DPAD >= 64 && DPAD <= 128) ? 32 : 64; }
 
-// DROP: dropout on the probabilities (the keep mask of dropout_block)
-template <int DT, int DPAD, bool CAUSAL, bool DROP>
+// DROP: dropout on the probabilities (the keep mask of dropout_block).
+// F8: q and k are E4M3 codes (p.q8, p.k8): Q stays in registers as codes, K
+// tiles hold DPAD code bytes per row, and S^T = K Q^T is taken on the 8-bit
+// 32 x 32 x 64 product, whose result tile has the layout of the 16-bit one.
+template <int DT, int DPAD, bool CAUSAL, bool DROP, bool F8 = false>
 __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParams p) {
-  constexpr int NT = DPAD / 16;        // 16-wide k chunks over the head dim
+  static_assert(!F8 || DPAD == 128, "the 8-bit scores are built for head dims 80..128");
+  constexpr int NT = F8 ? 1 : DPAD / 16;   // 16-wide k chunks over the head dim (16-bit Q)
+  constexpr int NT8 = DPAD / 64;           // 64-wide k chunks (E4M3 Q)
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
   constexpr int KS = fwd_step_keys<DPAD>();   // keys per step
   constexpr int NKB = KS / 32;         // 32-key blocks of S^T per step
-  using LK = Swz<DPAD>;          // K: row reads
+  // K: row reads (E4M3: DPAD bytes per row, addressed in 16-bit units)
+  using LK = std::conditional_t<F8, Swz<DPAD / 2>, Swz<DPAD>>;
   using LV = Swz<DPAD>;          // V: transposed reads
   using DmaK = TileDma<LK, KS, 4>;
   using DmaV = TileDma<LV, KS, 4>;
@@ -67,8 +75,11 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
   const int64_t qts = qrs * p.tsq, kvts = kvrs * p.tskv;
   const uint32_t kv_rs_bytes = (uint32_t)(kvts * 2);
+  const uint32_t k_rs_bytes = F8 ? (uint32_t)kvts : kv_rs_bytes;
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)s.oq * qrs + (int64_t)h * p.d;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
+  const uint8_t* qb8 = static_cast<const uint8_t*>(p.q8) + (int64_t)s.oq * qrs + (int64_t)h * p.d;
+  const uint8_t* kb8 = static_cast<const uint8_t*>(p.k8) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
 
@@ -83,20 +94,32 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 
   DmaK dma_k;
   DmaV dma_v;
-  dma_k.init(wave, lane, p.d, kv_rs_bytes);
+  dma_k.init(wave, lane, F8 ? p.d / 2 : p.d, k_rs_bytes);
   dma_v.init(wave, lane, p.d, kv_rs_bytes);
   auto issue = [&](int step, uint16_t* tK, uint16_t* tV) {
     const int n0 = step * KS;
-    dma_k.issue(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tK, nullptr, wave);
+    const uint16_t* krow = F8 ? reinterpret_cast<const uint16_t*>(kb8 + (int64_t)n0 * kvts)
+                              : kb + (int64_t)n0 * kvts;
+    dma_k.issue(krow, kend - n0, k_rs_bytes, tK, nullptr, wave);
     dma_v.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tV, nullptr, wave);
   };
   if (nsteps > 0) issue(0, sK0, sV0);
 
   u32x4 qreg[NT];
+  u32x4 q8lo[F8 ? NT8 : 1], q8hi[F8 ? NT8 : 1];   // E4M3 Q: codes 64 t + 32 hh + (0..31)
+  if constexpr (F8) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int c = 16 * t + 8 * hh;
-    qreg[t] = (qi < s.lq && c < p.d) ? ldg16(qb + (int64_t)qi * qts + c) : z4;
+    for (int t = 0; t < NT8; ++t) {
+      const int c = 64 * t + 32 * hh;
+      q8lo[t] = (qi < s.lq && c < p.d) ? ldg16(qb8 + (int64_t)qi * qts + c) : z4;
+      q8hi[t] = (qi < s.lq && c + 16 < p.d) ? ldg16(qb8 + (int64_t)qi * qts + c + 16) : z4;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int c = 16 * t + 8 * hh;
+      qreg[t] = (qi < s.lq && c < p.d) ? ldg16(qb + (int64_t)qi * qts + c) : z4;
+    }
   }
   wait_vm<0>();   // Q and the first step's tiles; keeps the compiler from re-waiting in the loop
 
@@ -118,9 +141,18 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2) {
         sc[kb2] = zero16();
+        if constexpr (F8) {
+          // key row 32 kb2 + li, code bytes 64 t + 32 hh .. +32 (16-bit columns 32 t + 16 hh)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          sc[kb2] = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
+          for (int t = 0; t < NT8; ++t)
+            sc[kb2] = mma_e4m3(lds_row8<LK>(tK, 32 * kb2 + li, 32 * t + 16 * hh),
+                               lds_row8<LK>(tK, 32 * kb2 + li, 32 * t + 16 * hh + 8),
+                               q8lo[t], q8hi[t], sc[kb2]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            sc[kb2] = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
+        }
       }
       const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo_k);
       if (need_mask) {
@@ -199,6 +231,13 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 
 template <int DT, int DPAD>
 static void launch_fwd_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
+  if constexpr (DPAD == 128) {
+    if (p.q8) {   // E4M3 q and k (no dropout on this path)
+      if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, false, true>), dim3(grid), dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, false, true>), dim3(grid), dim3(256), 0, st, p);
+      return;
+    }
+  }
   const bool drop = p.drop_t != 0;
   if (causal && drop) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, true>), dim3(grid), dim3(256), 0, st, p);
   else if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, false>), dim3(grid), dim3(256), 0, st, p);

@@ -82,3 +82,47 @@ def test_fp8_gqa_d128_bottom_right():
     rows = real_rows(cu(lq), cu(pq), Tq, cu(lk))
     assert_close("out", o, ro, "bf16", rows)
     assert_lse_close(l, rl, rows)
+
+
+@pytest.mark.parametrize("d,causal", [(80, True), (96, False), (128, True)])
+def test_fp8_scores_on_8bit_products(d, causal):
+    """Head dims 80..128 (multiples of 16) take the scores on the E4M3 MFMA."""
+    import bwd_thd_varlen_amd as A
+    rng = np.random.default_rng(92 + d)
+    L, P = [1, 77, 300, 129], [8, 80, 300, 136]
+    T = sum(P)
+    g = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32))
+    (q8, sq), (k8, sk), (v8, sv) = _quantize(g(T, 8, d)), _quantize(g(T, 2, d)), \
+        _quantize(g(T, 2, d))
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    cp = np.concatenate([[0], np.cumsum(P)]).astype(np.int32)
+    mask = "padding_causal" if causal else "padding"
+    o, l = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, cu_dev(cu), cu_dev(cu),
+                     cu_dev(cp), cu_dev(cp), attn_mask_type=mask)
+    ro, rl = attn_fwd_fp8(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv, cu, cu, cp, cp,
+                          causal=causal)
+    rows = real_rows(cu, cp, T)
+    assert_close("out", o, ro, "bf16", rows)
+    assert_lse_close(l, rl, rows)
+
+
+def test_fp8_paths_agree():
+    """The 8-bit-product path and the decode path (taken when the codes are only
+    8-byte aligned) compute the same scores up to summation order."""
+    import bwd_thd_varlen_amd as A
+    rng = np.random.default_rng(99)
+    L = [200, 57]
+    T, d = sum(L), 128
+    g = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32))
+    (q8, sq), (k8, sk), (v8, sv) = _quantize(g(T, 4, d)), _quantize(g(T, 4, d)), \
+        _quantize(g(T, 4, d))
+    cu = cu_dev(np.concatenate([[0], np.cumsum(L)]))
+    o1, l1 = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, cu, cu,
+                       attn_mask_type="padding_causal")
+    buf = torch.zeros(q8.numel() + 16, dtype=torch.uint8, device="cuda")
+    q8m = buf[8:8 + q8.numel()].view(q8.shape)          # 8-byte aligned only
+    q8m.copy_(q8.cuda())
+    o2, l2 = A.fwd_fp8(q8m, k8.cuda(), v8.cuda(), sq, sk, sv, cu, cu,
+                       attn_mask_type="padding_causal")
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-2 * o2.float().abs().max().item()
+    assert (l1 - l2).abs().max().item() <= 1e-3
