@@ -89,7 +89,7 @@ WORKLOADS = {
         metric="fwd TFLOP/s (THD FP8 E4M3 inputs, bf16 out, padding_causal, hq64/hkv8/d128) "
                "+ % MFMA peak",
         desc="fp8_65k: the throughput_65k sequences with q, k, v quantised to E4M3 (per-tensor "
-             "descale = amax / 448); one step = the FP8-input forward (decode + forward); "
+             "descale = amax / 448); one step = the FP8-input forward (decode of V + forward); "
              "FLOPs = F_fwd"),
     "chunked_bottom_right": dict(
         layout="thd",

@@ -2,7 +2,7 @@
 
 Two modes, each run on the databases a GPU run left behind:
 
-  python -m bwd_thd_varlen_amd.rocprof_summary trace DB OUT.md --command CMD
+  python -m bwd_thd_varlen_amd.rocprof_summary trace DB OUT.md --command CMD [--title T]
       kernel-trace summary (calls, average and total duration per kernel)
       from the ``top_kernels`` view of a ``rocprofv3 --kernel-trace --stats``
       database.
@@ -67,25 +67,35 @@ def _rows(db: str, sql: str):
         con.close()
 
 
-def trace(db: str, out: str, command: str) -> None:
+TRACE_TITLE = "throughput_65k (65536 tokens, hq=64 hkv=8 d=128, bf16, padding_causal)"
+
+
+def trace(db: str, out: str, command: str, title: str = TRACE_TITLE) -> None:
     rows = _rows(db, "select * from top_kernels")
     total = sum(r[2] for r in rows)
     lines = [
-        "# Kernel trace: throughput_65k (65536 tokens, hq=64 hkv=8 d=128, bf16, padding_causal)",
+        f"# Kernel trace: {title}",
         "",
         "Command (run from the repository root on one MI355X, `TMPDIR=/tmp`):",
         "",
         f"    {command}",
         "",
         "Durations in microseconds, from the `top_kernels` view of the rocprofv3",
-        "results database (every dispatch of the run: warm-up and timed steps).",
+        "results database (every dispatch of the run: warm-up and timed steps);",
+        "median and minimum from the per-dispatch `kernels` view.",
         "",
-        "| kernel | calls | avg us | total us | share |",
-        "|---|---|---|---|---|",
+        "| kernel | calls | avg us | median us | min us | total us | share |",
+        "|---|---|---|---|---|---|---|",
     ]
+    per = defaultdict(list)
+    for name, dur in _rows(db, "select name, end - start from kernels"):
+        per[name].append(dur / 1000.0)
     for name, calls, tot, avg, *_ in rows:
         short = name.split("(")[0].replace("void ", "")
-        lines.append(f"| {short} | {calls} | {avg:.1f} | {tot:.1f} | {100.0 * tot / total:.2f}% |")
+        ds = sorted(per.get(name, [avg]))
+        med = 0.5 * (ds[(len(ds) - 1) // 2] + ds[len(ds) // 2])
+        lines.append(f"| {short} | {calls} | {avg:.1f} | {med:.1f} | {ds[0]:.1f} | {tot:.1f} "
+                     f"| {100.0 * tot / total:.2f}% |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {out}")
@@ -151,6 +161,7 @@ def main(argv=None) -> None:
     t.add_argument("db")
     t.add_argument("out")
     t.add_argument("--command", required=True)
+    t.add_argument("--title", default=TRACE_TITLE)
     c = sub.add_parser("traffic")
     c.add_argument("fetch_db")
     c.add_argument("write_db")
@@ -158,7 +169,7 @@ def main(argv=None) -> None:
     c.add_argument("--command-write", required=True)
     a = ap.parse_args(argv)
     if a.mode == "trace":
-        trace(a.db, a.out, a.command)
+        trace(a.db, a.out, a.command, a.title)
     else:
         traffic(a.fetch_db, a.write_db, a.command_fetch, a.command_write)
 
