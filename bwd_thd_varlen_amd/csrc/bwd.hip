@@ -277,6 +277,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   const int nm = m_last > m_first ? m_last - m_first : 0;
   const int nsteps = nm * p.group;
   const int h0 = g * p.group;
+  // step -> (query tile, head of the group): query tiles from the last one
+  // down, the group's heads inside.  Key tiles of a sequence that start
+  // together then read the same Q / dO tiles at the same time (from L2).
+  auto step_tile = [&](int step, int& m, int& hg) {
+    const int t = step / p.group;
+    hg = step - t * p.group;
+    m = m_last - 1 - t;
+  };
 
   Dma dma_q;
   dma_q.init(wave, lane, p.d, q_rs_bytes);
@@ -288,8 +296,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     uint16_t* tQ = sQ[buf];
     uint16_t* tdO = sdO[buf];
     float* tvec = sVec[buf];
-    const int hg = step / nm;
-    const int m = m_first + (step - hg * nm);
+    int m, hg;
+    step_tile(step, m, hg);
     const int h = h0 + hg;
     const int i0 = m * BM;
     const int nrow = s.lq - i0;
@@ -343,8 +351,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     const RowReader<LQ> rq(sQ[buf], lane), rdo(sdO[buf], lane);
     const TrReader<LQ> trq(sQ[buf], lane), trdo(sdO[buf], lane);
     const float* tvec = sVec[buf];
-    const int hg = step / nm;
-    const int i0 = (m_first + (step - hg * nm)) * BM;
+    int m, hg;
+    step_tile(step, m, hg);
+    const int i0 = m * BM;
     const int h_step = h0 + hg;   // query head of this step
     // waves with no real key, or whose keys all follow every query, idle
     if (wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q)) {
