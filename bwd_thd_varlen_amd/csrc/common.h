@@ -43,7 +43,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kQTile = 128;      // query rows per forward / dQ work item (4 waves x 32)
 constexpr int kKVStep = 64;      // keys per inner step of the forward / dQ kernels
 constexpr int kMinTile = 64;     // smallest tile any list uses (sizes the lists)
-constexpr int kSchedKeys = 2048; // distinct work keys of the longest-first ordering
+constexpr int kSchedKeys = 2048; // distinct work keys of the heaviest-first ordering
 
 // Workspace header (int32 words at the start of the workspace).
 constexpr int kHdrStatus = 0;

@@ -7,8 +7,9 @@
 // Sequences without a real query or without a real key get no tile: their
 // rows are written by the zero fill, which also covers padding rows and rows
 // outside every slot (issue 2448, "Expected behavior": KV of a sequence with
-// no valid query must come back as zeros).  Tiles are listed heaviest first
-// so that the long causal tiles start early.
+// no valid query must come back as zeros).  Tiles are grouped by sequence,
+// heaviest sequence first and heaviest tile first within it, so that the long
+// causal tiles start early and a sequence's tiles run together.
 #include "common.h"
 
 namespace attn {
@@ -31,6 +32,17 @@ __device__ __forceinline__ int q_tile_key(const SeqInfo& s, int m, int tile, int
 __device__ __forceinline__ int kv_tile_key(const SeqInfo& s, int n, int tile, int causal) {
   int q = causal ? max(0, s.lq - max(0, n * tile - s.diag)) : s.lq;
   return min(cdiv(q, 64), kSchedKeys - 1);
+}
+
+// Work key of a sequence's key tiles: that of its first tile, the heaviest
+// (the queries that reach key tile n never grow with n).
+__device__ __forceinline__ int seq_kv_key(const SeqInfo& s, int tile, int causal) {
+  return kv_tile_key(s, 0, tile, causal);
+}
+
+// Work key of a sequence's n query tiles: that of its last, the heaviest.
+__device__ __forceinline__ int seq_q_key(const SeqInfo& s, int n, int tile, int causal) {
+  return q_tile_key(s, n - 1, tile, causal);
 }
 
 // Exclusive prefix over hist[] in DESCENDING key order, in place:
@@ -67,9 +79,14 @@ __device__ int scan_desc(int* hist, int* part) {
 }
 
 // Builds one list.  kv_side selects which length is tiled.  The order of
-// tiles with equal keys depends on LDS atomics and is not fixed; every output
+// items with equal keys depends on LDS atomics and is not fixed; every output
 // element is produced by exactly one work item with a fixed internal order,
 // so results do not depend on the list order.
+//
+// Tiles are listed by sequence, the sequence with the heaviest tile first,
+// each sequence's tiles contiguous and heaviest first: the tiles of a
+// sequence then run together and read the other side's tiles in step
+// (shared in L2).
 __device__ int build_list(const SchedParams& p, bool kv_side, int tile, int2* list, int* hist,
                           int* part) {
   const int tid = threadIdx.x;
@@ -79,10 +96,7 @@ __device__ int build_list(const SchedParams& p, bool kv_side, int tile, int2* li
     SeqInfo s = p.seq[b];
     if (s.lq == 0 || s.lk == 0) continue;
     const int n = cdiv(kv_side ? s.lk : s.lq, tile);
-    for (int t = 0; t < n; ++t) {
-      int key = kv_side ? kv_tile_key(s, t, tile, p.causal) : q_tile_key(s, t, tile, p.causal);
-      atomicAdd(&hist[key], 1);
-    }
+    atomicAdd(&hist[kv_side ? seq_kv_key(s, tile, p.causal) : seq_q_key(s, n, tile, p.causal)], n);
   }
   __syncthreads();
   const int total = scan_desc(hist, part);
@@ -90,11 +104,11 @@ __device__ int build_list(const SchedParams& p, bool kv_side, int tile, int2* li
     SeqInfo s = p.seq[b];
     if (s.lq == 0 || s.lk == 0) continue;
     const int n = cdiv(kv_side ? s.lk : s.lq, tile);
-    for (int t = 0; t < n; ++t) {
-      int key = kv_side ? kv_tile_key(s, t, tile, p.causal) : q_tile_key(s, t, tile, p.causal);
-      int pos = atomicAdd(&hist[key], 1);
-      list[pos] = make_int2(b, t);
-    }
+    const int pos =
+        atomicAdd(&hist[kv_side ? seq_kv_key(s, tile, p.causal) : seq_q_key(s, n, tile, p.causal)], n);
+    // tiles in decreasing work: causal key tiles are reached by fewer queries
+    // the later they sit, causal query tiles see more keys
+    for (int t = 0; t < n; ++t) list[pos + t] = make_int2(b, kv_side ? t : n - 1 - t);
   }
   __syncthreads();
   return total;
