@@ -94,11 +94,12 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   dma_k.init(wave, lane, p.d, kv_rs_bytes);
   dma_v.init(wave, lane, p.d, kv_rs_bytes);
   auto issue = [&](int step) {
-    uint16_t* tK = sK[step & 1];
-    uint16_t* tV = sV[step & 1];
+    const uint32_t buf = (uint32_t)(step & 1);
     const int n0 = step * KS;
-    dma_k.issue(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tK, sSink, wave);
-    dma_v.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tV, sSink, wave);
+    dma_k.issue(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sK[0]) + buf * sizeof(sK[0]),
+                lds_addr(sSink), wave);
+    dma_v.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sV[0]) + buf * sizeof(sV[0]),
+                lds_addr(sSink), wave);
   };
   if (nsteps > 0) issue(0);
 
@@ -277,39 +278,51 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   const int nm = m_last > m_first ? m_last - m_first : 0;
   const int nsteps = nm * p.group;
   const int h0 = g * p.group;
-  // step -> (query tile, head of the group): query tiles from the last one
-  // down, the group's heads inside.  Key tiles of a sequence that start
-  // together then read the same Q / dO tiles at the same time (from L2).
-  auto step_tile = [&](int step, int& m, int& hg) {
-    const int t = step / p.group;
-    hg = step - t * p.group;
-    m = m_last - 1 - t;
-  };
+  // Steps walk the query tiles from the last one down, the group's heads
+  // inside: key tiles of a sequence that start together then read the same
+  // Q / dO tiles at the same time (from L2).  Two cursors follow that order
+  // by increments (no division per step): the DMA's, NBUF-1 steps ahead, and
+  // the compute loop's.
 
   Dma dma_q;
   dma_q.init(wave, lane, p.d, q_rs_bytes);
   // 4-byte DMA of the vector (LSE2 or Delta) rows i0 .. i0+BM-1 of head h
   const uint32_t vec_rs_bytes = (uint32_t)p.hq * (uint32_t)p.tsq * 4u;
   const uint32_t vec_voff = lane < BM ? (uint32_t)lane * vec_rs_bytes : kOutOfRange;
+  // LDS byte addresses of ring buffer 0 (buffer b lies b buffer sizes on)
+  const uint32_t lds_q = lds_addr(sQ[0]), lds_do = lds_addr(sdO[0]), lds_sink = lds_addr(sSink);
+  const uint32_t lds_vec = wave == 0 ? lds_addr(sVec[0]) : (wave == 1 ? lds_addr(sVec[0]) + 256u : lds_addr(sDummy));
+  const uint32_t vec_buf = wave < 2 ? (uint32_t)sizeof(sVec[0]) : 0u;
+  const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q);
+  const uint16_t* dog = reinterpret_cast<const uint16_t*>(p.dout);
+  const float* vg = wave == 0 ? p.lse2 : p.delta;
+  // DMA cursor: element offsets of the first row of (query tile, head) in
+  // q / dout and in lse2 / delta, the head's index in the group, and the
+  // tile's rows before the real end (>= 1 for every tile walked)
+  const int64_t row_last = (int64_t)s.oq + (int64_t)(m_last - 1) * BM * p.tsq;
+  int64_t dc_q = row_last * qrs + (int64_t)h0 * p.d;
+  int64_t dc_v = row_last * p.hq + h0;
+  int dc_hg = 0, dc_nrow = s.lq - (m_last - 1) * BM;
+  // from the last head of a tile to the first head of the tile before it
+  const int64_t q_back = (int64_t)BM * qts + (int64_t)(p.group - 1) * p.d;
+  const int64_t v_back = (int64_t)BM * p.tsq * p.hq + (p.group - 1);
   auto issue = [&](int step) {
-    const int buf = step % NBUF;
-    uint16_t* tQ = sQ[buf];
-    uint16_t* tdO = sdO[buf];
-    float* tvec = sVec[buf];
-    int m, hg;
-    step_tile(step, m, hg);
-    const int h = h0 + hg;
-    const int i0 = m * BM;
-    const int nrow = s.lq - i0;
-    const int64_t row0 = (int64_t)s.oq + (int64_t)i0 * p.tsq;
-    const int64_t base = row0 * qrs + (int64_t)h * p.d;
-    dma_q.issue(reinterpret_cast<const uint16_t*>(p.q) + base, nrow, q_rs_bytes, tQ, sSink, wave);
-    dma_q.issue(reinterpret_cast<const uint16_t*>(p.dout) + base, nrow, q_rs_bytes, tdO, sSink, wave);
-    const int nr = uniform(nrow < 0 ? 0 : (nrow > BM ? BM : nrow));
-    const int64_t vbase = row0 * p.hq + h;
-    const float* src = wave == 0 ? p.lse2 + vbase : p.delta + vbase;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, wave < 2 ? (uint32_t)nr * vec_rs_bytes : 0u);
-    dma<4>(rs, wave == 0 ? tvec : (wave == 1 ? tvec + 64 : sDummy), vec_voff);
+    const uint32_t buf = (uint32_t)(step % NBUF);
+    const int nr = dc_nrow > BM ? BM : dc_nrow;
+    dma_q.issue_rsrc(make_rsrc(qg + dc_q, (uint32_t)nr * q_rs_bytes), lds_q + buf * (uint32_t)sizeof(sQ[0]),
+                     lds_sink, wave);
+    dma_q.issue_rsrc(make_rsrc(dog + dc_q, (uint32_t)nr * q_rs_bytes), lds_do + buf * (uint32_t)sizeof(sdO[0]),
+                     lds_sink, wave);
+    dma<4>(make_rsrc(vg + dc_v, wave < 2 ? (uint32_t)nr * vec_rs_bytes : 0u), lds_vec + buf * vec_buf, vec_voff);
+    if (++dc_hg == p.group) {
+      dc_hg = 0;
+      dc_q -= q_back;
+      dc_v -= v_back;
+      dc_nrow += BM;
+    } else {
+      dc_q += p.d;
+      dc_v += 1;
+    }
   };
 #pragma unroll
   for (int k = 0; k < NBUF - 1; ++k)
@@ -328,8 +341,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   if constexpr (K_LDS || V_LDS) {
     DmaKV dkv;
     dkv.init(wave, lane, p.d, kv_rs_bytes);
-    if constexpr (K_LDS) dkv.issue(kb + (int64_t)n0 * kvts, s.lk - n0, kv_rs_bytes, sK, sSink, wave);
-    if constexpr (V_LDS) dkv.issue(vb + (int64_t)n0 * kvts, s.lk - n0, kv_rs_bytes, sV, sSink, wave);
+    if constexpr (K_LDS) dkv.issue(kb + (int64_t)n0 * kvts, s.lk - n0, kv_rs_bytes, lds_addr(sK), lds_addr(sSink), wave);
+    if constexpr (V_LDS) dkv.issue(vb + (int64_t)n0 * kvts, s.lk - n0, kv_rs_bytes, lds_addr(sV), lds_addr(sSink), wave);
   }
   wait_vm<0>();
 
@@ -342,6 +355,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 
   // One barrier per step: the buffer refilled at step j (that of step j-1)
   // has been read by every wave once the wave passes step j's barrier.
+  int cm = m_last - 1, chg = 0;   // compute cursor: query tile, head in the group
   for (int step = 0; step < nsteps; ++step) {
     // this step's tiles have landed (up to NBUF-2 later steps may not have)
     wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1 - step));
@@ -351,10 +365,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     const RowReader<LQ> rq(sQ[buf], lane), rdo(sdO[buf], lane);
     const TrReader<LQ> trq(sQ[buf], lane), trdo(sdO[buf], lane);
     const float* tvec = sVec[buf];
-    int m, hg;
-    step_tile(step, m, hg);
-    const int i0 = m * BM;
-    const int h_step = h0 + hg;   // query head of this step
+    const int i0 = cm * BM;
+    const int h_step = h0 + chg;   // query head of this step
+    if (++chg == p.group) {
+      chg = 0;
+      --cm;
+    }
     // waves with no real key, or whose keys all follow every query, idle
     if (wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q)) {
       f32x16 sc[NIB], dp[NIB];
@@ -373,7 +389,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           dp[ib] = Mfma<DT>::mma(rdo.read(ib, t), vop, dp[ib]);
         }
       }
-      const bool need_mask = CAUSAL && (i0 < wk_hi_q);
+      // this lane's key on the query axis while the step touches the
+      // diagonal, else a bound no query reaches (one compare per element)
+      const int kq = (CAUSAL && i0 < wk_hi_q) ? kj_q - i0 : INT_MIN;
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
         // the key column of the 4 x 4 blocks at queries 32 ib + 8 q4 + 4 hh (+0..3)
@@ -390,7 +408,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * q4 + c;
             float pr = fast_exp2(__builtin_fmaf(sc[ib][r], sl2e, -l4[c]));
-            if (need_mask && kj_q > i0 + ibase + c) pr = 0.f;
+            if (CAUSAL && kq > ibase + c) pr = 0.f;
             if constexpr (DROP) {
               // P o D for dV, and dS = P o (D o dP - Delta)
               const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;

@@ -256,17 +256,24 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // a lane offset the range check
 // would wait for the DMA of the next step); the kernels wait for their own
 // DMA explicitly (wait_vm) and then barrier.  M0 is reserved by the
 // compiler, but nothing else in these kernels uses it.
+// LDS byte address of a location in a __shared__ array.  For a static array
+// (or an offset from one) this folds to a constant; callers that pick one of
+// several buffers at run time add a byte offset to such a constant rather than
+// converting a run-time pointer (that conversion costs a null test per use).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
 template <int BYTES>
-__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, const void* lds_wave_base, uint32_t voff) {
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, uint32_t lds_wave_base, uint32_t voff) {
   static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte lanes");
-  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-      (__attribute__((address_space(3))) const void*)lds_wave_base));
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_wave_base);
   if constexpr (BYTES == 16)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory");
+                 :: "s"(lds), "v"(voff), "s"(rs) : "memory");
   else
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory");
+                 :: "s"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
 // s_waitcnt for vector-memory operations only: at most n (< 64) outstanding.
@@ -329,16 +336,19 @@ struct TileDma {
       voff[k] = ok ? (uint32_t)r * rs_bytes + 16u * (uint32_t)x : kOutOfRange;
     }
   }
-  // rows [0, rows_valid) of the tile start at `row0`; `sink` (1 KB) is
-  // only used when SINK
+  // rows [0, rows_valid) of the tile start at `row0`; the tile and the sink
+  // (1 KB, only used when SINK) are LDS byte addresses
   __device__ __forceinline__ void issue(const uint16_t* row0, int rows_valid, uint32_t rs_bytes,
-                                        uint16_t* tile, uint16_t* sink, int wave) const {
+                                        uint32_t tile, uint32_t sink, int wave) const {
     const int nr = __builtin_amdgcn_readfirstlane(rows_valid < 0 ? 0 : (rows_valid > ROWS ? ROWS : rows_valid));
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(row0, (uint32_t)nr * rs_bytes);
+    issue_rsrc(make_rsrc(row0, (uint32_t)nr * rs_bytes), tile, sink, wave);
+  }
+  __device__ __forceinline__ void issue_rsrc(__amdgpu_buffer_rsrc_t rsrc, uint32_t tile, uint32_t sink,
+                                             int wave) const {
 #pragma unroll
     for (int k = 0; k < PER_WAVE; ++k) {
       const int i = wave * PER_WAVE + k;
-      dma<16>(rsrc, (!SINK || i < INSTR) ? tile + i * 512 : sink, voff[k]);
+      dma<16>(rsrc, (!SINK || i < INSTR) ? tile + 1024u * (uint32_t)i : sink, voff[k]);
     }
   }
 };

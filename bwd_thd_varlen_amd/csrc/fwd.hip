@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
     const int n0 = step * KS;
     const uint16_t* krow = F8 ? reinterpret_cast<const uint16_t*>(kb8 + (int64_t)n0 * kvts)
                               : kb + (int64_t)n0 * kvts;
-    dma_k.issue(krow, kend - n0, k_rs_bytes, tK, nullptr, wave);
-    dma_v.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, tV, nullptr, wave);
+    dma_k.issue(krow, kend - n0, k_rs_bytes, lds_addr(tK), 0u, wave);
+    dma_v.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(tV), 0u, wave);
   };
   if (nsteps > 0) issue(0, sK0, sV0);
 
