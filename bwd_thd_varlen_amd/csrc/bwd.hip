@@ -151,7 +151,9 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     const TrReader<LK> trk(sK[step & 1], lane);
     const int n0 = step * KS;
     if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi_k)) {
-      const bool need_mask = CAUSAL && (n0 + KS - 1 > wq_lo_k);
+      // this lane's query on the key axis, relative to the step, while the
+      // step touches the diagonal, else a bound no key exceeds
+      const int qk = (CAUSAL && n0 + KS - 1 > wq_lo_k) ? qi_k - n0 : INT_MAX;
       // the step's two 32-key halves one after the other (S, dP -> dS -> dQ
       // part), so that only one half's score tiles are live at a time
 #pragma unroll
@@ -169,10 +171,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = fast_exp2(__builtin_fmaf(sc[r], sl2e, -lse2));
-          if (need_mask) {
-            const int j = n0 + 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (j > qi_k) pr = 0.f;
-          }
+          if (CAUSAL && 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3) > qk) pr = 0.f;
           sc[r] = pr * (dp[r] - dlt);     // dS
         }
         const u32x4 b0 = pack_operand<DT>(sc, 0), b1 = pack_operand<DT>(sc, 1);
@@ -229,6 +228,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   constexpr int NU = BM / 16;          // 16-query chunks per step
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
+  // K and V in registers, one 32-query block per step: the operand reads are
+  // pinned a fixed distance ahead of their MFMAs (scheduling barriers), since
+  // at 256 VGPRs the scheduler otherwise waits on each read just before its
+  // MFMA
+  constexpr bool PIN = KVM == 0 && NIB == 1;
   using LQ = Lay<DPAD, true>;          // Q, dO: row reads (S, dP) and transposed reads (dK, dV)
   using LKV = Lay<DPAD, false>;        // K, V kept in LDS (KVM): row reads
   using Dma = TileDma<LQ, BM, NW>;
@@ -374,6 +378,28 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     // waves with no real key, or whose keys all follow every query, idle
     if (wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q)) {
       f32x16 sc[NIB], dp[NIB];
+      if constexpr (PIN) {
+        // S and dP interleaved, each Q / dO operand read two MFMAs ahead
+        constexpr int PD = 2;
+        u32x4 aq[NT], ado[NT];
+        sc[0] = zero16();
+        dp[0] = zero16();
+#pragma unroll
+        for (int t = 0; t < PD; ++t) {
+          aq[t] = rq.read(0, t);
+          ado[t] = rdo.read(0, t);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          __builtin_amdgcn_sched_barrier(0);
+          sc[0] = Mfma<DT>::mma(aq[t], kreg[t], sc[0]);
+          if (t + PD < NT) aq[t + PD] = rq.read(0, t + PD);
+          __builtin_amdgcn_sched_barrier(0);
+          dp[0] = Mfma<DT>::mma(ado[t], vreg[t], dp[0]);
+          if (t + PD < NT) ado[t + PD] = rdo.read(0, t + PD);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
         sc[ib] = zero16();
@@ -388,6 +414,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           sc[ib] = Mfma<DT>::mma(rq.read(ib, t), kop, sc[ib]);
           dp[ib] = Mfma<DT>::mma(rdo.read(ib, t), vop, dp[ib]);
         }
+      }
       }
       // this lane's key on the query axis while the step touches the
       // diagonal, else a bound no query reaches (one compare per element)
@@ -428,6 +455,27 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
         bp[u] = pack_operand<DT>(sc[u >> 1], u & 1);
         bds[u] = pack_operand<DT>(dp[u >> 1], u & 1);
       }
+      if constexpr (PIN) {
+        // dV and dK interleaved, each transposed operand read one MFMA ahead
+        constexpr int PD = 1, NO = NU * NCB;
+        u32x4 tdo[NO], tq[NO];
+#pragma unroll
+        for (int o = 0; o < PD; ++o) {
+          tdo[o] = trdo.read(o % NCB, o / NCB);
+          tq[o] = trq.read(o % NCB, o / NCB);
+        }
+#pragma unroll
+        for (int o = 0; o < NO; ++o) {
+          const int u = o / NCB, cb = o % NCB;
+          __builtin_amdgcn_sched_barrier(0);
+          adv[cb] = Mfma<DT>::mma(tdo[o], bp[u], adv[cb]);
+          if (o + PD < NO) tdo[o + PD] = trdo.read((o + PD) % NCB, (o + PD) / NCB);
+          __builtin_amdgcn_sched_barrier(0);
+          adk[cb] = Mfma<DT>::mma(tq[o], bds[u], adk[cb]);
+          if (o + PD < NO) tq[o + PD] = trq.read((o + PD) % NCB, (o + PD) / NCB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
 #pragma unroll
       for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -435,6 +483,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
           adv[cb] = Mfma<DT>::mma(trdo.read(cb, u), bp[u], adv[cb]);
           adk[cb] = Mfma<DT>::mma(trq.read(cb, u), bds[u], adk[cb]);
         }
+      }
     }
   }
 
