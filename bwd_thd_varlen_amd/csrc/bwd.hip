@@ -159,10 +159,33 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         f32x16 sc = zero16(), dp = zero16();
+        if constexpr (DPAD == 128) {
+          // S and dP interleaved, each K / V operand read two MFMAs ahead
+          // (pinned with scheduling barriers; left to itself the scheduler
+          // waits on each read just before its MFMA)
+          constexpr int PD = 2;
+          u32x4 ak[NT], av[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          sc = Mfma<DT>::mma(rk.read(kb2, t), qreg[t], sc);
-          dp = Mfma<DT>::mma(rv.read(kb2, t), doreg[t], dp);
+          for (int t = 0; t < PD; ++t) {
+            ak[t] = rk.read(kb2, t);
+            av[t] = rv.read(kb2, t);
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            sc = Mfma<DT>::mma(ak[t], qreg[t], sc);
+            if (t + PD < NT) ak[t + PD] = rk.read(kb2, t + PD);
+            __builtin_amdgcn_sched_barrier(0);
+            dp = Mfma<DT>::mma(av[t], doreg[t], dp);
+            if (t + PD < NT) av[t + PD] = rv.read(kb2, t + PD);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            sc = Mfma<DT>::mma(rk.read(kb2, t), qreg[t], sc);
+            dp = Mfma<DT>::mma(rv.read(kb2, t), doreg[t], dp);
+          }
         }
         if constexpr (DROP) {
           // dP = D o (dO V^T): dropped elements 0, kept ones scaled

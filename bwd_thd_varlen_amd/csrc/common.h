@@ -240,6 +240,56 @@ struct TrReader {
   }
 };
 
+// Operand readers for swizzled tiles (Swz), which hold one VGPR of
+// lane-dependent address each.  The swizzle XORs a row's 16-byte chunk index
+// with a function of the row's low four bits, and a row is a power of two
+// bytes long, so for a fixed lane the chunk of k step t of a row read lies at
+// base ^ 32 t bytes (chunk 2 t + hh), and that of column block cb of a
+// transposed read at base ^ 64 cb (chunk 4 cb + w); rows 32 rb and 16 u on
+// keep the swizzle and only add a constant.  One XOR per read replaces an
+// address register per (k step, tile), which the compiler would otherwise
+// hoist out of the loop.  `tile` is the tile's LDS byte address.
+__device__ __forceinline__ u32x4 lds_ld16(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(a);
+}
+__device__ __forceinline__ u32x2 lds_tr4_at(uint32_t a) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4i16*>(a));
+  return __builtin_bit_cast(u32x2, v);
+}
+template <int DPAD>
+struct SwzRowReader {   // = lds_row8<Swz<DPAD>>(tile, 32 rb + (lane & 31), 16 t + 8 (lane >> 5))
+  static constexpr uint32_t RB = 2 * DPAD;   // bytes per row
+  uint32_t base;
+  __device__ __forceinline__ explicit SwzRowReader(int lane)
+      : base(2u * (uint32_t)Swz<DPAD>::off(lane & 31, 8 * (lane >> 5))) {}
+  // makes the base opaque, so that the per-read XORs stay in the loop
+  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(base)); }
+  __device__ __forceinline__ u32x4 read(uint32_t tile, int rb, int t) const {
+    return lds_ld16(tile + 32u * RB * (uint32_t)rb + (base ^ (32u * (uint32_t)t)));
+  }
+};
+template <int DPAD>
+struct SwzTrReader {    // = lds_tr_operand<Swz<DPAD>>(tile, cb, u, lane)
+  static constexpr uint32_t RB = 2 * DPAD;
+  uint32_t b0, b8;      // rows r and r + 8 (their swizzles differ)
+  __device__ __forceinline__ explicit SwzTrReader(int lane) {
+    const int J = lane & 15;
+    const int c = 16 * ((lane >> 4) & 1) + 4 * (J & 3);
+    const int r = 4 * (lane >> 5) + (J >> 2);
+    b0 = 2u * (uint32_t)Swz<DPAD>::off(r, c);
+    b8 = 2u * (uint32_t)Swz<DPAD>::off(r + 8, c);
+  }
+  __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(b0), "+v"(b8)); }
+  __device__ __forceinline__ u32x4 read(uint32_t tile, int cb, int u) const {
+    const uint32_t t = tile + 16u * RB * (uint32_t)u, x = 64u * (uint32_t)cb;
+    const u32x2 a = lds_tr4_at(t + (b0 ^ x));
+    const u32x2 b = lds_tr4_at(t + (b8 ^ x));
+    u32x4 o = {a[0], a[1], b[0], b[1]};
+    return o;
+  }
+};
+
 // ----------------------------------------------------------------- LDS DMA
 // Raw buffer resource over `bytes` bytes at p (no stride; the hardware range
 // check returns zeros for any offset >= bytes and does not touch memory).

@@ -130,7 +130,11 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 
   // One barrier per step: after it, every wave has finished step - 1, so the
   // DMA of step + 1 can refill that step's buffer.
+  SwzRowReader<DPAD> rk(lane);   // K rows (16-bit K)
+  SwzTrReader<DPAD> rtv(lane);   // V, transposed
   auto do_step = [&](int step, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
+    rk.refresh();
+    rtv.refresh();
     wait_vm<0>();                                // this step's tiles have landed
     barrier_lds_dma();
     if (step + 1 < nsteps) issue(step + 1, nK, nV);
@@ -149,9 +153,18 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
                                lds_row8<LK>(tK, 32 * kb2 + li, 32 * t + 16 * hh + 8),
                                q8lo[t], q8hi[t], sc[kb2]);
         } else {
+          // K operands read two MFMAs ahead, pinned with scheduling barriers
+          constexpr int PD = 2;
+          u32x4 ak[NT];
 #pragma unroll
-          for (int t = 0; t < NT; ++t)
-            sc[kb2] = Mfma<DT>::mma(lds_row8<LK>(tK, 32 * kb2 + li, 16 * t + 8 * hh), qreg[t], sc[kb2]);
+          for (int t = 0; t < PD; ++t) ak[t] = rk.read(lds_addr(tK), kb2, t);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            sc[kb2] = Mfma<DT>::mma(ak[t], qreg[t], sc[kb2]);
+            if (t + PD < NT) ak[t + PD] = rk.read(lds_addr(tK), kb2, t + PD);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       const bool need_mask = (n0 + KS > kend) || (CAUSAL && n0 + KS - 1 > wq_lo_k);
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
         const u32x4 b = pack_operand<DT>(sc[u >> 1], u & 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          acc[cb] = Mfma<DT>::mma(lds_tr_operand<LV>(tV, cb, u, lane), b, acc[cb]);
+          acc[cb] = Mfma<DT>::mma(rtv.read(lds_addr(tV), cb, u), b, acc[cb]);
       }
     }
   };
