@@ -151,9 +151,10 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     const TrReader<LK> trk(sK[step & 1], lane);
     const int n0 = step * KS;
     if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi_k)) {
-      // this lane's query on the key axis, relative to the step, while the
-      // step touches the diagonal, else a bound no key exceeds
-      const int qk = (CAUSAL && n0 + KS - 1 > wq_lo_k) ? qi_k - n0 : INT_MAX;
+      // the causal mask only on steps that touch the diagonal (a wave-uniform
+      // branch): key n0 + j is hidden from this lane's query while j > qk
+      const bool diag_step = CAUSAL && n0 + KS - 1 > wq_lo_k;
+      const int qk = qi_k - n0;
       // the step's two 32-key halves one after the other (S, dP -> dS -> dQ
       // part), so that only one half's score tiles are live at a time
 #pragma unroll
@@ -192,11 +193,14 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
           dropout_row16(p, w.b, h, qi >> 2, (n0 + 32 * kb2 + 4 * hh) >> 2, li & 3, p.drop_scale, dp);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(__builtin_fmaf(sc[r], sl2e, -lse2));
-          if (CAUSAL && 32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3) > qk) pr = 0.f;
-          sc[r] = pr * (dp[r] - dlt);     // dS
+        for (int r = 0; r < 16; ++r) sc[r] = fast_exp2(__builtin_fmaf(sc[r], sl2e, -lse2));
+        if (diag_step) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3) > qk) sc[r] = 0.f;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = sc[r] * (dp[r] - dlt);     // dS
         const u32x4 b0 = pack_operand<DT>(sc, 0), b1 = pack_operand<DT>(sc, 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -439,9 +443,26 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
         }
       }
       }
-      // this lane's key on the query axis while the step touches the
-      // diagonal, else a bound no query reaches (one compare per element)
-      const int kq = (CAUSAL && i0 < wk_hi_q) ? kj_q - i0 : INT_MIN;
+      // P = exp2(S log2e - LSE log2e); the causal mask only on steps that
+      // touch the diagonal (a wave-uniform branch): key kj is hidden from
+      // query i0 + i while kj - diag > i0 + i
+#pragma unroll
+      for (int ib = 0; ib < NIB; ++ib)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[32 * ib + 8 * q4 + 4 * hh]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sc[ib][4 * q4 + c] = fast_exp2(__builtin_fmaf(sc[ib][4 * q4 + c], sl2e, -l4[c]));
+        }
+      if (CAUSAL && i0 < wk_hi_q) {
+        const int kq = kj_q - i0;
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kq > 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3)) sc[ib][r] = 0.f;
+      }
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
         // the key column of the 4 x 4 blocks at queries 32 ib + 8 q4 + 4 hh (+0..3)
@@ -450,22 +471,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int ibase = 32 * ib + 8 * q4 + 4 * hh;   // first of 4 consecutive queries
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[ibase]);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + ibase]);
           u32x4 x;
           if constexpr (DROP) x = (u32x4){xcol[q4][0], xcol[q4][1], xcol[q4][2], xcol[q4][3]};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * q4 + c;
-            float pr = fast_exp2(__builtin_fmaf(sc[ib][r], sl2e, -l4[c]));
-            if (CAUSAL && kq > ibase + c) pr = 0.f;
+            const float pr = sc[ib][r];
             if constexpr (DROP) {
               // P o D for dV, and dS = P o (D o dP - Delta)
               const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;
               sc[ib][r] = pr * dsc;
               dp[ib][r] = pr * (dp[ib][r] * dsc - d4[c]);
             } else {
-              sc[ib][r] = pr;
               dp[ib][r] = pr * (dp[ib][r] - d4[c]);
             }
           }
