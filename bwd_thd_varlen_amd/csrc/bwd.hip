@@ -1,12 +1,13 @@
 // Backward kernels.  With P recomputed from the saved LSE,
 //   P = exp(scale*S - LSE),  dP = dO V^T,  dS = P o (dP - Delta),
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
-// where Delta = rowsum(dO o O) comes from the preprocess kernel.
+// where Delta = rowsum(dO o O) is formed in the dQ kernel's prologue, which
+// also stores -Delta and LSE*log2(e) per (row, head) for dK/dV.
 //
 // dK/dV: one workgroup per (sequence, 32*NW-key tile, KV head g).  Each wave
 // owns 32 keys; K and V of those keys stay in registers (or LDS for d=256)
 // for the whole workgroup, which loops over the hq/hkv query heads of g and
-// over the 64-query tiles that reach the keys, in a fixed order, so the sum
+// over the query tiles that reach the keys, in a fixed order, so the sum
 // over the GQA group happens in registers: deterministic and without
 // atomics (TransformerEngine issue 2448, "Expected behavior"; the KV rows of
 // a tile no query reaches come out as exact zeros).
@@ -129,10 +130,11 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   const float delta = sum_halves(dpart);
   const float lse2 = qvalid ? p.lse[srow] * kLog2e : __builtin_inff();
   const float dlt = qvalid ? delta : 0.f;
-  // the dK/dV kernel (launched next) reads both per (row, head); each is
-  // written by the one work item that owns the row
+  // the dK/dV kernel (launched next) reads both per (row, head), Delta
+  // negated (its dP accumulators start from it); each is written by the one
+  // work item that owns the row
   if (qvalid && hh == 0) {
-    p.delta[srow] = delta;
+    p.delta[srow] = -delta;
     p.lse2[srow] = lse2;
   }
   wait_vm<0>();
@@ -238,8 +240,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 // (KVM: 0 both in registers, 1 V in LDS, 2 both in LDS), trading registers
 // (occupancy) against LDS traffic.  Each
 // step DMAs the Q and dO tiles of one (query head, query tile) pair plus
-// their LSE*log2(e) and Delta vectors (one 4-byte DMA per wave: wave 0 LSE,
-// wave 1 Delta, other waves a dummy so that every wave issues the same
+// their LSE*log2(e) and -Delta vectors (one 4-byte DMA per wave: wave 0 LSE,
+// wave 1 -Delta, other waves a dummy so that every wave issues the same
 // number of DMAs and can use the same wait count).  Query rows past the real
 // length arrive as zeros in Q, dO, LSE and Delta, so they add nothing.
 // The tiles come through a ring of NBUF buffers filled NBUF-1 steps ahead,
@@ -410,7 +412,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
         constexpr int PD = 2;
         u32x4 aq[NT], ado[NT];
         sc[0] = zero16();
-        dp[0] = zero16();
+        if constexpr (!DROP) {
+          // dP accumulates onto -Delta of its rows, so the chain ends at dP - Delta
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 nd = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dp[0][4 * q4 + c] = nd[c];
+          }
+        } else {
+          dp[0] = zero16();
+        }
 #pragma unroll
         for (int t = 0; t < PD; ++t) {
           aq[t] = rq.read(0, t);
@@ -482,9 +494,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
               // P o D for dV, and dS = P o (D o dP - Delta)
               const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;
               sc[ib][r] = pr * dsc;
-              dp[ib][r] = pr * (dp[ib][r] * dsc - d4[c]);
+              dp[ib][r] = pr * __builtin_fmaf(dp[ib][r], dsc, d4[c]);
+            } else if constexpr (PIN) {
+              dp[ib][r] = pr * dp[ib][r];
             } else {
-              dp[ib][r] = pr * (dp[ib][r] - d4[c]);
+              dp[ib][r] = pr * (dp[ib][r] + d4[c]);
             }
           }
         }

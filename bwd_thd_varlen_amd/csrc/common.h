@@ -552,8 +552,8 @@ struct AttnParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;
-  float* lse2;       // LSE * log2(e), written by the preprocess
+  float* delta;      // -Delta = -rowsum(dO o O), written by dQ's prologue
+  float* lse2;       // LSE * log2(e), written by dQ's prologue
   const int32_t* hdr;
   const SeqInfo* seq;
   const int2* list;
