@@ -161,7 +161,13 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
       // part), so that only one half's score tiles are live at a time
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
+        // dP accumulates onto -Delta (without dropout, which scales dP
+        // alone), so the chain ends at dP - Delta
         f32x16 sc = zero16(), dp = zero16();
+        if constexpr (!DROP) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[r] = -dlt;
+        }
         if constexpr (DPAD == 128) {
           // S and dP interleaved, each K / V operand read two MFMAs ahead
           // (pinned with scheduling barriers; left to itself the scheduler
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
             if (32 * kb2 + 8 * (r >> 2) + 4 * hh + (r & 3) > qk) sc[r] = 0.f;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] = sc[r] * (dp[r] - dlt);     // dS
+        for (int r = 0; r < 16; ++r) sc[r] = DROP ? sc[r] * (dp[r] - dlt) : sc[r] * dp[r];     // dS
         const u32x4 b0 = pack_operand<DT>(sc, 0), b1 = pack_operand<DT>(sc, 1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
