@@ -43,7 +43,9 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   constexpr int NT = F8 ? 1 : DPAD / 16;   // 16-wide k chunks over the head dim (16-bit Q)
   constexpr int NT8 = DPAD / 64;           // 64-wide k chunks (E4M3 Q)
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
-  constexpr int KS = fwd_step_keys<DPAD>();   // keys per step
+  // keys per step (the 8-bit K tiles are half the size: 64 keys fit three
+  // workgroups per CU)
+  constexpr int KS = F8 ? 64 : fwd_step_keys<DPAD>();
   constexpr int NKB = KS / 32;         // 32-key blocks of S^T per step
   // K: row reads (E4M3: DPAD bytes per row, addressed in 16-bit units)
   using LK = std::conditional_t<F8, Swz<DPAD / 2>, Swz<DPAD>>;
