@@ -446,20 +446,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
         __builtin_amdgcn_sched_barrier(0);
       } else {
 #pragma unroll
-      for (int ib = 0; ib < NIB; ++ib) {
-        sc[ib] = zero16();
-        dp[ib] = zero16();
+        for (int ib = 0; ib < NIB; ++ib) {
+          sc[ib] = zero16();
+          dp[ib] = zero16();
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          u32x4 kop, vop;
-          if constexpr (K_LDS) kop = lds_row8<LKV>(sK, 32 * wave + li, 16 * t + 8 * hh);
-          else kop = kreg[K_LDS ? 0 : t];
-          if constexpr (V_LDS) vop = lds_row8<LKV>(sV, 32 * wave + li, 16 * t + 8 * hh);
-          else vop = vreg[V_LDS ? 0 : t];
-          sc[ib] = Mfma<DT>::mma(rq.read(ib, t), kop, sc[ib]);
-          dp[ib] = Mfma<DT>::mma(rdo.read(ib, t), vop, dp[ib]);
+          for (int t = 0; t < NT; ++t) {
+            u32x4 kop, vop;
+            if constexpr (K_LDS) kop = lds_row8<LKV>(sK, 32 * wave + li, 16 * t + 8 * hh);
+            else kop = kreg[K_LDS ? 0 : t];
+            if constexpr (V_LDS) vop = lds_row8<LKV>(sV, 32 * wave + li, 16 * t + 8 * hh);
+            else vop = vreg[V_LDS ? 0 : t];
+            sc[ib] = Mfma<DT>::mma(rq.read(ib, t), kop, sc[ib]);
+            dp[ib] = Mfma<DT>::mma(rdo.read(ib, t), vop, dp[ib]);
+          }
         }
-      }
       }
       // P = exp2(S log2e - LSE log2e); the causal mask only on steps that
       // touch the diagonal (a wave-uniform branch): key kj is hidden from
@@ -538,12 +538,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
         __builtin_amdgcn_sched_barrier(0);
       } else {
 #pragma unroll
-      for (int u = 0; u < NU; ++u)
+        for (int u = 0; u < NU; ++u)
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          adv[cb] = Mfma<DT>::mma(trdo.read(cb, u), bp[u], adv[cb]);
-          adk[cb] = Mfma<DT>::mma(trq.read(cb, u), bds[u], adk[cb]);
-        }
+          for (int cb = 0; cb < NCB; ++cb) {
+            adv[cb] = Mfma<DT>::mma(trdo.read(cb, u), bp[u], adv[cb]);
+            adk[cb] = Mfma<DT>::mma(trq.read(cb, u), bds[u], adk[cb]);
+          }
       }
     }
   }
