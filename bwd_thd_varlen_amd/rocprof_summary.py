@@ -18,6 +18,11 @@ Two modes, each run on the databases a GPU run left behind:
       stamped with the hash of the kernel sources (``source_hash``);
       bench.py reports the traffic only while that hash matches.
 
+  python -m bwd_thd_varlen_amd.rocprof_summary counters OUT.txt DB [DB ...] --command CMD [...]
+      shader-sequencer counters of the three compute kernels from one or more
+      ``rocprofv3 --pmc`` runs (at most 8 SQ counters per run), averaged per
+      dispatch, with the wave-cycle ratios they give.
+
 Reads SQLite files only; nothing here touches the GPU.
 """
 from __future__ import annotations
@@ -154,6 +159,51 @@ def traffic(fetch_db: str, write_db: str, cmd_fetch: str, cmd_write: str) -> Non
         print(f"wrote {path}: {hbm / 2**30:.3f} GiB per launch")
 
 
+# ratios of wave-cycle counters (each summed over all waves of a dispatch)
+RATIOS = [
+    ("waiting on anything", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+    ("waiting on an instruction's dependency", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("waiting on LDS", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("issuing any instruction", "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("issuing VALU (MFMA included)", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+    ("issuing LDS", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("issuing scalar", "SQ_ACTIVE_INST_SCA", "SQ_WAVE_CYCLES"),
+]
+
+
+def counters(out: str, dbs, commands) -> None:
+    vals = defaultdict(lambda: defaultdict(list))
+    for db in dbs:
+        for name, counter, value in _rows(db, "select kernel_name, counter_name, value "
+                                              "from counters_collection"):
+            for stage, prefix in STAGE_KERNELS.items():
+                if name.startswith(prefix):
+                    vals[stage][counter].append(float(value))
+    names = sorted({c for st in vals.values() for c in st})
+    lines = ["# Shader-sequencer counters: throughput_65k workload, per dispatch (average)",
+             "# Counter runs, from the repository root on one MI355X (TMPDIR=/tmp):"]
+    lines += [f"#   {c}" for c in commands]
+    for stage in STAGE_KERNELS:
+        lines.append(f"kernel_source_sha256[{stage}] = {source_hash(stage)}")
+    lines += ["", "| counter | " + " | ".join(STAGE_KERNELS) + " |",
+              "|---|" + "---|" * len(STAGE_KERNELS)]
+    avg = {st: {c: sum(v) / len(v) for c, v in d.items()} for st, d in vals.items()}
+    for c in names:
+        lines.append(f"| {c} | " + " | ".join(f"{avg.get(st, {}).get(c, float('nan')):.4g}"
+                                              for st in STAGE_KERNELS) + " |")
+    lines += ["", "| share of wave-cycles | " + " | ".join(STAGE_KERNELS) + " |",
+              "|---|" + "---|" * len(STAGE_KERNELS)]
+    for label, num, den in RATIOS:
+        cells = []
+        for st in STAGE_KERNELS:
+            a = avg.get(st, {})
+            cells.append(f"{100.0 * a[num] / a[den]:.1f}%" if num in a and a.get(den) else "-")
+        lines.append(f"| {label} ({num} / {den}) | " + " | ".join(cells) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -167,8 +217,14 @@ def main(argv=None) -> None:
     c.add_argument("write_db")
     c.add_argument("--command-fetch", required=True)
     c.add_argument("--command-write", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("out")
+    k.add_argument("dbs", nargs="+")
+    k.add_argument("--command", action="append", required=True)
     a = ap.parse_args(argv)
-    if a.mode == "trace":
+    if a.mode == "counters":
+        counters(a.out, a.dbs, a.command)
+    elif a.mode == "trace":
         trace(a.db, a.out, a.command, a.title)
     else:
         traffic(a.fetch_db, a.write_db, a.command_fetch, a.command_write)
