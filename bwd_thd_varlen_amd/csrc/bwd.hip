@@ -395,6 +395,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   // One barrier per step: the buffer refilled at step j (that of step j-1)
   // has been read by every wave once the wave passes step j's barrier.
   int cm = m_last - 1, chg = 0;   // compute cursor: query tile, head in the group
+  // unrolled by two: each copy's ring buffer is a constant
+#pragma unroll 2
   for (int step = 0; step < nsteps; ++step) {
     // this step's tiles have landed (up to NBUF-2 later steps may not have)
     wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1 - step));
