@@ -54,7 +54,6 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][LK::template elems<KS>()];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][LV::template elems<KS>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sSink[DmaK::SINK || DmaV::SINK ? 512 : 8];
 
   const int ntiles = uniform(p.hdr[kHdrNQTiles]);
   int item, h;
@@ -97,10 +96,10 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   auto issue = [&](int step) {
     const uint32_t buf = (uint32_t)(step & 1);
     const int n0 = step * KS;
-    dma_k.issue(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sK[0]) + buf * sizeof(sK[0]),
-                lds_addr(sSink), wave);
-    dma_v.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sV[0]) + buf * sizeof(sV[0]),
-                lds_addr(sSink), wave);
+    // each step waits for all of the wave's DMAs, so the waves need not
+    // issue equal counts: no sink DMAs
+    dma_k.issue_exact(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sK[0]) + buf * sizeof(sK[0]), wave);
+    dma_v.issue_exact(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sV[0]) + buf * sizeof(sV[0]), wave);
   };
   if (nsteps > 0) issue(0);
 

@@ -401,6 +401,20 @@ struct TileDma {
       dma<16>(rsrc, (!SINK || i < INSTR) ? tile + 1024u * (uint32_t)i : sink, voff[k]);
     }
   }
+  // The same without the sink DMAs, for callers that wait for all of a
+  // wave's outstanding DMAs (then the waves need not issue equal counts).
+  __device__ __forceinline__ void issue_rsrc_exact(__amdgpu_buffer_rsrc_t rsrc, uint32_t tile, int wave) const {
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+      const int i = wave * PER_WAVE + k;
+      if (!SINK || i < INSTR) dma<16>(rsrc, tile + 1024u * (uint32_t)i, voff[k]);
+    }
+  }
+  __device__ __forceinline__ void issue_exact(const uint16_t* row0, int rows_valid, uint32_t rs_bytes,
+                                              uint32_t tile, int wave) const {
+    const int nr = __builtin_amdgcn_readfirstlane(rows_valid < 0 ? 0 : (rows_valid > ROWS ? ROWS : rows_valid));
+    issue_rsrc_exact(make_rsrc(row0, (uint32_t)nr * rs_bytes), tile, wave);
+  }
 };
 
 // A value the compiler cannot prove wave-uniform (e.g. loaded by a vector
