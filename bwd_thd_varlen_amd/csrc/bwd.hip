@@ -485,14 +485,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
         // the key column of the 4 x 4 blocks at queries 32 ib + 8 q4 + 4 hh (+0..3)
-        uint32_t xcol[4][4];
-        if constexpr (DROP) dropout_cols(p, w.b, h_step, (i0 + 32 * ib + 4 * hh) >> 2, kj >> 2, li & 3, xcol);
+        // this lane's Philox block (4 x 4: element (i, j) is byte j & 3 of word
+        // i & 3); the block of quad lane g is broadcast when q4 = g, so only four
+        // words are live at a time
+        u32x4 mine;
+        if constexpr (DROP)
+          mine = dropout_block(p, w.b, h_step, ((i0 + 32 * ib + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int ibase = 32 * ib + 8 * q4 + 4 * hh;   // first of 4 consecutive queries
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + ibase]);
           u32x4 x;
-          if constexpr (DROP) x = (u32x4){xcol[q4][0], xcol[q4][1], xcol[q4][2], xcol[q4][3]};
+          if constexpr (DROP)
+            x = (u32x4){quad_bcast_at(mine[0], q4), quad_bcast_at(mine[1], q4), quad_bcast_at(mine[2], q4),
+                        quad_bcast_at(mine[3], q4)};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * q4 + c;

@@ -659,19 +659,10 @@ __device__ __forceinline__ void dropout_row16(const AttnParams& p, int b, int h,
 #undef ATTN_DROP_APPLY
 }
 
-// Key-column words of the four 4 x 4 blocks at query quads i4_0 + 2g: all four
-// words of block g (element (i, j) is byte (j & 3) of word (i & 3)); lane c of
-// the quad computes block g = c.
-__device__ __forceinline__ void dropout_cols(const AttnParams& p, int b, int h, int i4_0, int j4,
-                                             int c, uint32_t (&x)[4][4]) {
-  const u32x4 mine = dropout_block(p, b, h, i4_0 + 2 * c, j4);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    x[0][r] = quad_bcast<0>(mine[r]);
-    x[1][r] = quad_bcast<1>(mine[r]);
-    x[2][r] = quad_bcast<2>(mine[r]);
-    x[3][r] = quad_bcast<3>(mine[r]);
-  }
+// quad_bcast with the source lane given by a value that is a constant after
+// unrolling
+__device__ __forceinline__ uint32_t quad_bcast_at(uint32_t x, int g) {
+  return g == 0 ? quad_bcast<0>(x) : g == 1 ? quad_bcast<1>(x) : g == 2 ? quad_bcast<2>(x) : quad_bcast<3>(x);
 }
 
 }  // namespace attn
