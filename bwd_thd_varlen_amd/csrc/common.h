@@ -299,13 +299,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // a lane offset the range check always rejects
 
-// Global -> LDS DMA of BYTES (4 or 16) per lane: lane l's bytes land at
-// lds_wave_base + BYTES * l (wave-uniform base); no VGPR is written.  Issued
-// from inline asm so that the compiler does not try to order LDS reads
-// against it (its alias tracking cannot tell the double buffers apart and
-// would wait for the DMA of the next step); the kernels wait for their own
-// DMA explicitly (wait_vm) and then barrier.  M0 is reserved by the
-// compiler, but nothing else in these kernels uses it.
 // LDS byte address of a location in a __shared__ array.  For a static array
 // (or an offset from one) this folds to a constant; callers that pick one of
 // several buffers at run time add a byte offset to such a constant rather than
@@ -314,6 +307,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
 }
 
+// Global -> LDS DMA of BYTES (4 or 16) per lane: lane l's bytes land at
+// lds_wave_base + BYTES * l (wave-uniform base); no VGPR is written.  Issued
+// from inline asm so that the compiler does not try to order LDS reads
+// against it (its alias tracking cannot tell the double buffers apart and
+// would wait for the DMA of the next step); the kernels wait for their own
+// DMA explicitly (wait_vm) and then barrier.  M0 is reserved by the
+// compiler, but nothing else in these kernels uses it.
 template <int BYTES>
 __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, uint32_t lds_wave_base, uint32_t voff) {
   static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte lanes");
