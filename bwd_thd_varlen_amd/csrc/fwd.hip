@@ -130,10 +130,10 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = zero16();
   float m_run = -__builtin_inff(), l_run = 0.f;
 
-  // One barrier per step: after it, every wave has finished step - 1, so the
-  // DMA of step + 1 can refill that step's buffer.
   SwzRowReader<DPAD> rk(lane);   // K rows (16-bit K)
   SwzTrReader<DPAD> rtv(lane);   // V, transposed
+  // One barrier per step: after it, every wave has finished step - 1, so the
+  // DMA of step + 1 can refill that step's buffer.
   auto do_step = [&](int step, const uint16_t* tK, const uint16_t* tV, uint16_t* nK, uint16_t* nV) {
     rk.refresh();
     rtv.refresh();
