@@ -147,9 +147,11 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     wait_vm<0>();
     barrier_lds_dma();
     if (step + 1 < nsteps) issue(step + 1);
-    const RowReader<LK> rk(sK[step & 1], lane);
-    const RowReader<LV> rv(sV[step & 1], lane);
-    const TrReader<LK> trk(sK[step & 1], lane);
+    const uint32_t tk = lds_addr(sK[0]) + (uint32_t)(step & 1) * (uint32_t)sizeof(sK[0]);
+    const uint32_t tv = lds_addr(sV[0]) + (uint32_t)(step & 1) * (uint32_t)sizeof(sV[0]);
+    const RowReader<LK> rk(tk, lane);
+    const RowReader<LV> rv(tv, lane);
+    const TrReader<LK> trk(tk, lane);
     const int n0 = step * KS;
     if (wq_lo < s.lq && !(CAUSAL && n0 > wq_hi_k)) {
       // the causal mask only on steps that touch the diagonal (a wave-uniform
@@ -402,8 +404,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     barrier_lds_dma();
     if (step + NBUF - 1 < nsteps) issue(step + NBUF - 1);
     const int buf = step % NBUF;
-    const RowReader<LQ> rq(sQ[buf], lane), rdo(sdO[buf], lane);
-    const TrReader<LQ> trq(sQ[buf], lane), trdo(sdO[buf], lane);
+    const uint32_t tq = lds_q + (uint32_t)buf * (uint32_t)sizeof(sQ[0]);
+    const uint32_t tdo = lds_do + (uint32_t)buf * (uint32_t)sizeof(sdO[0]);
+    const RowReader<LQ> rq(tq, lane), rdo(tdo, lane);
+    const TrReader<LQ> trq(tq, lane), trdo(tdo, lane);
     const float* tvec = sVec[buf];
     const int i0 = cm * BM;
     const int h_step = h0 + chg;   // query head of this step

@@ -207,35 +207,46 @@ __device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* tile, int cb, in
   return o;
 }
 
+// Reads at an LDS byte address: 16 bytes, and the 8-byte transpose read.
+__device__ __forceinline__ u32x4 lds_ld16(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(a);
+}
+__device__ __forceinline__ u32x2 lds_tr4_at(uint32_t a) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4i16*>(a));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Operand readers for padded tiles (Lay): the lane-dependent part of every
-// read's offset is formed once (one address per tile and step), and each
-// read adds a compile-time constant, which goes into the instruction's
-// offset field -- also when the tile is picked at run time from a ring.
+// read's offset is formed once (one 32-bit LDS address per tile and step),
+// and each read adds a compile-time constant, which goes into the
+// instruction's offset field -- also when the tile is picked at run time
+// from a ring.  `tile` is the tile's LDS byte address.
 //   RowReader(tile, lane).read(rb, t): the 16-byte row read of lds_row8 at
 //     row 32*rb + (lane & 31), columns 16*t + 8*(lane >> 5) ...
 //   TrReader(tile, lane).read(cb, u): lds_tr_operand(tile, cb, u, lane).
 template <class L>
 struct RowReader {
   static_assert(L::PADDED, "linear offsets need the padded layout");
-  const uint16_t* p;
-  __device__ __forceinline__ RowReader(const uint16_t* tile, int lane)
-      : p(tile + L::off(lane & 31, 8 * (lane >> 5))) {}
+  uint32_t a;
+  __device__ __forceinline__ RowReader(uint32_t tile, int lane)
+      : a(tile + 2u * (uint32_t)L::off(lane & 31, 8 * (lane >> 5))) {}
   __device__ __forceinline__ u32x4 read(int rb, int t) const {
-    return *reinterpret_cast<const u32x4*>(p + 32 * rb * L::RE + 16 * t);
+    return lds_ld16(a + 2u * (uint32_t)(32 * rb * L::RE + 16 * t));
   }
 };
 template <class L>
 struct TrReader {
   static_assert(L::PADDED, "linear offsets need the padded layout");
-  const uint16_t* p;
-  __device__ __forceinline__ TrReader(const uint16_t* tile, int lane)
-      : p(tile + L::off(4 * (lane >> 5) + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3))) {}
+  uint32_t a;
+  __device__ __forceinline__ TrReader(uint32_t tile, int lane)
+      : a(tile + 2u * (uint32_t)L::off(4 * (lane >> 5) + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3))) {}
   __device__ __forceinline__ u32x4 read(int cb, int u) const {
     // rows r and r + 8 of the same lane: rot(r + 8) = rot(r) + 2 (r & 15 < 8)
-    const uint16_t* q = p + 16 * u * L::RE + 32 * cb;
-    const u32x2 a = lds_tr4(q);
-    const u32x2 b = lds_tr4(q + 8 * L::RE + (L::ROT ? 16 : 0));
-    u32x4 o = {a[0], a[1], b[0], b[1]};
+    const uint32_t q = a + 2u * (uint32_t)(16 * u * L::RE + 32 * cb);
+    const u32x2 x = lds_tr4_at(q);
+    const u32x2 y = lds_tr4_at(q + 2u * (uint32_t)(8 * L::RE + (L::ROT ? 16 : 0)));
+    u32x4 o = {x[0], x[1], y[0], y[1]};
     return o;
   }
 };
@@ -249,14 +260,6 @@ struct TrReader {
 // keep the swizzle and only add a constant.  One XOR per read replaces an
 // address register per (k step, tile), which the compiler would otherwise
 // hoist out of the loop.  `tile` is the tile's LDS byte address.
-__device__ __forceinline__ u32x4 lds_ld16(uint32_t a) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(a);
-}
-__device__ __forceinline__ u32x2 lds_tr4_at(uint32_t a) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) v4i16*>(a));
-  return __builtin_bit_cast(u32x2, v);
-}
 template <int DPAD>
 struct SwzRowReader {   // = lds_row8<Swz<DPAD>>(tile, 32 rb + (lane & 31), 16 t + 8 (lane >> 5))
   static constexpr uint32_t RB = 2 * DPAD;   // bytes per row
