@@ -136,3 +136,27 @@ def test_dropout_zero_equals_plain_and_repeats_bitwise():
     r3 = _gpu(case, (0.4, 99, 2))
     assert not torch.equal(r1[0], r3[0])
     assert dropout_threshold(0.4) == 102
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_dropout_bottom_right_unequal_lengths(dtype):
+    """Dropout with the bottom-right causal mask: sequences with Lq < Lk, one
+    with Lq > Lk (its first queries see no key: zero output, -inf LSE), an
+    empty query side, and real != padded slots."""
+    lq = [5, 130, 64, 0, 257, 33]
+    lk = [40, 70, 200, 12, 300, 33]
+    pq = [8, 130, 70, 4, 260, 40]
+    pk = [40, 72, 200, 12, 300, 40]
+    case = _case(lq, lk, pq, pk, hq=6, hkv=2, d=128, causal="bottom_right", dtype=dtype, seed=77)
+    drop = (0.25, 0xC0FFEE, 7)
+    res = _gpu(case, drop)
+    ref = _oracle(case, drop)
+    Tq, Tk = case.q.shape[0], case.k.shape[0]
+    qrows = real_rows(case.cu_seqlens_q, case.cu_seqlens_q_padded, Tq, case.cu_seqlens_kv)
+    krows = real_rows(case.cu_seqlens_kv, case.cu_seqlens_kv_padded, Tk, case.cu_seqlens_q)
+    assert_close("out", res[0], ref[0], dtype, qrows)
+    assert_lse_close(res[1], ref[1], qrows)
+    form = _oracle(case, drop, out=f64(res[0]), lse=f64(res[1]), mode="formula")
+    assert_close("dq", res[2], form[2], dtype, qrows)
+    assert_close("dk", res[3], form[3], dtype, krows)
+    assert_close("dv", res[4], ref[4], dtype, krows)
