@@ -107,6 +107,15 @@ def test_ragged_lengths_all_head_dims(d, causal):
     check_case(_ragged_case(L, L, P, P, hq=4, hkv=2, d=d, causal=causal, dtype="bf16", seed=d))
 
 
+@pytest.mark.parametrize("d", list(range(8, 257, 8)))
+def test_every_supported_head_dim(d):
+    """Every head dim the library accepts (8..256 in steps of 8), including
+    those that only partly fill their padded width (e.g. 72, 136, 200, 248):
+    a short ragged causal case with real != padded slots."""
+    L, P = [1, 33, 130], [8, 40, 130]
+    check_case(_ragged_case(L, L, P, P, hq=4, hkv=2, d=d, causal=True, dtype="bf16", seed=100 + d))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_lq_differs_from_lk(causal):
     lq = [5, 130, 64, 0, 77, 300]
