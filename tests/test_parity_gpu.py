@@ -107,13 +107,14 @@ def test_ragged_lengths_all_head_dims(d, causal):
     check_case(_ragged_case(L, L, P, P, hq=4, hkv=2, d=d, causal=causal, dtype="bf16", seed=d))
 
 
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("fp16", False)])
 @pytest.mark.parametrize("d", list(range(8, 257, 8)))
-def test_every_supported_head_dim(d):
+def test_every_supported_head_dim(d, dtype, causal):
     """Every head dim the library accepts (8..256 in steps of 8), including
     those that only partly fill their padded width (e.g. 72, 136, 200, 248):
-    a short ragged causal case with real != padded slots."""
+    a short ragged case with real != padded slots."""
     L, P = [1, 33, 130], [8, 40, 130]
-    check_case(_ragged_case(L, L, P, P, hq=4, hkv=2, d=d, causal=True, dtype="bf16", seed=100 + d))
+    check_case(_ragged_case(L, L, P, P, hq=4, hkv=2, d=d, causal=causal, dtype=dtype, seed=100 + d))
 
 
 @pytest.mark.parametrize("causal", [False, True])
