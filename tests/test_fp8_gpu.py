@@ -126,3 +126,27 @@ def test_fp8_paths_agree():
                        attn_mask_type="padding_causal")
     assert (o1.float() - o2.float()).abs().max().item() <= 2e-2 * o2.float().abs().max().item()
     assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("d,causal", [(16, True), (64, False), (136, True), (256, True)])
+def test_fp8_decode_path_head_dims(d, causal):
+    """Head dims outside 80..128 decode q, k, v exactly and run the 16-bit
+    forward: parity at the bar of the output dtype."""
+    import bwd_thd_varlen_amd as A
+    rng = np.random.default_rng(200 + d)
+    L, P = [3, 90, 200], [8, 96, 200]
+    T = sum(P)
+    g = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32))
+    (q8, sq), (k8, sk), (v8, sv) = _quantize(g(T, 4, d)), _quantize(g(T, 2, d)), \
+        _quantize(g(T, 2, d))
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    cp = np.concatenate([[0], np.cumsum(P)]).astype(np.int32)
+    mask = "padding_causal" if causal else "padding"
+    o, l = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, cu_dev(cu), cu_dev(cu),
+                     cu_dev(cp), cu_dev(cp), attn_mask_type=mask)
+    ro, rl = attn_fwd_fp8(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv, cu, cu, cp, cp,
+                          causal=causal)
+    rows = real_rows(cu, cp, T)
+    assert_close("out", o, ro, "bf16", rows)
+    assert_lse_close(l, rl, rows)
+    assert int(torch.count_nonzero(o[torch.as_tensor(~rows, device="cuda")].float())) == 0
