@@ -169,6 +169,10 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 #pragma unroll
           for (int r = 0; r < 16; ++r) dp[r] = -dlt;
         }
+        // the product phases run at raised wave priority, so a wave that
+        // reaches them issues its MFMAs ahead of the other waves' softmax
+        // arithmetic, which then fills the matrix pipe's shadow
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (DPAD == 128) {
           // S and dP interleaved, each K / V operand read two MFMAs ahead
           // (pinned with scheduling barriers; left to itself the scheduler
@@ -197,6 +201,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
             dp = Mfma<DT>::mma(rv.read(kb2, t), doreg[t], dp);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (DROP) {
           // dP = D o (dO V^T): dropped elements 0, kept ones scaled
           dropout_row16(p, w.b, h, qi >> 2, (n0 + 32 * kb2 + 4 * hh) >> 2, li & 3, p.drop_scale, dp);
@@ -211,12 +216,14 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[r] = DROP ? sc[r] * (dp[r] - dlt) : sc[r] * dp[r];     // dS
         const u32x4 b0 = pack_operand<DT>(sc, 0), b1 = pack_operand<DT>(sc, 1);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           acc[cb] = Mfma<DT>::mma(trk.read(cb, 2 * kb2), b0, acc[cb]);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           acc[cb] = Mfma<DT>::mma(trk.read(cb, 2 * kb2 + 1), b1, acc[cb]);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
   }
