@@ -32,7 +32,7 @@ __all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
            "bwd_batched", "LAYOUTS", "attn_fwd_thd_chunk", "attn_bwd_thd_chunk",
            "attn_merge_thd", "fwd_chunk", "bwd_chunk", "merge", "attn_fwd_thd_dropout",
            "attn_bwd_thd_dropout", "attention_thd", "attn_fwd_thd_fp8", "fwd_fp8",
-           "fp8_workspace_size"]
+           "fp8_workspace_size", "attn_bwd_thd_fp8", "bwd_fp8"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
@@ -58,6 +58,7 @@ _FWD_ARGS = [_P, _P, _P, _P, _P,          # q k v out lse
 FWD_STAGES = ("sched", "fwd", "zero_fill_q")
 BWD_STAGES = ("sched", "dq", "dkdv", "zero_fill_q", "zero_fill_kv")
 FP8_FWD_STAGES = ("decode",) + FWD_STAGES
+FP8_BWD_STAGES = ("decode",) + BWD_STAGES
 _BWD_ARGS = [_P, _P, _P, _P, _P, _P,      # q k v out dout lse
              _P, _P, _P,                  # dq dk dv
              _P, _P, _P, _P,
@@ -154,6 +155,10 @@ def lib() -> ctypes.CDLL:
                                        _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P,
                                        ctypes.POINTER(_P), _I]
         L.attn_fwd_thd_fp8.restype = ctypes.c_int
+        L.attn_bwd_thd_fp8.argtypes = [_P, _P, _P, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P,
+                                       ctypes.POINTER(_P), _I]
+        L.attn_bwd_thd_fp8.restype = ctypes.c_int
         L.attn_fwd_thd_dropout.argtypes = _DFWD_ARGS
         L.attn_fwd_thd_dropout.restype = ctypes.c_int
         L.attn_bwd_thd_dropout.argtypes = _DBWD_ARGS
@@ -233,6 +238,11 @@ def attn_bwd_batched_timed(*args, events, n_events) -> int:
 def attn_fwd_thd_fp8(*args) -> int:
     """Same arguments as the C function (pointers as ints); returns the status code."""
     return int(lib().attn_fwd_thd_fp8(*args))
+
+
+def attn_bwd_thd_fp8(*args) -> int:
+    """Same arguments as the C function (pointers as ints); returns the status code."""
+    return int(lib().attn_bwd_thd_fp8(*args))
 
 
 def fp8_workspace_size(batch: int, total_q: int, total_kv: int, hq: int, hkv: int,
@@ -814,6 +824,63 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: flo
                           0 if events is None else events.n)
     _check(st, "attn_fwd_thd_fp8")
     return out, lse
+
+
+def bwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: float,
+            descale_k: float, descale_v: float, out: torch.Tensor, dout: torch.Tensor,
+            lse: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_kv: torch.Tensor,
+            cu_seqlens_q_padded: Optional[torch.Tensor] = None,
+            cu_seqlens_kv_padded: Optional[torch.Tensor] = None,
+            attn_mask_type: str = "padding", softmax_scale: Optional[float] = None,
+            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+            dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            events: Optional["StageEvents"] = None
+            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of ``fwd_fp8``: gradients (dq, dk, dv), in out's dtype, with respect to
+    the real-valued inputs descale_q * q8, descale_k * k8, descale_v * v8."""
+    dev = q8.device
+    codes = lambda t, n: _fp8_codes(t, n, dev)
+    q8, k8, v8 = codes(q8, "q8"), codes(k8, "k8"), codes(v8, "v8")
+    tq, hq, d = q8.shape
+    tk, hkv, dk_ = k8.shape
+    if v8.shape != k8.shape or dk_ != d:
+        raise AttnError("k8 and v8 must be [total_kv, hkv, d] with q8's d")
+    if out.dtype not in _DTYPE:
+        raise AttnError("out must be bf16 or fp16")
+    _need(out, "out", out.dtype, dev)
+    _need(dout, "dout", out.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if tuple(out.shape) != (tq, hq, d) or dout.shape != out.shape or tuple(lse.shape) != (tq, hq):
+        raise AttnError("out and dout must be [total_q, hq, d], lse [total_q, hq]")
+    cq = _cu(cu_seqlens_q, "cu_seqlens_q", dev)
+    ck = _cu(cu_seqlens_kv, "cu_seqlens_kv", dev)
+    cqp = _cu(cu_seqlens_q_padded, "cu_seqlens_q_padded", dev)
+    ckp = _cu(cu_seqlens_kv_padded, "cu_seqlens_kv_padded", dev)
+    batch = cq.numel() - 1
+    if ck.numel() != batch + 1 or any(c is not None and c.numel() != batch + 1 for c in (cqp, ckp)):
+        raise AttnError("all cu_seqlens arrays need batch + 1 entries")
+    if attn_mask_type not in _MASK:
+        raise AttnError(f"attn_mask_type must be one of {sorted(_MASK)}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty((tq, hq, d), dtype=out.dtype, device=dev) if dq is None else dq
+    dk = torch.empty((tk, hkv, d), dtype=out.dtype, device=dev) if dk is None else dk
+    dv = torch.empty((tk, hkv, d), dtype=out.dtype, device=dev) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, out.dtype, dev)
+    need = fp8_workspace_size(batch, tq, tk, hq, hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = attn_bwd_thd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), float(descale_q),
+                          float(descale_k), float(descale_v), out.data_ptr(), dout.data_ptr(),
+                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          cq.data_ptr(), ck.data_ptr(), _ptr(cqp), _ptr(ckp), batch, tq, tk, hq,
+                          hkv, d, scale, _MASK[attn_mask_type], _DTYPE[out.dtype],
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          torch.cuda.current_stream(dev).cuda_stream,
+                          None if events is None else events.ptr,
+                          0 if events is None else events.n)
+    _check(st, "attn_bwd_thd_fp8")
+    return dq, dk, dv
 
 
 def _fp8_codes(t: torch.Tensor, name: str, dev) -> torch.Tensor:

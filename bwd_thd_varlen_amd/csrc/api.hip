@@ -84,6 +84,9 @@ struct CallOpts {
   uint64_t seed = 0;
   uint32_t offset = 0;
   float out_scale = 1.f;      // forward output multiplier
+  float dq_scale = 0.f;       // backward dQ / dK multipliers (0: the softmax scale)
+  float dk_scale = 0.f;
+  float delta_scale = 1.f;    // backward: Delta is used times this
   const void* q8 = nullptr;   // E4M3 q and k for the forward's 8-bit scores
   const void* k8 = nullptr;
   int32_t tsq(int32_t batch) const { return layout == kLayoutSbhd ? batch : 1; }
@@ -180,6 +183,7 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.drop_c3 = geo.offset * (uint32_t)hq;
   a.drop_scale = 256.f / (float)(256u - geo.drop_t);
   a.out_scale = geo.out_scale;
+  a.delta_scale = geo.delta_scale;
   a.q8 = geo.q8;
   a.k8 = geo.k8;
   return a;
@@ -256,14 +260,15 @@ attn_thd_status fwd_impl(const void* q, const void* k, const void* v, void* out,
   return ATTN_THD_OK;
 }
 
-attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void* out,
-                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                         const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_qp,
-                         const int32_t* cu_kp, int32_t batch, int32_t total_q, int32_t total_kv,
-                         int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
-                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
-                         void* const* events, int32_t n_events, const CallOpts& geo) {
-  Common c;
+// Host checks of the backward; nothing is launched before they pass.
+static attn_thd_status bwd_check(const void* q, const void* k, const void* v, const void* out,
+                                 const void* dout, const float* lse, void* dq, void* dk,
+                                 void* dv, const int32_t* cu_q, const int32_t* cu_kv,
+                                 int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq,
+                                 int32_t hkv, int32_t d, float scale, int32_t mask_type,
+                                 int32_t dtype, void* workspace, size_t workspace_bytes,
+                                 void* const* events, int32_t n_events, const CallOpts& geo,
+                                 Common& c) {
   attn_thd_status st = check_common(q, k, v, cu_q, cu_kv, batch, total_q, total_kv, hq, hkv, d,
                                     scale, mask_type, dtype, workspace, workspace_bytes, geo, c);
   if (st != ATTN_THD_OK) return st;
@@ -273,6 +278,21 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
       (reinterpret_cast<uintptr_t>(lse) & 3u))
     return ATTN_THD_EINVAL;
   if (events && n_events != kBwdStages + 1) return ATTN_THD_EINVAL;
+  return ATTN_THD_OK;
+}
+
+attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_qp,
+                         const int32_t* cu_kp, int32_t batch, int32_t total_q, int32_t total_kv,
+                         int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type,
+                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* events, int32_t n_events, const CallOpts& geo) {
+  Common c;
+  attn_thd_status st = bwd_check(q, k, v, out, dout, lse, dq, dk, dv, cu_q, cu_kv, batch, total_q,
+                                 total_kv, hq, hkv, d, scale, mask_type, dtype, workspace,
+                                 workspace_bytes, events, n_events, geo, c);
+  if (st != ATTN_THD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Marks m{events, n_events, s};
   const bool causal = mask_type != ATTN_THD_MASK_PADDING;
@@ -295,8 +315,10 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
   ATTN_TRY(m.mark(1));
   // dQ also forms Delta and LSE * log2(e) for every row it owns and writes
   // them to the workspace for dK/dV
+  if (geo.dq_scale != 0.f) a.scale = geo.dq_scale;
   ATTN_TRY(launch_dq(a, dtype, causal, (int)c.q_tiles_max, s));
   a.list = reinterpret_cast<const int2*>(c.ws + c.L.kv_list);
+  if (geo.dk_scale != 0.f) a.scale = geo.dk_scale;
   ATTN_TRY(m.mark(2));
   ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
   ATTN_TRY(m.mark(3));
@@ -619,6 +641,66 @@ attn_thd_status attn_fwd_thd_fp8(const void* q8, const void* k8, const void* v8,
   return fwd_impl(q16, k16, v16, out, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
                   cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
                   scale * descale_q * descale_k, mask_type, out_dtype, workspace, f.base, stream,
+                  events ? events + 1 : nullptr, events ? n_events - 1 : 0, o);
+}
+
+attn_thd_status attn_bwd_thd_fp8(const void* q8, const void* k8, const void* v8, float descale_q,
+                                 float descale_k, float descale_v, const void* out,
+                                 const void* dout, const float* lse, void* dq, void* dk,
+                                 void* dv, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_kv,
+                                 const int32_t* cu_seqlens_q_padded,
+                                 const int32_t* cu_seqlens_kv_padded, int32_t batch,
+                                 int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv,
+                                 int32_t d, float scale, int32_t mask_type, int32_t dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events, int32_t n_events) {
+  if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return ATTN_THD_EINVAL;
+  if (events && n_events != kBwdStages + 2) return ATTN_THD_EINVAL;
+  for (float s : {descale_q, descale_k, descale_v})
+    if (!(s > 0.f) || !std::isfinite(s)) return ATTN_THD_EINVAL;
+  // the three factors the kernels take: the score scale, and the dQ / dK
+  // multipliers of dS' = dS / descale_v
+  const float s_qk = scale * descale_q * descale_k;
+  const float f_dq = scale * descale_k * descale_v, f_dk = scale * descale_q * descale_v;
+  for (float f : {s_qk, f_dq, f_dk, 1.f / descale_v})
+    if (!(f > 0.f) || !std::isfinite(f)) return ATTN_THD_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return ATTN_THD_EINVAL;
+  if ((total_q > 0 && !q8) || (total_kv > 0 && (!k8 || !v8))) return ATTN_THD_EINVAL;
+  auto al8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; };
+  if (!al8(q8) || !al8(k8) || !al8(v8)) return ATTN_THD_EINVAL;
+  if (d % 8 != 0 || d > 256) return ATTN_THD_EUNSUPPORTED;
+  if (dtype != ATTN_THD_BF16 && dtype != ATTN_THD_FP16) return ATTN_THD_EUNSUPPORTED;
+  const Fp8Layout f = fp8_layout(batch, total_q, total_kv, hq, hkv, d);
+  char* ws = static_cast<char*>(workspace);
+  void* q16 = ws + f.q;
+  void* k16 = ws + f.k;
+  void* v16 = ws + f.v;
+  CallOpts o = kThd;
+  o.dq_scale = f_dq;
+  o.dk_scale = f_dk;
+  o.delta_scale = 1.f / descale_v;
+  // the backward's own checks first, so that nothing is launched on bad
+  // arguments; then room for the decoded copies
+  Common c;
+  attn_thd_status st = bwd_check(q16, k16, v16, out, dout, lse, dq, dk, dv, cu_seqlens_q,
+                                 cu_seqlens_kv, batch, total_q, total_kv, hq, hkv, d, s_qk,
+                                 mask_type, dtype, workspace, f.base,
+                                 events ? events + 1 : nullptr, events ? n_events - 1 : 0, o, c);
+  if (st != ATTN_THD_OK) return st;
+  if (workspace_bytes < f.total) return ATTN_THD_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Marks m{events, n_events, s};
+  ATTN_TRY(m.mark(0));
+  // the codes themselves (exact in both 16-bit types); the descales enter
+  // through s_qk, f_dq, f_dk and the Delta factor
+  ATTN_TRY(launch_decode_e4m3(q8, q16, (int64_t)total_q * hq * d, dtype, s));
+  ATTN_TRY(launch_decode_e4m3(k8, k16, (int64_t)total_kv * hkv * d, dtype, s));
+  ATTN_TRY(launch_decode_e4m3(v8, v16, (int64_t)total_kv * hkv * d, dtype, s));
+  // the backward marks events[1..]
+  return bwd_impl(q16, k16, v16, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
+                  cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
+                  s_qk, mask_type, dtype, workspace, f.base, stream,
                   events ? events + 1 : nullptr, events ? n_events - 1 : 0, o);
 }
 

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
   }
   const int64_t qrow = (int64_t)s.oq + (int64_t)qi * p.tsq;
   const int64_t srow = qrow * p.hq + h;
-  const float delta = sum_halves(dpart);
+  const float delta = sum_halves(dpart) * p.delta_scale;
   const float lse2 = qvalid ? p.lse[srow] * kLog2e : __builtin_inff();
   const float dlt = qvalid ? delta : 0.f;
   // the dK/dV kernel (launched next) reads both per (row, head), Delta

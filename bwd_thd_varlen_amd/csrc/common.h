@@ -575,6 +575,8 @@ struct AttnParams {
   const SeqInfo* seq;
   const int2* list;
   int32_t hq, hkv, group, d;
+  // scale_log2e multiplies the scores; scale is the epilogue multiplier of dQ
+  // and dK (the softmax scale, or for E4M3 inputs each kernel's own factor)
   float scale, scale_log2e;
   int32_t tsq, tskv;   // token strides in rows (1 for THD and bshd, batch for sbhd)
   int32_t accumulate;  // backward: bit kAccDq adds into dq, bit kAccDkDv into dk and dv
@@ -583,6 +585,9 @@ struct AttnParams {
   uint32_t drop_t, seed_lo, seed_hi, drop_c3;   // drop_c3 = offset * hq
   float drop_scale;
   float out_scale;     // forward output multiplier (the V descale of FP8 inputs; else 1)
+  // backward: Delta is formed times delta_scale (1; 1 / descale_v for E4M3
+  // inputs, whose dS is then carried as dS / descale_v)
+  float delta_scale;
   const void* q8;      // forward with E4M3 q and k (the scores on the 8-bit products)
   const void* k8;
 };

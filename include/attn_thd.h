@@ -290,6 +290,40 @@ attn_thd_status attn_fwd_thd_fp8(
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int32_t n_events);
 
+/*
+ * Backward of attn_fwd_thd_fp8 (the same issue's inputs): the gradients with
+ * respect to the real-valued inputs Q = descale_q Q8, K = descale_k K8,
+ * V = descale_v V8 of the forward above, by the same softmax-gradient
+ * identity as attn_bwd_thd:
+ *   dV = P^T dO,  dS = P o (dO V^T - Delta),  Delta = rowsum(dO o O),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ * q8, k8, v8 and the descales as given to the forward (8-byte aligned codes);
+ * out and lse are the forward's results, dout the gradient of out; out, dout,
+ * dq, dk and dv are in dtype (ATTN_THD_BF16 or ATTN_THD_FP16), with the
+ * layouts of attn_bwd_thd.  The codes are decoded exactly into 16-bit copies
+ * in the workspace (attn_thd_fp8_workspace_size(...) bytes) and the descales
+ * are folded into three fp32 factors: the products run on the codes with
+ * score scale scale*descale_q*descale_k, dS is carried as dS / descale_v,
+ * and dQ, dK are multiplied out by scale*descale_k*descale_v and
+ * scale*descale_q*descale_v.  With dtype fp16, dS / descale_v is rounded to
+ * fp16 before its products, so it must stay below 65504 in magnitude.
+ * Returns ATTN_THD_EINVAL for a descale that is not finite and > 0 or makes
+ * one of the factors overflow; boundaries, masks, written rows, other errors
+ * and stream semantics as attn_bwd_thd.  events / n_events: NULL / 0, or 7
+ * events around the stages decode, scheduler, dQ (+ Delta), dK/dV, zero fill
+ * (q rows), zero fill (kv rows).
+ */
+attn_thd_status attn_bwd_thd_fp8(
+    const void* q8, const void* k8, const void* v8,
+    float descale_q, float descale_k, float descale_v,
+    const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events);
+
 enum { ATTN_THD_ACC_DQ = 1, ATTN_THD_ACC_DKDV = 2 };   /* accumulate bits */
 
 attn_thd_status attn_fwd_thd_chunk(

@@ -6,7 +6,7 @@ CPU-baseline leg may import it; the GPU library never does.
 """
 from .attention import (allowed_mask, attn_bwd, attn_bwd_seq, attn_fwd, attn_fwd_seq,
                         merge_partials, sequence_slots)
-from .fp8 import attn_fwd_fp8, decode_e4m3
+from .fp8 import attn_bwd_fp8, attn_fwd_fp8, decode_e4m3
 
 __all__ = ["allowed_mask", "attn_bwd", "attn_bwd_seq", "attn_fwd", "attn_fwd_seq",
-           "merge_partials", "sequence_slots", "attn_fwd_fp8", "decode_e4m3"]
+           "merge_partials", "sequence_slots", "attn_fwd_fp8", "attn_bwd_fp8", "decode_e4m3"]

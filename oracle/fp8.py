@@ -16,15 +16,18 @@ float32 descale factor per tensor:
     O = softmax(scale * s_q * s_k * Q8 K8^T + mask) (s_v * V8),
 
 LSE that of the scaled scores, with the THD boundaries and masks of the bf16
-path (``attention.attn_fwd``).
+path (``attention.attn_fwd``).  Its backward is the gradient with respect to
+the real-valued inputs s_q Q8, s_k K8, s_v V8 (the plain reading: the codes
+and descales define the values, the gradient is that of the attention over
+them), i.e. ``attention.attn_bwd`` on those values.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import attn_fwd
+from .attention import attn_bwd, attn_fwd
 
-__all__ = ["decode_e4m3", "attn_fwd_fp8"]
+__all__ = ["decode_e4m3", "attn_fwd_fp8", "attn_bwd_fp8"]
 
 
 def decode_e4m3(codes) -> np.ndarray:
@@ -49,3 +52,17 @@ def attn_fwd_fp8(q8, k8, v8, s_q: float, s_k: float, s_v: float, cu_seqlens_q, c
         scale = 1.0 / np.sqrt(d)
     return attn_fwd(q * s_q, k * s_k, v * s_v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded,
                     cu_seqlens_kv_padded, scale=scale, causal=causal)
+
+
+def attn_bwd_fp8(q8, k8, v8, s_q: float, s_k: float, s_v: float, dout, cu_seqlens_q,
+                 cu_seqlens_kv, cu_seqlens_q_padded=None, cu_seqlens_kv_padded=None,
+                 scale: float = None, causal=False):
+    """Backward of ``attn_fwd_fp8``: float64 (dq, dk, dv) with respect to s_q Q8, s_k K8,
+    s_v V8, for the output gradient dout."""
+    q, k, v = decode_e4m3(q8), decode_e4m3(k8), decode_e4m3(v8)
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    return attn_bwd(q * s_q, k * s_k, v * s_v, np.asarray(dout, dtype=np.float64), cu_seqlens_q,
+                    cu_seqlens_kv, cu_seqlens_q_padded, cu_seqlens_kv_padded, scale=scale,
+                    causal=causal)

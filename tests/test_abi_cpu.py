@@ -204,6 +204,29 @@ def test_fp8_forward_rejects_bad_host_arguments(A, over, code):
     assert A.attn_fwd_thd_fp8(*args.values()) == code
 
 
+@pytest.mark.parametrize("over,code", [
+    (dict(), 3), (dict(sq=0.0), 1), (dict(sv=float("nan")), 1), (dict(sk=-1.0), 1),
+    (dict(sv=1e-39), 1), (dict(sq=1e30, sv=1e30), 1), (dict(v8=FAKE + 2), 1), (dict(d=12), 2),
+    (dict(dtype=9), 2), (dict(mask=4), 2), (dict(hq=4, hkv=3), 1), (dict(dq=FAKE + 8), 1),
+    (dict(dout=None), 1), (dict(n_events=6), 1), (dict(n_events=7), 3),
+])
+def test_fp8_backward_rejects_bad_host_arguments(A, over, code):
+    """Host-checkable errors return before anything is enqueued (no GPU is touched).
+    With no workspace the size check answers first; with the plain backward's
+    workspace (smaller than the FP8 one) the pointer and event checks are reached."""
+    ev = (ctypes.c_void_p * 7)()
+    args = dict(q8=FAKE, k8=FAKE, v8=FAKE, sq=0.5, sk=0.5, sv=2.0, out=FAKE, dout=FAKE, lse=FAKE,
+                dq=FAKE, dk=FAKE, dv=FAKE, cu_q=FAKE, cu_kv=FAKE, cu_qp=None, cu_kp=None, batch=2,
+                total_q=16, total_kv=16, hq=4, hkv=2, d=64, scale=0.125, mask=1, dtype=0,
+                ws=None, wsb=0, stream=None, events=None, n_events=0)
+    args.update(over)
+    if "dq" in over or "dout" in over or "n_events" in over:
+        args["ws"], args["wsb"] = FAKE, A.workspace_size(2, 16, 16, 4, 2, 64)
+    if "n_events" in over:
+        args["events"] = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+    assert A.attn_bwd_thd_fp8(*args.values()) == code
+
+
 def test_fp8_workspace_is_larger(A):
     assert A.fp8_workspace_size(2, 100, 80, 8, 2, 64) >= \
         A.workspace_size(2, 100, 80, 8, 2, 64) + (100 * 8 + 2 * 80 * 2) * 64 * 2

@@ -5,14 +5,18 @@ and one key the output is the value row itself, so O must equal the decoded
 codes bit for bit for all 256 of them.  The forward on the FP8 page's THD
 shape (TE-2892 "Reproduction": real [100,150,120,130] in padded
 [112,160,128,144], 32 heads, d = 48, real != padded) and on a GQA d = 128 case
-is compared with the oracle at the bar of the 16-bit output dtype.
+is compared with the oracle at the bar of the 16-bit output dtype.  The
+backward from the same inputs (gradients with respect to the descaled values)
+is compared with the oracle's on those shapes, and with power-of-two descales,
+where every folded factor is an exact scaling, with the 16-bit backward on the
+decoded values bit for bit.
 """
 import numpy as np
 import pytest
 import torch
 
 from helpers import assert_close, assert_lse_close, cu_dev, f64, real_rows
-from oracle.fp8 import attn_fwd_fp8, decode_e4m3
+from oracle.fp8 import attn_bwd_fp8, attn_fwd_fp8, decode_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -150,3 +154,94 @@ def test_fp8_decode_path_head_dims(d, causal):
     assert_close("out", o, ro, "bf16", rows)
     assert_lse_close(l, rl, rows)
     assert int(torch.count_nonzero(o[torch.as_tensor(~rows, device="cuda")].float())) == 0
+
+
+# ---------------------------------------------------------------- backward
+def _bwd_case(rng, lq, lk, pq, pk, hq, hkv, d, extra=0):
+    Tq, Tk = sum(pq) + extra, sum(pk) + extra
+    g = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32))
+    (q8, sq), (k8, sk), (v8, sv) = _quantize(g(Tq, hq, d)), _quantize(g(Tk, hkv, d)), \
+        _quantize(g(Tk, hkv, d))
+    cu = lambda a: np.concatenate([[0], np.cumsum(a)]).astype(np.int32)
+    return q8, k8, v8, sq, sk, sv, g(Tq, hq, d), (cu(lq), cu(lk), cu(pq), cu(pk)), (Tq, Tk)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_fp8_backward_te2892_shape(causal, out_dtype):
+    import bwd_thd_varlen_amd as A
+    rng = np.random.default_rng(95)
+    real, padded = [100, 150, 120, 130], [112, 160, 128, 144]
+    q8, k8, v8, sq, sk, sv, do, cus, (Tq, Tk) = _bwd_case(rng, real, real, padded, padded, 32,
+                                                          32, 48, extra=32)
+    mask = "padding_causal" if causal else "padding"
+    print(f"[fp8 bwd] te2892 shape causal={causal} {out_dtype}", flush=True)
+    dev = [cu_dev(c) for c in cus]
+    o, l = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, *dev, attn_mask_type=mask,
+                     out_dtype=out_dtype)
+    dout = do.to(out_dtype)
+    dq, dk, dv = A.bwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, o, dout.cuda(), l, *dev,
+                           attn_mask_type=mask)
+    rdq, rdk, rdv = attn_bwd_fp8(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv, f64(dout), *cus,
+                                 causal=causal)
+    dt = "bf16" if out_dtype == torch.bfloat16 else "fp16"
+    rq, rk = real_rows(cus[0], cus[2], Tq), real_rows(cus[1], cus[3], Tk)
+    assert_close("dq", dq, rdq, dt, rq)
+    assert_close("dk", dk, rdk, dt, rk)
+    assert_close("dv", dv, rdv, dt, rk)
+    for t, rows in ((dq, rq), (dk, rk), (dv, rk)):
+        assert int(torch.count_nonzero(t[torch.as_tensor(~rows, device="cuda")].float())) == 0
+
+
+def test_fp8_backward_gqa_d128_bottom_right():
+    import bwd_thd_varlen_amd as A
+    rng = np.random.default_rng(96)
+    q8, k8, v8, sq, sk, sv, do, cus, (Tq, Tk) = _bwd_case(
+        rng, [64, 200, 33, 0], [130, 200, 9, 5], [64, 208, 40, 8], [136, 200, 16, 8], 8, 2, 128)
+    print("[fp8 bwd] gqa d128 bottom_right", flush=True)
+    dev = [cu_dev(c) for c in cus]
+    mask = "padding_causal_bottom_right"
+    o, l = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, *dev, attn_mask_type=mask)
+    dout = do.to(torch.bfloat16)
+    dq, dk, dv = A.bwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, o, dout.cuda(), l, *dev,
+                           attn_mask_type=mask)
+    rdq, rdk, rdv = attn_bwd_fp8(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv, f64(dout), *cus,
+                                 causal="bottom_right")
+    rq, rk = real_rows(cus[0], cus[2], Tq, cus[1]), real_rows(cus[1], cus[3], Tk, cus[0])
+    assert_close("dq", dq, rdq, "bf16", rq)
+    assert_close("dk", dk, rdk, "bf16", rk)
+    assert_close("dv", dv, rdv, "bf16", rk)
+    # the sequence with no queries: its key rows get zero gradients
+    assert int(torch.count_nonzero(dk[~torch.as_tensor(rk, device="cuda")].float())) == 0
+
+
+@pytest.mark.parametrize("dtype,sv", [(torch.bfloat16, 2.0 ** -5), (torch.float16, 1.0)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_backward_bitwise_16bit_with_power_of_two_descales(dtype, sv, d):
+    """Power-of-two descales make every folded factor an exact scaling, so the FP8
+    backward equals the 16-bit backward on the decoded, descaled values bit for bit
+    (fp16 keeps descale_v = 1: scaling dS there would move values across fp16's
+    subnormal boundary)."""
+    import bwd_thd_varlen_amd as A
+    rng = np.random.default_rng(97 + d)
+    L, P = [1, 77, 300, 129], [8, 80, 300, 136]
+    T = sum(P)
+    sq, sk = 2.0 ** -4, 2.0 ** -3
+    g = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32))
+    f8 = lambda x, s_: (x / s_).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    q8, k8, v8 = f8(g(T, 8, d), sq), f8(g(T, 2, d), sk), f8(g(T, 2, d) * 4, sv)
+    cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    cp = np.concatenate([[0], np.cumsum(P)]).astype(np.int32)
+    dev = [cu_dev(cu), cu_dev(cu), cu_dev(cp), cu_dev(cp)]
+    print(f"[fp8 bwd] bitwise {dtype} d={d}", flush=True)
+    o, l = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, *dev,
+                     attn_mask_type="padding_causal", out_dtype=dtype)
+    dout = g(T, 8, d).to(dtype).cuda()
+    got = A.bwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, o, dout, l, *dev,
+                    attn_mask_type="padding_causal")
+    dec = lambda c, s_: (c.view(torch.float8_e4m3fn).to(torch.float32) * s_).to(dtype).cuda()
+    want = A.bwd(dec(q8, sq), dec(k8, sk), dec(v8, sv), o, dout, l, *dev[:2],
+                 cu_seqlens_q_padded=dev[2], cu_seqlens_kv_padded=dev[3],
+                 attn_mask_type="padding_causal")
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        assert torch.equal(a, b), name

@@ -633,7 +633,7 @@ def test_dropout_is_unbiased_over_seeds():
 
 
 # ---------------------------------------------------------------- FP8 inputs
-from oracle.fp8 import attn_fwd_fp8, decode_e4m3  # noqa: E402
+from oracle.fp8 import attn_bwd_fp8, attn_fwd_fp8, decode_e4m3  # noqa: E402
 
 
 def test_e4m3_decoder_matches_torch_for_every_code():
@@ -666,3 +666,36 @@ def test_fp8_forward_folds_descales_into_the_bf16_definition():
     o3, l3 = attn_fwd_fp8(f8(q * 2), f8(k), f8(v), 0.25, 0.25, 3.0, cu, cu, causal=True)
     np.testing.assert_allclose(o3, o, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(l3, l, rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True, "bottom_right"])
+def test_fp8_backward_chain_rule_through_the_descales(causal):
+    """With the codes fixed, L = sum(dO o O) is a function of the three descales and
+    dL/ds_q = sum(dQ o Q8), dL/ds_k = sum(dK o K8), dL/ds_v = sum(dV o V8), where
+    dQ, dK, dV are the gradients with respect to the real-valued inputs.  Central
+    differences of the forward pin the backward, the descale placement included."""
+    rng = np.random.default_rng(33)
+    lq, lk, pq, pk = [5, 9], [7, 9], [8, 9], [8, 10]
+    hq, hkv, d = 4, 2, 8
+    Tq, Tk = sum(pq), sum(pk)
+    f8 = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32) * 8).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    q8, k8, v8 = f8(Tq, hq, d), f8(Tk, hkv, d), f8(Tk, hkv, d)
+    do = rng.standard_normal((Tq, hq, d))
+    cu = lambda a: np.concatenate([[0], np.cumsum(a)]).astype(np.int32)
+    args = (cu(lq), cu(lk), cu(pq), cu(pk))
+    s = np.array([0.07, 0.11, 0.3])
+
+    def loss(sv):
+        o, _ = attn_fwd_fp8(q8, k8, v8, *sv, *args, causal=causal)
+        return float(np.sum(do * o))
+
+    dq, dk, dv = attn_bwd_fp8(q8, k8, v8, *s, do, *args, causal=causal)
+    codes = (decode_e4m3(q8), decode_e4m3(k8), decode_e4m3(v8))
+    for i, (g, c) in enumerate(zip((dq, dk, dv), codes)):
+        h = 1e-6 * s[i]
+        e = np.zeros(3)
+        e[i] = h
+        fd = (loss(s + e) - loss(s - e)) / (2 * h)
+        an = float(np.sum(g * c))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (i, fd, an)
