@@ -33,6 +33,8 @@ FETCH_SIZE / WRITE_SIZE counters to bytes), --workload NAME:
                         backwards from the merged O/LSE, dQ accumulated)
   fp8_65k               the headline sequences with q, k, v as E4M3 codes and
                         per-tensor descales; the step is the FP8-input forward
+  fp8_train_65k         the fp8_65k inputs; the step is the FP8-input forward
+                        and backward (gradients in bf16)
   dropout_65k           the headline workload with dropout p = 0.1 (Philox keep
                         mask) in the forward and the backward
   chunked_bottom_right  THD query chunks of 2048 tokens (the last tokens of
@@ -91,6 +93,14 @@ WORKLOADS = {
         desc="fp8_65k: the throughput_65k sequences with q, k, v quantised to E4M3 (per-tensor "
              "descale = amax / 448); one step = the FP8-input forward (decode of V + forward); "
              "FLOPs = F_fwd"),
+    "fp8_train_65k": dict(
+        layout="fp8", case="throughput_65k", dtype="e4m3/bf16",
+        peak=1.0 / (0.5 / MFMA_PEAK_FP8_TFLOPS + 0.5 / MFMA_PEAK_BF16_TFLOPS),
+        metric="fwd+bwd TFLOP/s (THD FP8 E4M3 inputs, bf16 out and gradients, padding_causal, "
+               "hq64/hkv8/d128) + % MFMA peak",
+        desc="fp8_train_65k: the fp8_65k inputs; one step = the FP8-input forward and the "
+             "FP8-input backward (q, k, v decoded exactly, 16-bit backward products, gradients "
+             "in bf16 with respect to the descaled inputs); FLOPs = F_fwd + F_bwd"),
     "chunked_bottom_right": dict(
         layout="thd",
         metric="fwd+bwd TFLOP/s (THD bf16 padding_causal_bottom_right, query chunks, "
@@ -255,12 +265,15 @@ def main():
         (q8, sq), (k8, sk), (v8, sv) = quant(q), quant(k), quant(v)
         ws8 = torch.empty(A.fp8_workspace_size(case.batch, q.shape[0], k.shape[0], case.hq,
                                                case.hkv, case.d), dtype=torch.uint8, device=dev)
-        n_fwd, n_bwd = 1, 0
+        n_fwd, n_bwd = 1, 0 if wl.get("fwd_only") else 1
         fkw = dict(cu_seqlens_q_padded=cqp, cu_seqlens_kv_padded=ckp,
                    attn_mask_type=case.mask_type, softmax_scale=case.scale, workspace=ws8)
 
-        def step(ev_f=(None,), ev_b=(), ev_m=None):
+        def step(ev_f=(None,), ev_b=(None,) * n_bwd, ev_m=None):
             A.fwd_fp8(q8, k8, v8, sq, sk, sv, cq, ck, out=out, lse=lse, events=ev_f[0], **fkw)
+            if n_bwd:
+                A.bwd_fp8(q8, k8, v8, sq, sk, sv, out, do, lse, cq, ck, dq=dq, dk=dk, dv=dv,
+                          events=ev_b[0], **fkw)
     elif wl["layout"] == "chunks":
         # every sequence's keys in C chunks of consecutive positions (outside
         # the timed region: gathered into THD chunk tensors)
@@ -312,8 +325,9 @@ def main():
         step()
     torch.cuda.synchronize()
     fwd_stage_names = A.FP8_FWD_STAGES if wl["layout"] == "fp8" else A.FWD_STAGES
+    bwd_stage_names = A.FP8_BWD_STAGES if wl["layout"] == "fp8" else A.BWD_STAGES
     evs = [([A.StageEvents(len(fwd_stage_names) + 1) for _ in range(n_fwd)],
-            [A.StageEvents(len(A.BWD_STAGES) + 1) for _ in range(n_bwd)],
+            [A.StageEvents(len(bwd_stage_names) + 1) for _ in range(n_bwd)],
             [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(n_fwd - 1)] if merge_ev else None)
            for _ in range(args.steps)]
@@ -335,7 +349,7 @@ def main():
             for name, ms in zip(("fwd." + s for s in fwd_stage_names), e.stage_ms()):
                 tot[name] = tot.get(name, 0.0) + ms
         for e in eb:
-            for name, ms in zip(("bwd." + s for s in A.BWD_STAGES), e.stage_ms()):
+            for name, ms in zip(("bwd." + s for s in bwd_stage_names), e.stage_ms()):
                 tot[name] = tot.get(name, 0.0) + ms
         if em:
             tot["fwd.merge"] = sum(a.elapsed_time(b_) for a, b_ in em)
@@ -353,7 +367,8 @@ def main():
     dom = max(work, key=lambda s: avg[s])
     kname, flops = work[dom]
     achieved = flops / (avg[dom] * 1e-3) / 1e12
-    peak = wl.get("peak", MFMA_PEAK_BF16_TFLOPS)
+    # the FP8 forward mixes E4M3 and bf16 products; every other kernel is bf16
+    peak = wl.get("peak", MFMA_PEAK_BF16_TFLOPS) if dom == "fwd.fwd" else MFMA_PEAK_BF16_TFLOPS
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 # counter summaries are taken on the headline workload only

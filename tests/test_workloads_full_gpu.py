@@ -184,6 +184,7 @@ def test_chunks4_65k_sampled(thr):
 
 
 def test_fp8_65k_sampled(thr):
+    """The FP8 forward and backward (the fp8_65k and fp8_train_65k steps) at full size."""
     import bwd_thd_varlen_amd as A
     case = thr
     print("[fp8_65k] FP8-input forward at full size", flush=True)
@@ -210,3 +211,26 @@ def test_fp8_65k_sampled(thr):
         assert_lse_close(l[oq:oq + L, hs], rl, np.ones(L, bool))
     qrows = real_rows(case.cu_seqlens_q, case.cu_seqlens_q_padded, case.q.shape[0])
     assert int(torch.count_nonzero(o[torch.as_tensor(~qrows, device="cuda")].view(torch.int16))) == 0
+
+    # the FP8 backward of the fp8_train_65k step, from this forward's O and LSE
+    print("[fp8_65k] FP8-input backward at full size", flush=True)
+    dout = case.dout.cuda()
+    dq, dk, dv = A.bwd_fp8(q8, k8, v8, sq, sk, sv, o, dout, l, cu_dev(case.cu_seqlens_q),
+                           cu_dev(case.cu_seqlens_kv), cu_dev(case.cu_seqlens_q_padded),
+                           cu_dev(case.cu_seqlens_kv_padded), attn_mask_type=case.mask_type,
+                           softmax_scale=case.scale)
+    torch.cuda.synchronize()
+    for b, g in _samples(case):
+        oq = int(case.cu_seqlens_q_padded[b])
+        L = int(case.cu_seqlens_q[b + 1] - case.cu_seqlens_q[b])
+        hs = slice(g * G, (g + 1) * G)
+        # self-attention workload: key rows share the query rows' offsets
+        rdq, rdk, rdv = oracle.attn_bwd_seq(dec(q8[oq:oq + L, hs]) * sq,
+                                            dec(k8[oq:oq + L, g:g + 1]) * sk,
+                                            dec(v8[oq:oq + L, g:g + 1]) * sv,
+                                            f64(case.dout[oq:oq + L, hs]), case.scale, True)
+        assert_close(f"dq fp8[b{b},g{g}]", dq[oq:oq + L, hs], rdq, case.dtype)
+        assert_close(f"dk fp8[b{b},g{g}]", dk[oq:oq + L, g:g + 1], rdk, case.dtype)
+        assert_close(f"dv fp8[b{b},g{g}]", dv[oq:oq + L, g:g + 1], rdv, case.dtype)
+    for t in (dq, dk, dv):
+        assert int(torch.count_nonzero(t[torch.as_tensor(~qrows, device="cuda")].view(torch.int16))) == 0
