@@ -347,9 +347,14 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, dev=None) -> None:
+def _need(t: torch.Tensor, name: str, dtype=None, dev=None, shape=None) -> None:
+    """Checks a tensor argument; `shape` (checked first) guards the outputs,
+    which the kernels write through raw pointers: an undersized tensor would
+    be written past its end."""
     if not isinstance(t, torch.Tensor):
         raise AttnError(f"{name} must be a tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise AttnError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_cuda:
         raise AttnError(f"{name} must be on the GPU")
     if not t.is_contiguous():
@@ -412,8 +417,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.T
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=dev)
-    _need(out, "out", q.dtype, dev)
-    _need(lse, "lse", torch.float32, dev)
+    _need(out, "out", q.dtype, dev, q.shape)
+    _need(lse, "lse", torch.float32, dev, (tq, hq))
     ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     if dropout_p:
@@ -475,9 +480,9 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _need(dq, "dq", q.dtype, dev)
-    _need(dk, "dk", q.dtype, dev)
-    _need(dv, "dv", q.dtype, dev)
+    _need(dq, "dq", q.dtype, dev, q.shape)
+    _need(dk, "dk", q.dtype, dev, k.shape)
+    _need(dv, "dv", q.dtype, dev, k.shape)
     ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     if dropout_p:
@@ -601,9 +606,9 @@ def bwd_batched(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _need(dq, "dq", q.dtype, dev)
-    _need(dk, "dk", q.dtype, dev)
-    _need(dv, "dv", q.dtype, dev)
+    _need(dq, "dq", q.dtype, dev, q.shape)
+    _need(dk, "dk", q.dtype, dev, k.shape)
+    _need(dv, "dv", q.dtype, dev, k.shape)
     ws = _workspace(workspace, b, b * sq, b * skv, hq, hkv, d, dev)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(cq), _ptr(ck),
@@ -657,8 +662,8 @@ def fwd_chunk(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_padded=None,
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((tq, hq), dtype=torch.float32, device=dev) if lse is None else lse
-    _need(out, "out", q.dtype, dev)
-    _need(lse, "lse", torch.float32, dev)
+    _need(out, "out", q.dtype, dev, q.shape)
+    _need(lse, "lse", torch.float32, dev, (tq, hq))
     ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
     st = attn_fwd_thd_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             lse.data_ptr(), *[_ptr(c) for c in cs], *[_ptr(t) for t in ps], batch,
@@ -702,9 +707,9 @@ def bwd_chunk(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _need(dq, "dq", q.dtype, dev)
-    _need(dk, "dk", q.dtype, dev)
-    _need(dv, "dv", q.dtype, dev)
+    _need(dq, "dq", q.dtype, dev, q.shape)
+    _need(dk, "dk", q.dtype, dev, k.shape)
+    _need(dv, "dv", q.dtype, dev, k.shape)
     ws = _workspace(workspace, batch, tq, tk, hq, hkv, d, dev)
     st = attn_bwd_thd_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
@@ -809,8 +814,8 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: flo
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     out = torch.empty((tq, hq, d), dtype=out_dtype, device=dev) if out is None else out
     lse = torch.empty((tq, hq), dtype=torch.float32, device=dev) if lse is None else lse
-    _need(out, "out", out_dtype, dev)
-    _need(lse, "lse", torch.float32, dev)
+    _need(out, "out", out_dtype, dev, (tq, hq, d))
+    _need(lse, "lse", torch.float32, dev, (tq, hq))
     need = fp8_workspace_size(batch, tq, tk, hq, hkv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -865,8 +870,8 @@ def bwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: flo
     dq = torch.empty((tq, hq, d), dtype=out.dtype, device=dev) if dq is None else dq
     dk = torch.empty((tk, hkv, d), dtype=out.dtype, device=dev) if dk is None else dk
     dv = torch.empty((tk, hkv, d), dtype=out.dtype, device=dev) if dv is None else dv
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _need(t, n, out.dtype, dev)
+    for t, n, shp in ((dq, "dq", (tq, hq, d)), (dk, "dk", (tk, hkv, d)), (dv, "dv", (tk, hkv, d))):
+        _need(t, n, out.dtype, dev, shp)
     need = fp8_workspace_size(batch, tq, tk, hq, hkv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)

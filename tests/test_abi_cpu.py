@@ -230,3 +230,19 @@ def test_fp8_backward_rejects_bad_host_arguments(A, over, code):
 def test_fp8_workspace_is_larger(A):
     assert A.fp8_workspace_size(2, 100, 80, 8, 2, 64) >= \
         A.workspace_size(2, 100, 80, 8, 2, 64) + (100 * 8 + 2 * 80 * 2) * 64 * 2
+
+
+def test_output_shape_checked_before_anything_else(A):
+    """Outputs reach the kernels as raw pointers, so the binding checks their
+    shapes first: an undersized out / lse / dq / dk / dv must raise, not be
+    written past its end."""
+    import torch
+    t = torch.empty((10, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(A.AttnError, match="shape"):
+        A._need(t, "out", torch.bfloat16, None, (12, 4, 64))
+    with pytest.raises(A.AttnError, match="shape"):
+        A._need(torch.empty((10, 3), dtype=torch.float32), "lse", torch.float32, None, (10, 4))
+    # the right shape gets past the shape check (and stops at the device check on the CPU)
+    with pytest.raises(A.AttnError, match="GPU"):
+        A._need(t, "out", torch.bfloat16, None, (10, 4, 64))
+

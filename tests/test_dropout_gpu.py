@@ -5,7 +5,9 @@ threshold), so it is checked bit-exactly against the oracle's mask: with
 V = identity rows the forward's O[i, j] is the dropped probability itself,
 and with dO = identity rows the backward's dV[j, i] is; zeros must sit
 exactly where the oracle drops (or masks) an element.  Values and gradients
-then follow the usual bar against the oracle with the same (p, seed, offset).
+then follow the usual bar against the oracle with the same (p, seed, offset):
+every gradient against the exact one (definition mode), dQ and dK also
+against the formula the kernels evaluate on the GPU forward's own O and LSE.
 """
 import math
 
@@ -107,7 +109,10 @@ def test_dropout_parity(d, dtype, causal, p):
     assert_close("dq", res[2], form[2], dtype, qrows)
     assert_close("dk", res[3], form[3], dtype, krows)
     assert_close("dv", res[4], form[4], dtype, krows)
-    # and the exact gradient of the dropped attention
+    # and the exact gradient of the dropped attention (definition mode), so
+    # that an error shared by the forward and the backward cannot pass
+    assert_close("dq(exact)", res[2], ref[2], dtype, qrows)
+    assert_close("dk(exact)", res[3], ref[3], dtype, krows)
     assert_close("dv(exact)", res[4], ref[4], dtype, krows)
     for name, t, rows in (("out", res[0], ~qrows), ("dq", res[2], ~qrows),
                           ("dk", res[3], ~krows), ("dv", res[4], ~krows)):
@@ -159,4 +164,6 @@ def test_dropout_bottom_right_unequal_lengths(dtype):
     form = _oracle(case, drop, out=f64(res[0]), lse=f64(res[1]), mode="formula")
     assert_close("dq", res[2], form[2], dtype, qrows)
     assert_close("dk", res[3], form[3], dtype, krows)
+    assert_close("dq(exact)", res[2], ref[2], dtype, qrows)
+    assert_close("dk(exact)", res[3], ref[3], dtype, krows)
     assert_close("dv", res[4], ref[4], dtype, krows)

@@ -554,6 +554,65 @@ def test_keep_mask_rate_and_determinism():
     assert keep_mask(5, 7, 0, 0, 1, seed=1, offset=0, t=0).all()
 
 
+def _philox_scalar(ctr, key):
+    """Philox4x32-10 on Python integers, one counter at a time, written from the
+    generator's description (Salmon et al., SC'11, "Philox"): per round, the
+    64-bit products of words 0 and 2 with the two multipliers; new words =
+    (hi(w2 product) ^ w1 ^ k0, lo(w2 product), hi(w0 product) ^ w3 ^ k1,
+    lo(w0 product)); the key is bumped by the two Weyl constants between rounds."""
+    c0, c1, c2, c3 = ctr
+    k0, k1 = key
+    M = 0xFFFFFFFF
+    for rnd in range(10):
+        if rnd:
+            k0, k1 = (k0 + 0x9E3779B9) & M, (k1 + 0xBB67AE85) & M
+        p0, p1 = 0xD2511F53 * c0, 0xCD9E8D57 * c2
+        c0, c1, c2, c3 = (p1 >> 32) ^ c1 ^ k0, p1 & M, (p0 >> 32) ^ c3 ^ k1, p0 & M
+    return [c0, c1, c2, c3]
+
+
+def test_philox_scalar_matches_known_answers():
+    assert _philox_scalar([0, 0, 0, 0], [0, 0]) == [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]
+    assert _philox_scalar([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344],
+                          [0xA4093822, 0x299F31D0]) == [0xD16CFE09, 0x94FDCCEB, 0x5001E420,
+                                                        0x24126EA1]
+
+
+# (query i, key j, sequence b, head h, hq, seed, offset): i and j differ in both
+# their quad (>> 2) and their position in it (& 3), so a transposed counter or
+# a word / byte mix-up picks another byte
+KEEP_POINTS = [(6, 13, 0, 0, 1, 1, 0), (13, 6, 2, 3, 8, 0xDEADBEEF12345678, 5),
+               (1, 10, 5, 7, 8, 2024, 7), (250, 97, 1, 2, 4, 0x5EED, 0),
+               (33, 70, 15, 63, 64, 0xC0FFEE, 3)]
+
+
+def _keep_byte(i, j, b, h, hq, seed, offset, word_of=lambda i, j: i & 3,
+               byte_of=lambda i, j: j & 3, ctr_of=lambda i, j: (j >> 2, i >> 2)):
+    c0, c1 = ctr_of(i, j)
+    words = _philox_scalar([c0, c1, b, (offset * hq + h) & 0xFFFFFFFF],
+                           [seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF])
+    return (words[word_of(i, j)] >> (8 * byte_of(i, j))) & 0xFF
+
+
+def test_keep_mask_layout_by_hand():
+    """Element (i, j) of keep_mask is decided by byte (j & 3) of word (i & 3) of
+    the Philox call with counter (j >> 2, i >> 2, b, offset * hq + h) and key
+    (seed_lo, seed_hi): thresholds t = byte and t = byte + 1 straddle it, so the
+    mask pins the byte exactly at every point."""
+    for i, j, b, h, hq, seed, offset in KEEP_POINTS:
+        byte = _keep_byte(i, j, b, h, hq, seed, offset)
+        for t, want in ((byte, True), (byte + 1, False)):
+            if t > 255:
+                continue
+            m = keep_mask(i + 1, j + 1, b, h, hq, seed=seed, offset=offset, t=t)
+            assert bool(m[i, j]) is want, (i, j, b, h, t)
+    # the points tell the plausible mistakes apart
+    swaps = [dict(ctr_of=lambda i, j: (i >> 2, j >> 2)),
+             dict(word_of=lambda i, j: j & 3, byte_of=lambda i, j: i & 3)]
+    for sw in swaps:
+        assert any(_keep_byte(*pt, **sw) != _keep_byte(*pt) for pt in KEEP_POINTS)
+
+
 def _dropout_case(seed=21, causal=True):
     rng = np.random.default_rng(seed)
     return small_case(rng, lq=[5, 9], lk=[7, 9], pq=[6, 10], pk=[8, 9], hq=4, hkv=2, d=8,

@@ -175,7 +175,9 @@ def test_mha_group_of_one_and_large_group():
 def test_throughput_workload_sampled():
     """The 65536-token workload at full size and launch shape; the oracle
     recomputes sampled (sequence, KV group) pairs: the shortest sequence in
-    every group and a mid-length one in groups 0 and 7."""
+    every group, a mid-length one in groups 0 and 7, and the longest sequence
+    (7960 tokens: 63 query tiles, scheduled first) in group 7 -- every row of
+    all 8 query heads of that group."""
     case = workloads.throughput_65k()
     o, l, dq, dk, dv = gpu_run(case)
     torch.cuda.synchronize()
@@ -183,7 +185,10 @@ def test_throughput_workload_sampled():
     G = case.hq // case.hkv
     b_short = int(np.argmin(real))
     b_mid = int(np.argsort(real)[len(real) // 4])
-    samples = [(b_short, g) for g in range(case.hkv)] + [(b_mid, 0), (b_mid, case.hkv - 1)]
+    b_long = int(np.argmax(real))
+    assert real[b_long] == 7960
+    samples = [(b_short, g) for g in range(case.hkv)] + [(b_mid, 0), (b_mid, case.hkv - 1),
+                                                         (b_long, case.hkv - 1)]
     for b, g in samples:
         oq, L = int(case.cu_seqlens_q_padded[b]), int(real[b])
         hs = slice(g * G, (g + 1) * G)
