@@ -32,14 +32,16 @@ __all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
            "bwd_batched", "LAYOUTS", "attn_fwd_thd_chunk", "attn_bwd_thd_chunk",
            "attn_merge_thd", "fwd_chunk", "bwd_chunk", "merge", "attn_fwd_thd_dropout",
            "attn_bwd_thd_dropout", "attention_thd", "attn_fwd_thd_fp8", "fwd_fp8",
-           "fp8_workspace_size", "attn_bwd_thd_fp8", "bwd_fp8"]
+           "fp8_workspace_size", "attn_bwd_thd_fp8", "bwd_fp8", "attn_bwd_thd_noalloc",
+           "bwd_noalloc", "NOALLOC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
 _LIB = None
 
 STATUS = {0: "ATTN_THD_OK", 1: "ATTN_THD_EINVAL", 2: "ATTN_THD_EUNSUPPORTED",
-          3: "ATTN_THD_EWORKSPACE", 4: "ATTN_THD_ELAUNCH"}
+          3: "ATTN_THD_EWORKSPACE", 4: "ATTN_THD_ELAUNCH", 5: "ATTN_THD_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20    # ATTN_THD_NOALLOC_SCRATCH_BYTES
 DEV_BAD_SEQLENS = 1
 _DTYPE = {torch.bfloat16: 0, torch.float16: 1}
 _MASK = {"padding": 0, "padding_causal": 1, "padding_causal_bottom_right": 2}
@@ -163,6 +165,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_thd_dropout.restype = ctypes.c_int
         L.attn_bwd_thd_dropout.argtypes = _DBWD_ARGS
         L.attn_bwd_thd_dropout.restype = ctypes.c_int
+        L.attn_bwd_thd_noalloc.argtypes = _BWD_ARGS[:-3] + [_P]   # no workspace arguments
+        L.attn_bwd_thd_noalloc.restype = ctypes.c_int
         L.attn_thd_status_string.argtypes = [_I]
         L.attn_thd_status_string.restype = ctypes.c_char_p
         L.attn_thd_read_device_status.argtypes = [_P, _P, ctypes.POINTER(_I)]
@@ -273,6 +277,11 @@ def attn_bwd_thd_chunk(*args) -> int:
 def attn_merge_thd(out, lse, out_part, lse_part, total_q, hq, d, dtype, stream) -> int:
     """Same arguments as the C function (pointers as ints); returns the status code."""
     return int(lib().attn_merge_thd(out, lse, out_part, lse_part, total_q, hq, d, dtype, stream))
+
+
+def attn_bwd_thd_noalloc(*args) -> int:
+    """C ABI attn_bwd_thd_noalloc: attn_bwd_thd's arguments without the workspace pair."""
+    return lib().attn_bwd_thd_noalloc(*args)
 
 
 def attn_fwd_thd_timed(*args, events, n_events) -> int:
@@ -506,6 +515,49 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     else:
         st = attn_bwd_thd_timed(*args, events=events.ptr, n_events=events.n)
     _check(st, "attn_bwd_thd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                dout: torch.Tensor, lse: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                cu_seqlens_kv: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor,
+                dv: torch.Tensor, cu_seqlens_q_padded: Optional[torch.Tensor] = None,
+                cu_seqlens_kv_padded: Optional[torch.Tensor] = None, max_seqlen_q: int = 0,
+                max_seqlen_kv: int = 0, attn_mask_type: str = "padding",
+                softmax_scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """``bwd`` through attn_bwd_thd_noalloc: the caller passes every output, and
+    neither this wrapper nor the library allocates device memory (the scratch
+    is the library's static per-GPU array; calls that overlap on one GPU race)."""
+    dev = q.device
+    _need(q, "q", None, dev)
+    if q.dtype not in _DTYPE:
+        raise AttnError(f"q must be bf16 or fp16, got {q.dtype}")
+    for t, n in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, n, q.dtype, dev)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or k.shape[2] != d:
+        raise AttnError("shape mismatch among q, k, v, out, dout")
+    _need(lse, "lse", torch.float32, dev, (tq, hq))
+    _need(dq, "dq", q.dtype, dev, q.shape)
+    _need(dk, "dk", q.dtype, dev, k.shape)
+    _need(dv, "dv", q.dtype, dev, k.shape)
+    cq = _cu(cu_seqlens_q, "cu_seqlens_q", dev)
+    ck = _cu(cu_seqlens_kv, "cu_seqlens_kv", dev)
+    cqp = _cu(cu_seqlens_q_padded, "cu_seqlens_q_padded", dev)
+    ckp = _cu(cu_seqlens_kv_padded, "cu_seqlens_kv_padded", dev)
+    batch = cq.numel() - 1
+    if ck.numel() != batch + 1 or any(c is not None and c.numel() != batch + 1 for c in (cqp, ckp)):
+        raise AttnError("all cu_seqlens arrays need batch + 1 entries")
+    if attn_mask_type not in _MASK:
+        raise AttnError(f"attn_mask_type must be one of {sorted(_MASK)}")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    st = attn_bwd_thd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cq.data_ptr(), ck.data_ptr(),
+        _ptr(cqp), _ptr(ckp), batch, tq, tk, int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, d,
+        scale, _MASK[attn_mask_type], _DTYPE[q.dtype], torch.cuda.current_stream(dev).cuda_stream)
+    _check(st, "attn_bwd_thd_noalloc")
     return dq, dk, dv
 
 

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/attn_thd.h: argument checks,
 // workspace layout and the launch sequence on the caller's stream.  Nothing
 // here allocates device memory, synchronises or keeps state between calls.
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -763,6 +764,64 @@ attn_thd_status attn_merge_thd(void* out, float* lse, const void* out_part,
   return ATTN_THD_OK;
 }
 
+}  // extern "C"
+
+// ----------------------------------------------------------------- no-allocation backward
+// Scratch of attn_bwd_thd_noalloc: each GPU the library runs on holds its own
+// copy of this array.  In host code the name is only a stand-in for the
+// symbol; the device address of the current GPU's copy comes from
+// hipGetSymbolAddress and is the only form passed to kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_THD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];   // device address of `scratch`, per device
+
+// The current device's copy of `scratch`, looked up on the first call there.
+// Two threads racing on a first call both store the same address.
+attn_thd_status scratch_for(void* stream, void** ptr) {
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_THD_ELAUNCH;
+  if (stream) {
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return ATTN_THD_EINVAL;
+    if (sdev != dev) return ATTN_THD_EINVAL;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_THD_ELAUNCH;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return ATTN_THD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_thd_status attn_bwd_thd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                     const void* dout, const float* lse, void* dq, void* dk,
+                                     void* dv, const int32_t* cu_seqlens_q,
+                                     const int32_t* cu_seqlens_kv,
+                                     const int32_t* cu_seqlens_q_padded,
+                                     const int32_t* cu_seqlens_kv_padded, int32_t batch,
+                                     int32_t total_q, int32_t total_kv, int32_t max_seqlen_q,
+                                     int32_t max_seqlen_kv, int32_t hq, int32_t hkv, int32_t d,
+                                     float scale, int32_t mask_type, int32_t dtype, void* stream) {
+  (void)max_seqlen_q;
+  (void)max_seqlen_kv;
+  if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return ATTN_THD_EINVAL;
+  if (layout(batch, total_q, total_kv, hq).total > ATTN_THD_NOALLOC_SCRATCH_BYTES) return ATTN_THD_ESCRATCH;
+  void* ws = nullptr;
+  const attn_thd_status st = scratch_for(stream, &ws);
+  if (st != ATTN_THD_OK) return st;
+  return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
+                  cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
+                  scale, mask_type, dtype, ws, ATTN_THD_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0,
+                  kThd);
+}
+
 const char* attn_thd_status_string(int32_t status) {
   switch (status) {
     case ATTN_THD_OK: return "ok";
@@ -770,6 +829,7 @@ const char* attn_thd_status_string(int32_t status) {
     case ATTN_THD_EUNSUPPORTED: return "unsupported head dim, dtype or mask";
     case ATTN_THD_EWORKSPACE: return "workspace missing, too small or misaligned";
     case ATTN_THD_ELAUNCH: return "kernel launch failed";
+    case ATTN_THD_ESCRATCH: return "problem exceeds the static scratch of the no-allocation backward";
     default: return "unknown status";
   }
 }

@@ -81,7 +81,8 @@ typedef enum {
   ATTN_THD_EINVAL = 1,        /* bad argument: null pointer, negative size, hq % hkv != 0, ... */
   ATTN_THD_EUNSUPPORTED = 2,  /* d not a multiple of 8 in [8, 256], or unknown dtype / mask */
   ATTN_THD_EWORKSPACE = 3,    /* workspace NULL, too small or not 256-byte aligned */
-  ATTN_THD_ELAUNCH = 4        /* the HIP runtime rejected a kernel launch */
+  ATTN_THD_ELAUNCH = 4,       /* the HIP runtime rejected a kernel launch */
+  ATTN_THD_ESCRATCH = 5       /* attn_bwd_thd_noalloc: the problem needs more than its static scratch */
 } attn_thd_status;
 
 enum { ATTN_THD_BF16 = 0, ATTN_THD_FP16 = 1 };                        /* dtype     */
@@ -142,6 +143,43 @@ attn_thd_status attn_bwd_thd(
     int32_t max_seqlen_q, int32_t max_seqlen_kv,
     int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same operation, arguments,
+ * layouts, outputs and error codes as attn_bwd_thd, and the same kernels; the
+ * scratch they need (the work lists, the per-sequence table and the per-row
+ * Delta and LSE*log2(e) vectors) lives in a file-scope device array of
+ * ATTN_THD_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine); it looks up that GPU's copy of the array once
+ * per device, on its first call there.
+ *   - Problems whose workspace (attn_thd_workspace_size) exceeds
+ *     ATTN_THD_NOALLOC_SCRATCH_BYTES are rejected with ATTN_THD_ESCRATCH
+ *     before anything is launched (the 65536-token, 64-head problem needs
+ *     about 34 MB).
+ *   - The stream must belong to the current device (else ATTN_THD_EINVAL).
+ *   - Every call on a GPU shares that GPU's array, and the array keeps the
+ *     last call's contents: calls that overlap on one GPU (two streams, two
+ *     threads) race and must be serialised by the caller.  Nothing in the
+ *     array needs to start at zero: every call writes what it reads first,
+ *     as with a caller-owned workspace.
+ *   - Bad device data zero-fill the outputs as in attn_bwd_thd; the status
+ *     word stays inside the library (attn_thd_read_device_status cannot
+ *     reach it).
+ */
+#define ATTN_THD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+attn_thd_status attn_bwd_thd_noalloc(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    const int32_t* cu_seqlens_q_padded, const int32_t* cu_seqlens_kv_padded,
+    int32_t batch, int32_t total_q, int32_t total_kv,
+    int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t hq, int32_t hkv, int32_t d, float scale, int32_t mask_type, int32_t dtype,
+    void* stream);
 
 /*
  * Batched layouts read in place, as THD views (TransformerEngine issue 3216,

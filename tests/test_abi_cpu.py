@@ -246,3 +246,22 @@ def test_output_shape_checked_before_anything_else(A):
     with pytest.raises(A.AttnError, match="GPU"):
         A._need(t, "out", torch.bfloat16, None, (10, 4, 64))
 
+
+def test_noalloc_rejects_oversized_and_invalid_problems(A):
+    """attn_bwd_thd_noalloc refuses, before any HIP call, a problem whose
+    workspace exceeds its static scratch (ATTN_THD_ESCRATCH) and invalid sizes."""
+    args = lambda **o: [dict(FAKE_ARGS, **o)[n] for n in NOALLOC_ORDER]
+    big_tq, hq = 1 << 20, 16    # Delta and LSE rows alone: 2 x 4 B x 2^24 = 128 MiB
+    assert A.workspace_size(1, big_tq, big_tq, hq, 1, 64) > A.NOALLOC_SCRATCH_BYTES
+    assert A.attn_bwd_thd_noalloc(*args(total_q=big_tq, total_kv=big_tq, hq=hq)) == 5
+    assert A.attn_bwd_thd_noalloc(*args(hq=0)) == 1
+    assert A.attn_bwd_thd_noalloc(*args(batch=-1)) == 1
+    assert A.status_string(5).startswith("problem exceeds")
+
+
+NOALLOC_ORDER = ["q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "cu_q", "cu_kv", "cu_qp",
+                 "cu_kp", "batch", "total_q", "total_kv", "max_q", "max_kv", "hq", "hkv", "d",
+                 "scale", "mask", "dtype", "stream"]
+FAKE_ARGS = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+                 cu_q=FAKE, cu_kv=FAKE, cu_qp=None, cu_kp=None, batch=1, total_q=16, total_kv=16,
+                 max_q=0, max_kv=0, hq=1, hkv=1, d=64, scale=0.125, mask=0, dtype=0, stream=None)
