@@ -23,7 +23,9 @@ Prints ONE JSON line.  Besides the metric it carries
 Options: --gpus N (only 1 is supported: the library runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --copy-calibration (adds a plain
 1 GiB device copy after the timed region, used to scale rocprofv3's
-FETCH_SIZE / WRITE_SIZE counters to bytes), --workload NAME:
+FETCH_SIZE / WRITE_SIZE counters to bytes), --smi (samples board power and
+graphics clocks with amd-smi during the timed steps; give enough --steps for
+a few seconds), --workload NAME:
   throughput_65k        the headline configuration above (default)
   sbhd_65k              sbhd [4096, 16, 64, 128] bf16 padding_causal, read in
                         place by the batched entry points (same FLOP model)
@@ -145,6 +147,57 @@ def visible_pairs(lq: int, lk: int, causal) -> float:
     return lq * lk / 2.0 if causal else float(lq * lk)
 
 
+class SmiSampler:
+    """Board power and graphics clocks, sampled with ``amd-smi metric -p -c``
+    from a host thread while the timed steps run (``--smi``): shows whether
+    the chip holds its nominal clock or sits at its power limit."""
+
+    def __init__(self, gpu: int = 0):
+        import threading
+        self.gpu, self.samples, self._stop = gpu, [], threading.Event()
+        self._th = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import subprocess
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", str(self.gpu), "-p", "-c"],
+                                   capture_output=True, text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            pw = re.search(r"SOCKET_POWER:\s*(\d+)", r.stdout)
+            clk = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+) MHz", r.stdout)]
+            if pw and clk:
+                self.samples.append((int(pw.group(1)), sum(clk) / len(clk)))
+
+    def __enter__(self):
+        self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._th.join()
+
+    def summary(self):
+        # the first sample may precede the load
+        s = self.samples[1:] or self.samples
+        if not s:
+            return None
+        return {"power_w": round(sum(p for p, _ in s) / len(s), 1),
+                "gfx_clock_mhz": round(sum(c for _, c in s) / len(s), 1),
+                "samples": len(s), "source": "amd-smi metric -p -c during the timed steps"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), with the logical CPU count."""
+    try:
+        names = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                 if l.startswith("model name")]
+    except OSError:
+        names = []
+    return f"{names[0]} ({len(names)} logical CPUs)" if names else "unknown"
+
+
 def cpu_baseline(case, budget_s: float = 12.0, dropout=None, fwd_only=False):
     """The fp64 oracle, as it stands, on (sequence, KV group) units of the same
     workload: the sequences closest to 2400 query tokens first, KV groups 0,
@@ -194,7 +247,7 @@ def cpu_baseline(case, budget_s: float = 12.0, dropout=None, fwd_only=False):
     desc = ", ".join(f"sequence {b} (L={L}) x {sum(1 for u in units if u[0] == b)} KV group(s)"
                      for b, L in seqs)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": (f"fp64 numpy oracle {'fwd' if fwd_only else 'fwd+bwd'} of {desc} ({G} query "
                        f"heads per group) of the "
                        f"same workload, {spent:.1f} s; FLOPs by the workload's pair model")}
@@ -207,6 +260,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--smi", action="store_true",
+                    help="sample board power and clocks (amd-smi) during the timed steps")
     ap.add_argument("--workload", default="throughput_65k", choices=sorted(WORKLOADS))
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -333,11 +388,16 @@ def main():
            for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
+    smi = SmiSampler() if args.smi else None
+    if smi:
+        smi.__enter__()
     t0 = time.perf_counter()
     for ef, eb, em in evs:
         step(ef, eb, em)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if smi:
+        smi.__exit__(None, None, None)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
 
@@ -406,6 +466,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if smi:
+        rec["board"] = smi.summary()
     print(json.dumps(rec), flush=True)
 
 

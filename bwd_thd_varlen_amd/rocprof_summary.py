@@ -169,16 +169,24 @@ RATIOS = [
     ("issuing LDS", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
     ("issuing scalar", "SQ_ACTIVE_INST_SCA", "SQ_WAVE_CYCLES"),
 ]
+# per LDS instruction: bank-conflict cycles (0 = conflict-free)
+LDS_RATIOS = [
+    ("bank-conflict cycles per LDS instruction", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS"),
+    ("bank-conflict cycles per LDS-busy cycle", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS"),
+]
+XCDS = 8   # GRBM counters are summed over the accelerator's 8 XCDs
 
 
 def counters(out: str, dbs, commands) -> None:
     vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(list)
     for db in dbs:
-        for name, counter, value in _rows(db, "select kernel_name, counter_name, value "
-                                              "from counters_collection"):
+        for name, counter, value, dur in _rows(db, "select kernel_name, counter_name, value, "
+                                                   "duration from counters_collection"):
             for stage, prefix in STAGE_KERNELS.items():
                 if name.startswith(prefix):
                     vals[stage][counter].append(float(value))
+                    durs[stage].append(float(dur))
     names = sorted({c for st in vals.values() for c in st})
     lines = ["# Shader-sequencer counters: throughput_65k workload, per dispatch (average)",
              "# Counter runs, from the repository root on one MI355X (TMPDIR=/tmp):"]
@@ -199,6 +207,21 @@ def counters(out: str, dbs, commands) -> None:
             a = avg.get(st, {})
             cells.append(f"{100.0 * a[num] / a[den]:.1f}%" if num in a and a.get(den) else "-")
         lines.append(f"| {label} ({num} / {den}) | " + " | ".join(cells) + " |")
+    for label, num, den in LDS_RATIOS:
+        cells = []
+        for st in STAGE_KERNELS:
+            a = avg.get(st, {})
+            cells.append(f"{a[num] / a[den]:.4g}" if num in a and a.get(den) else "-")
+        if any(c != "-" for c in cells):
+            lines.append(f"| {label} ({num} / {den}) | " + " | ".join(cells) + " |")
+    if any("GRBM_GUI_ACTIVE" in avg.get(st, {}) for st in STAGE_KERNELS):
+        cells = []
+        for st in STAGE_KERNELS:
+            a, d = avg.get(st, {}), durs.get(st)
+            ok = "GRBM_GUI_ACTIVE" in a and d
+            cells.append(f"{a['GRBM_GUI_ACTIVE'] / XCDS / (sum(d) / len(d)):.2f} GHz" if ok else "-")
+        lines.append(f"| shader clock while the kernel runs (GRBM_GUI_ACTIVE / {XCDS} XCDs / "
+                     "dispatch duration) | " + " | ".join(cells) + " |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {out}")
