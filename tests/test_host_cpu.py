@@ -56,9 +56,10 @@ def _db(path, kernels=(), counters=()):
                 "sum(end - start) / 1000.0 as total, avg(end - start) / 1000.0 as average "
                 "from kernels group by name order by total desc")
     con.execute("create table counters_collection (dispatch_id integer primary key, kernel_name text, "
-                "counter_name text, value real)")
-    con.executemany("insert into counters_collection (kernel_name, counter_name, value) "
-                    "values (?, ?, ?)", counters)
+                "counter_name text, value real, duration real)")
+    # (kernel, counter, value) or (kernel, counter, value, dispatch duration in ns)
+    con.executemany("insert into counters_collection (kernel_name, counter_name, value, duration) "
+                    "values (?, ?, ?, ?)", [tuple(c) + (1000.0,) * (4 - len(c)) for c in counters])
     con.commit()
     con.close()
 
@@ -111,3 +112,19 @@ def test_counter_summary_ratios(tmp_path):
     text = open(out).read()
     row = next(l for l in text.splitlines() if l.startswith("| waiting on LDS"))
     assert row.rstrip().endswith("| - | - | 10.0% |")   # 200 / 2000, dkdv only
+
+
+def test_counter_summary_lds_conflicts_and_clock(tmp_path):
+    """Conflict cycles per LDS instruction, and the clock from GRBM_GUI_ACTIVE
+    summed over the 8 XCDs: 8 x 1.6e6 cycles in a 1 ms dispatch is 1.6 GHz."""
+    db = str(tmp_path / "c.db")
+    _db(db, counters=[(DKDV, "SQ_LDS_BANK_CONFLICT", 30.0, 1e6), (DKDV, "SQ_INSTS_LDS", 120.0, 1e6),
+                      (DKDV, "SQ_ACTIVE_INST_LDS", 600.0, 1e6),
+                      (DKDV, "GRBM_GUI_ACTIVE", 8 * 1.6e6, 1e6)])
+    out = str(tmp_path / "c.txt")
+    rs.counters(out, [db], ["CMD"])
+    lines = open(out).read().splitlines()
+    row = next(l for l in lines if l.startswith("| bank-conflict cycles per LDS instruction"))
+    assert row.rstrip().endswith("| - | - | 0.25 |")
+    row = next(l for l in lines if l.startswith("| shader clock"))
+    assert row.rstrip().endswith("| - | - | 1.60 GHz |")
