@@ -36,7 +36,8 @@ __all__ = ["lib", "lib_path", "workspace_size", "attn_fwd_thd", "attn_bwd_thd",
            "bwd_noalloc", "NOALLOC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libattn_thd.so")
+# ATTN_THD_LIB: another build of the same library (e.g. for A/B timing runs)
+_LIB_PATH = os.environ.get("ATTN_THD_LIB") or os.path.join(_HERE, "libattn_thd.so")
 _LIB = None
 
 STATUS = {0: "ATTN_THD_OK", 1: "ATTN_THD_EINVAL", 2: "ATTN_THD_EUNSUPPORTED",

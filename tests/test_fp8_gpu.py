@@ -168,14 +168,18 @@ def _bwd_case(rng, lq, lk, pq, pk, hq, hkv, d, extra=0):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
-def test_fp8_backward_te2892_shape(causal, out_dtype):
+@pytest.mark.parametrize("d", [48, 128])
+def test_fp8_backward_te2892_shape(causal, out_dtype, d):
+    """The TE-2892 lengths (real != padded, 32 rows past every slot) at its head
+    dim 48 and at 128 (8 heads), with and without the causal mask."""
     import bwd_thd_varlen_amd as A
-    rng = np.random.default_rng(95)
+    rng = np.random.default_rng(95 + d)
     real, padded = [100, 150, 120, 130], [112, 160, 128, 144]
-    q8, k8, v8, sq, sk, sv, do, cus, (Tq, Tk) = _bwd_case(rng, real, real, padded, padded, 32,
-                                                          32, 48, extra=32)
+    h = 32 if d == 48 else 8
+    q8, k8, v8, sq, sk, sv, do, cus, (Tq, Tk) = _bwd_case(rng, real, real, padded, padded, h,
+                                                          h, d, extra=32)
     mask = "padding_causal" if causal else "padding"
-    print(f"[fp8 bwd] te2892 shape causal={causal} {out_dtype}", flush=True)
+    print(f"[fp8 bwd] te2892 shape causal={causal} {out_dtype} d={d}", flush=True)
     dev = [cu_dev(c) for c in cus]
     o, l = A.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), sq, sk, sv, *dev, attn_mask_type=mask,
                      out_dtype=out_dtype)
