@@ -609,10 +609,11 @@ attn_thd_status attn_fwd_thd_fp8(const void* q8, const void* k8, const void* v8,
   void* q16 = ws + f.q;
   void* k16 = ws + f.k;
   void* v16 = ws + f.v;
-  // head dims 80..128 (multiples of 16) with 16-byte aligned codes take the
-  // scores on the 8-bit products straight from q8 / k8; other shapes decode
-  // q and k too and run the 16-bit forward
-  const bool s8 = d % 16 == 0 && d > 64 && d <= 128 && aligned16(q8) && aligned16(k8);
+  // head dims 48..256 (multiples of 16) with 16-byte aligned codes take the
+  // scores on the 8-bit products straight from q8 / k8 (64-code chunks, the
+  // last one zero-padded past d); other shapes decode q and k too and run the
+  // 16-bit forward
+  const bool s8 = d % 16 == 0 && d > 32 && d <= 256 && aligned16(q8) && aligned16(k8);
   // the forward's own checks first (in its order), so that nothing is
   // launched on bad arguments; then room for the decoded copies
   Common c;

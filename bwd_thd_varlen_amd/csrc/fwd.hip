@@ -39,12 +39,13 @@ constexpr int fwd_step_keys() { return (DPAD >= 64 && DPAD <= 128) ? 32 : 64; }
 // 32 x 32 x 64 product, whose result tile has the layout of the 16-bit one.
 template <int DT, int DPAD, bool CAUSAL, bool DROP, bool F8 = false>
 __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParams p) {
-  static_assert(!F8 || DPAD == 128, "the 8-bit scores are built for head dims 80..128");
+  // E4M3 K rows of DPAD bytes hold whole 64-code chunks of the 8-bit product
+  static_assert(!F8 || DPAD >= 64, "the 8-bit scores are built for head dims 48..256");
   constexpr int NT = F8 ? 1 : DPAD / 16;   // 16-wide k chunks over the head dim (16-bit Q)
   constexpr int NT8 = DPAD / 64;           // 64-wide k chunks (E4M3 Q)
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
-  // keys per step (the 8-bit K tiles are half the size: 64 keys fit three
-  // workgroups per CU)
+  // keys per step (the 8-bit K tiles are half the size: 64 keys still fit
+  // three workgroups per CU at head dims up to 128)
   constexpr int KS = F8 ? 64 : fwd_step_keys<DPAD>();
   constexpr int NKB = KS / 32;         // 32-key blocks of S^T per step
   // K: row reads (E4M3: DPAD bytes per row, addressed in 16-bit units)
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParam
 
 template <int DT, int DPAD>
 static void launch_fwd_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if constexpr (DPAD == 128) {
+  if constexpr (DPAD >= 64) {
     if (p.q8) {   // E4M3 q and k (no dropout on this path)
       if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, false, true>), dim3(grid), dim3(256), 0, st, p);
       else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, false, true>), dim3(grid), dim3(256), 0, st, p);

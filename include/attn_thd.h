@@ -305,7 +305,7 @@ attn_thd_status attn_bwd_thd_dropout(
  *   O   = softmax(scale * descale_q * descale_k * Q8 K8^T + mask) (descale_v * V8)
  *   LSE = natural log-sum-exp of those scaled scores (float32 [total_q, hq])
  * out is written in out_dtype (ATTN_THD_BF16 or ATTN_THD_FP16).  For head
- * dims 80..128 that are multiples of 16, with q8 and k8 16-byte aligned, the
+ * dims 48..256 that are multiples of 16, with q8 and k8 16-byte aligned, the
  * scores are taken on the 8-bit products (gfx950 E4M3 MFMA) straight from the
  * codes; otherwise q and k are decoded too.  v is always decoded (exactly:
  * every E4M3 value is a bf16 and an fp16 value) into a 16-bit copy in the

@@ -88,9 +88,11 @@ def test_fp8_gqa_d128_bottom_right():
     assert_lse_close(l, rl, rows)
 
 
-@pytest.mark.parametrize("d,causal", [(80, True), (96, False), (128, True)])
+@pytest.mark.parametrize("d,causal", [(48, True), (64, False), (80, True), (96, False),
+                                      (128, True), (176, False), (256, True)])
 def test_fp8_scores_on_8bit_products(d, causal):
-    """Head dims 80..128 (multiples of 16) take the scores on the E4M3 MFMA."""
+    """Head dims 48..256 (multiples of 16) take the scores on the E4M3 MFMA, in
+    64-code chunks of the head dim (48, 80, 176: the last chunk part zeros)."""
     import bwd_thd_varlen_amd as A
     rng = np.random.default_rng(92 + d)
     L, P = [1, 77, 300, 129], [8, 80, 300, 136]
@@ -110,13 +112,14 @@ def test_fp8_scores_on_8bit_products(d, causal):
     assert_lse_close(l, rl, rows)
 
 
-def test_fp8_paths_agree():
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_paths_agree(d):
     """The 8-bit-product path and the decode path (taken when the codes are only
     8-byte aligned) compute the same scores up to summation order."""
     import bwd_thd_varlen_amd as A
-    rng = np.random.default_rng(99)
+    rng = np.random.default_rng(99 + d)
     L = [200, 57]
-    T, d = sum(L), 128
+    T = sum(L)
     g = lambda *s: torch.from_numpy(rng.standard_normal(s, dtype=np.float32))
     (q8, sq), (k8, sk), (v8, sv) = _quantize(g(T, 4, d)), _quantize(g(T, 4, d)), \
         _quantize(g(T, 4, d))
@@ -132,10 +135,10 @@ def test_fp8_paths_agree():
     assert (l1 - l2).abs().max().item() <= 1e-3
 
 
-@pytest.mark.parametrize("d,causal", [(16, True), (64, False), (136, True), (256, True)])
+@pytest.mark.parametrize("d,causal", [(16, True), (40, False), (136, True), (248, True)])
 def test_fp8_decode_path_head_dims(d, causal):
-    """Head dims outside 80..128 decode q, k, v exactly and run the 16-bit
-    forward: parity at the bar of the output dtype."""
+    """Head dims up to 32, and those that are not multiples of 16, decode q, k,
+    v exactly and run the 16-bit forward: parity at the bar of the output dtype."""
     import bwd_thd_varlen_amd as A
     rng = np.random.default_rng(200 + d)
     L, P = [3, 90, 200], [8, 96, 200]
