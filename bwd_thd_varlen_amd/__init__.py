@@ -297,13 +297,18 @@ def attn_bwd_thd_timed(*args, events, n_events) -> int:
 
 class StageEvents:
     """n HIP events (created with the HIP runtime torch loaded) to hand to the
-    instrumented entry points; ``stage_ms()`` reads the stage durations."""
+    instrumented entry points; ``stage_ms()`` reads the stage durations.
 
-    def __init__(self, n: int):
+    ``only=i`` creates just the two events around stage i (the other slots
+    stay NULL, so the call records nothing else); ``stage_ms()`` then gives
+    None for the stages it did not time."""
+
+    def __init__(self, n: int, only: Optional[int] = None):
         self.n = n
         self._hip = _hip_runtime()
         self._arr = (_P * n)()
-        for i in range(n):
+        self._made = [i for i in range(n) if only is None or i in (only, only + 1)]
+        for i in self._made:
             ev = _P()
             if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise AttnError("hipEventCreate failed")
@@ -311,9 +316,12 @@ class StageEvents:
         self.ptr = ctypes.cast(self._arr, ctypes.POINTER(_P))
 
     def stage_ms(self):
-        self._hip.hipEventSynchronize(self._arr[self.n - 1])
+        self._hip.hipEventSynchronize(self._arr[self._made[-1]])
         out = []
         for i in range(self.n - 1):
+            if not (self._arr[i] and self._arr[i + 1]):
+                out.append(None)
+                continue
             ms = ctypes.c_float(0.0)
             if self._hip.hipEventElapsedTime(ctypes.byref(ms), self._arr[i], self._arr[i + 1]) != 0:
                 raise AttnError("hipEventElapsedTime failed")
@@ -322,7 +330,7 @@ class StageEvents:
 
     def __del__(self):
         try:
-            for i in range(self.n):
+            for i in self._made:
                 self._hip.hipEventDestroy(self._arr[i])
         except Exception:
             pass

@@ -213,13 +213,14 @@ ZeroParams zero_params(const Common& c, int32_t batch, int rows, int width, bool
     if ((expr) != hipSuccess) return ATTN_THD_ELAUNCH;   \
   } while (0)
 
-// Optional per-stage event marks (benchmark instrumentation).
+// Optional per-stage event marks (benchmark instrumentation); a NULL entry
+// is a boundary the caller does not time.
 struct Marks {
   void* const* ev;
   int n;
   hipStream_t s;
   hipError_t mark(int i) const {
-    return (ev && i < n) ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+    return (ev && i < n && ev[i]) ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
   }
 };
 

@@ -406,7 +406,10 @@ attn_thd_status attn_merge_thd(void* out, float* lse, const void* out_part, cons
  *   backward (n_events = 6): scheduler, dQ kernel (which also forms
  *                            Delta = rowsum(dO o O)), dK/dV kernel,
  *                            zero fill (query rows), zero fill (key rows)
- * A NULL `events` or another n_events returns ATTN_THD_EINVAL.
+ * A NULL `events` or another n_events returns ATTN_THD_EINVAL.  An entry
+ * of `events` may be NULL: that boundary is not recorded (a caller timing one
+ * stage passes only the two events around it, and adds no other records to
+ * the stream).
  */
 attn_thd_status attn_fwd_thd_timed(
     const void* q, const void* k, const void* v, void* out, float* lse,
