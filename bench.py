@@ -15,6 +15,8 @@ Prints ONE JSON line.  Besides the metric it carries
   stages_ms    -- per-stage times of a few instrumented steps run after the
                   warmup, outside the timed region (a HIP event at every
                   stage boundary costs ~1% of a step);
+  split        -- the forward alone and the backward alone from those steps
+                  (their stages summed), in ms and TFLOP/s by the FLOP model;
   roofline     -- the dominant kernel's algorithmic FLOP/s (from the two HIP
                   events recorded around its launches in the timed region,
                   the only events the timed steps record) against
@@ -460,6 +462,14 @@ def main():
     dom_ms = sum(stage_sums(*e)[dom] for e in evs) / len(evs)
     log(f"[bench] {dom} in the timed steps: {dom_ms:.3f} ms per step")
 
+    # forward alone and backward alone (their stages summed, instrumented pass)
+    fwd_ms = sum(v_ for k_, v_ in avg.items() if k_.startswith("fwd."))
+    bwd_ms = sum(v_ for k_, v_ in avg.items() if k_.startswith("bwd."))
+    split = {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2)}
+    if bwd_ms > 0:
+        split.update({"bwd_ms": round(bwd_ms, 4),
+                      "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2)})
+
     achieved = flops / (dom_ms * 1e-3) / 1e12
     # the FP8 forward mixes E4M3 and bf16 products; every other kernel is bf16
     peak = wl.get("peak", MFMA_PEAK_BF16_TFLOPS) if dom == "fwd.fwd" else MFMA_PEAK_BF16_TFLOPS
@@ -499,6 +509,7 @@ def main():
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         # from the instrumented steps after the warmup (outside the timed region)
         "stages_ms": {k_: round(v_, 4) for k_, v_ in avg.items()},
+        "split": split,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
