@@ -194,14 +194,26 @@ class SmiSampler:
                 "samples": len(s), "source": "amd-smi metric -p -c during the timed steps"}
 
 
-def cpu_model() -> str:
-    """The host CPU's model name (/proc/cpuinfo), with the logical CPU count."""
+def cpu_model(path: str = "/proc/cpuinfo") -> str:
+    """The host CPU's model name (/proc/cpuinfo) with its family / model /
+    stepping numbers (which identify the part where a virtual machine reports
+    only a generic name) and the logical CPU count."""
+    fields = {}
+    names = 0
     try:
-        names = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
-                 if l.startswith("model name")]
+        for line in open(path):
+            key, _, val = line.partition(":")
+            key = key.strip()
+            if key == "model name":
+                names += 1
+            if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                fields[key] = val.strip()
     except OSError:
-        names = []
-    return f"{names[0]} ({len(names)} logical CPUs)" if names else "unknown"
+        pass
+    if "model name" not in fields:
+        return "unknown"
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{fields['model name']} ({ids + '; ' if ids else ''}{names} logical CPUs)"
 
 
 def cpu_baseline(case, budget_s: float = 12.0, dropout=None, fwd_only=False):

@@ -48,6 +48,20 @@ def test_visible_pairs_against_brute_force():
         assert bench.visible_pairs(lq, lk, True) == lq * lk / 2
 
 
+def test_cpu_model_names_the_part(tmp_path):
+    """A generic model name (as some virtual machines report it) still comes
+    with the family / model / stepping numbers and the logical CPU count."""
+    import bench
+    block = ("processor\t: {i}\nvendor_id\t: AuthenticAMD\ncpu family\t: 25\nmodel\t\t: 17\n"
+             "model name\t: AMD EPYC\nstepping\t: 1\nflags\t\t: fpu vme\n\n")
+    path = tmp_path / "cpuinfo"
+    path.write_text("".join(block.format(i=i) for i in range(3)))
+    assert bench.cpu_model(str(path)) == "AMD EPYC (cpu family 25, model 17, stepping 1; 3 logical CPUs)"
+    (tmp_path / "empty").write_text("")
+    assert bench.cpu_model(str(tmp_path / "empty")) == "unknown"
+    assert bench.cpu_model(str(tmp_path / "missing")) == "unknown"
+
+
 def _db(path, kernels=(), counters=()):
     con = sqlite3.connect(path)
     con.execute("create table kernels (name text, start integer, end integer)")
