@@ -62,6 +62,21 @@ def test_cpu_model_names_the_part(tmp_path):
     assert bench.cpu_model(str(tmp_path / "missing")) == "unknown"
 
 
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "4"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """The library runs on one GPU: bench.py exits with a message (status 2)
+    before touching a device when asked for more."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(__file__), "..", "bench.py"),
+                        *argv], capture_output=True, text=True, timeout=120,
+                       env={**os.environ, **env})
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
 def _db(path, kernels=(), counters=()):
     con = sqlite3.connect(path)
     con.execute("create table kernels (name text, start integer, end integer)")
