@@ -35,6 +35,11 @@ Workloads (each named by what it is, with its sizes):
 * ``throughput_65k``      -- 65536 packed tokens, lengths uniform in
   [256, 8192] padded to multiples of 64, hq=64, hkv=8, d=128, bf16,
   ``padding_causal``.
+* ``large_offsets``       -- 266304 tokens (260 slots of 1024, 64 trailing
+  rows), hq=64, hkv=8, d=128, bf16, ``padding_causal``: the query-side
+  tensors pass 2^31 elements and 2^32 bytes.  The one workload drawn on the
+  GPU (torch's seeded generator): numpy would spend about a minute on its
+  4.4e9 draws.
 """
 from __future__ import annotations
 
@@ -53,7 +58,8 @@ _TORCH_DTYPE = {BF16: torch.bfloat16, FP16: torch.float16}
 
 @dataclass
 class Case:
-    """One attention call's inputs (CPU tensors in the storage dtype)."""
+    """One attention call's inputs (tensors in the storage dtype, on the CPU
+    except where a workload says otherwise)."""
 
     name: str
     q: torch.Tensor            # [total_q, hq, d]
@@ -247,6 +253,34 @@ def throughput_65k(seed: int = 0, hq: int = 64, hkv: int = 8, d: int = 128,
                 cu_seqlens_q_padded=cu_pad, cu_seqlens_kv_padded=cu_pad.copy(),
                 scale=1.0 / math.sqrt(d), causal=True, dtype=BF16, max_seqlen_q=max(real),
                 max_seqlen_kv=max(real))
+
+
+def large_offsets(seed: int = 0, device: str = "cuda") -> Case:
+    """Tensors whose rows run past element 2^31: 260 slots of 1024 tokens (the
+    last holding 1000 real tokens, 24 padding rows) and 64 trailing rows after
+    the last slot, T = 266304, hq=64, hkv=8, d=128, bf16, ``padding_causal``,
+    scale 1/sqrt(d).  q, dout (and the out / dq the call writes) hold 2.18e9
+    elements, 4.36 GB each; every row from token 262144 on lies past element
+    2^31 and byte 2^32 of them.
+
+    The tensors are drawn on ``device`` with ``torch.Generator`` seeded with
+    ``seed`` (N(0,1) in bf16; padding and trailing rows too, so a leak of them
+    shows); callers copy the rows the oracle needs to the host.
+    """
+    slots, slot, last_real, trailing = 260, 1024, 1000, 64
+    real = [slot] * (slots - 1) + [last_real]
+    padded = [slot] * slots
+    T = slots * slot + trailing
+    hq, hkv, d = 64, 8, 128
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    draw = lambda *shape: torch.randn(shape, generator=gen, device=device, dtype=torch.bfloat16)
+    q, k, v, dout = draw(T, hq, d), draw(T, hkv, d), draw(T, hkv, d), draw(T, hq, d)
+    cu, cu_pad = _cu(real), _cu(padded)
+    return Case(name="large_offsets", q=q, k=k, v=v, dout=dout, cu_seqlens_q=cu,
+                cu_seqlens_kv=cu.copy(), cu_seqlens_q_padded=cu_pad,
+                cu_seqlens_kv_padded=cu_pad.copy(), scale=1.0 / math.sqrt(d), causal=True,
+                dtype=BF16, max_seqlen_q=slot, max_seqlen_kv=slot)
 
 
 def sbhd_65k(seed: int = 0, S: int = 4096, B: int = 16, hq: int = 64, hkv: int = 8,
