@@ -4,13 +4,14 @@
 // where Delta = rowsum(dO o O) is formed in the dQ kernel's prologue, which
 // also stores -Delta and LSE*log2(e) per (row, head) for dK/dV.
 //
-// dK/dV: one workgroup per (sequence, 32*NW-key tile, KV head g).  Each wave
-// owns 32 keys; K and V of those keys stay in registers (or LDS for d=256)
-// for the whole workgroup, which loops over the hq/hkv query heads of g and
-// over the query tiles that reach the keys, in a fixed order, so the sum
-// over the GQA group happens in registers: deterministic and without
-// atomics (TransformerEngine issue 2448, "Expected behavior"; the KV rows of
-// a tile no query reaches come out as exact zeros).
+// dK/dV: one workgroup per (sequence, 128-key tile, KV head g).  Each wave
+// owns 32 keys (head dims above 128: two waves own 32 keys, one half of the
+// head dim each); K and V of those keys stay in registers for the whole
+// workgroup, which loops over the hq/hkv query heads of g and over the query
+// tiles that reach the keys, in a fixed order, so the sum over the GQA group
+// happens in registers: deterministic and without atomics (TransformerEngine
+// issue 2448, "Expected behavior"; the KV rows of a tile no query reaches
+// come out as exact zeros).
 //
 // dQ: one workgroup per (sequence, 128-query tile, query head): Q, dO,
 // LSE and Delta of its queries stay in registers while K/V steps stream
@@ -249,49 +250,37 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 }
 
 // ----------------------------------------------------------------- dK / dV
-// NW waves (32 keys each), BM queries per step; the K and V operands of the
-// wave's keys stay in registers or are re-read from LDS tiles loaded once
-// (KVM: 0 both in registers, 1 V in LDS, 2 both in LDS), trading registers
-// (occupancy) against LDS traffic.  Each
-// step DMAs the Q and dO tiles of one (query head, query tile) pair plus
+// Head dims up to 128: 4 waves x 32 keys, 32 queries per step; the K and V
+// operands of the wave's keys stay in registers for the whole workgroup.
+// Each step DMAs the Q and dO tiles of one (query head, query tile) pair plus
 // their LSE*log2(e) and -Delta vectors (one 4-byte DMA per wave: wave 0 LSE,
 // wave 1 -Delta, other waves a dummy so that every wave issues the same
 // number of DMAs and can use the same wait count).  Query rows past the real
 // length arrive as zeros in Q, dO, LSE and Delta, so they add nothing.
-// The tiles come through a ring of NBUF buffers filled NBUF-1 steps ahead,
-// with one barrier per step.
+// The tiles come through a ring of two buffers filled one step ahead, with
+// one barrier per step.  The operand reads are pinned a fixed distance ahead
+// of their MFMAs (scheduling barriers), since at 256 VGPRs the scheduler
+// otherwise waits on each read just before its MFMA.
 // ACC: add into dk / dv instead of writing them; DROP: dropout on the
-// probabilities (the keep mask of dropout_block)
-template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, int NW, int BM, int KVM, int OCC, int NBUF>
-__global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
-  constexpr bool K_LDS = KVM == 2;     // K operand re-read from LDS
-  constexpr bool V_LDS = KVM >= 1;     // V operand re-read from LDS
+// probabilities (the keep mask of dropout_block); OCC: workgroups per CU the
+// register budget is sized for.
+template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, int OCC>
+__global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
+  constexpr int NW = 4, BM = 32, NBUF = 2;
   constexpr int BN = 32 * NW;
-  constexpr int NIB = BM / 32;         // 32-query blocks per step
   constexpr int NU = BM / 16;          // 16-query chunks per step
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
-  // K and V in registers, one 32-query block per step: the operand reads are
-  // pinned a fixed distance ahead of their MFMAs (scheduling barriers), since
-  // at 256 VGPRs the scheduler otherwise waits on each read just before its
-  // MFMA
-  constexpr bool PIN = KVM == 0 && NIB == 1;
   using LQ = Lay<DPAD, true>;          // Q, dO: row reads (S, dP) and transposed reads (dK, dV)
-  using LKV = Lay<DPAD, false>;        // K, V kept in LDS (KVM): row reads
   using Dma = TileDma<LQ, BM, NW>;
-  using DmaKV = TileDma<LKV, BN, NW>;
   constexpr int DMA_PER_STEP = 2 * Dma::PER_WAVE + 1;
 
-  static_assert(NBUF >= 2 && NBUF <= 6, "ring depth");
   // ring of NBUF buffers of the Q and dO tiles and their LSE2 | Delta vectors
   __shared__ __attribute__((aligned(16))) uint16_t sQ[NBUF][LQ::template elems<BM>()];
   __shared__ __attribute__((aligned(16))) uint16_t sdO[NBUF][LQ::template elems<BM>()];
   __shared__ __attribute__((aligned(16))) float sVec[NBUF][2 * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sSink[Dma::SINK || DmaKV::SINK ? 512 : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sSink[Dma::SINK ? 512 : 8];
   __shared__ __attribute__((aligned(16))) float sDummy[64];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[K_LDS ? LKV::template elems<BN>() : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[V_LDS ? LKV::template elems<BN>() : 8];
-
   const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
   int item, g;
   xcd_split(blockIdx.x, p.hkv, item, g);
@@ -307,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   // elements per row, and between consecutive tokens of a sequence
   const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
   const int64_t qts = qrs * p.tsq, kvts = kvrs * p.tskv;
-  const uint32_t q_rs_bytes = (uint32_t)(qts * 2), kv_rs_bytes = (uint32_t)(kvts * 2);
+  const uint32_t q_rs_bytes = (uint32_t)(qts * 2);
   const int64_t kvoff = (int64_t)s.ok * kvrs + (int64_t)g * p.d;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + kvoff;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + kvoff;
@@ -375,21 +364,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   for (int k = 0; k < NBUF - 1; ++k)
     if (k < nsteps) issue(k);
 
-  // K and V operands of this wave's 32 keys (zero beyond the real keys),
-  // held in registers or re-read from a resident LDS tile
-  u32x4 kreg[K_LDS ? 1 : NT], vreg[V_LDS ? 1 : NT];
+  // K and V operands of this wave's 32 keys (zero beyond the real keys)
+  u32x4 kreg[NT], vreg[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int c = 16 * t + 8 * hh;
     const bool ok = kj < s.lk && c < p.d;
-    if constexpr (!K_LDS) kreg[t] = ok ? ldg16(kb + (int64_t)kj * kvts + c) : z4;
-    if constexpr (!V_LDS) vreg[t] = ok ? ldg16(vb + (int64_t)kj * kvts + c) : z4;
-  }
-  if constexpr (K_LDS || V_LDS) {
-    DmaKV dkv;
-    dkv.init(wave, lane, p.d, kv_rs_bytes);
-    if constexpr (K_LDS) dkv.issue(kb + (int64_t)n0 * kvts, s.lk - n0, kv_rs_bytes, lds_addr(sK), lds_addr(sSink), wave);
-    if constexpr (V_LDS) dkv.issue(vb + (int64_t)n0 * kvts, s.lk - n0, kv_rs_bytes, lds_addr(sV), lds_addr(sSink), wave);
+    kreg[t] = ok ? ldg16(kb + (int64_t)kj * kvts + c) : z4;
+    vreg[t] = ok ? ldg16(vb + (int64_t)kj * kvts + c) : z4;
   }
   wait_vm<0>();
 
@@ -406,7 +388,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
   // unrolled by two: each copy's ring buffer is a constant
 #pragma unroll 2
   for (int step = 0; step < nsteps; ++step) {
-    // this step's tiles have landed (up to NBUF-2 later steps may not have)
+    // this step's tiles have landed
     wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1 - step));
     barrier_lds_dma();
     if (step + NBUF - 1 < nsteps) issue(step + NBUF - 1);
@@ -424,106 +406,76 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
     }
     // waves with no real key, or whose keys all follow every query, idle
     if (wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q)) {
-      f32x16 sc[NIB], dp[NIB];
-      if constexpr (PIN) {
-        // S and dP interleaved, each Q / dO operand read two MFMAs ahead
-        constexpr int PD = 2;
-        u32x4 aq[NT], ado[NT];
-        sc[0] = zero16();
-        if constexpr (!DROP) {
-          // dP accumulates onto -Delta of its rows, so the chain ends at dP - Delta
+      // S and dP interleaved, each Q / dO operand read two MFMAs ahead
+      constexpr int PD = 2;
+      u32x4 aq[NT], ado[NT];
+      f32x16 sc = zero16(), dp;
+      if constexpr (!DROP) {
+        // dP accumulates onto -Delta of its rows, so the chain ends at dP - Delta
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 nd = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dp[0][4 * q4 + c] = nd[c];
-          }
-        } else {
-          dp[0] = zero16();
+          for (int c = 0; c < 4; ++c) dp[4 * q4 + c] = nd[c];
         }
-#pragma unroll
-        for (int t = 0; t < PD; ++t) {
-          aq[t] = rq.read(0, t);
-          ado[t] = rdo.read(0, t);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          __builtin_amdgcn_sched_barrier(0);
-          sc[0] = Mfma<DT>::mma(aq[t], kreg[t], sc[0]);
-          if (t + PD < NT) aq[t + PD] = rq.read(0, t + PD);
-          __builtin_amdgcn_sched_barrier(0);
-          dp[0] = Mfma<DT>::mma(ado[t], vreg[t], dp[0]);
-          if (t + PD < NT) ado[t + PD] = rdo.read(0, t + PD);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       } else {
-#pragma unroll
-        for (int ib = 0; ib < NIB; ++ib) {
-          sc[ib] = zero16();
-          dp[ib] = zero16();
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            u32x4 kop, vop;
-            if constexpr (K_LDS) kop = lds_row8<LKV>(sK, 32 * wave + li, 16 * t + 8 * hh);
-            else kop = kreg[K_LDS ? 0 : t];
-            if constexpr (V_LDS) vop = lds_row8<LKV>(sV, 32 * wave + li, 16 * t + 8 * hh);
-            else vop = vreg[V_LDS ? 0 : t];
-            sc[ib] = Mfma<DT>::mma(rq.read(ib, t), kop, sc[ib]);
-            dp[ib] = Mfma<DT>::mma(rdo.read(ib, t), vop, dp[ib]);
-          }
-        }
+        dp = zero16();
       }
+#pragma unroll
+      for (int t = 0; t < PD; ++t) {
+        aq[t] = rq.read(0, t);
+        ado[t] = rdo.read(0, t);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        sc = Mfma<DT>::mma(aq[t], kreg[t], sc);
+        if (t + PD < NT) aq[t + PD] = rq.read(0, t + PD);
+        __builtin_amdgcn_sched_barrier(0);
+        dp = Mfma<DT>::mma(ado[t], vreg[t], dp);
+        if (t + PD < NT) ado[t + PD] = rdo.read(0, t + PD);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // P = exp2(S log2e - LSE log2e); the causal mask only on steps that
       // touch the diagonal (a wave-uniform branch): key kj is hidden from
       // query i0 + i while kj - diag > i0 + i
 #pragma unroll
-      for (int ib = 0; ib < NIB; ++ib)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[8 * q4 + 4 * hh]);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[32 * ib + 8 * q4 + 4 * hh]);
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            sc[ib][4 * q4 + c] = fast_exp2(__builtin_fmaf(sc[ib][4 * q4 + c], sl2e, -l4[c]));
-        }
+        for (int c = 0; c < 4; ++c)
+          sc[4 * q4 + c] = fast_exp2(__builtin_fmaf(sc[4 * q4 + c], sl2e, -l4[c]));
+      }
       if (CAUSAL && i0 < wk_hi_q) {
         const int kq = kj_q - i0;
 #pragma unroll
-        for (int ib = 0; ib < NIB; ++ib)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kq > 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3)) sc[ib][r] = 0.f;
+        for (int r = 0; r < 16; ++r)
+          if (kq > 8 * (r >> 2) + 4 * hh + (r & 3)) sc[r] = 0.f;
       }
+      // the key column of the 4 x 4 blocks at queries 8 q4 + 4 hh (+0..3):
+      // this lane's Philox block (4 x 4: element (i, j) is byte j & 3 of word
+      // i & 3); the block of quad lane g is broadcast when q4 = g, so only
+      // four words are live at a time
+      u32x4 mine;
+      if constexpr (DROP) mine = dropout_block(p, w.b, h_step, ((i0 + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2);
 #pragma unroll
-      for (int ib = 0; ib < NIB; ++ib) {
-        // the key column of the 4 x 4 blocks at queries 32 ib + 8 q4 + 4 hh (+0..3)
-        // this lane's Philox block (4 x 4: element (i, j) is byte j & 3 of word
-        // i & 3); the block of quad lane g is broadcast when q4 = g, so only four
-        // words are live at a time
-        u32x4 mine;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
+        u32x4 x;
         if constexpr (DROP)
-          mine = dropout_block(p, w.b, h_step, ((i0 + 32 * ib + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2);
+          x = (u32x4){quad_bcast_at(mine[0], q4), quad_bcast_at(mine[1], q4), quad_bcast_at(mine[2], q4),
+                      quad_bcast_at(mine[3], q4)};
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ibase = 32 * ib + 8 * q4 + 4 * hh;   // first of 4 consecutive queries
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + ibase]);
-          u32x4 x;
-          if constexpr (DROP)
-            x = (u32x4){quad_bcast_at(mine[0], q4), quad_bcast_at(mine[1], q4), quad_bcast_at(mine[2], q4),
-                        quad_bcast_at(mine[3], q4)};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = 4 * q4 + c;
-            const float pr = sc[ib][r];
-            if constexpr (DROP) {
-              // P o D for dV, and dS = P o (D o dP - Delta)
-              const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;
-              sc[ib][r] = pr * dsc;
-              dp[ib][r] = pr * __builtin_fmaf(dp[ib][r], dsc, d4[c]);
-            } else if constexpr (PIN) {
-              dp[ib][r] = pr * dp[ib][r];
-            } else {
-              dp[ib][r] = pr * (dp[ib][r] + d4[c]);
-            }
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * q4 + c;
+          const float pr = sc[r];
+          if constexpr (DROP) {
+            // P o D for dV, and dS = P o (D o dP - Delta)
+            const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;
+            sc[r] = pr * dsc;
+            dp[r] = pr * __builtin_fmaf(dp[r], dsc, d4[c]);
+          } else {
+            dp[r] = pr * dp[r];
           }
         }
       }
@@ -531,38 +483,28 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
       u32x4 bp[NU], bds[NU];
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        bp[u] = pack_operand<DT>(sc[u >> 1], u & 1);
-        bds[u] = pack_operand<DT>(dp[u >> 1], u & 1);
+        bp[u] = pack_operand<DT>(sc, u);
+        bds[u] = pack_operand<DT>(dp, u);
       }
-      if constexpr (PIN) {
-        // dV and dK interleaved, each transposed operand read one MFMA ahead
-        constexpr int PD = 1, NO = NU * NCB;
-        u32x4 tdo[NO], tq[NO];
+      // dV and dK interleaved, each transposed operand read one MFMA ahead
+      constexpr int PDT = 1, NO = NU * NCB;
+      u32x4 tdo[NO], tqo[NO];
 #pragma unroll
-        for (int o = 0; o < PD; ++o) {
-          tdo[o] = trdo.read(o % NCB, o / NCB);
-          tq[o] = trq.read(o % NCB, o / NCB);
-        }
+      for (int o = 0; o < PDT; ++o) {
+        tdo[o] = trdo.read(o % NCB, o / NCB);
+        tqo[o] = trq.read(o % NCB, o / NCB);
+      }
 #pragma unroll
-        for (int o = 0; o < NO; ++o) {
-          const int u = o / NCB, cb = o % NCB;
-          __builtin_amdgcn_sched_barrier(0);
-          adv[cb] = Mfma<DT>::mma(tdo[o], bp[u], adv[cb]);
-          if (o + PD < NO) tdo[o + PD] = trdo.read((o + PD) % NCB, (o + PD) / NCB);
-          __builtin_amdgcn_sched_barrier(0);
-          adk[cb] = Mfma<DT>::mma(tq[o], bds[u], adk[cb]);
-          if (o + PD < NO) tq[o + PD] = trq.read((o + PD) % NCB, (o + PD) / NCB);
-        }
+      for (int o = 0; o < NO; ++o) {
+        const int u = o / NCB, cb = o % NCB;
         __builtin_amdgcn_sched_barrier(0);
-      } else {
-#pragma unroll
-        for (int u = 0; u < NU; ++u)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            adv[cb] = Mfma<DT>::mma(trdo.read(cb, u), bp[u], adv[cb]);
-            adk[cb] = Mfma<DT>::mma(trq.read(cb, u), bds[u], adk[cb]);
-          }
+        adv[cb] = Mfma<DT>::mma(tdo[o], bp[u], adv[cb]);
+        if (o + PDT < NO) tdo[o + PDT] = trdo.read((o + PDT) % NCB, (o + PDT) / NCB);
+        __builtin_amdgcn_sched_barrier(0);
+        adk[cb] = Mfma<DT>::mma(tqo[o], bds[u], adk[cb]);
+        if (o + PDT < NO) tqo[o + PDT] = trq.read((o + PDT) % NCB, (o + PDT) / NCB);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -576,6 +518,278 @@ __global__ __launch_bounds__(NW * 64, OCC) void dkdv_kernel(AttnParams p) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int c0 = 32 * cb + 8 * q4 + 4 * hh;
+        if (c0 < p.d) {
+          float xk[4], xv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xk[e] = adk[cb][4 * q4 + e] * sc0;
+            xv[e] = adv[cb][4 * q4 + e];
+          }
+          if constexpr (ACC) {
+            add_stored<DT>(xk, *reinterpret_cast<const u32x2*>(dkb + c0));
+            add_stored<DT>(xv, *reinterpret_cast<const u32x2*>(dvb + c0));
+          }
+          u32x2 vk = {Mfma<DT>::pack2(xk[0], xk[1]), Mfma<DT>::pack2(xk[2], xk[3])};
+          u32x2 vv = {Mfma<DT>::pack2(xv[0], xv[1]), Mfma<DT>::pack2(xv[2], xv[3])};
+          *reinterpret_cast<u32x2*>(dkb + c0) = vk;
+          *reinterpret_cast<u32x2*>(dvb + c0) = vv;
+        }
+      }
+  }
+}
+
+// ----------------------------------------------------------------- dK / dV, head dims 136..256
+// At these head dims the fp32 dK and dV accumulators of 32 keys alone take
+// 256 registers, which leaves no room for two waves per SIMD.  Here eight
+// waves share 128 keys: waves 2 kb and 2 kb + 1 own key block kb (32 keys)
+// and split the head dim between them, each accumulating dK and dV over its
+// half (128 registers).  Each step, wave 2 kb forms S^T = K Q^T and wave
+// 2 kb + 1 forms dP^T = V dO^T (onto -Delta), each over the whole head dim
+// from one full-width K or V operand held in registers; both tiles go
+// through LDS, so the two waves read the same S and dP and form the same P
+// and dS; then each forms dV += P^T dO and dK += dS^T Q over its own four
+// column blocks.  Two barriers per step: the ring's, and the one after the
+// tiles are written.  Steps, DMA ring, cursors, masks and dropout are those
+// of dkdv_kernel with NW = 8, BM = 32, NBUF = 2.
+template <int DT, bool CAUSAL, bool ACC, bool DROP>
+__global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
+  constexpr int DPAD = 256, NW = 8, BM = 32, NBUF = 2;
+  constexpr int BN = 16 * NW;          // keys per workgroup: NW / 2 blocks of 32
+  constexpr int NT = DPAD / 16;        // 16-wide k chunks of the whole head dim
+  constexpr int NCBH = DPAD / 64;      // 32-column blocks of one half
+  constexpr int NU = BM / 16;          // 16-query chunks per step
+  using LQ = Lay<DPAD, true>;          // Q, dO: row reads (S, dP) and transposed reads (dK, dV)
+  using Dma = TileDma<LQ, BM, NW>;
+  constexpr int DMA_PER_STEP = 2 * Dma::PER_WAVE + 1;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[NBUF][LQ::template elems<BM>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[NBUF][LQ::template elems<BM>()];
+  __shared__ __attribute__((aligned(16))) float sVec[NBUF][2 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sSink[Dma::SINK ? 512 : 8];
+  __shared__ __attribute__((aligned(16))) float sDummy[64];
+  // the S^T (even wave) and dP^T (odd wave) tiles of each key block, as the
+  // 16 accumulator registers of every lane: [wave][register / 4][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 sX[NW][4][64];
+
+  const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
+  int item, g;
+  xcd_split(blockIdx.x, p.hkv, item, g);
+  if (item >= ntiles) return;
+  const WorkItem w = load_item(p.list, p.seq, item);
+  const SeqInfo s = w.s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kblk = wave >> 1, half = wave & 1;
+  const int li = lane & 31, hh = lane >> 5;
+  const int n0 = w.tile * BN;
+  const int kj = n0 + kblk * 32 + li;          // this lane's key (B-operand column)
+  const int wk_lo = n0 + kblk * 32, wk_hi = wk_lo + 31;
+  const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
+  const int64_t qts = qrs * p.tsq, kvts = kvrs * p.tskv;
+  const uint32_t q_rs_bytes = (uint32_t)(qts * 2);
+  const int64_t kvoff = (int64_t)s.ok * kvrs + (int64_t)g * p.d;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const float sl2e = p.scale_log2e;
+
+  const int diag = CAUSAL ? s.diag : 0;
+  const int m_first = CAUSAL ? max(0, n0 - diag) / BM : 0;
+  const int wk_lo_q = wk_lo - diag, wk_hi_q = wk_hi - diag, kj_q = kj - diag;
+  const int m_last = (s.lq + BM - 1) / BM;
+  const int nm = m_last > m_first ? m_last - m_first : 0;
+  const int nsteps = nm * p.group;
+  const int h0 = g * p.group;
+
+  Dma dma_q;
+  dma_q.init(wave, lane, p.d, q_rs_bytes);
+  const uint32_t vec_rs_bytes = (uint32_t)p.hq * (uint32_t)p.tsq * 4u;
+  const uint32_t vec_voff = lane < BM ? (uint32_t)lane * vec_rs_bytes : kOutOfRange;
+  const uint32_t lds_q = lds_addr(sQ[0]), lds_do = lds_addr(sdO[0]), lds_sink = lds_addr(sSink);
+  const uint32_t lds_vec = wave == 0 ? lds_addr(sVec[0]) : (wave == 1 ? lds_addr(sVec[0]) + 256u : lds_addr(sDummy));
+  const uint32_t vec_buf = wave < 2 ? (uint32_t)sizeof(sVec[0]) : 0u;
+  const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q);
+  const uint16_t* dog = reinterpret_cast<const uint16_t*>(p.dout);
+  const float* vg = wave == 0 ? p.lse2 : p.delta;
+  const int64_t row_last = (int64_t)s.oq + (int64_t)(m_last - 1) * BM * p.tsq;
+  int64_t dc_q = row_last * qrs + (int64_t)h0 * p.d;
+  int64_t dc_v = row_last * p.hq + h0;
+  int dc_hg = 0, dc_nrow = s.lq - (m_last - 1) * BM;
+  const int64_t q_back = (int64_t)BM * qts + (int64_t)(p.group - 1) * p.d;
+  const int64_t v_back = (int64_t)BM * p.tsq * p.hq + (p.group - 1);
+  auto issue = [&](int step) {
+    const uint32_t buf = (uint32_t)(step % NBUF);
+    const int nr = dc_nrow > BM ? BM : dc_nrow;
+    dma_q.issue_rsrc(make_rsrc(qg + dc_q, (uint32_t)nr * q_rs_bytes), lds_q + buf * (uint32_t)sizeof(sQ[0]),
+                     lds_sink, wave);
+    dma_q.issue_rsrc(make_rsrc(dog + dc_q, (uint32_t)nr * q_rs_bytes), lds_do + buf * (uint32_t)sizeof(sdO[0]),
+                     lds_sink, wave);
+    dma<4>(make_rsrc(vg + dc_v, wave < 2 ? (uint32_t)nr * vec_rs_bytes : 0u), lds_vec + buf * vec_buf, vec_voff);
+    if (++dc_hg == p.group) {
+      dc_hg = 0;
+      dc_q -= q_back;
+      dc_v -= v_back;
+      dc_nrow += BM;
+    } else {
+      dc_q += p.d;
+      dc_v += 1;
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k)
+    if (k < nsteps) issue(k);
+
+  // the full-width operand of this wave's product: K (even waves) or V (odd)
+  const uint16_t* kvb = reinterpret_cast<const uint16_t*>(half ? p.v : p.k) + kvoff;
+  u32x4 kvreg[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int c = 16 * t + 8 * hh;
+    kvreg[t] = (kj < s.lk && c < p.d) ? ldg16(kvb + (int64_t)kj * kvts + c) : z4;
+  }
+  wait_vm<0>();
+
+  f32x16 adk[NCBH], adv[NCBH];
+#pragma unroll
+  for (int cb = 0; cb < NCBH; ++cb) {
+    adk[cb] = zero16();
+    adv[cb] = zero16();
+  }
+
+  int cm = m_last - 1, chg = 0;
+  for (int step = 0; step < nsteps; ++step) {
+    wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1 - step));
+    barrier_lds_dma();
+    if (step + NBUF - 1 < nsteps) issue(step + NBUF - 1);
+    const int buf = step % NBUF;
+    const uint32_t tq = lds_q + (uint32_t)buf * (uint32_t)sizeof(sQ[0]);
+    const uint32_t tdo = lds_do + (uint32_t)buf * (uint32_t)sizeof(sdO[0]);
+    const float* tvec = sVec[buf];
+    const int i0 = cm * BM;
+    const int h_step = h0 + chg;
+    if (++chg == p.group) {
+      chg = 0;
+      --cm;
+    }
+    // both waves of a key block are active or idle together
+    const bool active = wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q);
+    if (active) {
+      // S^T (even wave) or dP^T onto -Delta (odd wave), operands read two
+      // MFMAs ahead
+      constexpr int PD = 2;
+      const RowReader<LQ> rd(half ? tdo : tq, lane);
+      f32x16 acc;
+      if (half && !DROP) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[4 * q4 + c] = nd[c];
+        }
+      } else {
+        acc = zero16();
+      }
+      u32x4 a[NT];
+#pragma unroll
+      for (int t = 0; t < PD; ++t) a[t] = rd.read(0, t);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc = Mfma<DT>::mma(a[t], kvreg[t], acc);
+        if (t + PD < NT) a[t + PD] = rd.read(0, t + PD);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        sX[wave][q4][lane] = (f32x4){acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+    }
+    // the tiles are in LDS for the partner (the ring's DMA may still run)
+    barrier_lds_writes();
+    if (active) {
+      f32x16 sc, dp;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 x = sX[2 * kblk][q4][lane], y = sX[2 * kblk + 1][q4][lane];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          sc[4 * q4 + c] = x[c];
+          dp[4 * q4 + c] = y[c];
+        }
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[8 * q4 + 4 * hh]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          sc[4 * q4 + c] = fast_exp2(__builtin_fmaf(sc[4 * q4 + c], sl2e, -l4[c]));
+      }
+      if (CAUSAL && i0 < wk_hi_q) {
+        const int kq = kj_q - i0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kq > 8 * (r >> 2) + 4 * hh + (r & 3)) sc[r] = 0.f;
+      }
+      u32x4 mine;
+      if constexpr (DROP) mine = dropout_block(p, w.b, h_step, ((i0 + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
+        u32x4 x;
+        if constexpr (DROP)
+          x = (u32x4){quad_bcast_at(mine[0], q4), quad_bcast_at(mine[1], q4), quad_bcast_at(mine[2], q4),
+                      quad_bcast_at(mine[3], q4)};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * q4 + c;
+          const float pr = sc[r];
+          if constexpr (DROP) {
+            const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;
+            sc[r] = pr * dsc;
+            dp[r] = pr * __builtin_fmaf(dp[r], dsc, d4[c]);
+          } else {
+            dp[r] = pr * dp[r];
+          }
+        }
+      }
+      u32x4 bp[NU], bds[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        bp[u] = pack_operand<DT>(sc, u);
+        bds[u] = pack_operand<DT>(dp, u);
+      }
+      // dV and dK over this wave's column blocks, each transposed operand
+      // read one MFMA ahead
+      const TrReader<LQ> trq(tq, lane), trdo(tdo, lane);
+      constexpr int PD = 1, NO = NU * NCBH;
+      const int cb0 = half * NCBH;
+      u32x4 tdv[NO], tqv[NO];
+#pragma unroll
+      for (int o = 0; o < PD; ++o) {
+        tdv[o] = trdo.read(cb0 + o % NCBH, o / NCBH);
+        tqv[o] = trq.read(cb0 + o % NCBH, o / NCBH);
+      }
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        const int u = o / NCBH, cb = o % NCBH;
+        __builtin_amdgcn_sched_barrier(0);
+        adv[cb] = Mfma<DT>::mma(tdv[o], bp[u], adv[cb]);
+        if (o + PD < NO) tdv[o + PD] = trdo.read(cb0 + (o + PD) % NCBH, (o + PD) / NCBH);
+        __builtin_amdgcn_sched_barrier(0);
+        adk[cb] = Mfma<DT>::mma(tqv[o], bds[u], adk[cb]);
+        if (o + PD < NO) tqv[o + PD] = trq.read(cb0 + (o + PD) % NCBH, (o + PD) / NCBH);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if (kj < s.lk) {
+    const int64_t row = (int64_t)kj * kvts;
+    uint16_t* dkb = reinterpret_cast<uint16_t*>(p.dk) + kvoff + row;
+    uint16_t* dvb = reinterpret_cast<uint16_t*>(p.dv) + kvoff + row;
+    const float sc0 = p.scale;
+#pragma unroll
+    for (int cb = 0; cb < NCBH; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c0 = 32 * (half * NCBH + cb) + 8 * q4 + 4 * hh;
         if (c0 < p.d) {
           float xk[4], xv[4];
 #pragma unroll
@@ -629,31 +843,46 @@ hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tile
 }
 
 // keys per dK/dV work item for a head dim
-int dkdv_tile(int d) { return d <= 128 ? 128 : 64; }
+int dkdv_tile(int d) { (void)d; return 128; }
 
-template <int DT, int DPAD, bool CAUSAL, int NW, int BM, int KVM, int OCC, int NBUF>
-static void launch_dkdv_c(const AttnParams& p, int grid, hipStream_t st) {
-  const dim3 g(grid), blk(NW * 64);
-  if (p.accumulate & kAccDkDv)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, true, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
-  else if (p.drop_t)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
-  else
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, NW, BM, KVM, OCC, NBUF>), g, blk, 0, st, p);
+template <int DT, bool CAUSAL>
+static void launch_dkdv_split_c(const AttnParams& p, int grid, hipStream_t st) {
+  const dim3 g(grid), blk(512);
+  if (p.accumulate & kAccDkDv) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, true, false>), g, blk, 0, st, p);
+  else if (p.drop_t) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, true>), g, blk, 0, st, p);
+  else hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, false>), g, blk, 0, st, p);
 }
 
-template <int DT, int DPAD, int NW, int BM, int KVM, int OCC, int NBUF>
+template <int DT>
+static void launch_dkdv_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
+  if (causal) launch_dkdv_split_c<DT, true>(p, grid, st);
+  else launch_dkdv_split_c<DT, false>(p, grid, st);
+}
+
+template <int DT, int DPAD, bool CAUSAL, int OCC>
+static void launch_dkdv_c(const AttnParams& p, int grid, hipStream_t st) {
+  const dim3 g(grid), blk(256);
+  if (p.accumulate & kAccDkDv)
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, true, false, OCC>), g, blk, 0, st, p);
+  else if (p.drop_t)
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, OCC>), g, blk, 0, st, p);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, OCC>), g, blk, 0, st, p);
+}
+
+template <int DT, int DPAD, int OCC>
 static void launch_dkdv_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (causal) launch_dkdv_c<DT, DPAD, true, NW, BM, KVM, OCC, NBUF>(p, grid, st);
-  else launch_dkdv_c<DT, DPAD, false, NW, BM, KVM, OCC, NBUF>(p, grid, st);
+  if (causal) launch_dkdv_c<DT, DPAD, true, OCC>(p, grid, st);
+  else launch_dkdv_c<DT, DPAD, false, OCC>(p, grid, st);
 }
 
 template <int DT>
 static void launch_dkdv_dt(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (p.d <= 32) launch_dkdv_d<DT, 32, 4, 64, 0, 1, 2>(p, causal, grid, st);
-  else if (p.d <= 64) launch_dkdv_d<DT, 64, 4, 64, 0, 1, 2>(p, causal, grid, st);
-  else if (p.d <= 128) launch_dkdv_d<DT, 128, 4, 32, 0, 2, 2>(p, causal, grid, st);
-  else launch_dkdv_d<DT, 256, 2, 32, 2, 1, 2>(p, causal, grid, st);
+  // three workgroups per CU up to d = 64 (<= 168 VGPRs), two at 128
+  if (p.d <= 32) launch_dkdv_d<DT, 32, 3>(p, causal, grid, st);
+  else if (p.d <= 64) launch_dkdv_d<DT, 64, 3>(p, causal, grid, st);
+  else if (p.d <= 128) launch_dkdv_d<DT, 128, 2>(p, causal, grid, st);
+  else launch_dkdv_split<DT>(p, causal, grid, st);
 }
 
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st) {

@@ -360,6 +360,16 @@ __device__ __forceinline__ void barrier_lds_dma() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier after LDS stores that other waves read next: waits for
+// this wave's LDS operations only (lgkmcnt), not for its outstanding DMA
+// (vmcnt), so a ring refill issued earlier keeps running across it.
+__device__ __forceinline__ void barrier_lds_writes() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Fills a ROWS-row tile of layout L from global rows (row stride
 // `rs_bytes`), NWAVES waves sharing the work.  Each 64-lane DMA instruction
 // writes 1 KB of the tile, i.e. slots [64i, 64i + 64) of 16 bytes; slot s is
