@@ -45,6 +45,8 @@ a few seconds), --workload NAME:
                         and backward (gradients in bf16)
   dropout_65k           the headline workload with dropout p = 0.1 (Philox keep
                         mask) in the forward and the backward
+  d64_65k, d256_65k     the headline sequences at head dim 64 / 256 (hq 64,
+                        hkv 8, bf16, causal)
   chunked_bottom_right  THD query chunks of 2048 tokens (the last tokens of
                         each context) against contexts U[2048, 8192] (65536
                         key tokens), bottom-right causal; FLOPs counted on
@@ -109,6 +111,16 @@ WORKLOADS = {
         desc="fp8_train_65k: the fp8_65k inputs; one step = the FP8-input forward and the "
              "FP8-input backward (q, k, v decoded exactly, 16-bit backward products, gradients "
              "in bf16 with respect to the descaled inputs); FLOPs = F_fwd + F_bwd"),
+    "d64_65k": dict(
+        layout="thd",
+        metric="fwd+bwd TFLOP/s (THD bf16 padding_causal, hq64/hkv8/d64) + % MFMA peak",
+        desc="d64_65k: the throughput_65k sequences at head dim 64 (hq=64 hkv=8), bf16, "
+             "padding_causal, fwd+bwd; same FLOP model"),
+    "d256_65k": dict(
+        layout="thd",
+        metric="fwd+bwd TFLOP/s (THD bf16 padding_causal, hq64/hkv8/d256) + % MFMA peak",
+        desc="d256_65k: the throughput_65k sequences at head dim 256 (hq=64 hkv=8), bf16, "
+             "padding_causal, fwd+bwd; same FLOP model"),
     "chunked_bottom_right": dict(
         layout="thd",
         metric="fwd+bwd TFLOP/s (THD bf16 padding_causal_bottom_right, query chunks, "

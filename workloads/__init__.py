@@ -35,6 +35,8 @@ Workloads (each named by what it is, with its sizes):
 * ``throughput_65k``      -- 65536 packed tokens, lengths uniform in
   [256, 8192] padded to multiples of 64, hq=64, hkv=8, d=128, bf16,
   ``padding_causal``.
+* ``d64_65k``, ``d256_65k`` -- the throughput_65k sequences at head dims 64
+  and 256 (hq=64, hkv=8, bf16, causal).
 * ``large_offsets``       -- 266304 tokens (260 slots of 1024, 64 trailing
   rows), hq=64, hkv=8, d=128, bf16, ``padding_causal``: the query-side
   tensors pass 2^31 elements and 2^32 bytes.  The one workload drawn on the
@@ -253,6 +255,20 @@ def throughput_65k(seed: int = 0, hq: int = 64, hkv: int = 8, d: int = 128,
                 cu_seqlens_q_padded=cu_pad, cu_seqlens_kv_padded=cu_pad.copy(),
                 scale=1.0 / math.sqrt(d), causal=True, dtype=BF16, max_seqlen_q=max(real),
                 max_seqlen_kv=max(real))
+
+
+def d64_65k(seed: int = 0) -> Case:
+    """The throughput_65k sequences at head dim 64 (hq=64, hkv=8, bf16, causal)."""
+    c = throughput_65k(seed, d=64)
+    c.name = "d64_65k"
+    return c
+
+
+def d256_65k(seed: int = 0) -> Case:
+    """The throughput_65k sequences at head dim 256 (hq=64, hkv=8, bf16, causal)."""
+    c = throughput_65k(seed, d=256)
+    c.name = "d256_65k"
+    return c
 
 
 def large_offsets(seed: int = 0, device: str = "cuda") -> Case:
