@@ -15,8 +15,10 @@
 //
 // dQ: one workgroup per (sequence, 128-query tile, query head): Q, dO,
 // LSE and Delta of its queries stay in registers while K/V steps stream
-// through LDS; S and dP are recomputed here instead of accumulating dQ across
-// key-tile workgroups, which keeps every dQ element owned by one workgroup.
+// through LDS (head dims above 128: two waves per 32 queries, one holding Q
+// and one dO, each accumulating half of dQ); S and dP are recomputed here
+// instead of accumulating dQ across key-tile workgroups, which keeps every dQ
+// element owned by one workgroup.
 //
 // Both kernels fill LDS tiles by global->LDS DMA ahead of the compute (see
 // TileDma in common.h): dQ double-buffers one step ahead, dK/dV uses a ring.
@@ -237,6 +239,204 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int c0 = 32 * cb + 8 * q4 + 4 * hh;
+        if (c0 < p.d) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = acc[cb][4 * q4 + e] * sc0;
+          if constexpr (ACC) add_stored<DT>(x, *reinterpret_cast<const u32x2*>(out + c0));
+          u32x2 val = {Mfma<DT>::pack2(x[0], x[1]), Mfma<DT>::pack2(x[2], x[3])};
+          *reinterpret_cast<u32x2*>(out + c0) = val;
+        }
+      }
+  }
+}
+
+// ----------------------------------------------------------------- dQ, head dims 136..256
+// Q, dO and the fp32 dQ accumulator of 32 queries take 256 registers at these
+// head dims, and 64-key K / V tiles 141 KB of LDS: one wave per SIMD.  Here
+// eight waves share the 128-query tile: waves 2 qb and 2 qb + 1 own query
+// block qb and split the head dim of dQ between them (64 accumulator
+// registers each).  Each 32-key step, wave 2 qb forms S^T = K Q^T from Q and
+// wave 2 qb + 1 forms dP^T = V dO^T (onto -Delta) from dO, each over the whole
+// head dim; both tiles go through LDS, so the pair forms the same dS and each
+// adds dS K over its own four column blocks.  K and V use the same padded
+// tile layout; both waves of a pair form Delta from dO and O (the same
+// arithmetic, so the same value).  Two barriers per step: the ring's, and the
+// one after the tiles are written.
+template <int DT, bool CAUSAL, bool ACC, bool DROP>
+__global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
+  constexpr int DPAD = 256, NW = 8, KS = 32;
+  constexpr int NT = DPAD / 16;
+  constexpr int NCBH = DPAD / 64;      // 32-column blocks of one half
+  using LK = Lay<DPAD, true>;          // K and V: row reads (S, dP); K also transposed (dQ)
+  using Dma = TileDma<LK, KS, NW>;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][LK::template elems<KS>()];
+  // the S^T (even wave) and dP^T (odd wave) tiles of each query block, as the
+  // 16 accumulator registers of every lane: [wave][register / 4][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 sX[NW][4][64];
+
+  const int ntiles = uniform(p.hdr[kHdrNQTiles]);
+  int item, h;
+  xcd_split(blockIdx.x, p.hq, item, h);
+  if (item >= ntiles) return;
+  const WorkItem w = load_item(p.list, p.seq, item);
+  const SeqInfo s = w.s;
+  const int g = h / p.group;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qblk = wave >> 1, half = wave & 1;
+  const int li = lane & 31, hh = lane >> 5;
+  const int m0 = w.tile * kQTile;
+  const int qi = m0 + qblk * 32 + li;
+  const int wq_lo = m0 + qblk * 32, wq_hi = wq_lo + 31;
+  const int64_t qrs = (int64_t)p.hq * p.d, kvrs = (int64_t)p.hkv * p.d;
+  const int64_t qts = qrs * p.tsq, kvts = kvrs * p.tskv;
+  const uint32_t kv_rs_bytes = (uint32_t)(kvts * 2);
+  const int64_t qoff = (int64_t)s.oq * qrs + (int64_t)h * p.d;
+  const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + qoff;
+  const uint16_t* dob = reinterpret_cast<const uint16_t*>(p.dout) + qoff;
+  const uint16_t* obase = reinterpret_cast<const uint16_t*>(p.o) + qoff;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)s.ok * kvrs + (int64_t)g * p.d;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const bool qvalid = qi < s.lq;
+
+  const int diag = CAUSAL ? s.diag : 0;
+  const int q_end = min(s.lq, m0 + kQTile);
+  const int kend = CAUSAL ? max(0, min(s.lk, q_end + diag)) : s.lk;
+  const int nsteps = (kend + KS - 1) / KS;
+  const float sl2e = p.scale_log2e;
+  const int wq_lo_k = wq_lo + diag, wq_hi_k = wq_hi + diag, qi_k = qi + diag;
+
+  Dma dma;
+  dma.init(wave, lane, p.d, kv_rs_bytes);
+  auto issue = [&](int step) {
+    const uint32_t buf = (uint32_t)(step & 1);
+    const int n0 = step * KS;
+    dma.issue_exact(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sK[0]) + buf * sizeof(sK[0]), wave);
+    dma.issue_exact(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sV[0]) + buf * sizeof(sV[0]), wave);
+  };
+  if (nsteps > 0) issue(0);
+
+  // this wave's operand (Q on even waves, dO on odd) stays in registers;
+  // Delta = sum_c dO_c O_c in fp32 over the two halves of the wave
+  u32x4 opreg[NT];
+  float dpart = 0.f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int c = 16 * t + 8 * hh;
+    const bool ok = qvalid && c < p.d;
+    const u32x4 d4 = ok ? ldg16(dob + (int64_t)qi * qts + c) : z4;
+    const u32x4 o4 = ok ? ldg16(obase + (int64_t)qi * qts + c) : z4;
+    opreg[t] = half ? d4 : (ok ? ldg16(qb + (int64_t)qi * qts + c) : z4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 x = Mfma<DT>::unpack2(d4[e]), y = Mfma<DT>::unpack2(o4[e]);
+      dpart = __builtin_fmaf(x[0], y[0], dpart);
+      dpart = __builtin_fmaf(x[1], y[1], dpart);
+    }
+  }
+  const int64_t qrow = (int64_t)s.oq + (int64_t)qi * p.tsq;
+  const int64_t srow = qrow * p.hq + h;
+  const float delta = sum_halves(dpart) * p.delta_scale;
+  const float lse2 = qvalid ? p.lse[srow] * kLog2e : __builtin_inff();
+  const float dlt = qvalid ? delta : 0.f;
+  // for the dK/dV kernel (launched next): -Delta and LSE*log2(e) per (row,
+  // head), written by the odd wave of the pair that owns the row
+  if (qvalid && hh == 0 && half) {
+    p.delta[srow] = -delta;
+    p.lse2[srow] = lse2;
+  }
+  wait_vm<0>();
+
+  f32x16 acc[NCBH];
+#pragma unroll
+  for (int cb = 0; cb < NCBH; ++cb) acc[cb] = zero16();
+  const int cb0 = half * NCBH;
+
+  for (int step = 0; step < nsteps; ++step) {
+    wait_vm<0>();
+    barrier_lds_dma();
+    if (step + 1 < nsteps) issue(step + 1);
+    const uint32_t tk = lds_addr(sK[0]) + (uint32_t)(step & 1) * (uint32_t)sizeof(sK[0]);
+    const uint32_t tv = lds_addr(sV[0]) + (uint32_t)(step & 1) * (uint32_t)sizeof(sV[0]);
+    const int n0 = step * KS;
+    // both waves of a query block are active or idle together
+    const bool active = wq_lo < s.lq && !(CAUSAL && n0 > wq_hi_k);
+    if (active) {
+      // S^T (even wave) or dP^T onto -Delta (odd wave; without dropout, which
+      // scales dP alone), each K / V operand read two MFMAs ahead
+      constexpr int PD = 2;
+      const RowReader<LK> rd(half ? tv : tk, lane);
+      f32x16 t16 = zero16();
+      if (half && !DROP) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t16[r] = -dlt;
+      }
+      u32x4 a[NT];
+#pragma unroll
+      for (int t = 0; t < PD; ++t) a[t] = rd.read(0, t);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        t16 = Mfma<DT>::mma(a[t], opreg[t], t16);
+        if (t + PD < NT) a[t + PD] = rd.read(0, t + PD);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        sX[wave][q4][lane] = (f32x4){t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2], t16[4 * q4 + 3]};
+    }
+    // the tiles are in LDS for the partner (the ring's DMA may still run)
+    barrier_lds_writes();
+    if (active) {
+      f32x16 sc, dp;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 x = sX[2 * qblk][q4][lane], y = sX[2 * qblk + 1][q4][lane];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          sc[4 * q4 + c] = x[c];
+          dp[4 * q4 + c] = y[c];
+        }
+      }
+      if constexpr (DROP) {
+        // dP = D o (dO V^T): dropped elements 0, kept ones scaled
+        dropout_row16(p, w.b, h, qi >> 2, (n0 + 4 * hh) >> 2, li & 3, p.drop_scale, dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = fast_exp2(__builtin_fmaf(sc[r], sl2e, -lse2));
+      // the causal mask only on steps that touch the diagonal (a wave-uniform
+      // branch): key n0 + j is hidden from this lane's query while j > qk
+      if (CAUSAL && n0 + KS - 1 > wq_lo_k) {
+        const int qk = qi_k - n0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + 4 * hh + (r & 3) > qk) sc[r] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = DROP ? sc[r] * (dp[r] - dlt) : sc[r] * dp[r];     // dS
+      const u32x4 b0 = pack_operand<DT>(sc, 0), b1 = pack_operand<DT>(sc, 1);
+      const TrReader<LK> trk(tk, lane);
+#pragma unroll
+      for (int cb = 0; cb < NCBH; ++cb)
+        acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 0), b0, acc[cb]);
+#pragma unroll
+      for (int cb = 0; cb < NCBH; ++cb)
+        acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 1), b1, acc[cb]);
+    }
+  }
+
+  if (qvalid) {
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d;
+    const float sc0 = p.scale;
+#pragma unroll
+    for (int cb = 0; cb < NCBH; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c0 = 32 * (cb0 + cb) + 8 * q4 + 4 * hh;
         if (c0 < p.d) {
           float x[4];
 #pragma unroll
@@ -820,6 +1020,20 @@ static void launch_dq_c(const AttnParams& p, int grid, hipStream_t st) {
   else hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, false, false>), g, blk, 0, st, p);
 }
 
+template <int DT, bool CAUSAL>
+static void launch_dq_split_c(const AttnParams& p, int grid, hipStream_t st) {
+  const dim3 g(grid), blk(512);
+  if (p.accumulate & kAccDq) hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, true, false>), g, blk, 0, st, p);
+  else if (p.drop_t) hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, false, true>), g, blk, 0, st, p);
+  else hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, false, false>), g, blk, 0, st, p);
+}
+
+template <int DT>
+static void launch_dq_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
+  if (causal) launch_dq_split_c<DT, true>(p, grid, st);
+  else launch_dq_split_c<DT, false>(p, grid, st);
+}
+
 template <int DT, int DPAD>
 static void launch_dq_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
   if (causal) launch_dq_c<DT, DPAD, true>(p, grid, st);
@@ -831,7 +1045,7 @@ static void launch_dq_dt(const AttnParams& p, bool causal, int grid, hipStream_t
   if (p.d <= 32) launch_dq_d<DT, 32>(p, causal, grid, st);
   else if (p.d <= 64) launch_dq_d<DT, 64>(p, causal, grid, st);
   else if (p.d <= 128) launch_dq_d<DT, 128>(p, causal, grid, st);
-  else launch_dq_d<DT, 256>(p, causal, grid, st);
+  else launch_dq_split<DT>(p, causal, grid, st);
 }
 
 hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st) {

@@ -28,17 +28,18 @@ namespace attn {
 // same softmax, since the final normalisation uses the same reference.
 constexpr float kRescaleSlack = 8.0f;
 
-// Keys per step: 32 for head dims 64..128, so that the tiles (32 KB of LDS)
-// and registers (< 168) of three workgroups fit one CU; 64 otherwise.
+// Keys per step: 32 from head dim 64 on, so that the tiles and registers of
+// three workgroups fit one CU up to head dim 128 (32 KB of LDS, < 168
+// VGPRs) and of two at 256 (64 KB, < 256 VGPRs); 64 for head dims up to 32.
 template <int DPAD>
-constexpr int fwd_step_keys() { return (DPAD >= 64 && DPAD <= 128) ? 32 : 64; }
+constexpr int fwd_step_keys() { return DPAD >= 64 ? 32 : 64; }
 
 // DROP: dropout on the probabilities (the keep mask of dropout_block).
 // F8: q and k are E4M3 codes (p.q8, p.k8): Q stays in registers as codes, K
 // tiles hold DPAD code bytes per row, and S^T = K Q^T is taken on the 8-bit
 // 32 x 32 x 64 product, whose result tile has the layout of the 16-bit one.
 template <int DT, int DPAD, bool CAUSAL, bool DROP, bool F8 = false>
-__global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 1) void fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 2) void fwd_kernel(AttnParams p) {
   // E4M3 K rows of DPAD bytes hold whole 64-code chunks of the 8-bit product
   static_assert(!F8 || DPAD >= 64, "the 8-bit scores are built for head dims 48..256");
   constexpr int NT = F8 ? 1 : DPAD / 16;   // 16-wide k chunks over the head dim (16-bit Q)
