@@ -46,8 +46,8 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 2) void fwd_kernel(AttnParam
   constexpr int NT8 = DPAD / 64;           // 64-wide k chunks (E4M3 Q)
   constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
   // keys per step (the 8-bit K tiles are half the size: 64 keys still fit
-  // three workgroups per CU at head dims up to 128)
-  constexpr int KS = F8 ? 64 : fwd_step_keys<DPAD>();
+  // three workgroups per CU at head dims up to 128; 32 above, for two)
+  constexpr int KS = F8 ? (DPAD <= 128 ? 64 : 32) : fwd_step_keys<DPAD>();
   constexpr int NKB = KS / 32;         // 32-key blocks of S^T per step
   // K: row reads (E4M3: DPAD bytes per row, addressed in 16-bit units)
   using LK = std::conditional_t<F8, Swz<DPAD / 2>, Swz<DPAD>>;
