@@ -42,6 +42,61 @@ __device__ __forceinline__ void add_stored(float* x, u32x2 w) {
   x[3] += b[1];
 }
 
+// dQ of this lane's query over column blocks [cb0, cb0 + NB) of the head dim,
+// scaled and rounded once (ACC: added to what `out` holds); `out` is the
+// query's row of the head, lane half hh holds columns 4 hh .. +3 of each
+// 8-column group.
+template <int DT, bool ACC, int NB>
+__device__ __forceinline__ void store_dq(const AttnParams& p, uint16_t* out, int cb0, int hh,
+                                         const f32x16 (&acc)[NB]) {
+  const float sc0 = p.scale;
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int c0 = 32 * (cb0 + cb) + 8 * q4 + 4 * hh;
+      if (c0 < p.d) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[cb][4 * q4 + e] * sc0;
+        if constexpr (ACC) add_stored<DT>(x, *reinterpret_cast<const u32x2*>(out + c0));
+        u32x2 val = {Mfma<DT>::pack2(x[0], x[1]), Mfma<DT>::pack2(x[2], x[3])};
+        *reinterpret_cast<u32x2*>(out + c0) = val;
+      }
+    }
+}
+
+// dK (scaled) and dV of this lane's key over column blocks [cb0, cb0 + NB),
+// rounded once (ACC: added to what the rows hold); dkb / dvb are the key's
+// rows of the KV head.
+template <int DT, bool ACC, int NB>
+__device__ __forceinline__ void store_dkdv(const AttnParams& p, uint16_t* dkb, uint16_t* dvb, int cb0, int hh,
+                                           const f32x16 (&adk)[NB], const f32x16 (&adv)[NB]) {
+  const float sc0 = p.scale;
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int c0 = 32 * (cb0 + cb) + 8 * q4 + 4 * hh;
+      if (c0 < p.d) {
+        float xk[4], xv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xk[e] = adk[cb][4 * q4 + e] * sc0;
+          xv[e] = adv[cb][4 * q4 + e];
+        }
+        if constexpr (ACC) {
+          add_stored<DT>(xk, *reinterpret_cast<const u32x2*>(dkb + c0));
+          add_stored<DT>(xv, *reinterpret_cast<const u32x2*>(dvb + c0));
+        }
+        u32x2 vk = {Mfma<DT>::pack2(xk[0], xk[1]), Mfma<DT>::pack2(xk[2], xk[3])};
+        u32x2 vv = {Mfma<DT>::pack2(xv[0], xv[1]), Mfma<DT>::pack2(xv[2], xv[3])};
+        *reinterpret_cast<u32x2*>(dkb + c0) = vk;
+        *reinterpret_cast<u32x2*>(dvb + c0) = vv;
+      }
+    }
+}
+
 // ----------------------------------------------------------------- dQ
 // ACC: add into dq (the chunked, accumulating backward) instead of writing it;
 // DROP: dropout on the probabilities (the keep mask of dropout_block)
@@ -231,24 +286,8 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     }
   }
 
-  if (qvalid) {
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d;
-    const float sc0 = p.scale;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c0 = 32 * cb + 8 * q4 + 4 * hh;
-        if (c0 < p.d) {
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = acc[cb][4 * q4 + e] * sc0;
-          if constexpr (ACC) add_stored<DT>(x, *reinterpret_cast<const u32x2*>(out + c0));
-          u32x2 val = {Mfma<DT>::pack2(x[0], x[1]), Mfma<DT>::pack2(x[2], x[3])};
-          *reinterpret_cast<u32x2*>(out + c0) = val;
-        }
-      }
-  }
+  if (qvalid)
+    store_dq<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d, 0, hh, acc);
 }
 
 // ----------------------------------------------------------------- dQ, head dims 136..256
@@ -429,24 +468,8 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
     }
   }
 
-  if (qvalid) {
-    uint16_t* out = reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d;
-    const float sc0 = p.scale;
-#pragma unroll
-    for (int cb = 0; cb < NCBH; ++cb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c0 = 32 * (cb0 + cb) + 8 * q4 + 4 * hh;
-        if (c0 < p.d) {
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = acc[cb][4 * q4 + e] * sc0;
-          if constexpr (ACC) add_stored<DT>(x, *reinterpret_cast<const u32x2*>(out + c0));
-          u32x2 val = {Mfma<DT>::pack2(x[0], x[1]), Mfma<DT>::pack2(x[2], x[3])};
-          *reinterpret_cast<u32x2*>(out + c0) = val;
-        }
-      }
-  }
+  if (qvalid)
+    store_dq<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d, cb0, hh, acc);
 }
 
 // ----------------------------------------------------------------- dK / dV
@@ -710,31 +733,8 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
 
   if (kj < s.lk) {
     const int64_t row = (int64_t)kj * kvts;
-    uint16_t* dkb = reinterpret_cast<uint16_t*>(p.dk) + kvoff + row;
-    uint16_t* dvb = reinterpret_cast<uint16_t*>(p.dv) + kvoff + row;
-    const float sc0 = p.scale;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c0 = 32 * cb + 8 * q4 + 4 * hh;
-        if (c0 < p.d) {
-          float xk[4], xv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xk[e] = adk[cb][4 * q4 + e] * sc0;
-            xv[e] = adv[cb][4 * q4 + e];
-          }
-          if constexpr (ACC) {
-            add_stored<DT>(xk, *reinterpret_cast<const u32x2*>(dkb + c0));
-            add_stored<DT>(xv, *reinterpret_cast<const u32x2*>(dvb + c0));
-          }
-          u32x2 vk = {Mfma<DT>::pack2(xk[0], xk[1]), Mfma<DT>::pack2(xk[2], xk[3])};
-          u32x2 vv = {Mfma<DT>::pack2(xv[0], xv[1]), Mfma<DT>::pack2(xv[2], xv[3])};
-          *reinterpret_cast<u32x2*>(dkb + c0) = vk;
-          *reinterpret_cast<u32x2*>(dvb + c0) = vv;
-        }
-      }
+    store_dkdv<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dk) + kvoff + row,
+                        reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, 0, hh, adk, adv);
   }
 }
 
@@ -982,31 +982,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
 
   if (kj < s.lk) {
     const int64_t row = (int64_t)kj * kvts;
-    uint16_t* dkb = reinterpret_cast<uint16_t*>(p.dk) + kvoff + row;
-    uint16_t* dvb = reinterpret_cast<uint16_t*>(p.dv) + kvoff + row;
-    const float sc0 = p.scale;
-#pragma unroll
-    for (int cb = 0; cb < NCBH; ++cb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c0 = 32 * (half * NCBH + cb) + 8 * q4 + 4 * hh;
-        if (c0 < p.d) {
-          float xk[4], xv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xk[e] = adk[cb][4 * q4 + e] * sc0;
-            xv[e] = adv[cb][4 * q4 + e];
-          }
-          if constexpr (ACC) {
-            add_stored<DT>(xk, *reinterpret_cast<const u32x2*>(dkb + c0));
-            add_stored<DT>(xv, *reinterpret_cast<const u32x2*>(dvb + c0));
-          }
-          u32x2 vk = {Mfma<DT>::pack2(xk[0], xk[1]), Mfma<DT>::pack2(xk[2], xk[3])};
-          u32x2 vv = {Mfma<DT>::pack2(xv[0], xv[1]), Mfma<DT>::pack2(xv[2], xv[3])};
-          *reinterpret_cast<u32x2*>(dkb + c0) = vk;
-          *reinterpret_cast<u32x2*>(dvb + c0) = vv;
-        }
-      }
+    store_dkdv<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dk) + kvoff + row,
+                        reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, half * NCBH, hh, adk, adv);
   }
 }
 
