@@ -18,6 +18,7 @@ hipError_t launch_zero_fill(const ZeroParams& p, hipStream_t st);
 hipError_t launch_fwd(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st);
 hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st);
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st);
+hipError_t launch_dkdv_reduce(const AttnParams& p, int dtype, int max_kv_tiles, hipStream_t st);
 hipError_t launch_merge(void* out, float* lse, const void* out_part, const float* lse_part,
                         int64_t rows, int d, int dtype, hipStream_t st);
 hipError_t launch_decode_e4m3(const void* src, void* dst, int64_t n, int dtype, hipStream_t st);
@@ -36,15 +37,32 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t hdr, seq, q_list, kv_list, delta, lse2, total;
+  size_t hdr, seq, q_list, kv_list, delta, lse2, part, total;
   int64_t q_cap, kv_cap;   // list capacities for the smallest tile
+  int32_t split;           // dK/dV workgroups per (key tile, KV head); > 1: partial planes at `part`
 };
 
 bool sizes_ok(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv, int32_t d) {
   return batch >= 0 && total_q >= 0 && total_kv >= 0 && hq >= 1 && hkv >= 1 && d >= 1;
 }
 
-Layout layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq) {
+// Workgroups that share a GQA group's query heads per (key tile, KV head) in
+// dK/dV: 1, unless the group holds at least 8 query heads and the key tiles
+// alone give fewer than 4096 workgroups (with few KV heads one workgroup
+// would walk every query head of its group, and the longest one would set the
+// kernel's time); then doubled while it divides the group, up to 4096.
+int32_t dkdv_heads_split(int32_t batch, int32_t total_kv, int32_t hq, int32_t hkv) {
+  const int32_t group = hq / hkv;
+  if (group < 8) return 1;
+  const int64_t wgs = (((int64_t)total_kv + kKVTile - 1) / kKVTile + batch) * hkv;
+  int32_t split = 1;
+  while (group % (2 * split) == 0 && wgs * split < 4096) split *= 2;
+  return split;
+}
+
+// allow_split = false: no partial planes (the caller runs an unsplit dK/dV)
+Layout layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv, int32_t d,
+              bool allow_split) {
   Layout L;
   L.q_cap = ((int64_t)total_q + kMinTile - 1) / kMinTile + batch;
   L.kv_cap = ((int64_t)total_kv + kMinTile - 1) / kMinTile + batch;
@@ -61,6 +79,9 @@ Layout layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq) {
   off += round_up((size_t)total_q * (size_t)hq * sizeof(float));
   L.lse2 = off;
   off += round_up((size_t)total_q * (size_t)hq * sizeof(float));
+  L.split = allow_split ? dkdv_heads_split(batch, total_kv, hq, hkv) : 1;
+  L.part = off;
+  if (L.split > 1) off += round_up(2 * (size_t)L.split * (size_t)total_kv * (size_t)hkv * (size_t)d * sizeof(float));
   L.total = off;
   return L;
 }
@@ -90,6 +111,7 @@ struct CallOpts {
   float delta_scale = 1.f;    // backward: Delta is used times this
   const void* q8 = nullptr;   // E4M3 q and k for the forward's 8-bit scores
   const void* k8 = nullptr;
+  bool no_split = false;      // backward: never split a GQA group over dK/dV workgroups
   int32_t tsq(int32_t batch) const { return layout == kLayoutSbhd ? batch : 1; }
 };
 constexpr CallOpts kThd = {};
@@ -124,7 +146,7 @@ attn_thd_status check_common(const void* q, const void* k, const void* v,
   const int64_t kv_tiles = ((int64_t)total_kv + dkdv_tile(d) - 1) / dkdv_tile(d) + batch;
   if (q_tiles * hq > INT32_MAX || kv_tiles * hkv > INT32_MAX) return ATTN_THD_EINVAL;
   if ((int64_t)total_q * hq > INT32_MAX || (int64_t)total_kv + 256 > INT32_MAX) return ATTN_THD_EINVAL;
-  c.L = layout(batch, total_q, total_kv, hq);
+  c.L = layout(batch, total_q, total_kv, hq, hkv, d, !geo.no_split);
   if (!workspace || workspace_bytes < c.L.total) return ATTN_THD_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return ATTN_THD_EWORKSPACE;
   c.ws = static_cast<char*>(workspace);
@@ -187,6 +209,8 @@ AttnParams attn_params(const Common& c, int32_t hq, int32_t hkv, int32_t d, floa
   a.delta_scale = geo.delta_scale;
   a.q8 = geo.q8;
   a.k8 = geo.k8;
+  a.kv_split = 1;
+  a.kv_heads = a.group;
   return a;
 }
 
@@ -322,7 +346,15 @@ attn_thd_status bwd_impl(const void* q, const void* k, const void* v, const void
   a.list = reinterpret_cast<const int2*>(c.ws + c.L.kv_list);
   if (geo.dk_scale != 0.f) a.scale = geo.dk_scale;
   ATTN_TRY(m.mark(2));
+  if (c.L.split > 1) {
+    // the group's query heads over c.L.split workgroups, then their sum
+    a.kv_split = c.L.split;
+    a.kv_heads = a.group / c.L.split;
+    a.part = reinterpret_cast<float*>(c.ws + c.L.part);
+    a.part_plane = (int64_t)total_kv * hkv * d;
+  }
   ATTN_TRY(launch_dkdv(a, dtype, causal, (int)c.kv_tiles_max, s));
+  if (c.L.split > 1) ATTN_TRY(launch_dkdv_reduce(a, dtype, (int)c.kv_tiles_max, s));
   ATTN_TRY(m.mark(3));
   // an accumulated output keeps every row the call does not reach
   if (!(geo.accumulate & kAccDq))
@@ -341,7 +373,7 @@ extern "C" {
 size_t attn_thd_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq,
                                int32_t hkv, int32_t d) {
   if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return 0;
-  return layout(batch, total_q, total_kv, hq).total;
+  return layout(batch, total_q, total_kv, hq, hkv, d, true).total;
 }
 
 attn_thd_status attn_fwd_thd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -569,7 +601,7 @@ struct Fp8Layout {
 static Fp8Layout fp8_layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq,
                             int32_t hkv, int32_t d) {
   Fp8Layout f;
-  f.base = layout(batch, total_q, total_kv, hq).total;
+  f.base = layout(batch, total_q, total_kv, hq, hkv, d, true).total;
   f.q = f.base;
   f.k = f.q + round_up((size_t)total_q * hq * d * 2);
   f.v = f.k + round_up((size_t)total_kv * hkv * d * 2);
@@ -814,14 +846,17 @@ attn_thd_status attn_bwd_thd_noalloc(const void* q, const void* k, const void* v
   (void)max_seqlen_q;
   (void)max_seqlen_kv;
   if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return ATTN_THD_EINVAL;
-  if (layout(batch, total_q, total_kv, hq).total > ATTN_THD_NOALLOC_SCRATCH_BYTES) return ATTN_THD_ESCRATCH;
+  // the unsplit dK/dV: the scratch holds no partial planes
+  if (layout(batch, total_q, total_kv, hq, hkv, d, false).total > ATTN_THD_NOALLOC_SCRATCH_BYTES)
+    return ATTN_THD_ESCRATCH;
   void* ws = nullptr;
   const attn_thd_status st = scratch_for(stream, &ws);
   if (st != ATTN_THD_OK) return st;
+  CallOpts o = kThd;
+  o.no_split = true;
   return bwd_impl(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv,
                   cu_seqlens_q_padded, cu_seqlens_kv_padded, batch, total_q, total_kv, hq, hkv, d,
-                  scale, mask_type, dtype, ws, ATTN_THD_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0,
-                  kThd);
+                  scale, mask_type, dtype, ws, ATTN_THD_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0, o);
 }
 
 const char* attn_thd_status_string(int32_t status) {

@@ -97,6 +97,25 @@ __device__ __forceinline__ void store_dkdv(const AttnParams& p, uint16_t* dkb, u
     }
 }
 
+// This workgroup's fp32 dK and dV of this lane's key (unscaled) over column
+// blocks [cb0, cb0 + NB), into its partial planes (split GQA group).
+template <int NB>
+__device__ __forceinline__ void store_dkdv_part(const AttnParams& p, float* dkp, float* dvp, int cb0, int hh,
+                                                const f32x16 (&adk)[NB], const f32x16 (&adv)[NB]) {
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int c0 = 32 * (cb0 + cb) + 8 * q4 + 4 * hh;
+      if (c0 < p.d) {
+        *reinterpret_cast<f32x4*>(dkp + c0) =
+            (f32x4){adk[cb][4 * q4], adk[cb][4 * q4 + 1], adk[cb][4 * q4 + 2], adk[cb][4 * q4 + 3]};
+        *reinterpret_cast<f32x4*>(dvp + c0) =
+            (f32x4){adv[cb][4 * q4], adv[cb][4 * q4 + 1], adv[cb][4 * q4 + 2], adv[cb][4 * q4 + 3]};
+      }
+    }
+}
+
 // ----------------------------------------------------------------- dQ
 // ACC: add into dq (the chunked, accumulating backward) instead of writing it;
 // DROP: dropout on the probabilities (the keep mask of dropout_block)
@@ -485,12 +504,14 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
 // of their MFMAs (scheduling barriers), since at 256 VGPRs the scheduler
 // otherwise waits on each read just before its MFMA.
 // ACC: add into dk / dv instead of writing them; DROP: dropout on the
-// probabilities (the keep mask of dropout_block); OCC: workgroups per CU the
-// register budget is sized for.
-template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, int OCC>
+// probabilities (the keep mask of dropout_block); PART: this workgroup takes
+// kv_heads of the group's query heads and writes fp32 partial dK / dV planes
+// (split GQA group); OCC: workgroups per CU the register budget is sized for.
+template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, bool PART, int OCC>
 __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
   constexpr int NW = 4, BM = 32, NBUF = 2;
   constexpr int BN = 32 * NW;
+  static_assert(BN == kKVTile, "the work lists are built for kKVTile keys per item");
   constexpr int NU = BM / 16;          // 16-query chunks per step
   constexpr int NT = DPAD / 16;
   constexpr int NCB = DPAD / 32;
@@ -505,9 +526,13 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sSink[Dma::SINK ? 512 : 8];
   __shared__ __attribute__((aligned(16))) float sDummy[64];
   const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
-  int item, g;
-  xcd_split(blockIdx.x, p.hkv, item, g);
+  int item, vh;
+  xcd_split(blockIdx.x, PART ? p.hkv * p.kv_split : p.hkv, item, vh);
   if (item >= ntiles) return;
+  // KV head g; with a split group, this workgroup's share of its query heads
+  const int g = PART ? vh / p.kv_split : vh;
+  const int sub = PART ? vh - g * p.kv_split : 0;
+  const int ng = PART ? p.kv_heads : p.group;
   const WorkItem w = load_item(p.list, p.seq, item);
   const SeqInfo s = w.s;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -535,8 +560,8 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
   const int wk_lo_q = wk_lo - diag, wk_hi_q = wk_hi - diag, kj_q = kj - diag;
   const int m_last = (s.lq + BM - 1) / BM;
   const int nm = m_last > m_first ? m_last - m_first : 0;
-  const int nsteps = nm * p.group;
-  const int h0 = g * p.group;
+  const int nsteps = nm * ng;
+  const int h0 = g * p.group + sub * ng;
   // Steps walk the query tiles from the last one down, the group's heads
   // inside: key tiles of a sequence that start together then read the same
   // Q / dO tiles at the same time (from L2).  Two cursors follow that order
@@ -563,8 +588,8 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
   int64_t dc_v = row_last * p.hq + h0;
   int dc_hg = 0, dc_nrow = s.lq - (m_last - 1) * BM;
   // from the last head of a tile to the first head of the tile before it
-  const int64_t q_back = (int64_t)BM * qts + (int64_t)(p.group - 1) * p.d;
-  const int64_t v_back = (int64_t)BM * p.tsq * p.hq + (p.group - 1);
+  const int64_t q_back = (int64_t)BM * qts + (int64_t)(ng - 1) * p.d;
+  const int64_t v_back = (int64_t)BM * p.tsq * p.hq + (ng - 1);
   auto issue = [&](int step) {
     const uint32_t buf = (uint32_t)(step % NBUF);
     const int nr = dc_nrow > BM ? BM : dc_nrow;
@@ -573,7 +598,7 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
     dma_q.issue_rsrc(make_rsrc(dog + dc_q, (uint32_t)nr * q_rs_bytes), lds_do + buf * (uint32_t)sizeof(sdO[0]),
                      lds_sink, wave);
     dma<4>(make_rsrc(vg + dc_v, wave < 2 ? (uint32_t)nr * vec_rs_bytes : 0u), lds_vec + buf * vec_buf, vec_voff);
-    if (++dc_hg == p.group) {
+    if (++dc_hg == ng) {
       dc_hg = 0;
       dc_q -= q_back;
       dc_v -= v_back;
@@ -623,7 +648,7 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
     const float* tvec = sVec[buf];
     const int i0 = cm * BM;
     const int h_step = h0 + chg;   // query head of this step
-    if (++chg == p.group) {
+    if (++chg == ng) {
       chg = 0;
       --cm;
     }
@@ -733,8 +758,13 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
 
   if (kj < s.lk) {
     const int64_t row = (int64_t)kj * kvts;
-    store_dkdv<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dk) + kvoff + row,
-                        reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, 0, hh, adk, adv);
+    if constexpr (PART) {
+      float* dkp = p.part + (int64_t)sub * p.part_plane + kvoff + row;
+      store_dkdv_part(p, dkp, dkp + (int64_t)p.kv_split * p.part_plane, 0, hh, adk, adv);
+    } else {
+      store_dkdv<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dk) + kvoff + row,
+                          reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, 0, hh, adk, adv);
+    }
   }
 }
 
@@ -749,12 +779,13 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
 // through LDS, so the two waves read the same S and dP and form the same P
 // and dS; then each forms dV += P^T dO and dK += dS^T Q over its own four
 // column blocks.  Two barriers per step: the ring's, and the one after the
-// tiles are written.  Steps, DMA ring, cursors, masks and dropout are those
-// of dkdv_kernel with NW = 8, BM = 32, NBUF = 2.
-template <int DT, bool CAUSAL, bool ACC, bool DROP>
+// tiles are written.  Steps, DMA ring, cursors, masks, dropout and the
+// split GQA group (PART) are those of dkdv_kernel with NW = 8, BM = 32, NBUF = 2.
+template <int DT, bool CAUSAL, bool ACC, bool DROP, bool PART>
 __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   constexpr int DPAD = 256, NW = 8, BM = 32, NBUF = 2;
   constexpr int BN = 16 * NW;          // keys per workgroup: NW / 2 blocks of 32
+  static_assert(BN == kKVTile, "the work lists are built for kKVTile keys per item");
   constexpr int NT = DPAD / 16;        // 16-wide k chunks of the whole head dim
   constexpr int NCBH = DPAD / 64;      // 32-column blocks of one half
   constexpr int NU = BM / 16;          // 16-query chunks per step
@@ -772,9 +803,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) f32x4 sX[NW][4][64];
 
   const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
-  int item, g;
-  xcd_split(blockIdx.x, p.hkv, item, g);
+  int item, vh;
+  xcd_split(blockIdx.x, PART ? p.hkv * p.kv_split : p.hkv, item, vh);
   if (item >= ntiles) return;
+  // KV head g; with a split group, this workgroup's share of its query heads
+  const int g = PART ? vh / p.kv_split : vh;
+  const int sub = PART ? vh - g * p.kv_split : 0;
+  const int ng = PART ? p.kv_heads : p.group;
   const WorkItem w = load_item(p.list, p.seq, item);
   const SeqInfo s = w.s;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -796,8 +831,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   const int wk_lo_q = wk_lo - diag, wk_hi_q = wk_hi - diag, kj_q = kj - diag;
   const int m_last = (s.lq + BM - 1) / BM;
   const int nm = m_last > m_first ? m_last - m_first : 0;
-  const int nsteps = nm * p.group;
-  const int h0 = g * p.group;
+  const int nsteps = nm * ng;
+  const int h0 = g * p.group + sub * ng;
 
   Dma dma_q;
   dma_q.init(wave, lane, p.d, q_rs_bytes);
@@ -813,8 +848,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   int64_t dc_q = row_last * qrs + (int64_t)h0 * p.d;
   int64_t dc_v = row_last * p.hq + h0;
   int dc_hg = 0, dc_nrow = s.lq - (m_last - 1) * BM;
-  const int64_t q_back = (int64_t)BM * qts + (int64_t)(p.group - 1) * p.d;
-  const int64_t v_back = (int64_t)BM * p.tsq * p.hq + (p.group - 1);
+  const int64_t q_back = (int64_t)BM * qts + (int64_t)(ng - 1) * p.d;
+  const int64_t v_back = (int64_t)BM * p.tsq * p.hq + (ng - 1);
   auto issue = [&](int step) {
     const uint32_t buf = (uint32_t)(step % NBUF);
     const int nr = dc_nrow > BM ? BM : dc_nrow;
@@ -823,7 +858,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
     dma_q.issue_rsrc(make_rsrc(dog + dc_q, (uint32_t)nr * q_rs_bytes), lds_do + buf * (uint32_t)sizeof(sdO[0]),
                      lds_sink, wave);
     dma<4>(make_rsrc(vg + dc_v, wave < 2 ? (uint32_t)nr * vec_rs_bytes : 0u), lds_vec + buf * vec_buf, vec_voff);
-    if (++dc_hg == p.group) {
+    if (++dc_hg == ng) {
       dc_hg = 0;
       dc_q -= q_back;
       dc_v -= v_back;
@@ -865,7 +900,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
     const float* tvec = sVec[buf];
     const int i0 = cm * BM;
     const int h_step = h0 + chg;
-    if (++chg == p.group) {
+    if (++chg == ng) {
       chg = 0;
       --cm;
     }
@@ -982,8 +1017,64 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
 
   if (kj < s.lk) {
     const int64_t row = (int64_t)kj * kvts;
-    store_dkdv<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dk) + kvoff + row,
-                        reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, half * NCBH, hh, adk, adv);
+    if constexpr (PART) {
+      float* dkp = p.part + (int64_t)sub * p.part_plane + kvoff + row;
+      store_dkdv_part(p, dkp, dkp + (int64_t)p.kv_split * p.part_plane, half * NCBH, hh, adk, adv);
+    } else {
+      store_dkdv<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dk) + kvoff + row,
+                          reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, half * NCBH, hh, adk, adv);
+    }
+  }
+}
+
+// ----------------------------------------------------------------- split GQA group: the sum
+// Sums the kv_split partial dK and dV planes of every key row of a work item
+// in plane order (fixed, so the result is bitwise repeatable), scales dK,
+// rounds once and writes dk / dv (ACC: adds into them).  One workgroup per
+// (key tile, KV head) of the dK/dV work list; rows past the real length are
+// left to the zero fill, as in the dK/dV kernels.
+template <int DT, bool ACC>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnParams p) {
+  const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
+  const int item = blockIdx.x / p.hkv, g = blockIdx.x - item * p.hkv;
+  if (item >= ntiles) return;
+  const WorkItem w = load_item(p.list, p.seq, item);
+  const SeqInfo s = w.s;
+  const int64_t kvrs = (int64_t)p.hkv * p.d, kvts = kvrs * p.tskv;
+  const int64_t kvoff = (int64_t)s.ok * kvrs + (int64_t)g * p.d;
+  const int n0 = w.tile * kKVTile;
+  const int rows = min(kKVTile, s.lk - n0);
+  const int chunks = p.d >> 2;   // 4-column pieces per row
+  const int64_t plane = p.part_plane;
+  const float* dvp = p.part + (int64_t)p.kv_split * plane;
+  for (int i = threadIdx.x; i < rows * chunks; i += 256) {
+    const int r = i / chunks, c = 4 * (i - r * chunks);
+    const int64_t off = kvoff + (int64_t)(n0 + r) * kvts + c;
+    f32x4 sk = *reinterpret_cast<const f32x4*>(p.part + off);
+    f32x4 sv = *reinterpret_cast<const f32x4*>(dvp + off);
+    for (int j = 1; j < p.kv_split; ++j) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(p.part + j * plane + off);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(dvp + j * plane + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sk[e] += a[e];
+        sv[e] += b[e];
+      }
+    }
+    float xk[4], xv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xk[e] = sk[e] * p.scale;
+      xv[e] = sv[e];
+    }
+    uint16_t* dkb = reinterpret_cast<uint16_t*>(p.dk) + off;
+    uint16_t* dvb = reinterpret_cast<uint16_t*>(p.dv) + off;
+    if constexpr (ACC) {
+      add_stored<DT>(xk, *reinterpret_cast<const u32x2*>(dkb));
+      add_stored<DT>(xv, *reinterpret_cast<const u32x2*>(dvb));
+    }
+    *reinterpret_cast<u32x2*>(dkb) = (u32x2){Mfma<DT>::pack2(xk[0], xk[1]), Mfma<DT>::pack2(xk[2], xk[3])};
+    *reinterpret_cast<u32x2*>(dvb) = (u32x2){Mfma<DT>::pack2(xv[0], xv[1]), Mfma<DT>::pack2(xv[2], xv[3])};
   }
 }
 
@@ -1034,14 +1125,32 @@ hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tile
 }
 
 // keys per dK/dV work item for a head dim
-int dkdv_tile(int d) { (void)d; return 128; }
+int dkdv_tile(int d) { (void)d; return kKVTile; }
+
+hipError_t launch_dkdv_reduce(const AttnParams& p, int dtype, int max_kv_tiles, hipStream_t st) {
+  const int grid = max_kv_tiles * p.hkv;
+  if (grid <= 0) return hipSuccess;
+  const bool acc = p.accumulate & kAccDkDv;
+  if (dtype == kBF16) {
+    if (acc) hipLaunchKernelGGL((dkdv_reduce_kernel<kBF16, true>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((dkdv_reduce_kernel<kBF16, false>), dim3(grid), dim3(256), 0, st, p);
+  } else {
+    if (acc) hipLaunchKernelGGL((dkdv_reduce_kernel<kFP16, true>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((dkdv_reduce_kernel<kFP16, false>), dim3(grid), dim3(256), 0, st, p);
+  }
+  return hipGetLastError();
+}
 
 template <int DT, bool CAUSAL>
 static void launch_dkdv_split_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(512);
-  if (p.accumulate & kAccDkDv) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, true, false>), g, blk, 0, st, p);
-  else if (p.drop_t) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, true>), g, blk, 0, st, p);
-  else hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, false>), g, blk, 0, st, p);
+  if (p.kv_split > 1) {
+    if (p.drop_t) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, true, true>), g, blk, 0, st, p);
+    else hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, false, true>), g, blk, 0, st, p);
+  } else if (p.accumulate & kAccDkDv)
+    hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, true, false, false>), g, blk, 0, st, p);
+  else if (p.drop_t) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, true, false>), g, blk, 0, st, p);
+  else hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, false, false>), g, blk, 0, st, p);
 }
 
 template <int DT>
@@ -1050,15 +1159,22 @@ static void launch_dkdv_split(const AttnParams& p, bool causal, int grid, hipStr
   else launch_dkdv_split_c<DT, false>(p, grid, st);
 }
 
+// a split group writes partial planes; dropout and accumulation then act in
+// the kernel and in the sum respectively
 template <int DT, int DPAD, bool CAUSAL, int OCC>
 static void launch_dkdv_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(256);
-  if (p.accumulate & kAccDkDv)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, true, false, OCC>), g, blk, 0, st, p);
+  if (p.kv_split > 1) {
+    if (p.drop_t)
+      hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, true, OCC>), g, blk, 0, st, p);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, true, OCC>), g, blk, 0, st, p);
+  } else if (p.accumulate & kAccDkDv)
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, true, false, false, OCC>), g, blk, 0, st, p);
   else if (p.drop_t)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, OCC>), g, blk, 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, false, OCC>), g, blk, 0, st, p);
   else
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, OCC>), g, blk, 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, false, OCC>), g, blk, 0, st, p);
 }
 
 template <int DT, int DPAD, int OCC>
@@ -1077,7 +1193,7 @@ static void launch_dkdv_dt(const AttnParams& p, bool causal, int grid, hipStream
 }
 
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st) {
-  const int grid = max_kv_tiles * p.hkv;
+  const int grid = max_kv_tiles * p.hkv * p.kv_split;
   if (grid <= 0) return hipSuccess;
   if (dtype == kBF16) launch_dkdv_dt<kBF16>(p, causal, grid, st);
   else launch_dkdv_dt<kFP16>(p, causal, grid, st);

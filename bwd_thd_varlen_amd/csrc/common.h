@@ -41,6 +41,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Tile geometry shared by host and device.
 constexpr int kQTile = 128;      // query rows per forward / dQ work item (4 waves x 32)
+constexpr int kKVTile = 128;     // key rows per dK/dV work item
 constexpr int kKVStep = 64;      // keys per inner step of the forward / dQ kernels
 constexpr int kMinTile = 64;     // smallest tile any list uses (sizes the lists)
 constexpr int kSchedKeys = 2048; // distinct work keys of the heaviest-first ordering
@@ -600,6 +601,14 @@ struct AttnParams {
   float delta_scale;
   const void* q8;      // forward with E4M3 q and k (the scores on the 8-bit products)
   const void* k8;
+  // dK/dV with a split GQA group: the query heads of a KV head are spread
+  // over kv_split workgroups per key tile (kv_heads heads each), which write
+  // fp32 partial dK (planes 0 .. kv_split-1 of part) and dV (planes kv_split
+  // .. 2 kv_split-1), each plane part_plane floats laid out as dk; a second
+  // kernel sums them in plane order
+  int32_t kv_split, kv_heads;
+  float* part;
+  int64_t part_plane;
 };
 constexpr int32_t kAccDq = 1, kAccDkDv = 2;
 

@@ -100,7 +100,13 @@ enum {
 
 /*
  * Bytes of workspace attn_fwd_thd / attn_bwd_thd need for these sizes
- * (the same figure serves both).  Returns 0 on invalid sizes.
+ * (the same figure serves both).  Returns 0 on invalid sizes.  It holds the
+ * work lists, the per-sequence table and two fp32 [total_q, hq] vectors,
+ * and, when the backward spreads a GQA group's query heads over several
+ * dK/dV workgroups per key tile (groups of 8 or more query heads whose key
+ * tiles alone give fewer than 4096 workgroups), fp32 partial dK / dV planes
+ * of 2 x split x total_kv x hkv x d floats, split being a power of two that
+ * divides the group.
  */
 size_t attn_thd_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv,
                                int32_t hq, int32_t hkv, int32_t d);
@@ -148,14 +154,18 @@ attn_thd_status attn_bwd_thd(
  * The backward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  Same operation, arguments,
- * layouts, outputs and error codes as attn_bwd_thd, and the same kernels; the
- * scratch they need (the work lists, the per-sequence table and the per-row
- * Delta and LSE*log2(e) vectors) lives in a file-scope device array of
+ * layouts, outputs and error codes as attn_bwd_thd, and the same kernels,
+ * except that it never spreads a GQA group over several dK/dV workgroups
+ * (where attn_bwd_thd does, see attn_thd_workspace_size, its dK and dV are
+ * summed in another order and can differ from attn_bwd_thd's in the last
+ * bits; both are deterministic).  The scratch the kernels need (the work
+ * lists, the per-sequence table and the per-row Delta and LSE*log2(e)
+ * vectors) lives in a file-scope device array of
  * ATTN_THD_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
  * on until the process ends.  The call allocates nothing (no hipMalloc, no
  * allocating library routine); it looks up that GPU's copy of the array once
  * per device, on its first call there.
- *   - Problems whose workspace (attn_thd_workspace_size) exceeds
+ *   - Problems whose workspace without partial planes exceeds
  *     ATTN_THD_NOALLOC_SCRATCH_BYTES are rejected with ATTN_THD_ESCRATCH
  *     before anything is launched (the 65536-token, 64-head problem needs
  *     about 34 MB).
@@ -404,8 +414,9 @@ attn_thd_status attn_merge_thd(void* out, float* lse, const void* out_part, cons
  * last stage, so hipEventElapsedTime(events[i], events[i+1]) is stage i.
  *   forward  (n_events = 4): scheduler, forward kernel, zero fill
  *   backward (n_events = 6): scheduler, dQ kernel (which also forms
- *                            Delta = rowsum(dO o O)), dK/dV kernel,
- *                            zero fill (query rows), zero fill (key rows)
+ *                            Delta = rowsum(dO o O)), dK/dV kernel (and the
+ *                            sum of its partial planes for a spread GQA
+ *                            group), zero fill (query rows), zero fill (key rows)
  * A NULL `events` or another n_events returns ATTN_THD_EINVAL.  An entry
  * of `events` may be NULL: that boundary is not recorded (a caller timing one
  * stage passes only the two events around it, and adds no other records to

@@ -265,3 +265,21 @@ NOALLOC_ORDER = ["q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "cu_q", 
 FAKE_ARGS = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
                  cu_q=FAKE, cu_kv=FAKE, cu_qp=None, cu_kp=None, batch=1, total_q=16, total_kv=16,
                  max_q=0, max_kv=0, hq=1, hkv=1, d=64, scale=0.125, mask=0, dtype=0, stream=None)
+
+
+def test_split_group_workspace_rule(A):
+    """Groups of 8 or more query heads with few key tiles get fp32 partial
+    dK / dV planes (2 x split x total_kv x hkv x d) in the workspace: split
+    doubles while it divides the group and the dK/dV workgroups (key tiles of
+    128 plus one per sequence, times hkv) stay below 4096.  Read off the size's
+    growth with d, the only term that depends on it."""
+    def split(batch, t, hq, hkv, d=128):
+        grow = A.workspace_size(batch, t, t, hq, hkv, d) - A.workspace_size(batch, t, t, hq, hkv, d - 8)
+        return round(grow / (2 * t * hkv * 8 * 4))
+    assert split(16, 65536, 64, 1) == 8      # 528 workgroups -> 4224
+    assert split(16, 65536, 64, 2) == 4      # 1056 -> 4224
+    assert split(16, 65536, 64, 4) == 2      # 2112 -> 4224
+    assert split(16, 65536, 64, 8) == 0      # 4224 workgroups already: no partial planes
+    assert split(8, 16384, 64, 1) == 32      # 136 -> 4352, below the group of 64
+    assert split(4, 1000, 4, 1) == 0         # a group of 4: never split
+    assert split(4, 1000, 24, 1) == 8        # 24 = 8 x 3: doubling stops where 2 split no longer divides

@@ -117,12 +117,15 @@ def _run_chunked(L, qcuts, kcuts, hq, hkv, d, dtype, seed):
     return case, (out_w, lse_w, dq_w, dk_w, dv_w)
 
 
-@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "fp16"), (256, "bf16")])
-def test_chunked_causal_matches_whole(d, dtype):
+@pytest.mark.parametrize("d,dtype,hq,hkv", [(128, "bf16", 4, 2), (64, "fp16", 4, 2), (256, "bf16", 4, 2),
+                                            (128, "bf16", 8, 1), (256, "fp16", 16, 2)])
+def test_chunked_causal_matches_whole(d, dtype, hq, hkv):
+    """Groups of 8 and more query heads take the split dK/dV (partial planes
+    summed, then added into the accumulated dk / dv)."""
     L = [300, 77, 513, 1]
     qcuts = [[128, 200], [40], [100, 256, 400], []]
     kcuts = [[64, 150, 299], [5], [256], []]
-    case, res = _run_chunked(L, qcuts, kcuts, hq=4, hkv=2, d=d, dtype=dtype, seed=50 + d)
+    case, res = _run_chunked(L, qcuts, kcuts, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=50 + d + hq)
     o, l, dq, dk, dv = res
     ref_o, ref_l, *_ = oracle_run(case)
     rows = np.ones(case.q.shape[0], bool)

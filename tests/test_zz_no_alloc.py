@@ -66,3 +66,29 @@ def test_noalloc_equals_workspace_call_twice_second_smaller():
                                  ("dv", ref[2], got[2], krows)):
             assert torch.equal(r, g), f"{name}: not bitwise equal to attn_bwd_thd"
             assert_close(name, g, r.float().cpu().numpy(), "bf16", rows)
+
+
+def test_noalloc_split_group_within_bar():
+    """A group of 16 query heads on one KV head: attn_bwd_thd spreads the
+    group over several dK/dV workgroups and sums their fp32 partials, while
+    the no-allocation call (whose scratch holds no partial planes) keeps the
+    group in one workgroup.  dQ is bitwise equal; dK / dV agree to the
+    acceptance bar, and both sit within it of the oracle."""
+    import bwd_thd_varlen_amd as A
+    import oracle
+    from helpers import f64
+    A.lib()
+    case = _case([200, 129, 64], [200, 129, 64], [208, 136, 64], [208, 136, 64],
+                 hq=16, hkv=1, d=128, causal=True, seed=13)
+    ref, got = _both(A, case)
+    Tq, Tk = case.q.shape[0], case.k.shape[0]
+    qrows = real_rows(case.cu_seqlens_q, case.cu_seqlens_q_padded, Tq, case.cu_seqlens_kv)
+    krows = real_rows(case.cu_seqlens_kv, case.cu_seqlens_kv_padded, Tk, case.cu_seqlens_q)
+    assert torch.equal(ref[0], got[0])
+    args = (case.cu_seqlens_q, case.cu_seqlens_kv, case.cu_seqlens_q_padded, case.cu_seqlens_kv_padded)
+    rdq, rdk, rdv = oracle.attn_bwd(f64(case.q), f64(case.k), f64(case.v), f64(case.dout), *args,
+                                    scale=case.scale, causal=True)
+    for name, r, g, o, rows in (("dk", ref[1], got[1], rdk, krows), ("dv", ref[2], got[2], rdv, krows)):
+        assert_close(name + " (no-alloc vs split)", g, r.float().cpu().numpy(), "bf16", rows)
+        assert_close(name + " (no-alloc vs oracle)", g, o, "bf16", rows)
+        assert_close(name + " (split vs oracle)", r, o, "bf16", rows)
