@@ -391,11 +391,14 @@ def _cu(t, name, dev):
 
 
 def _workspace(ws, batch, tq, tk, hq, hkv, d, dev):
-    need = workspace_size(batch, tq, tk, hq, hkv, d)
+    """The caller's workspace, or a new one of workspace_size bytes.  A
+    caller's workspace below workspace_size is passed on as it is: the library
+    accepts any that holds the layout without partial dK/dV planes (the
+    backward then spreads a GQA group over fewer workgroups) and answers
+    ATTN_THD_EWORKSPACE below that."""
     if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    if ws.numel() * ws.element_size() < need:
-        raise AttnError(f"workspace of {ws.numel() * ws.element_size()} bytes < {need}")
+        ws = torch.empty(max(workspace_size(batch, tq, tk, hq, hkv, d), 256), dtype=torch.uint8,
+                         device=dev)
     return ws
 
 

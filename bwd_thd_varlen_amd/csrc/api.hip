@@ -60,9 +60,9 @@ int32_t dkdv_heads_split(int32_t batch, int32_t total_kv, int32_t hq, int32_t hk
   return split;
 }
 
-// allow_split = false: no partial planes (the caller runs an unsplit dK/dV)
+// split: dK/dV workgroups per (key tile, KV head), >= 1 (1: no partial planes)
 Layout layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv, int32_t d,
-              bool allow_split) {
+              int32_t split) {
   Layout L;
   L.q_cap = ((int64_t)total_q + kMinTile - 1) / kMinTile + batch;
   L.kv_cap = ((int64_t)total_kv + kMinTile - 1) / kMinTile + batch;
@@ -79,7 +79,7 @@ Layout layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq, int3
   off += round_up((size_t)total_q * (size_t)hq * sizeof(float));
   L.lse2 = off;
   off += round_up((size_t)total_q * (size_t)hq * sizeof(float));
-  L.split = allow_split ? dkdv_heads_split(batch, total_kv, hq, hkv) : 1;
+  L.split = split;
   L.part = off;
   if (L.split > 1) off += round_up(2 * (size_t)L.split * (size_t)total_kv * (size_t)hkv * (size_t)d * sizeof(float));
   L.total = off;
@@ -146,7 +146,13 @@ attn_thd_status check_common(const void* q, const void* k, const void* v,
   const int64_t kv_tiles = ((int64_t)total_kv + dkdv_tile(d) - 1) / dkdv_tile(d) + batch;
   if (q_tiles * hq > INT32_MAX || kv_tiles * hkv > INT32_MAX) return ATTN_THD_EINVAL;
   if ((int64_t)total_q * hq > INT32_MAX || (int64_t)total_kv + 256 > INT32_MAX) return ATTN_THD_EINVAL;
-  c.L = layout(batch, total_q, total_kv, hq, hkv, d, !geo.no_split);
+  // a workspace below attn_thd_workspace_size (one sized for a problem with
+  // more key tokens and so fewer partial planes, say) takes a smaller split,
+  // down to none
+  int32_t split = geo.no_split ? 1 : dkdv_heads_split(batch, total_kv, hq, hkv);
+  while (split > 1 && layout(batch, total_q, total_kv, hq, hkv, d, split).total > workspace_bytes)
+    split /= 2;
+  c.L = layout(batch, total_q, total_kv, hq, hkv, d, split);
   if (!workspace || workspace_bytes < c.L.total) return ATTN_THD_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return ATTN_THD_EWORKSPACE;
   c.ws = static_cast<char*>(workspace);
@@ -373,7 +379,7 @@ extern "C" {
 size_t attn_thd_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq,
                                int32_t hkv, int32_t d) {
   if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return 0;
-  return layout(batch, total_q, total_kv, hq, hkv, d, true).total;
+  return layout(batch, total_q, total_kv, hq, hkv, d, dkdv_heads_split(batch, total_kv, hq, hkv)).total;
 }
 
 attn_thd_status attn_fwd_thd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -601,7 +607,7 @@ struct Fp8Layout {
 static Fp8Layout fp8_layout(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq,
                             int32_t hkv, int32_t d) {
   Fp8Layout f;
-  f.base = layout(batch, total_q, total_kv, hq, hkv, d, true).total;
+  f.base = layout(batch, total_q, total_kv, hq, hkv, d, dkdv_heads_split(batch, total_kv, hq, hkv)).total;
   f.q = f.base;
   f.k = f.q + round_up((size_t)total_q * hq * d * 2);
   f.v = f.k + round_up((size_t)total_kv * hkv * d * 2);
@@ -847,7 +853,7 @@ attn_thd_status attn_bwd_thd_noalloc(const void* q, const void* k, const void* v
   (void)max_seqlen_kv;
   if (!sizes_ok(batch, total_q, total_kv, hq, hkv, d)) return ATTN_THD_EINVAL;
   // the unsplit dK/dV: the scratch holds no partial planes
-  if (layout(batch, total_q, total_kv, hq, hkv, d, false).total > ATTN_THD_NOALLOC_SCRATCH_BYTES)
+  if (layout(batch, total_q, total_kv, hq, hkv, d, 1).total > ATTN_THD_NOALLOC_SCRATCH_BYTES)
     return ATTN_THD_ESCRATCH;
   void* ws = nullptr;
   const attn_thd_status st = scratch_for(stream, &ws);

@@ -106,7 +106,12 @@ enum {
  * dK/dV workgroups per key tile (groups of 8 or more query heads whose key
  * tiles alone give fewer than 4096 workgroups), fp32 partial dK / dV planes
  * of 2 x split x total_kv x hkv x d floats, split being a power of two that
- * divides the group.
+ * divides the group.  Since fewer key tokens can mean more planes, the calls
+ * also accept a smaller workspace as long as it holds the rest (one sized
+ * for a problem with more key tokens does): the backward then halves split
+ * until its planes fit, down to 1.  Results are deterministic for a given
+ * workspace_bytes; two calls that differ only in it may round dK / dV
+ * differently.
  */
 size_t attn_thd_workspace_size(int32_t batch, int32_t total_q, int32_t total_kv,
                                int32_t hq, int32_t hkv, int32_t d);

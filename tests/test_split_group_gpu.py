@@ -123,3 +123,34 @@ def test_split_group_bitwise_repeat():
     for x, y in zip(r1, r2):
         assert torch.equal(x.view(torch.int16) if x.element_size() == 2 else x.view(torch.int32),
                            y.view(torch.int16) if y.element_size() == 2 else y.view(torch.int32))
+
+
+def test_smaller_workspace_takes_a_smaller_split():
+    """Fewer key tokens can mean more partial planes, so a workspace sized for
+    a larger problem may be below workspace_size: the backward then halves the
+    split until its planes fit (down to none) and the results stay at the
+    bar; below the size without planes the call fails with EWORKSPACE."""
+    import bwd_thd_varlen_amd as A
+    from helpers import cu_dev, oracle_run, real_rows
+    case = _case([200, 129, 64], [200, 129, 64], [208, 136, 64], [208, 136, 64], 16, 1, 128,
+                 True, "bf16", seed=17)
+    B, tq, tk = case.batch, case.q.shape[0], case.k.shape[0]
+    assert split_of(B, tq, tk, 16, 1, 128) == 16
+    base = A.workspace_size(B, tq, tk, 16, 16, 128)   # the same layout without planes (a group of 1)
+    plane_pair = 2 * tk * 1 * 128 * 4                   # one dK and one dV plane
+    ref = oracle_run(case)
+    qrows = real_rows(case.cu_seqlens_q, case.cu_seqlens_q_padded, tq, case.cu_seqlens_kv)
+    krows = real_rows(case.cu_seqlens_kv, case.cu_seqlens_kv_padded, tk, case.cu_seqlens_q)
+    for nbytes in (base, base + 2 * plane_pair + 256):   # no split; room for split 2
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+        o, l, dq, dk, dv = gpu_run(case, workspace=ws)
+        assert_close("dq", dq, ref[2], "bf16", qrows)
+        assert_close("dk", dk, ref[3], "bf16", krows)
+        assert_close("dv", dv, ref[4], "bf16", krows)
+    q, k, v, do = (t.cuda() for t in (case.q, case.k, case.v, case.dout))
+    cq, ck = cu_dev(case.cu_seqlens_q), cu_dev(case.cu_seqlens_kv)
+    kw = dict(cu_seqlens_q_padded=cu_dev(case.cu_seqlens_q_padded),
+              cu_seqlens_kv_padded=cu_dev(case.cu_seqlens_kv_padded), attn_mask_type="padding_causal")
+    small = torch.empty(base - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(A.AttnError, match="WORKSPACE|workspace"):
+        A.bwd(q, k, v, o, do, l, cq, ck, workspace=small, **kw)
