@@ -373,6 +373,12 @@ def main():
             chunks.append(dict(k=kc, v=vc, cu=cu(np.concatenate([[0], np.cumsum(e - a)])),
                                pos=cu(a), dk=torch.empty_like(kc), dv=torch.empty_like(vc)))
         o_part, l_part = torch.empty_like(out), torch.empty_like(lse)
+        # one workspace for every chunk call, of the largest size they ask for
+        # (fewer key tokens per call can mean partial dK/dV planes)
+        need = max(A.workspace_size(case.batch, tq, int(ch["k"].shape[0]), case.hq, case.hkv, case.d)
+                   for ch in chunks)
+        if need > ws.numel():
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
         n_fwd = n_bwd = C
         merge_ev = True
         ckw = dict(cu_seqlens_q_padded=cqp, attn_mask_type=case.mask_type,
