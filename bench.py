@@ -47,6 +47,7 @@ a few seconds), --workload NAME:
                         mask) in the forward and the backward
   d64_65k, d256_65k     the headline sequences at head dim 64 / 256 (hq 64,
                         hkv 8, bf16, causal)
+  mqa_65k               the headline sequences with one KV head (hq 64, d 128)
   chunked_bottom_right  THD query chunks of 2048 tokens (the last tokens of
                         each context) against contexts U[2048, 8192] (65536
                         key tokens), bottom-right causal; FLOPs counted on
@@ -121,6 +122,11 @@ WORKLOADS = {
         metric="fwd+bwd TFLOP/s (THD bf16 padding_causal, hq64/hkv8/d256) + % MFMA peak",
         desc="d256_65k: the throughput_65k sequences at head dim 256 (hq=64 hkv=8), bf16, "
              "padding_causal, fwd+bwd; same FLOP model"),
+    "mqa_65k": dict(
+        layout="thd",
+        metric="fwd+bwd TFLOP/s (THD bf16 padding_causal, hq64/hkv1/d128) + % MFMA peak",
+        desc="mqa_65k: the throughput_65k sequences with one KV head for 64 query heads, d=128, "
+             "bf16, padding_causal, fwd+bwd; same FLOP model"),
     "chunked_bottom_right": dict(
         layout="thd",
         metric="fwd+bwd TFLOP/s (THD bf16 padding_causal_bottom_right, query chunks, "

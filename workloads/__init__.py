@@ -36,7 +36,7 @@ Workloads (each named by what it is, with its sizes):
   [256, 8192] padded to multiples of 64, hq=64, hkv=8, d=128, bf16,
   ``padding_causal``.
 * ``d64_65k``, ``d256_65k`` -- the throughput_65k sequences at head dims 64
-  and 256 (hq=64, hkv=8, bf16, causal).
+  and 256 (hq=64, hkv=8, bf16, causal); ``mqa_65k`` with one KV head.
 * ``large_offsets``       -- 266304 tokens (260 slots of 1024, 64 trailing
   rows), hq=64, hkv=8, d=128, bf16, ``padding_causal``: the query-side
   tensors pass 2^31 elements and 2^32 bytes.  The one workload drawn on the
@@ -268,6 +268,14 @@ def d256_65k(seed: int = 0) -> Case:
     """The throughput_65k sequences at head dim 256 (hq=64, hkv=8, bf16, causal)."""
     c = throughput_65k(seed, d=256)
     c.name = "d256_65k"
+    return c
+
+
+def mqa_65k(seed: int = 0) -> Case:
+    """The throughput_65k sequences with one KV head for 64 query heads (d=128,
+    bf16, causal)."""
+    c = throughput_65k(seed, hkv=1)
+    c.name = "mqa_65k"
     return c
 
 
