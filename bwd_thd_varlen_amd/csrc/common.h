@@ -42,7 +42,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Tile geometry shared by host and device.
 constexpr int kQTile = 128;      // query rows per forward / dQ work item (4 waves x 32)
 constexpr int kKVTile = 128;     // key rows per dK/dV work item
-constexpr int kKVStep = 64;      // keys per inner step of the forward / dQ kernels
+constexpr int kKVStep = 64;      // keys per inner step of dq_kernel (head dims up to 128)
 constexpr int kMinTile = 64;     // smallest tile any list uses (sizes the lists)
 constexpr int kSchedKeys = 2048; // distinct work keys of the heaviest-first ordering
 

@@ -30,6 +30,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import os
+import re
 import sqlite3
 import sys
 from collections import defaultdict
@@ -56,11 +57,21 @@ COPY_BYTES = 1 << 30          # bench.py --copy-calibration: 1 GiB copies
 COPY_MIN_KIB = (COPY_BYTES >> 10) // 4   # smaller copies (argument uploads) are ignored
 
 
+def code_only(text: str) -> str:
+    """A C++ source without its comments, trailing blanks and blank lines, so
+    that an edit to a comment leaves the hash below (and with it every stored
+    summary) as it is."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_hash(stage: str) -> str:
+    """sha256 (16 hex digits) of the code of the stage's kernel sources."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES.get(stage, []):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

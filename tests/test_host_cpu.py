@@ -157,3 +157,11 @@ def test_counter_summary_lds_conflicts_and_clock(tmp_path):
     assert row.rstrip().endswith("| - | - | 0.25 |")
     row = next(l for l in lines if l.startswith("| shader clock"))
     assert row.rstrip().endswith("| - | - | 1.60 GHz |")
+
+
+def test_source_hash_ignores_comments():
+    """Comments and blank lines do not change the code hash of a stage; code does."""
+    src = "int a; // one\n/* two\n three */\nint b;   \n\n"
+    assert rs.code_only(src) == "int a;\nint b;"
+    assert rs.code_only("int a;\nint b;") == rs.code_only(src)
+    assert rs.code_only("int a;\nint c;") != rs.code_only(src)
