@@ -50,13 +50,15 @@ bool sizes_ok(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq, int3
 // dK/dV: 1, unless the group holds at least 8 query heads and the key tiles
 // alone give fewer than 4096 workgroups (with few KV heads one workgroup
 // would walk every query head of its group, and the longest one would set the
-// kernel's time); then doubled while it divides the group, up to 4096.
+// kernel's time); then doubled, up to 4096 workgroups, while it divides the
+// group and leaves every workgroup at least 2 of its heads (a workgroup per
+// head writes the most partial planes for the least work).
 int32_t dkdv_heads_split(int32_t batch, int32_t total_kv, int32_t hq, int32_t hkv) {
   const int32_t group = hq / hkv;
   if (group < 8) return 1;
   const int64_t wgs = (((int64_t)total_kv + kKVTile - 1) / kKVTile + batch) * hkv;
   int32_t split = 1;
-  while (group % (2 * split) == 0 && wgs * split < 4096) split *= 2;
+  while (group % (2 * split) == 0 && group / (2 * split) >= 2 && wgs * split < 4096) split *= 2;
   return split;
 }
 

@@ -106,7 +106,7 @@ enum {
  * dK/dV workgroups per key tile (groups of 8 or more query heads whose key
  * tiles alone give fewer than 4096 workgroups), fp32 partial dK / dV planes
  * of 2 x split x total_kv x hkv x d floats, split being a power of two that
- * divides the group.  Since fewer key tokens can mean more planes, the calls
+ * divides the group and leaves every workgroup at least 2 of its heads.  Since fewer key tokens can mean more planes, the calls
  * also accept a smaller workspace as long as it holds the rest (one sized
  * for a problem with more key tokens does): the backward then halves split
  * until its planes fit, down to 1.  Results are deterministic for a given

@@ -270,9 +270,10 @@ FAKE_ARGS = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE,
 def test_split_group_workspace_rule(A):
     """Groups of 8 or more query heads with few key tiles get fp32 partial
     dK / dV planes (2 x split x total_kv x hkv x d) in the workspace: split
-    doubles while it divides the group and the dK/dV workgroups (key tiles of
-    128 plus one per sequence, times hkv) stay below 4096.  Read off the size's
-    growth with d, the only term that depends on it."""
+    doubles while it divides the group, leaves every workgroup at least 2 of
+    its heads, and the dK/dV workgroups (key tiles of 128 plus one per
+    sequence, times hkv) stay below 4096.  Read off the size's growth with d,
+    the only term that depends on it."""
     def split(batch, t, hq, hkv, d=128):
         grow = A.workspace_size(batch, t, t, hq, hkv, d) - A.workspace_size(batch, t, t, hq, hkv, d - 8)
         return round(grow / (2 * t * hkv * 8 * 4))
@@ -283,3 +284,5 @@ def test_split_group_workspace_rule(A):
     assert split(8, 16384, 64, 1) == 32      # 136 -> 4352, below the group of 64
     assert split(4, 1000, 4, 1) == 0         # a group of 4: never split
     assert split(4, 1000, 24, 1) == 8        # 24 = 8 x 3: doubling stops where 2 split no longer divides
+    assert split(4, 1000, 8, 1) == 4         # a group of 8: 2 heads per workgroup at most split
+    assert split(4, 1000, 16, 1) == 8
