@@ -27,6 +27,10 @@
 // computed so that the lane index runs over the dimension that survives the
 // next product, and the operand that contracts over a tile's rows is read
 // from the same row-major LDS tile with the transpose read.
+//
+// Head dims below the padded tile width: the products run over the head dim
+// rounded up to 16 (160, 192 or 256 for the split kernels) and skip the
+// column blocks of the outputs past it, whose operands are zero.
 #include "common.h"
 
 namespace attn {
@@ -42,20 +46,20 @@ __device__ __forceinline__ void add_stored(float* x, u32x2 w) {
   x[3] += b[1];
 }
 
-// dQ of this lane's query over column blocks [cb0, cb0 + NB) of the head dim,
-// scaled and rounded once (ACC: added to what `out` holds); `out` is the
-// query's row of the head, lane half hh holds columns 4 hh .. +3 of each
-// 8-column group.
+// dQ of this lane's query over column blocks [cb0, cb0 + nb) of the head dim
+// (nb <= NB), scaled and rounded once (ACC: added to what `out` holds); `out`
+// is the query's row of the head, lane half hh holds columns 4 hh .. +3 of
+// each 8-column group.
 template <int DT, bool ACC, int NB>
 __device__ __forceinline__ void store_dq(const AttnParams& p, uint16_t* out, int cb0, int hh,
-                                         const f32x16 (&acc)[NB]) {
+                                         const f32x16 (&acc)[NB], int nb = NB) {
   const float sc0 = p.scale;
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int c0 = 32 * (cb0 + cb) + 8 * q4 + 4 * hh;
-      if (c0 < p.d) {
+      if (cb < nb && c0 < p.d) {
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = acc[cb][4 * q4 + e] * sc0;
@@ -66,19 +70,19 @@ __device__ __forceinline__ void store_dq(const AttnParams& p, uint16_t* out, int
     }
 }
 
-// dK (scaled) and dV of this lane's key over column blocks [cb0, cb0 + NB),
-// rounded once (ACC: added to what the rows hold); dkb / dvb are the key's
+// dK (scaled) and dV of this lane's key over column blocks [cb0, cb0 + nb)
+// (nb <= NB), rounded once (ACC: added to what the rows hold); dkb / dvb are the key's
 // rows of the KV head.
 template <int DT, bool ACC, int NB>
 __device__ __forceinline__ void store_dkdv(const AttnParams& p, uint16_t* dkb, uint16_t* dvb, int cb0, int hh,
-                                           const f32x16 (&adk)[NB], const f32x16 (&adv)[NB]) {
+                                           const f32x16 (&adk)[NB], const f32x16 (&adv)[NB], int nb = NB) {
   const float sc0 = p.scale;
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int c0 = 32 * (cb0 + cb) + 8 * q4 + 4 * hh;
-      if (c0 < p.d) {
+      if (cb < nb && c0 < p.d) {
         float xk[4], xv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -98,16 +102,17 @@ __device__ __forceinline__ void store_dkdv(const AttnParams& p, uint16_t* dkb, u
 }
 
 // This workgroup's fp32 dK and dV of this lane's key (unscaled) over column
-// blocks [cb0, cb0 + NB), into its partial planes (split GQA group).
+// blocks [cb0, cb0 + nb) (nb <= NB), into its partial planes (split GQA group).
 template <int NB>
 __device__ __forceinline__ void store_dkdv_part(const AttnParams& p, float* dkp, float* dvp, int cb0, int hh,
-                                                const f32x16 (&adk)[NB], const f32x16 (&adv)[NB]) {
+                                                const f32x16 (&adk)[NB], const f32x16 (&adv)[NB],
+                                                int nb = NB) {
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int c0 = 32 * (cb0 + cb) + 8 * q4 + 4 * hh;
-      if (c0 < p.d) {
+      if (cb < nb && c0 < p.d) {
         *reinterpret_cast<f32x4*>(dkp + c0) =
             (f32x4){adk[cb][4 * q4], adk[cb][4 * q4 + 1], adk[cb][4 * q4 + 2], adk[cb][4 * q4 + 3]};
         *reinterpret_cast<f32x4*>(dvp + c0) =
@@ -118,11 +123,14 @@ __device__ __forceinline__ void store_dkdv_part(const AttnParams& p, float* dkp,
 
 // ----------------------------------------------------------------- dQ
 // ACC: add into dq (the chunked, accumulating backward) instead of writing it;
-// DROP: dropout on the probabilities (the keep mask of dropout_block)
-template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP>
+// DROP: dropout on the probabilities (the keep mask of dropout_block); DE:
+// the head dim rounded up to 16, the extent of the products (tiles and
+// layouts keep the padded width DPAD)
+template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, int DE>
 __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void dq_kernel(AttnParams p) {
-  constexpr int NT = DPAD / 16;
-  constexpr int NCB = DPAD / 32;
+  static_assert(DE <= DPAD, "the products cover at most the padded head dim");
+  constexpr int NT = (DE + 15) / 16;   // 16-wide k chunks of the products
+  constexpr int NCB = (DE + 31) / 32;  // 32-column blocks of dQ
   constexpr int KS = kKVStep;
   using LK = Lay<DPAD, true>;          // K: row reads (S) and transposed reads (dQ)
   using LV = Lay<DPAD, false>;         // V: row reads (dP)
@@ -320,12 +328,16 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 // adds dS K over its own four column blocks.  K and V use the same padded
 // tile layout; both waves of a pair form Delta from dO and O (the same
 // arithmetic, so the same value).  Two barriers per step: the ring's, and the
-// one after the tiles are written.
-template <int DT, bool CAUSAL, bool ACC, bool DROP>
+// one after the tiles are written.  DE (160, 192 or 256): the extent of the
+// products; with an odd count of column blocks the even wave takes the extra
+// one.
+template <int DT, bool CAUSAL, bool ACC, bool DROP, int DE>
 __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
   constexpr int DPAD = 256, NW = 8, KS = 32;
-  constexpr int NT = DPAD / 16;
-  constexpr int NCBH = DPAD / 64;      // 32-column blocks of one half
+  static_assert(DE % 32 == 0 && DE > 128 && DE <= DPAD, "products over whole 32-column blocks");
+  constexpr int NT = DE / 16;          // 16-wide k chunks of the products
+  constexpr int NCB = DE / 32;         // 32-column blocks of dQ
+  constexpr int NCBH = (NCB + 1) / 2;  // blocks of the even wave of a pair (the odd one: NCB - NCBH)
   using LK = Lay<DPAD, true>;          // K and V: row reads (S, dP); K also transposed (dQ)
   using Dma = TileDma<LK, KS, NW>;
 
@@ -412,7 +424,9 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
   f32x16 acc[NCBH];
 #pragma unroll
   for (int cb = 0; cb < NCBH; ++cb) acc[cb] = zero16();
+  // this wave's column blocks of dQ: cb0 .. cb0 + nb - 1
   const int cb0 = half * NCBH;
+  const int nb = half ? NCB - NCBH : NCBH;
 
   for (int step = 0; step < nsteps; ++step) {
     wait_vm<0>();
@@ -480,15 +494,15 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
       const TrReader<LK> trk(tk, lane);
 #pragma unroll
       for (int cb = 0; cb < NCBH; ++cb)
-        acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 0), b0, acc[cb]);
+        if (cb < nb) acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 0), b0, acc[cb]);
 #pragma unroll
       for (int cb = 0; cb < NCBH; ++cb)
-        acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 1), b1, acc[cb]);
+        if (cb < nb) acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 1), b1, acc[cb]);
     }
   }
 
   if (qvalid)
-    store_dq<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d, cb0, hh, acc);
+    store_dq<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d, cb0, hh, acc, nb);
 }
 
 // ----------------------------------------------------------------- dK / dV
@@ -506,15 +520,17 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
 // ACC: add into dk / dv instead of writing them; DROP: dropout on the
 // probabilities (the keep mask of dropout_block); PART: this workgroup takes
 // kv_heads of the group's query heads and writes fp32 partial dK / dV planes
-// (split GQA group); OCC: workgroups per CU the register budget is sized for.
-template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, bool PART, int OCC>
+// (split GQA group); OCC: workgroups per CU the register budget is sized for;
+// DE: the head dim rounded up to 16, the extent of the products.
+template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, bool PART, int OCC, int DE>
 __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
   constexpr int NW = 4, BM = 32, NBUF = 2;
   constexpr int BN = 32 * NW;
   static_assert(BN == kKVTile, "the work lists are built for kKVTile keys per item");
   constexpr int NU = BM / 16;          // 16-query chunks per step
-  constexpr int NT = DPAD / 16;
-  constexpr int NCB = DPAD / 32;
+  static_assert(DE <= DPAD, "the products cover at most the padded head dim");
+  constexpr int NT = (DE + 15) / 16;   // 16-wide k chunks of the products
+  constexpr int NCB = (DE + 31) / 32;  // 32-column blocks of dK and dV
   using LQ = Lay<DPAD, true>;          // Q, dO: row reads (S, dP) and transposed reads (dK, dV)
   using Dma = TileDma<LQ, BM, NW>;
   constexpr int DMA_PER_STEP = 2 * Dma::PER_WAVE + 1;
@@ -633,8 +649,6 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
   // One barrier per step: the buffer refilled at step j (that of step j-1)
   // has been read by every wave once the wave passes step j's barrier.
   int cm = m_last - 1, chg = 0;   // compute cursor: query tile, head in the group
-  // unrolled by two: each copy's ring buffer is a constant
-#pragma unroll 2
   for (int step = 0; step < nsteps; ++step) {
     // this step's tiles have landed
     wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1 - step));
@@ -781,13 +795,17 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
 // column blocks.  Two barriers per step: the ring's, and the one after the
 // tiles are written.  Steps, DMA ring, cursors, masks, dropout and the
 // split GQA group (PART) are those of dkdv_kernel with NW = 8, BM = 32, NBUF = 2.
-template <int DT, bool CAUSAL, bool ACC, bool DROP, bool PART>
+// DE (160, 192 or 256): the extent of the products; with an odd count of
+// column blocks the even wave of a pair takes the extra one.
+template <int DT, bool CAUSAL, bool ACC, bool DROP, bool PART, int DE>
 __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   constexpr int DPAD = 256, NW = 8, BM = 32, NBUF = 2;
   constexpr int BN = 16 * NW;          // keys per workgroup: NW / 2 blocks of 32
   static_assert(BN == kKVTile, "the work lists are built for kKVTile keys per item");
-  constexpr int NT = DPAD / 16;        // 16-wide k chunks of the whole head dim
-  constexpr int NCBH = DPAD / 64;      // 32-column blocks of one half
+  static_assert(DE % 32 == 0 && DE > 128 && DE <= DPAD, "products over whole 32-column blocks");
+  constexpr int NT = DE / 16;          // 16-wide k chunks of the products
+  constexpr int NCB = DE / 32;         // 32-column blocks of dK and dV
+  constexpr int NCBH = (NCB + 1) / 2;  // blocks of the even wave of a pair (the odd one: NCB - NCBH)
   constexpr int NU = BM / 16;          // 16-query chunks per step
   using LQ = Lay<DPAD, true>;          // Q, dO: row reads (S, dP) and transposed reads (dK, dV)
   using Dma = TileDma<LQ, BM, NW>;
@@ -832,6 +850,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   const int m_last = (s.lq + BM - 1) / BM;
   const int nm = m_last > m_first ? m_last - m_first : 0;
   const int nsteps = nm * ng;
+  // this wave's column blocks of dK and dV: cb0 .. cb0 + nb - 1
+  const int cb0 = half * NCBH;
+  const int nb = half ? NCB - NCBH : NCBH;
   const int h0 = g * p.group + sub * ng;
 
   Dma dma_q;
@@ -994,7 +1015,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
       // read one MFMA ahead
       const TrReader<LQ> trq(tq, lane), trdo(tdo, lane);
       constexpr int PD = 1, NO = NU * NCBH;
-      const int cb0 = half * NCBH;
       u32x4 tdv[NO], tqv[NO];
 #pragma unroll
       for (int o = 0; o < PD; ++o) {
@@ -1004,12 +1024,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
 #pragma unroll
       for (int o = 0; o < NO; ++o) {
         const int u = o / NCBH, cb = o % NCBH;
+        const bool ahead = o + PD < NO && (o + PD) % NCBH < nb;
         __builtin_amdgcn_sched_barrier(0);
-        adv[cb] = Mfma<DT>::mma(tdv[o], bp[u], adv[cb]);
-        if (o + PD < NO) tdv[o + PD] = trdo.read(cb0 + (o + PD) % NCBH, (o + PD) / NCBH);
+        if (cb < nb) adv[cb] = Mfma<DT>::mma(tdv[o], bp[u], adv[cb]);
+        if (ahead) tdv[o + PD] = trdo.read(cb0 + (o + PD) % NCBH, (o + PD) / NCBH);
         __builtin_amdgcn_sched_barrier(0);
-        adk[cb] = Mfma<DT>::mma(tqv[o], bds[u], adk[cb]);
-        if (o + PD < NO) tqv[o + PD] = trq.read(cb0 + (o + PD) % NCBH, (o + PD) / NCBH);
+        if (cb < nb) adk[cb] = Mfma<DT>::mma(tqv[o], bds[u], adk[cb]);
+        if (ahead) tqv[o + PD] = trq.read(cb0 + (o + PD) % NCBH, (o + PD) / NCBH);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1019,10 +1040,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
     const int64_t row = (int64_t)kj * kvts;
     if constexpr (PART) {
       float* dkp = p.part + (int64_t)sub * p.part_plane + kvoff + row;
-      store_dkdv_part(p, dkp, dkp + (int64_t)p.kv_split * p.part_plane, half * NCBH, hh, adk, adv);
+      store_dkdv_part(p, dkp, dkp + (int64_t)p.kv_split * p.part_plane, cb0, hh, adk, adv, nb);
     } else {
       store_dkdv<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dk) + kvoff + row,
-                          reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, half * NCBH, hh, adk, adv);
+                          reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, cb0, hh, adk, adv, nb);
     }
   }
 }
@@ -1080,40 +1101,58 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnParams p) {
 
 // ----------------------------------------------------------------- launchers
 // dropout is not combined with accumulation (the chunked entry points take none)
-template <int DT, int DPAD, bool CAUSAL>
+// DE: the extent of the products, the head dim rounded up to 16 (split
+// kernels: to 160, 192 or 256; at 224 the odd column count spills); the k
+// chunks and column blocks past it hold no real column
+template <int DT, int DPAD, bool CAUSAL, int DE>
 static void launch_dq_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(256);
-  if (p.accumulate & kAccDq) hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, true, false>), g, blk, 0, st, p);
-  else if (p.drop_t) hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, false, true>), g, blk, 0, st, p);
-  else hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, false, false>), g, blk, 0, st, p);
+  if (p.accumulate & kAccDq) hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, true, false, DE>), g, blk, 0, st, p);
+  else if (p.drop_t) hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, false, true, DE>), g, blk, 0, st, p);
+  else hipLaunchKernelGGL((dq_kernel<DT, DPAD, CAUSAL, false, false, DE>), g, blk, 0, st, p);
 }
 
-template <int DT, bool CAUSAL>
+template <int DT, bool CAUSAL, int DE>
 static void launch_dq_split_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(512);
-  if (p.accumulate & kAccDq) hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, true, false>), g, blk, 0, st, p);
-  else if (p.drop_t) hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, false, true>), g, blk, 0, st, p);
-  else hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, false, false>), g, blk, 0, st, p);
+  if (p.accumulate & kAccDq) hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, true, false, DE>), g, blk, 0, st, p);
+  else if (p.drop_t) hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, false, true, DE>), g, blk, 0, st, p);
+  else hipLaunchKernelGGL((dq_split_kernel<DT, CAUSAL, false, false, DE>), g, blk, 0, st, p);
+}
+
+template <int DT, int DE>
+static void launch_dq_split_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
+  if (causal) launch_dq_split_c<DT, true, DE>(p, grid, st);
+  else launch_dq_split_c<DT, false, DE>(p, grid, st);
 }
 
 template <int DT>
 static void launch_dq_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (causal) launch_dq_split_c<DT, true>(p, grid, st);
-  else launch_dq_split_c<DT, false>(p, grid, st);
+  switch ((p.d + 31) >> 5) {
+    case 5: launch_dq_split_d<DT, 160>(p, causal, grid, st); break;
+    case 6: launch_dq_split_d<DT, 192>(p, causal, grid, st); break;
+    default: launch_dq_split_d<DT, 256>(p, causal, grid, st);
+  }
 }
 
-template <int DT, int DPAD>
+template <int DT, int DPAD, int DE>
 static void launch_dq_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (causal) launch_dq_c<DT, DPAD, true>(p, grid, st);
-  else launch_dq_c<DT, DPAD, false>(p, grid, st);
+  if (causal) launch_dq_c<DT, DPAD, true, DE>(p, grid, st);
+  else launch_dq_c<DT, DPAD, false, DE>(p, grid, st);
 }
 
 template <int DT>
 static void launch_dq_dt(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (p.d <= 32) launch_dq_d<DT, 32>(p, causal, grid, st);
-  else if (p.d <= 64) launch_dq_d<DT, 64>(p, causal, grid, st);
-  else if (p.d <= 128) launch_dq_d<DT, 128>(p, causal, grid, st);
-  else launch_dq_split<DT>(p, causal, grid, st);
+  switch ((p.d + 15) >> 4) {
+    case 1: case 2: launch_dq_d<DT, 32, 32>(p, causal, grid, st); break;
+    case 3: launch_dq_d<DT, 64, 48>(p, causal, grid, st); break;
+    case 4: launch_dq_d<DT, 64, 64>(p, causal, grid, st); break;
+    case 5: launch_dq_d<DT, 128, 80>(p, causal, grid, st); break;
+    case 6: launch_dq_d<DT, 128, 96>(p, causal, grid, st); break;
+    case 7: launch_dq_d<DT, 128, 112>(p, causal, grid, st); break;
+    case 8: launch_dq_d<DT, 128, 128>(p, causal, grid, st); break;
+    default: launch_dq_split<DT>(p, causal, grid, st);
+  }
 }
 
 hipError_t launch_dq(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st) {
@@ -1141,55 +1180,70 @@ hipError_t launch_dkdv_reduce(const AttnParams& p, int dtype, int max_kv_tiles, 
   return hipGetLastError();
 }
 
-template <int DT, bool CAUSAL>
+template <int DT, bool CAUSAL, int DE>
 static void launch_dkdv_split_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(512);
   if (p.kv_split > 1) {
-    if (p.drop_t) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, true, true>), g, blk, 0, st, p);
-    else hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, false, true>), g, blk, 0, st, p);
+    if (p.drop_t) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, true, true, DE>), g, blk, 0, st, p);
+    else hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, false, true, DE>), g, blk, 0, st, p);
   } else if (p.accumulate & kAccDkDv)
-    hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, true, false, false>), g, blk, 0, st, p);
-  else if (p.drop_t) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, true, false>), g, blk, 0, st, p);
-  else hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, false, false>), g, blk, 0, st, p);
+    hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, true, false, false, DE>), g, blk, 0, st, p);
+  else if (p.drop_t) hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, true, false, DE>), g, blk, 0, st, p);
+  else hipLaunchKernelGGL((dkdv_split_kernel<DT, CAUSAL, false, false, false, DE>), g, blk, 0, st, p);
+}
+
+template <int DT, int DE>
+static void launch_dkdv_split_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
+  if (causal) launch_dkdv_split_c<DT, true, DE>(p, grid, st);
+  else launch_dkdv_split_c<DT, false, DE>(p, grid, st);
 }
 
 template <int DT>
 static void launch_dkdv_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (causal) launch_dkdv_split_c<DT, true>(p, grid, st);
-  else launch_dkdv_split_c<DT, false>(p, grid, st);
+  switch ((p.d + 31) >> 5) {
+    case 5: launch_dkdv_split_d<DT, 160>(p, causal, grid, st); break;
+    case 6: launch_dkdv_split_d<DT, 192>(p, causal, grid, st); break;
+    default: launch_dkdv_split_d<DT, 256>(p, causal, grid, st);
+  }
 }
 
 // a split group writes partial planes; dropout and accumulation then act in
 // the kernel and in the sum respectively
-template <int DT, int DPAD, bool CAUSAL, int OCC>
+template <int DT, int DPAD, bool CAUSAL, int OCC, int DE>
 static void launch_dkdv_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(256);
   if (p.kv_split > 1) {
     if (p.drop_t)
-      hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, true, OCC>), g, blk, 0, st, p);
+      hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, true, OCC, DE>), g, blk, 0, st, p);
     else
-      hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, true, OCC>), g, blk, 0, st, p);
+      hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, true, OCC, DE>), g, blk, 0, st, p);
   } else if (p.accumulate & kAccDkDv)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, true, false, false, OCC>), g, blk, 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, true, false, false, OCC, DE>), g, blk, 0, st, p);
   else if (p.drop_t)
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, false, OCC>), g, blk, 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, true, false, OCC, DE>), g, blk, 0, st, p);
   else
-    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, false, OCC>), g, blk, 0, st, p);
+    hipLaunchKernelGGL((dkdv_kernel<DT, DPAD, CAUSAL, false, false, false, OCC, DE>), g, blk, 0, st, p);
 }
 
-template <int DT, int DPAD, int OCC>
+template <int DT, int DPAD, int OCC, int DE>
 static void launch_dkdv_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (causal) launch_dkdv_c<DT, DPAD, true, OCC>(p, grid, st);
-  else launch_dkdv_c<DT, DPAD, false, OCC>(p, grid, st);
+  if (causal) launch_dkdv_c<DT, DPAD, true, OCC, DE>(p, grid, st);
+  else launch_dkdv_c<DT, DPAD, false, OCC, DE>(p, grid, st);
 }
 
 template <int DT>
 static void launch_dkdv_dt(const AttnParams& p, bool causal, int grid, hipStream_t st) {
   // three workgroups per CU up to d = 64 (<= 168 VGPRs), two at 128
-  if (p.d <= 32) launch_dkdv_d<DT, 32, 3>(p, causal, grid, st);
-  else if (p.d <= 64) launch_dkdv_d<DT, 64, 3>(p, causal, grid, st);
-  else if (p.d <= 128) launch_dkdv_d<DT, 128, 2>(p, causal, grid, st);
-  else launch_dkdv_split<DT>(p, causal, grid, st);
+  switch ((p.d + 15) >> 4) {
+    case 1: case 2: launch_dkdv_d<DT, 32, 3, 32>(p, causal, grid, st); break;
+    case 3: launch_dkdv_d<DT, 64, 3, 48>(p, causal, grid, st); break;
+    case 4: launch_dkdv_d<DT, 64, 3, 64>(p, causal, grid, st); break;
+    case 5: launch_dkdv_d<DT, 128, 2, 80>(p, causal, grid, st); break;
+    case 6: launch_dkdv_d<DT, 128, 2, 96>(p, causal, grid, st); break;
+    case 7: launch_dkdv_d<DT, 128, 2, 112>(p, causal, grid, st); break;
+    case 8: launch_dkdv_d<DT, 128, 2, 128>(p, causal, grid, st); break;
+    default: launch_dkdv_split<DT>(p, causal, grid, st);
+  }
 }
 
 hipError_t launch_dkdv(const AttnParams& p, int dtype, bool causal, int max_kv_tiles, hipStream_t st) {

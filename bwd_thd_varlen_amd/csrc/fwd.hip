@@ -38,13 +38,17 @@ constexpr int fwd_step_keys() { return DPAD >= 64 ? 32 : 64; }
 // F8: q and k are E4M3 codes (p.q8, p.k8): Q stays in registers as codes, K
 // tiles hold DPAD code bytes per row, and S^T = K Q^T is taken on the 8-bit
 // 32 x 32 x 64 product, whose result tile has the layout of the 16-bit one.
-template <int DT, int DPAD, bool CAUSAL, bool DROP, bool F8 = false>
+// DE: the extent of the products, at most DPAD (tiles and layouts keep the
+// padded width); the k chunks and the column blocks of O past it hold no
+// real column.
+template <int DT, int DPAD, bool CAUSAL, bool DROP, bool F8 = false, int DE = DPAD>
 __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 2) void fwd_kernel(AttnParams p) {
   // E4M3 K rows of DPAD bytes hold whole 64-code chunks of the 8-bit product
   static_assert(!F8 || DPAD >= 64, "the 8-bit scores are built for head dims 48..256");
-  constexpr int NT = F8 ? 1 : DPAD / 16;   // 16-wide k chunks over the head dim (16-bit Q)
-  constexpr int NT8 = DPAD / 64;           // 64-wide k chunks (E4M3 Q)
-  constexpr int NCB = DPAD / 32;       // 32-row blocks of O^T
+  static_assert(DE <= DPAD, "the products cover at most the padded head dim");
+  constexpr int NT = F8 ? 1 : (DE + 15) / 16;   // 16-wide k chunks of the products (16-bit Q)
+  constexpr int NT8 = (DE + 63) / 64;           // 64-wide k chunks (E4M3 Q)
+  constexpr int NCB = (DE + 31) / 32;           // 32-row blocks of O^T
   // keys per step (the 8-bit K tiles are half the size: 64 keys still fit
   // three workgroups per CU at head dims up to 128; 32 above, for two)
   constexpr int KS = F8 ? (DPAD <= 128 ? 64 : 32) : fwd_step_keys<DPAD>();
@@ -152,10 +156,11 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 2) void fwd_kernel(AttnParam
         if constexpr (F8) {
           // key row 32 kb2 + li, code bytes 64 t + 32 hh .. +32 (16-bit columns 32 t + 16 hh)
 #pragma unroll
-          for (int t = 0; t < NT8; ++t)
+          for (int t = 0; t < NT8; ++t) {
             sc[kb2] = mma_e4m3(lds_row8<LK>(tK, 32 * kb2 + li, 32 * t + 16 * hh),
                                lds_row8<LK>(tK, 32 * kb2 + li, 32 * t + 16 * hh + 8),
                                q8lo[t], q8hi[t], sc[kb2]);
+          }
         } else {
           // K operands read two MFMAs ahead, pinned with scheduling barriers
           constexpr int PD = 2;
@@ -246,28 +251,38 @@ __global__ __launch_bounds__(256, DPAD <= 128 ? 3 : 2) void fwd_kernel(AttnParam
   }
 }
 
-template <int DT, int DPAD>
+template <int DT, int DPAD, int DE>
 static void launch_fwd_d(const AttnParams& p, bool causal, int grid, hipStream_t st) {
   if constexpr (DPAD >= 64) {
     if (p.q8) {   // E4M3 q and k (no dropout on this path)
-      if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, false, true>), dim3(grid), dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, false, true>), dim3(grid), dim3(256), 0, st, p);
+      if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, false, true, DE>), dim3(grid), dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, false, true, DE>), dim3(grid), dim3(256), 0, st, p);
       return;
     }
   }
   const bool drop = p.drop_t != 0;
-  if (causal && drop) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, true>), dim3(grid), dim3(256), 0, st, p);
-  else if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, false>), dim3(grid), dim3(256), 0, st, p);
-  else if (drop) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, true>), dim3(grid), dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, false>), dim3(grid), dim3(256), 0, st, p);
+  if (causal && drop) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, true, false, DE>), dim3(grid), dim3(256), 0, st, p);
+  else if (causal) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, true, false, false, DE>), dim3(grid), dim3(256), 0, st, p);
+  else if (drop) hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, true, false, DE>), dim3(grid), dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, false, false, DE>), dim3(grid), dim3(256), 0, st, p);
 }
 
+// the extent of the products: the head dim rounded up to 16 (to 32 above 128)
 template <int DT>
 static void launch_fwd_dt(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (p.d <= 32) launch_fwd_d<DT, 32>(p, causal, grid, st);
-  else if (p.d <= 64) launch_fwd_d<DT, 64>(p, causal, grid, st);
-  else if (p.d <= 128) launch_fwd_d<DT, 128>(p, causal, grid, st);
-  else launch_fwd_d<DT, 256>(p, causal, grid, st);
+  switch ((p.d + 15) >> 4) {
+    case 1: case 2: launch_fwd_d<DT, 32, 32>(p, causal, grid, st); break;
+    case 3: launch_fwd_d<DT, 64, 48>(p, causal, grid, st); break;
+    case 4: launch_fwd_d<DT, 64, 64>(p, causal, grid, st); break;
+    case 5: launch_fwd_d<DT, 128, 80>(p, causal, grid, st); break;
+    case 6: launch_fwd_d<DT, 128, 96>(p, causal, grid, st); break;
+    case 7: launch_fwd_d<DT, 128, 112>(p, causal, grid, st); break;
+    case 8: launch_fwd_d<DT, 128, 128>(p, causal, grid, st); break;
+    case 9: case 10: launch_fwd_d<DT, 256, 160>(p, causal, grid, st); break;
+    case 11: case 12: launch_fwd_d<DT, 256, 192>(p, causal, grid, st); break;
+    case 13: case 14: launch_fwd_d<DT, 256, 224>(p, causal, grid, st); break;
+    default: launch_fwd_d<DT, 256, 256>(p, causal, grid, st);
+  }
 }
 
 hipError_t launch_fwd(const AttnParams& p, int dtype, bool causal, int max_q_tiles, hipStream_t st) {

@@ -118,7 +118,8 @@ def _run_chunked(L, qcuts, kcuts, hq, hkv, d, dtype, seed):
 
 
 @pytest.mark.parametrize("d,dtype,hq,hkv", [(128, "bf16", 4, 2), (64, "fp16", 4, 2), (256, "bf16", 4, 2),
-                                            (128, "bf16", 8, 1), (256, "fp16", 16, 2)])
+                                            (128, "bf16", 8, 1), (256, "fp16", 16, 2), (96, "bf16", 4, 2),
+                                            (160, "fp16", 4, 2), (112, "bf16", 16, 2)])
 def test_chunked_causal_matches_whole(d, dtype, hq, hkv):
     """Groups of 8 and more query heads take the split dK/dV (partial planes
     summed, then added into the accumulated dk / dv)."""

@@ -89,7 +89,8 @@ def test_keep_mask_bit_exact_forward_and_dkdv(causal):
 
 @pytest.mark.parametrize("d,dtype,causal,p", [(64, "bf16", True, 0.1), (128, "bf16", False, 0.5),
                                               (128, "fp16", True, 0.2), (256, "bf16", True, 0.1),
-                                              (32, "bf16", False, 0.3)])
+                                              (32, "bf16", False, 0.3), (80, "fp16", True, 0.3),
+                                              (192, "fp16", False, 0.2)])
 def test_dropout_parity(d, dtype, causal, p):
     lq = [5, 130, 64, 0, 257, 33]
     lk = [5, 130, 64, 12, 257, 33] if causal else [9, 70, 64, 12, 300, 1]

@@ -47,6 +47,8 @@ CASES = [  # (hq, hkv, d, causal, dtype)
     (16, 2, 256, True, "bf16"),
     (8, 1, 32, "bottom_right", "bf16"),
     (64, 8, 96, True, "fp16"),
+    (8, 1, 80, "bottom_right", "bf16"),
+    (16, 2, 160, False, "fp16"),
 ]
 
 
