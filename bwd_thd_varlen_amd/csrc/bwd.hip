@@ -15,7 +15,7 @@
 //
 // dQ: one workgroup per (sequence, 128-query tile, query head): Q, dO,
 // LSE and Delta of its queries stay in registers while K/V steps stream
-// through LDS (head dims above 128: two waves per 32 queries, one holding Q
+// through LDS (head dims above 160: two waves per 32 queries, one holding Q
 // and one dO, each accumulating half of dQ); S and dP are recomputed here
 // instead of accumulating dQ across key-tile workgroups, which keeps every dQ
 // element owned by one workgroup.
@@ -127,11 +127,14 @@ __device__ __forceinline__ void store_dkdv_part(const AttnParams& p, float* dkp,
 // the head dim rounded up to 16, the extent of the products (tiles and
 // layouts keep the padded width DPAD)
 template <int DT, int DPAD, bool CAUSAL, bool ACC, bool DROP, int DE>
-__global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void dq_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
   static_assert(DE <= DPAD, "the products cover at most the padded head dim");
   constexpr int NT = (DE + 15) / 16;   // 16-wide k chunks of the products
   constexpr int NCB = (DE + 31) / 32;  // 32-column blocks of dQ
-  constexpr int KS = kKVStep;
+  // keys per step: 64 up to d = 128; 32 at the 192-wide tiles, so that two
+  // workgroups still fit a CU's LDS
+  constexpr int KS = DPAD <= 128 ? kKVStep : 32;
+  constexpr int NKB = KS / 32;         // 32-key halves per step
   using LK = Lay<DPAD, true>;          // K: row reads (S) and transposed reads (dQ)
   using LV = Lay<DPAD, false>;         // V: row reads (dP)
   using DmaK = TileDma<LK, KS, 4>;
@@ -243,10 +246,10 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
       // branch): key n0 + j is hidden from this lane's query while j > qk
       const bool diag_step = CAUSAL && n0 + KS - 1 > wq_lo_k;
       const int qk = qi_k - n0;
-      // the step's two 32-key halves one after the other (S, dP -> dS -> dQ
+      // the step's 32-key halves one after the other (S, dP -> dS -> dQ
       // part), so that only one half's score tiles are live at a time
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
         // dP accumulates onto -Delta (without dropout, which scales dP
         // alone), so the chain ends at dP - Delta
         f32x16 sc = zero16(), dp = zero16();
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
         // reaches them issues its MFMAs ahead of the other waves' softmax
         // arithmetic, which then fills the matrix pipe's shadow
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (DPAD == 128) {
+        if constexpr (DPAD >= 128) {
           // S and dP interleaved, each K / V operand read two MFMAs ahead
           // (pinned with scheduling barriers; left to itself the scheduler
           // waits on each read just before its MFMA)
@@ -317,9 +320,10 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
     store_dq<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d, 0, hh, acc);
 }
 
-// ----------------------------------------------------------------- dQ, head dims 136..256
-// Q, dO and the fp32 dQ accumulator of 32 queries take 256 registers at these
-// head dims, and 64-key K / V tiles 141 KB of LDS: one wave per SIMD.  Here
+// ----------------------------------------------------------------- dQ, head dims 168..256
+// Q, dO and the fp32 dQ accumulator of 32 queries outgrow 256 registers at
+// these head dims (up to 160 dq_kernel runs on 192-wide tiles), and 64-key
+// K / V tiles at d = 256 take 141 KB of LDS: one wave per SIMD.  Here
 // eight waves share the 128-query tile: waves 2 qb and 2 qb + 1 own query
 // block qb and split the head dim of dQ between them (64 accumulator
 // registers each).  Each 32-key step, wave 2 qb forms S^T = K Q^T from Q and
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(256, DPAD <= 64 ? 2 : (DPAD <= 128 ? 2 : 1)) void d
 // adds dS K over its own four column blocks.  K and V use the same padded
 // tile layout; both waves of a pair form Delta from dO and O (the same
 // arithmetic, so the same value).  Two barriers per step: the ring's, and the
-// one after the tiles are written.  DE (160, 192 or 256): the extent of the
+// one after the tiles are written.  DE (192 or 256): the extent of the
 // products; with an odd count of column blocks the even wave takes the extra
 // one.
 template <int DT, bool CAUSAL, bool ACC, bool DROP, int DE>
@@ -1102,8 +1106,9 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnParams p) {
 // ----------------------------------------------------------------- launchers
 // dropout is not combined with accumulation (the chunked entry points take none)
 // DE: the extent of the products, the head dim rounded up to 16 (split
-// kernels: to 160, 192 or 256; at 224 the odd column count spills); the k
-// chunks and column blocks past it hold no real column
+// kernels: dK/dV to 160, 192 or 256, dQ to 192 or 256; at 224 the odd column
+// count spills the split dK/dV); the k chunks and column blocks past it hold
+// no real column
 template <int DT, int DPAD, bool CAUSAL, int DE>
 static void launch_dq_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(256);
@@ -1128,11 +1133,8 @@ static void launch_dq_split_d(const AttnParams& p, bool causal, int grid, hipStr
 
 template <int DT>
 static void launch_dq_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  switch ((p.d + 31) >> 5) {
-    case 5: launch_dq_split_d<DT, 160>(p, causal, grid, st); break;
-    case 6: launch_dq_split_d<DT, 192>(p, causal, grid, st); break;
-    default: launch_dq_split_d<DT, 256>(p, causal, grid, st);
-  }
+  if (p.d <= 192) launch_dq_split_d<DT, 192>(p, causal, grid, st);
+  else launch_dq_split_d<DT, 256>(p, causal, grid, st);
 }
 
 template <int DT, int DPAD, int DE>
@@ -1151,6 +1153,10 @@ static void launch_dq_dt(const AttnParams& p, bool causal, int grid, hipStream_t
     case 6: launch_dq_d<DT, 128, 96>(p, causal, grid, st); break;
     case 7: launch_dq_d<DT, 128, 112>(p, causal, grid, st); break;
     case 8: launch_dq_d<DT, 128, 128>(p, causal, grid, st); break;
+    // head dims 136..160 on 192-wide tiles (at 176 and 192 Q, dO and the dQ
+    // accumulator outgrow the registers: the split kernel)
+    case 9: launch_dq_d<DT, 192, 144>(p, causal, grid, st); break;
+    case 10: launch_dq_d<DT, 192, 160>(p, causal, grid, st); break;
     default: launch_dq_split<DT>(p, causal, grid, st);
   }
 }
