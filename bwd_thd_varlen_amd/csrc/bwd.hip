@@ -797,13 +797,13 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
 // through LDS, so the two waves read the same S and dP and form the same P
 // and dS; then each forms dV += P^T dO and dK += dS^T Q over its own four
 // column blocks.  Two barriers per step: the ring's, and the one after the
-// tiles are written.  Steps, DMA ring, cursors, masks, dropout and the
-// split GQA group (PART) are those of dkdv_kernel with NW = 8, BM = 32, NBUF = 2.
-// DE (160, 192 or 256): the extent of the products; with an odd count of
-// column blocks the even wave of a pair takes the extra one.
+// tiles are written; waves 4..7 run half a step behind waves 0..3 (below).
+// Steps, cursors, masks, dropout and the split GQA group (PART) are those of
+// dkdv_kernel with NW = 8, BM = 32; the DMA ring holds three buffers.
+// DE (192 or 256): the extent of the products.
 template <int DT, bool CAUSAL, bool ACC, bool DROP, bool PART, int DE>
 __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
-  constexpr int DPAD = 256, NW = 8, BM = 32, NBUF = 2;
+  constexpr int DPAD = 256, NW = 8, BM = 32, NBUF = 3;
   constexpr int BN = 16 * NW;          // keys per workgroup: NW / 2 blocks of 32
   static_assert(BN == kKVTile, "the work lists are built for kKVTile keys per item");
   static_assert(DE % 32 == 0 && DE > 128 && DE <= DPAD, "products over whole 32-column blocks");
@@ -875,8 +875,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   int dc_hg = 0, dc_nrow = s.lq - (m_last - 1) * BM;
   const int64_t q_back = (int64_t)BM * qts + (int64_t)(ng - 1) * p.d;
   const int64_t v_back = (int64_t)BM * p.tsq * p.hq + (ng - 1);
-  auto issue = [&](int step) {
-    const uint32_t buf = (uint32_t)(step % NBUF);
+  // DMA of the next tile in the cursor's order into ring buffer `buf`
+  auto issue = [&](uint32_t buf) {
     const int nr = dc_nrow > BM ? BM : dc_nrow;
     dma_q.issue_rsrc(make_rsrc(qg + dc_q, (uint32_t)nr * q_rs_bytes), lds_q + buf * (uint32_t)sizeof(sQ[0]),
                      lds_sink, wave);
@@ -893,9 +893,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
       dc_v += 1;
     }
   };
-#pragma unroll
-  for (int k = 0; k < NBUF - 1; ++k)
-    if (k < nsteps) issue(k);
+  // waves 4..7 run half a step behind waves 0..3 (see the loop)
+  const int late = wave >= NW / 2 ? 1 : 0;
+  for (int j = 0; j <= late; ++j)
+    if (j < nsteps) issue((uint32_t)j);
+  // ring buffer of the next tile this wave issues
+  uint32_t ibuf = (uint32_t)late + 1u;
 
   // the full-width operand of this wave's product: K (even waves) or V (odd)
   const uint16_t* kvb = reinterpret_cast<const uint16_t*>(half ? p.v : p.k) + kvoff;
@@ -914,11 +917,30 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
     adv[cb] = zero16();
   }
 
+  // Waves 4..7 (key blocks 2, 3) run half a step behind waves 0..3: they
+  // take one barrier before the loop (waves 0..3 one after it), so that a
+  // late wave forms its tiles while the early wave on its SIMD (wave w - 4)
+  // finishes its step, and finishes while that one forms the next step's
+  // tiles: the softmax arithmetic of one runs under the products of the
+  // other (in the same phase the matrix pipe idled through it).  Each wave
+  // issues its share of a Q / dO tile's DMA at the start of its own step and
+  // waits for it before the barrier that precedes the tile's first read: the
+  // early waves tile step + 1 (first read after their next ring barrier),
+  // the late waves tile step + 2 (after their exchange barrier of step + 1).
+  // A tile is read until the late waves' ring barrier of the next step,
+  // hence a ring of three.
+  if (late) {
+    wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1));
+    barrier_lds_writes();
+  }
   int cm = m_last - 1, chg = 0;
   for (int step = 0; step < nsteps; ++step) {
-    wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1 - step));
-    barrier_lds_dma();
-    if (step + NBUF - 1 < nsteps) issue(step + NBUF - 1);
+    // early waves: this step's tile has landed; late waves: the early waves'
+    // S^T / dP^T tiles are in LDS
+    if (!late) wait_vm<0>();
+    barrier_lds_writes();
+    if (step + 1 + late < nsteps) issue(ibuf);
+    ibuf = ibuf == NBUF - 1 ? 0u : ibuf + 1u;
     const int buf = step % NBUF;
     const uint32_t tq = lds_q + (uint32_t)buf * (uint32_t)sizeof(sQ[0]);
     const uint32_t tdo = lds_do + (uint32_t)buf * (uint32_t)sizeof(sdO[0]);
@@ -932,8 +954,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
     // both waves of a key block are active or idle together
     const bool active = wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q);
     if (active) {
-      // S^T (even wave) or dP^T onto -Delta (odd wave), operands read two
-      // MFMAs ahead
+      // S^T (even wave) or dP^T onto -Delta (odd wave), into sX; operands
+      // read two MFMAs ahead
       constexpr int PD = 2;
       const RowReader<LQ> rd(half ? tdo : tq, lane);
       f32x16 acc;
@@ -961,7 +983,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
       for (int q4 = 0; q4 < 4; ++q4)
         sX[wave][q4][lane] = (f32x4){acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
     }
-    // the tiles are in LDS for the partner (the ring's DMA may still run)
+    // late waves: the next step's tile has landed (the one after may still
+    // be in flight)
+    if (late) wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 2 - step));
+    // the pair's tiles are in LDS (the ring's DMA runs on across the barrier)
     barrier_lds_writes();
     if (active) {
       f32x16 sc, dp;
@@ -1039,6 +1064,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if (!late) barrier_lds_writes();
 
   if (kj < s.lk) {
     const int64_t row = (int64_t)kj * kvts;
@@ -1106,9 +1132,9 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnParams p) {
 // ----------------------------------------------------------------- launchers
 // dropout is not combined with accumulation (the chunked entry points take none)
 // DE: the extent of the products, the head dim rounded up to 16 (split
-// kernels: dK/dV to 160, 192 or 256, dQ to 192 or 256; at 224 the odd column
-// count spills the split dK/dV); the k chunks and column blocks past it hold
-// no real column
+// kernels: to 192 or 256; with an odd count of column blocks, 160 or 224, the
+// uneven halves of a wave pair ran slower than the 192-wide products, or
+// spilled); the k chunks and column blocks past it hold no real column
 template <int DT, int DPAD, bool CAUSAL, int DE>
 static void launch_dq_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(256);
@@ -1206,11 +1232,8 @@ static void launch_dkdv_split_d(const AttnParams& p, bool causal, int grid, hipS
 
 template <int DT>
 static void launch_dkdv_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  switch ((p.d + 31) >> 5) {
-    case 5: launch_dkdv_split_d<DT, 160>(p, causal, grid, st); break;
-    case 6: launch_dkdv_split_d<DT, 192>(p, causal, grid, st); break;
-    default: launch_dkdv_split_d<DT, 256>(p, causal, grid, st);
-  }
+  if (p.d <= 192) launch_dkdv_split_d<DT, 192>(p, causal, grid, st);
+  else launch_dkdv_split_d<DT, 256>(p, causal, grid, st);
 }
 
 // a split group writes partial planes; dropout and accumulation then act in
