@@ -15,7 +15,7 @@
 //
 // dQ: one workgroup per (sequence, 128-query tile, query head): Q, dO,
 // LSE and Delta of its queries stay in registers while K/V steps stream
-// through LDS (head dims above 160: two waves per 32 queries, one holding Q
+// through LDS (head dims above 176: two waves per 32 queries, one holding Q
 // and one dO, each accumulating half of dQ); S and dP are recomputed here
 // instead of accumulating dQ across key-tile workgroups, which keeps every dQ
 // element owned by one workgroup.
@@ -136,7 +136,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
   constexpr int KS = DPAD <= 128 ? kKVStep : 32;
   constexpr int NKB = KS / 32;         // 32-key halves per step
   using LK = Lay<DPAD, true>;          // K: row reads (S) and transposed reads (dQ)
-  using LV = Lay<DPAD, false>;         // V: row reads (dP)
+  // V: row reads (dP); at the 192-wide tiles in K's layout, so that both
+  // tiles' DMA share one set of lane offsets (registers are that tight there)
+  using LV = std::conditional_t<DPAD == 192, Lay<DPAD, true>, Lay<DPAD, false>>;
   using DmaK = TileDma<LK, KS, 4>;
   using DmaV = TileDma<LV, KS, 4>;
 
@@ -264,8 +266,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
         if constexpr (DPAD >= 128) {
           // S and dP interleaved, each K / V operand read two MFMAs ahead
           // (pinned with scheduling barriers; left to itself the scheduler
-          // waits on each read just before its MFMA)
-          constexpr int PD = 2;
+          // waits on each read just before its MFMA); one ahead above 160
+          // columns, where Q, dO and the dQ accumulator leave no room for more
+          constexpr int PD = DE > 160 ? 1 : 2;
           u32x4 ak[NT], av[NT];
 #pragma unroll
           for (int t = 0; t < PD; ++t) {
@@ -320,9 +323,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
     store_dq<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d, 0, hh, acc);
 }
 
-// ----------------------------------------------------------------- dQ, head dims 168..256
+// ----------------------------------------------------------------- dQ, head dims 184..256
 // Q, dO and the fp32 dQ accumulator of 32 queries outgrow 256 registers at
-// these head dims (up to 160 dq_kernel runs on 192-wide tiles), and 64-key
+// these head dims (up to 176 dq_kernel runs on 192-wide tiles), and 64-key
 // K / V tiles at d = 256 take 141 KB of LDS: one wave per SIMD.  Here
 // eight waves share the 128-query tile: waves 2 qb and 2 qb + 1 own query
 // block qb and split the head dim of dQ between them (64 accumulator
@@ -1179,10 +1182,11 @@ static void launch_dq_dt(const AttnParams& p, bool causal, int grid, hipStream_t
     case 6: launch_dq_d<DT, 128, 96>(p, causal, grid, st); break;
     case 7: launch_dq_d<DT, 128, 112>(p, causal, grid, st); break;
     case 8: launch_dq_d<DT, 128, 128>(p, causal, grid, st); break;
-    // head dims 136..160 on 192-wide tiles (at 176 and 192 Q, dO and the dQ
+    // head dims 136..176 on 192-wide tiles (at 192 Q, dO and the dQ
     // accumulator outgrow the registers: the split kernel)
     case 9: launch_dq_d<DT, 192, 144>(p, causal, grid, st); break;
     case 10: launch_dq_d<DT, 192, 160>(p, causal, grid, st); break;
+    case 11: launch_dq_d<DT, 192, 176>(p, causal, grid, st); break;
     default: launch_dq_split<DT>(p, causal, grid, st);
   }
 }
