@@ -15,7 +15,7 @@
 //
 // dQ: one workgroup per (sequence, 128-query tile, query head): Q, dO,
 // LSE and Delta of its queries stay in registers while K/V steps stream
-// through LDS (head dims above 176: two waves per 32 queries, one holding Q
+// through LDS (head dims above 192: two waves per 32 queries, one holding Q
 // and one dO, each accumulating half of dQ); S and dP are recomputed here
 // instead of accumulating dQ across key-tile workgroups, which keeps every dQ
 // element owned by one workgroup.
@@ -263,11 +263,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
         // reaches them issues its MFMAs ahead of the other waves' softmax
         // arithmetic, which then fills the matrix pipe's shadow
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (DPAD >= 128) {
+        if constexpr (DPAD >= 128 && DE <= 176) {
           // S and dP interleaved, each K / V operand read two MFMAs ahead
           // (pinned with scheduling barriers; left to itself the scheduler
           // waits on each read just before its MFMA); one ahead above 160
           // columns, where Q, dO and the dQ accumulator leave no room for more
+          // (at 192 the operands are left to the scheduler, which keeps the
+          // DMA lane offsets in registers)
           constexpr int PD = DE > 160 ? 1 : 2;
           u32x4 ak[NT], av[NT];
 #pragma unroll
@@ -323,9 +325,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
     store_dq<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d, 0, hh, acc);
 }
 
-// ----------------------------------------------------------------- dQ, head dims 184..256
+// ----------------------------------------------------------------- dQ, head dims 200..256
 // Q, dO and the fp32 dQ accumulator of 32 queries outgrow 256 registers at
-// these head dims (up to 176 dq_kernel runs on 192-wide tiles), and 64-key
+// these head dims (up to 192 dq_kernel runs on 192-wide tiles), and 64-key
 // K / V tiles at d = 256 take 141 KB of LDS: one wave per SIMD.  Here
 // eight waves share the 128-query tile: waves 2 qb and 2 qb + 1 own query
 // block qb and split the head dim of dQ between them (64 accumulator
@@ -335,9 +337,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
 // adds dS K over its own four column blocks.  K and V use the same padded
 // tile layout; both waves of a pair form Delta from dO and O (the same
 // arithmetic, so the same value).  Two barriers per step: the ring's, and the
-// one after the tiles are written.  DE (192 or 256): the extent of the
-// products; with an odd count of column blocks the even wave takes the extra
-// one.
+// one after the tiles are written.  DE (256): the extent of the products.
 template <int DT, bool CAUSAL, bool ACC, bool DROP, int DE>
 __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
   constexpr int DPAD = 256, NW = 8, KS = 32;
@@ -1134,10 +1134,10 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnParams p) {
 
 // ----------------------------------------------------------------- launchers
 // dropout is not combined with accumulation (the chunked entry points take none)
-// DE: the extent of the products, the head dim rounded up to 16 (split
-// kernels: to 192 or 256; with an odd count of column blocks, 160 or 224, the
-// uneven halves of a wave pair ran slower than the 192-wide products, or
-// spilled); the k chunks and column blocks past it hold no real column
+// DE: the extent of the products, the head dim rounded up to 16 (split dK/dV:
+// to 192 or 256; with an odd count of column blocks, 160 or 224, the uneven
+// halves of a wave pair ran slower than the 192-wide products, or spilled);
+// the k chunks and column blocks past it hold no real column
 template <int DT, int DPAD, bool CAUSAL, int DE>
 static void launch_dq_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(256);
@@ -1162,8 +1162,7 @@ static void launch_dq_split_d(const AttnParams& p, bool causal, int grid, hipStr
 
 template <int DT>
 static void launch_dq_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (p.d <= 192) launch_dq_split_d<DT, 192>(p, causal, grid, st);
-  else launch_dq_split_d<DT, 256>(p, causal, grid, st);
+  launch_dq_split_d<DT, 256>(p, causal, grid, st);
 }
 
 template <int DT, int DPAD, int DE>
@@ -1182,11 +1181,12 @@ static void launch_dq_dt(const AttnParams& p, bool causal, int grid, hipStream_t
     case 6: launch_dq_d<DT, 128, 96>(p, causal, grid, st); break;
     case 7: launch_dq_d<DT, 128, 112>(p, causal, grid, st); break;
     case 8: launch_dq_d<DT, 128, 128>(p, causal, grid, st); break;
-    // head dims 136..176 on 192-wide tiles (at 192 Q, dO and the dQ
+    // head dims 136..192 on 192-wide tiles (above, Q, dO and the dQ
     // accumulator outgrow the registers: the split kernel)
     case 9: launch_dq_d<DT, 192, 144>(p, causal, grid, st); break;
     case 10: launch_dq_d<DT, 192, 160>(p, causal, grid, st); break;
     case 11: launch_dq_d<DT, 192, 176>(p, causal, grid, st); break;
+    case 12: launch_dq_d<DT, 192, 192>(p, causal, grid, st); break;
     default: launch_dq_split<DT>(p, causal, grid, st);
   }
 }
