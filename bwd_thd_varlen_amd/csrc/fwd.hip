@@ -267,7 +267,7 @@ static void launch_fwd_d(const AttnParams& p, bool causal, int grid, hipStream_t
   else hipLaunchKernelGGL((fwd_kernel<DT, DPAD, false, false, false, DE>), dim3(grid), dim3(256), 0, st, p);
 }
 
-// the extent of the products: the head dim rounded up to 16 (to 32 above 128)
+// the extent of the products: the head dim rounded up to 16
 template <int DT>
 static void launch_fwd_dt(const AttnParams& p, bool causal, int grid, hipStream_t st) {
   switch ((p.d + 15) >> 4) {
@@ -278,9 +278,13 @@ static void launch_fwd_dt(const AttnParams& p, bool causal, int grid, hipStream_
     case 6: launch_fwd_d<DT, 128, 96>(p, causal, grid, st); break;
     case 7: launch_fwd_d<DT, 128, 112>(p, causal, grid, st); break;
     case 8: launch_fwd_d<DT, 128, 128>(p, causal, grid, st); break;
-    case 9: case 10: launch_fwd_d<DT, 256, 160>(p, causal, grid, st); break;
-    case 11: case 12: launch_fwd_d<DT, 256, 192>(p, causal, grid, st); break;
-    case 13: case 14: launch_fwd_d<DT, 256, 224>(p, causal, grid, st); break;
+    case 9: launch_fwd_d<DT, 256, 144>(p, causal, grid, st); break;
+    case 10: launch_fwd_d<DT, 256, 160>(p, causal, grid, st); break;
+    case 11: launch_fwd_d<DT, 256, 176>(p, causal, grid, st); break;
+    case 12: launch_fwd_d<DT, 256, 192>(p, causal, grid, st); break;
+    case 13: launch_fwd_d<DT, 256, 208>(p, causal, grid, st); break;
+    case 14: launch_fwd_d<DT, 256, 224>(p, causal, grid, st); break;
+    case 15: launch_fwd_d<DT, 256, 240>(p, causal, grid, st); break;
     default: launch_fwd_d<DT, 256, 256>(p, causal, grid, st);
   }
 }
