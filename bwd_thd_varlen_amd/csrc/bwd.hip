@@ -803,16 +803,19 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
 // tiles are written; waves 4..7 run half a step behind waves 0..3 (below).
 // Steps, cursors, masks, dropout and the split GQA group (PART) are those of
 // dkdv_kernel with NW = 8, BM = 32; the DMA ring holds three buffers.
-// DE (192 or 256): the extent of the products.
+// DE: the extent of the S / dP products (the head dim rounded up to 16); dK
+// and dV cover it in an even count of 32-column blocks.
 template <int DT, bool CAUSAL, bool ACC, bool DROP, bool PART, int DE>
 __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   constexpr int DPAD = 256, NW = 8, BM = 32, NBUF = 3;
   constexpr int BN = 16 * NW;          // keys per workgroup: NW / 2 blocks of 32
   static_assert(BN == kKVTile, "the work lists are built for kKVTile keys per item");
-  static_assert(DE % 32 == 0 && DE > 128 && DE <= DPAD, "products over whole 32-column blocks");
-  constexpr int NT = DE / 16;          // 16-wide k chunks of the products
-  constexpr int NCB = DE / 32;         // 32-column blocks of dK and dV
-  constexpr int NCBH = (NCB + 1) / 2;  // blocks of the even wave of a pair (the odd one: NCB - NCBH)
+  static_assert(DE % 16 == 0 && DE > 128 && DE <= DPAD, "products over whole 16-wide k chunks");
+  constexpr int NT = DE / 16;          // 16-wide k chunks of the S / dP products
+  // 32-column blocks of dK and dV: an even count, so that the two waves of a
+  // pair take equal shares (a block past the head dim adds zeros)
+  constexpr int NCB = 2 * ((DE + 63) / 64);
+  constexpr int NCBH = NCB / 2;        // blocks of each wave of a pair
   constexpr int NU = BM / 16;          // 16-query chunks per step
   using LQ = Lay<DPAD, true>;          // Q, dO: row reads (S, dP) and transposed reads (dK, dV)
   using Dma = TileDma<LQ, BM, NW>;
@@ -1134,10 +1137,9 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(AttnParams p) {
 
 // ----------------------------------------------------------------- launchers
 // dropout is not combined with accumulation (the chunked entry points take none)
-// DE: the extent of the products, the head dim rounded up to 16 (split dK/dV:
-// to 192 or 256; with an odd count of column blocks, 160 or 224, the uneven
-// halves of a wave pair ran slower than the 192-wide products, or spilled);
-// the k chunks and column blocks past it hold no real column
+// DE: the extent of the products, the head dim rounded up to 16 (the split
+// dK/dV takes its column blocks in pairs); the k chunks and column blocks
+// past it hold no real column
 template <int DT, int DPAD, bool CAUSAL, int DE>
 static void launch_dq_c(const AttnParams& p, int grid, hipStream_t st) {
   const dim3 g(grid), blk(256);
@@ -1236,8 +1238,16 @@ static void launch_dkdv_split_d(const AttnParams& p, bool causal, int grid, hipS
 
 template <int DT>
 static void launch_dkdv_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  if (p.d <= 192) launch_dkdv_split_d<DT, 192>(p, causal, grid, st);
-  else launch_dkdv_split_d<DT, 256>(p, causal, grid, st);
+  switch ((p.d + 15) >> 4) {
+    case 9: launch_dkdv_split_d<DT, 144>(p, causal, grid, st); break;
+    case 10: launch_dkdv_split_d<DT, 160>(p, causal, grid, st); break;
+    case 11: launch_dkdv_split_d<DT, 176>(p, causal, grid, st); break;
+    case 12: launch_dkdv_split_d<DT, 192>(p, causal, grid, st); break;
+    case 13: launch_dkdv_split_d<DT, 208>(p, causal, grid, st); break;
+    case 14: launch_dkdv_split_d<DT, 224>(p, causal, grid, st); break;
+    case 15: launch_dkdv_split_d<DT, 240>(p, causal, grid, st); break;
+    default: launch_dkdv_split_d<DT, 256>(p, causal, grid, st);
+  }
 }
 
 // a split group writes partial planes; dropout and accumulation then act in
