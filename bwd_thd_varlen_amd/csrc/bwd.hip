@@ -337,14 +337,18 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
 // adds dS K over its own four column blocks.  K and V use the same padded
 // tile layout; both waves of a pair form Delta from dO and O (the same
 // arithmetic, so the same value).  Two barriers per step: the ring's, and the
-// one after the tiles are written.  DE (256): the extent of the products.
+// one after the tiles are written.  DE: the extent of the S / dP products
+// (the head dim rounded up to 16); dQ covers it in an even count of
+// 32-column blocks.
 template <int DT, bool CAUSAL, bool ACC, bool DROP, int DE>
 __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
   constexpr int DPAD = 256, NW = 8, KS = 32;
-  static_assert(DE % 32 == 0 && DE > 128 && DE <= DPAD, "products over whole 32-column blocks");
-  constexpr int NT = DE / 16;          // 16-wide k chunks of the products
-  constexpr int NCB = DE / 32;         // 32-column blocks of dQ
-  constexpr int NCBH = (NCB + 1) / 2;  // blocks of the even wave of a pair (the odd one: NCB - NCBH)
+  static_assert(DE % 16 == 0 && DE > 128 && DE <= DPAD, "products over whole 16-wide k chunks");
+  constexpr int NT = DE / 16;          // 16-wide k chunks of the S / dP products
+  // 32-column blocks of dQ: an even count, so that the two waves of a pair
+  // take equal shares (a block past the head dim adds zeros)
+  constexpr int NCB = 2 * ((DE + 63) / 64);
+  constexpr int NCBH = NCB / 2;        // blocks of each wave of a pair
   using LK = Lay<DPAD, true>;          // K and V: row reads (S, dP); K also transposed (dQ)
   using Dma = TileDma<LK, KS, NW>;
 
@@ -1164,7 +1168,12 @@ static void launch_dq_split_d(const AttnParams& p, bool causal, int grid, hipStr
 
 template <int DT>
 static void launch_dq_split(const AttnParams& p, bool causal, int grid, hipStream_t st) {
-  launch_dq_split_d<DT, 256>(p, causal, grid, st);
+  switch ((p.d + 15) >> 4) {
+    case 13: launch_dq_split_d<DT, 208>(p, causal, grid, st); break;
+    case 14: launch_dq_split_d<DT, 224>(p, causal, grid, st); break;
+    case 15: launch_dq_split_d<DT, 240>(p, causal, grid, st); break;
+    default: launch_dq_split_d<DT, 256>(p, causal, grid, st);
+  }
 }
 
 template <int DT, int DPAD, int DE>
