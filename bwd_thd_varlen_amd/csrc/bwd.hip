@@ -351,9 +351,12 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
   constexpr int NCBH = NCB / 2;        // blocks of each wave of a pair
   using LK = Lay<DPAD, true>;          // K and V: row reads (S, dP); K also transposed (dQ)
   using Dma = TileDma<LK, KS, NW>;
+  constexpr int NBUF = 3;
+  constexpr int DMA_PER_STEP = 2 * Dma::PER_WAVE;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][LK::template elems<KS>()];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][LK::template elems<KS>()];
+  __shared__ __attribute__((aligned(16))) uint16_t sSink[Dma::SINK ? 512 : 8];
   // the S^T (even wave) and dP^T (odd wave) tiles of each query block, as the
   // 16 accumulator registers of every lane: [wave][register / 4][lane]
   __shared__ __attribute__((aligned(16))) f32x4 sX[NW][4][64];
@@ -393,13 +396,21 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
 
   Dma dma;
   dma.init(wave, lane, p.d, kv_rs_bytes);
-  auto issue = [&](int step) {
-    const uint32_t buf = (uint32_t)(step & 1);
+  // every wave issues the same number of DMAs per tile (sink DMAs fill up
+  // the uneven split), so that each can wait for a given step's share
+  auto issue = [&](int step, uint32_t buf) {
     const int n0 = step * KS;
-    dma.issue_exact(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sK[0]) + buf * sizeof(sK[0]), wave);
-    dma.issue_exact(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sV[0]) + buf * sizeof(sV[0]), wave);
+    dma.issue(kb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sK[0]) + buf * (uint32_t)sizeof(sK[0]),
+              lds_addr(sSink), wave);
+    dma.issue(vb + (int64_t)n0 * kvts, kend - n0, kv_rs_bytes, lds_addr(sV[0]) + buf * (uint32_t)sizeof(sV[0]),
+              lds_addr(sSink), wave);
   };
-  if (nsteps > 0) issue(0);
+  // waves 4..7 run half a step behind waves 0..3 (see the loop)
+  const int late = wave >= NW / 2 ? 1 : 0;
+  for (int j = 0; j <= late; ++j)
+    if (j < nsteps) issue(j, (uint32_t)j);
+  // ring buffer of the next tile this wave issues
+  uint32_t ibuf = (uint32_t)late + 1u;
 
   // this wave's operand (Q on even waves, dO on odd) stays in registers;
   // Delta = sum_c dO_c O_c in fp32 over the two halves of the wave
@@ -439,12 +450,25 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
   const int cb0 = half * NCBH;
   const int nb = half ? NCB - NCBH : NCBH;
 
+  // Waves 4..7 (query blocks 2, 3) run half a step behind waves 0..3, as in
+  // dkdv_split_kernel: one barrier more before the loop (waves 0..3 one after
+  // it), each wave issuing its share of a K / V tile at the start of its own
+  // step (early waves tile step + 1, late ones step + 2) and waiting for it
+  // before the barrier that precedes the tile's first read; a ring of three.
+  if (late) {
+    wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 1));
+    barrier_lds_writes();
+  }
   for (int step = 0; step < nsteps; ++step) {
-    wait_vm<0>();
-    barrier_lds_dma();
-    if (step + 1 < nsteps) issue(step + 1);
-    const uint32_t tk = lds_addr(sK[0]) + (uint32_t)(step & 1) * (uint32_t)sizeof(sK[0]);
-    const uint32_t tv = lds_addr(sV[0]) + (uint32_t)(step & 1) * (uint32_t)sizeof(sV[0]);
+    // early waves: this step's tile has landed; late waves: the early waves'
+    // S^T / dP^T tiles are in LDS
+    if (!late) wait_vm<0>();
+    barrier_lds_writes();
+    if (step + 1 + late < nsteps) issue(step + 1 + late, ibuf);
+    ibuf = ibuf == NBUF - 1 ? 0u : ibuf + 1u;
+    const int buf = step % NBUF;
+    const uint32_t tk = lds_addr(sK[0]) + (uint32_t)buf * (uint32_t)sizeof(sK[0]);
+    const uint32_t tv = lds_addr(sV[0]) + (uint32_t)buf * (uint32_t)sizeof(sV[0]);
     const int n0 = step * KS;
     // both waves of a query block are active or idle together
     const bool active = wq_lo < s.lq && !(CAUSAL && n0 > wq_hi_k);
@@ -472,7 +496,10 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
       for (int q4 = 0; q4 < 4; ++q4)
         sX[wave][q4][lane] = (f32x4){t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2], t16[4 * q4 + 3]};
     }
-    // the tiles are in LDS for the partner (the ring's DMA may still run)
+    // late waves: the next step's tile has landed (the one after may still
+    // be in flight)
+    if (late) wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 2 - step));
+    // the pair's tiles are in LDS (the ring's DMA runs on across the barrier)
     barrier_lds_writes();
     if (active) {
       f32x16 sc, dp;
@@ -511,6 +538,7 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
         if (cb < nb) acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 1), b1, acc[cb]);
     }
   }
+  if (!late) barrier_lds_writes();
 
   if (qvalid)
     store_dq<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dq) + qrow * qrs + (int64_t)h * p.d, cb0, hh, acc, nb);
