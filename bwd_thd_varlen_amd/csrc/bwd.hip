@@ -337,7 +337,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
 // adds dS K over its own four column blocks.  K and V use the same padded
 // tile layout; both waves of a pair form Delta from dO and O (the same
 // arithmetic, so the same value).  Two barriers per step: the ring's, and the
-// one after the tiles are written.  DE: the extent of the S / dP products
+// one after the tiles are written; waves 4..7 run half a step behind waves
+// 0..3 (below).  DE: the extent of the S / dP products
 // (the head dim rounded up to 16); dQ covers it in an even count of
 // 32-column blocks.
 template <int DT, bool CAUSAL, bool ACC, bool DROP, int DE>
