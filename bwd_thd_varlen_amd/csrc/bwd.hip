@@ -21,16 +21,19 @@
 // element owned by one workgroup.
 //
 // Both kernels fill LDS tiles by global->LDS DMA ahead of the compute (see
-// TileDma in common.h): dQ double-buffers one step ahead, dK/dV uses a ring.
+// TileDma in common.h): dQ double-buffers one step ahead, dK/dV uses a ring
+// (the split kernels, one workgroup per CU, a ring of three with half their
+// waves half a step behind the others).
 //
 // Layout tricks are those of the forward kernel (common.h): score tiles are
 // computed so that the lane index runs over the dimension that survives the
 // next product, and the operand that contracts over a tile's rows is read
 // from the same row-major LDS tile with the transpose read.
 //
-// Head dims below the padded tile width: the products run over the head dim
-// rounded up to 16 (160, 192 or 256 for the split kernels) and skip the
-// column blocks of the outputs past it, whose operands are zero.
+// Head dims below the padded tile width (32, 64, 128, 192 or 256 columns):
+// the products run over the head dim rounded up to 16 and skip the column
+// blocks of the outputs past it, whose operands are zero (the split kernels
+// keep their output blocks in pairs).
 #include "common.h"
 
 namespace attn {
