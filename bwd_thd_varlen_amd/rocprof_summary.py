@@ -19,9 +19,12 @@ Two modes, each run on the databases a GPU run left behind:
       bench.py reports the traffic only while that hash matches.
 
   python -m bwd_thd_varlen_amd.rocprof_summary counters OUT.txt DB [DB ...] --command CMD [...]
+          [--workload throughput_65k|d256_65k]
       shader-sequencer counters of the three compute kernels from one or more
       ``rocprofv3 --pmc`` runs (at most 8 SQ counters per run), averaged per
-      dispatch, with the wave-cycle ratios they give.
+      dispatch, with the wave-cycle ratios they give.  ``--workload d256_65k``
+      picks the head-dim-256 kernels (the split dQ and dK/dV kernels) instead
+      of the d=128 ones.
 
 Reads SQLite files only; nothing here touches the GPU.
 """
@@ -51,6 +54,12 @@ STAGE_KERNELS = {
     "fwd": "void attn::fwd_kernel<0, 128, true",
     "dq": "void attn::dq_kernel<0, 128, true",
     "dkdv": "void attn::dkdv_kernel<0, 128, true",
+}
+# the same for the head-dim-256 workload (split dQ and dK/dV kernels)
+STAGE_KERNELS_D256 = {
+    "fwd": "void attn::fwd_kernel<0, 256, true",
+    "dq": "void attn::dq_split_kernel<0, true",
+    "dkdv": "void attn::dkdv_split_kernel<0, true",
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30          # bench.py --copy-calibration: 1 GiB copies
@@ -188,18 +197,20 @@ LDS_RATIOS = [
 XCDS = 8   # GRBM counters are summed over the accelerator's 8 XCDs
 
 
-def counters(out: str, dbs, commands) -> None:
+def counters(out: str, dbs, commands, workload: str = "throughput_65k") -> None:
+    kernels = STAGE_KERNELS_D256 if workload == "d256_65k" else STAGE_KERNELS
     vals = defaultdict(lambda: defaultdict(list))
     durs = defaultdict(list)
     for db in dbs:
         for name, counter, value, dur in _rows(db, "select kernel_name, counter_name, value, "
                                                    "duration from counters_collection"):
-            for stage, prefix in STAGE_KERNELS.items():
+            for stage, prefix in kernels.items():
                 if name.startswith(prefix):
                     vals[stage][counter].append(float(value))
                     durs[stage].append(float(dur))
     names = sorted({c for st in vals.values() for c in st})
-    lines = ["# Shader-sequencer counters: throughput_65k workload, per dispatch (average)",
+    lines = [f"# Shader-sequencer counters: {workload} workload, per dispatch (average)",
+             "# kernels: " + ", ".join(f"{st} = {pre.split('attn::')[1]}..." for st, pre in kernels.items()),
              "# Counter runs, from the repository root on one MI355X (TMPDIR=/tmp):"]
     lines += [f"#   {c}" for c in commands]
     for stage in STAGE_KERNELS:
@@ -255,9 +266,10 @@ def main(argv=None) -> None:
     k.add_argument("out")
     k.add_argument("dbs", nargs="+")
     k.add_argument("--command", action="append", required=True)
+    k.add_argument("--workload", default="throughput_65k", choices=["throughput_65k", "d256_65k"])
     a = ap.parse_args(argv)
     if a.mode == "counters":
-        counters(a.out, a.dbs, a.command)
+        counters(a.out, a.dbs, a.command, a.workload)
     elif a.mode == "trace":
         trace(a.db, a.out, a.command, a.title)
     else:

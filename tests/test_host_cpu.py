@@ -159,6 +159,21 @@ def test_counter_summary_lds_conflicts_and_clock(tmp_path):
     assert row.rstrip().endswith("| - | - | 1.60 GHz |")
 
 
+def test_counter_summary_d256_picks_the_split_kernels(tmp_path):
+    """With the head-dim-256 workload the dq / dkdv columns come from the
+    split kernels; d=128 kernels in the same database are not counted."""
+    split_dkdv = rs.STAGE_KERNELS_D256["dkdv"] + ", false, false, false, 256>(attn::AttnParams)"
+    db = str(tmp_path / "c.db")
+    _db(db, counters=[(split_dkdv, "SQ_WAVE_CYCLES", 1000.0), (split_dkdv, "SQ_WAIT_INST_LDS", 250.0),
+                      (DKDV, "SQ_WAVE_CYCLES", 1000.0), (DKDV, "SQ_WAIT_INST_LDS", 900.0)])
+    out = str(tmp_path / "c.txt")
+    rs.counters(out, [db], ["CMD"], workload="d256_65k")
+    text = open(out).read()
+    assert text.startswith("# Shader-sequencer counters: d256_65k workload")
+    row = next(l for l in text.splitlines() if l.startswith("| waiting on LDS"))
+    assert row.rstrip().endswith("| - | - | 25.0% |")
+
+
 def test_source_hash_ignores_comments():
     """Comments and blank lines do not change the code hash of a stage; code does."""
     src = "int a; // one\n/* two\n three */\nint b;   \n\n"
