@@ -296,6 +296,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(AttnParams p) {
             sc = Mfma<DT>::mma(rk.read(kb2, t), qreg[t], sc);
             dp = Mfma<DT>::mma(rv.read(kb2, t), doreg[t], dp);
           }
+          // both chains end here: in the loop without the causal branch the
+          // scheduler otherwise defers the dP products behind the softmax, and
+          // at 192 columns Q and dO then spill and are reloaded every step
+          if constexpr (DPAD == 192) asm volatile("" : "+v"(sc), "+v"(dp));
         }
         __builtin_amdgcn_s_setprio(0);
         if constexpr (DROP) {
@@ -758,25 +762,24 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
           if (kq > 8 * (r >> 2) + 4 * hh + (r & 3)) sc[r] = 0.f;
       }
       // the key column of the 4 x 4 blocks at queries 8 q4 + 4 hh (+0..3):
-      // this lane's Philox block (4 x 4: element (i, j) is byte j & 3 of word
-      // i & 3); the block of quad lane g is broadcast when q4 = g, so only
-      // four words are live at a time
+      // this lane computes the Philox block of q4 = li & 3 (4 x 4: element
+      // (i, j) is byte j & 3 of word i & 3); byte and quad transposes leave
+      // in slot q4 this lane's key byte (j & 3 = li & 3) of that block's four
+      // query rows, byte c for row c
       u32x4 mine;
-      if constexpr (DROP) mine = dropout_block(p, w.b, h_step, ((i0 + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2);
+      if constexpr (DROP)
+        mine = quad_transpose(
+            byte_transpose(dropout_block(p, w.b, h_step, ((i0 + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2)), li & 3);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
-        u32x4 x;
-        if constexpr (DROP)
-          x = (u32x4){quad_bcast_at(mine[0], q4), quad_bcast_at(mine[1], q4), quad_bcast_at(mine[2], q4),
-                      quad_bcast_at(mine[3], q4)};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * q4 + c;
           const float pr = sc[r];
           if constexpr (DROP) {
             // P o D for dV, and dS = P o (D o dP - Delta)
-            const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;
+            const float dsc = keep_byte(mine[q4], c, p.drop_t) ? p.drop_scale : 0.f;
             sc[r] = pr * dsc;
             dp[r] = pr * __builtin_fmaf(dp[r], dsc, d4[c]);
           } else {
@@ -1055,20 +1058,18 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
           if (kq > 8 * (r >> 2) + 4 * hh + (r & 3)) sc[r] = 0.f;
       }
       u32x4 mine;
-      if constexpr (DROP) mine = dropout_block(p, w.b, h_step, ((i0 + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2);
+      if constexpr (DROP)
+        mine = quad_transpose(
+            byte_transpose(dropout_block(p, w.b, h_step, ((i0 + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2)), li & 3);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
-        u32x4 x;
-        if constexpr (DROP)
-          x = (u32x4){quad_bcast_at(mine[0], q4), quad_bcast_at(mine[1], q4), quad_bcast_at(mine[2], q4),
-                      quad_bcast_at(mine[3], q4)};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * q4 + c;
           const float pr = sc[r];
           if constexpr (DROP) {
-            const float dsc = keep_byte(x[c], kj & 3, p.drop_t) ? p.drop_scale : 0.f;
+            const float dsc = keep_byte(mine[q4], c, p.drop_t) ? p.drop_scale : 0.f;
             sc[r] = pr * dsc;
             dp[r] = pr * __builtin_fmaf(dp[r], dsc, d4[c]);
           } else {

@@ -649,47 +649,58 @@ __device__ __forceinline__ bool keep_byte(uint32_t word, int byte, uint32_t t) {
   return ((word >> (8 * byte)) & 0xFFu) >= t;
 }
 
-// x as held by lane G of this lane's quad (lanes 4k .. 4k+3; DPP quad_perm
-// broadcast).  The four lanes of a quad share their query quad in the
-// forward and dQ kernels and their key quad in dK/dV, so each computes one
-// of the four generator calls they all need and the words are exchanged.
-template <int G>
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, G * 0x55, 0xF, 0xF, false);
+// The four lanes of a quad (lanes 4k .. 4k+3) share their query quad in the
+// forward and dQ kernels and their key quad in dK/dV, so each computes one of
+// the four generator calls they all need and the words are exchanged.
+// 4 x 4 word transpose across a quad: on entry lane c (= lane & 3) holds the
+// four words of block c, on return word c of blocks 0..3 (slot g = block g).
+// Swapping bit 0, then bit 1, between the lane index and the slot index moves
+// every word to its transposed place; each swap sends two words per lane to
+// the partner lane (DPP quad permutations [1,0,3,2] and [2,3,0,1]).
+__device__ __forceinline__ u32x4 quad_transpose(const u32x4& m, int c) {
+  const bool o0 = (c & 1) != 0, o1 = (c & 2) != 0;
+  const uint32_t m0 = m.x, m1 = m.y, m2 = m.z, m3 = m.w;
+  // bit 0: lanes with c odd send words 0 and 2 and take the partner's 1 and 3
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(o0 ? m0 : m1), 0xB1, 0xF, 0xF, false);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(o0 ? m2 : m3), 0xB1, 0xF, 0xF, false);
+  const uint32_t n0 = o0 ? r0 : m0, n1 = o0 ? m1 : r0, n2 = o0 ? r1 : m2, n3 = o0 ? m3 : r1;
+  // bit 1: lanes with c & 2 send words 0 and 1 and take the partner's 2 and 3
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(o1 ? n0 : n2), 0x4E, 0xF, 0xF, false);
+  const uint32_t t1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(o1 ? n1 : n3), 0x4E, 0xF, 0xF, false);
+  return (u32x4){o1 ? t0 : n0, o1 ? t1 : n1, o1 ? n2 : t0, o1 ? n3 : t1};
 }
 
-// Word (i & 3) of block g (computed by lane g of the quad) for this lane's
-// query i, c = i & 3.
-template <int G>
-__device__ __forceinline__ uint32_t row_word(const u32x4& mine, int c) {
-  const uint32_t x0 = quad_bcast<G>(mine[0]), x1 = quad_bcast<G>(mine[1]);
-  const uint32_t x2 = quad_bcast<G>(mine[2]), x3 = quad_bcast<G>(mine[3]);
-  return c == 0 ? x0 : c == 1 ? x1 : c == 2 ? x2 : x3;
+// Byte transpose of a block's four words: word e of the result holds byte e
+// of words 0..3, in that order (v_perm_b32 picks bytes of {hi, lo}: selector
+// values 0-3 are lo's bytes, 4-7 hi's).  For the dK/dV kernels, whose lanes
+// hold one key of every query row: after this and the quad transpose, slot g
+// holds this lane's key byte of block g's four query rows.
+__device__ __forceinline__ u32x4 byte_transpose(const u32x4& w) {
+  const uint32_t a0 = __builtin_amdgcn_perm(w[1], w[0], 0x06020400u);
+  const uint32_t a1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030501u);
+  const uint32_t a2 = __builtin_amdgcn_perm(w[3], w[2], 0x06020400u);
+  const uint32_t a3 = __builtin_amdgcn_perm(w[3], w[2], 0x07030501u);
+  return (u32x4){__builtin_amdgcn_perm(a2, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a1, 0x05040100u),
+                 __builtin_amdgcn_perm(a2, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a1, 0x07060302u)};
 }
 
 // Applies the keep mask to the 16 values of this lane's query row in the four
 // 4 x 4 blocks at key quads j4_0 + 2g (value 4g + e is key 4 (j4_0 + 2g) + e):
 // dropped values become 0, kept ones are multiplied by `kept` (1, or the
-// dropout scale).  Lane c of the quad computes block g = c.
+// dropout scale).  Lane c of the quad computes block g = c; after the quad
+// transpose slot g holds word c (this lane's query row) of block g.
 __device__ __forceinline__ void dropout_row16(const AttnParams& p, int b, int h, int i4, int j4_0,
                                               int c, float kept, f32x16& v) {
-  const u32x4 mine = dropout_block(p, b, h, i4, j4_0 + 2 * c);
-  uint32_t w;
-#define ATTN_DROP_APPLY(G)                                                   \
-  w = row_word<G>(mine, c);                                                  \
-  _Pragma("unroll") for (int e = 0; e < 4; ++e)                              \
-      v[4 * G + e] = keep_byte(w, e, p.drop_t) ? v[4 * G + e] * kept : 0.f;
-  ATTN_DROP_APPLY(0)
-  ATTN_DROP_APPLY(1)
-  ATTN_DROP_APPLY(2)
-  ATTN_DROP_APPLY(3)
+  const u32x4 w = quad_transpose(dropout_block(p, b, h, i4, j4_0 + 2 * c), c);
+  const uint32_t t = p.drop_t;
+#define ATTN_DROP_APPLY(G, x)                                      \
+  _Pragma("unroll") for (int e = 0; e < 4; ++e)                    \
+      v[4 * G + e] = keep_byte(x, e, t) ? v[4 * G + e] * kept : 0.f;
+  ATTN_DROP_APPLY(0, w.x)
+  ATTN_DROP_APPLY(1, w.y)
+  ATTN_DROP_APPLY(2, w.z)
+  ATTN_DROP_APPLY(3, w.w)
 #undef ATTN_DROP_APPLY
-}
-
-// quad_bcast with the source lane given by a value that is a constant after
-// unrolling
-__device__ __forceinline__ uint32_t quad_bcast_at(uint32_t x, int g) {
-  return g == 0 ? quad_bcast<0>(x) : g == 1 ? quad_bcast<1>(x) : g == 2 ? quad_bcast<2>(x) : quad_bcast<3>(x);
 }
 
 }  // namespace attn
