@@ -49,14 +49,13 @@ __device__ __forceinline__ void add_stored(float* x, u32x2 w) {
   x[3] += b[1];
 }
 
-// dQ of this lane's query over column blocks [cb0, cb0 + nb) of the head dim
-// (nb <= NB), scaled and rounded once (ACC: added to what `out` holds); `out`
-// is the query's row of the head, lane half hh holds columns 4 hh .. +3 of
-// each 8-column group.
+// One row (of dQ, dK or dV) over column blocks [cb0, cb0 + nb) of the head
+// dim (nb <= NB), times `mul` and rounded once (ACC: added to what `out`
+// holds); `out` is the row of the head, lane half hh holds columns 4 hh .. +3
+// of each 8-column group.
 template <int DT, bool ACC, int NB>
-__device__ __forceinline__ void store_dq(const AttnParams& p, uint16_t* out, int cb0, int hh,
-                                         const f32x16 (&acc)[NB], int nb = NB) {
-  const float sc0 = p.scale;
+__device__ __forceinline__ void store_row(const AttnParams& p, uint16_t* out, int cb0, int hh,
+                                          const f32x16 (&acc)[NB], float mul, int nb = NB) {
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
@@ -65,11 +64,32 @@ __device__ __forceinline__ void store_dq(const AttnParams& p, uint16_t* out, int
       if (cb < nb && c0 < p.d) {
         float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = acc[cb][4 * q4 + e] * sc0;
+        for (int e = 0; e < 4; ++e) x[e] = acc[cb][4 * q4 + e] * mul;
         if constexpr (ACC) add_stored<DT>(x, *reinterpret_cast<const u32x2*>(out + c0));
         u32x2 val = {Mfma<DT>::pack2(x[0], x[1]), Mfma<DT>::pack2(x[2], x[3])};
         *reinterpret_cast<u32x2*>(out + c0) = val;
       }
+    }
+}
+
+// dQ of this lane's query: the row scaled by the softmax scale
+template <int DT, bool ACC, int NB>
+__device__ __forceinline__ void store_dq(const AttnParams& p, uint16_t* out, int cb0, int hh,
+                                         const f32x16 (&acc)[NB], int nb = NB) {
+  store_row<DT, ACC, NB>(p, out, cb0, hh, acc, p.scale, nb);
+}
+
+// One fp32 row (unscaled) into a partial plane of a split GQA group.
+template <int NB>
+__device__ __forceinline__ void store_row_part(const AttnParams& p, float* out, int hh, const f32x16 (&acc)[NB]) {
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int c0 = 32 * cb + 8 * q4 + 4 * hh;
+      if (c0 < p.d)
+        *reinterpret_cast<f32x4*>(out + c0) =
+            (f32x4){acc[cb][4 * q4], acc[cb][4 * q4 + 1], acc[cb][4 * q4 + 2], acc[cb][4 * q4 + 3]};
     }
 }
 
@@ -832,18 +852,18 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
 // At these head dims the fp32 dK and dV accumulators of 32 keys alone take
 // 256 registers, which leaves no room for two waves per SIMD.  Here eight
 // waves share 128 keys: waves 2 kb and 2 kb + 1 own key block kb (32 keys)
-// and split the head dim between them, each accumulating dK and dV over its
-// half (128 registers).  Each step, wave 2 kb forms S^T = K Q^T and wave
-// 2 kb + 1 forms dP^T = V dO^T (onto -Delta), each over the whole head dim
-// from one full-width K or V operand held in registers; both tiles go
-// through LDS, so the two waves read the same S and dP and form the same P
-// and dS; then each forms dV += P^T dO and dK += dS^T Q over its own four
-// column blocks.  Two barriers per step: the ring's, and the one after the
-// tiles are written; waves 4..7 run half a step behind waves 0..3 (below).
-// Steps, cursors, masks, dropout and the split GQA group (PART) are those of
-// dkdv_kernel with NW = 8, BM = 32; the DMA ring holds three buffers.
-// DE: the extent of the S / dP products (the head dim rounded up to 16); dK
-// and dV cover it in an even count of 32-column blocks.
+// and split the work by role.  Wave 2 kb holds K and accumulates dV: each
+// step it forms S^T = K Q^T, P = exp(S - LSE) (masked), writes P to LDS and
+// forms dV += P^T dO.  Wave 2 kb + 1 holds V and accumulates dK: it forms
+// dP^T = V dO^T (onto -Delta), reads P back, forms dS = P o (dP - Delta) and
+// dK += dS^T Q.  Each holds one full-width K or V operand and one full-width
+// fp32 accumulator (128 registers at d = 256), P crosses LDS once, and the
+// softmax and dS are each formed once per key block.  Two barriers per step:
+// the ring's, and the one after P is written; waves 4..7 run half a step
+// behind waves 0..3 (below).  Steps, cursors, masks, dropout and the split
+// GQA group (PART) are those of dkdv_kernel with NW = 8, BM = 32; the DMA
+// ring holds three buffers.  DE: the extent of the S / dP products (the head
+// dim rounded up to 16).
 template <int DT, bool CAUSAL, bool ACC, bool DROP, bool PART, int DE>
 __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   constexpr int DPAD = 256, NW = 8, BM = 32, NBUF = 3;
@@ -851,10 +871,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   static_assert(BN == kKVTile, "the work lists are built for kKVTile keys per item");
   static_assert(DE % 16 == 0 && DE > 128 && DE <= DPAD, "products over whole 16-wide k chunks");
   constexpr int NT = DE / 16;          // 16-wide k chunks of the S / dP products
-  // 32-column blocks of dK and dV: an even count, so that the two waves of a
-  // pair take equal shares (a block past the head dim adds zeros)
-  constexpr int NCB = 2 * ((DE + 63) / 64);
-  constexpr int NCBH = NCB / 2;        // blocks of each wave of a pair
+  constexpr int NCB = (DE + 31) / 32;  // 32-column blocks of dK and dV
   constexpr int NU = BM / 16;          // 16-query chunks per step
   using LQ = Lay<DPAD, true>;          // Q, dO: row reads (S, dP) and transposed reads (dK, dV)
   using Dma = TileDma<LQ, BM, NW>;
@@ -865,9 +882,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) float sVec[NBUF][2 * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sSink[Dma::SINK ? 512 : 8];
   __shared__ __attribute__((aligned(16))) float sDummy[64];
-  // the S^T (even wave) and dP^T (odd wave) tiles of each key block, as the
-  // 16 accumulator registers of every lane: [wave][register / 4][lane]
-  __shared__ __attribute__((aligned(16))) f32x4 sX[NW][4][64];
+  // P of each key block (written by the even wave for the odd one), as the
+  // 16 accumulator registers of every lane: [key block][register / 4][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 sX[NW / 2][4][64];
 
   const int ntiles = uniform(p.hdr[kHdrNKVTiles]);
   int item, vh;
@@ -899,9 +916,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   const int m_last = (s.lq + BM - 1) / BM;
   const int nm = m_last > m_first ? m_last - m_first : 0;
   const int nsteps = nm * ng;
-  // this wave's column blocks of dK and dV: cb0 .. cb0 + nb - 1
-  const int cb0 = half * NCBH;
-  const int nb = half ? NCB - NCBH : NCBH;
   const int h0 = g * p.group + sub * ng;
 
   Dma dma_q;
@@ -955,12 +969,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   }
   wait_vm<0>();
 
-  f32x16 adk[NCBH], adv[NCBH];
+  // dV (even waves) or dK (odd waves, unscaled) of this lane's key
+  f32x16 ad[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCBH; ++cb) {
-    adk[cb] = zero16();
-    adv[cb] = zero16();
-  }
+  for (int cb = 0; cb < NCB; ++cb) ad[cb] = zero16();
 
   // Waves 4..7 (key blocks 2, 3) run half a step behind waves 0..3: they
   // take one barrier before the loop (waves 0..3 one after it), so that a
@@ -998,12 +1010,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
     }
     // both waves of a key block are active or idle together
     const bool active = wk_lo < s.lk && !(CAUSAL && i0 + BM - 1 < wk_lo_q);
+    f32x16 acc;   // S^T, then P (even waves); dP^T onto -Delta (odd waves)
     if (active) {
-      // S^T (even wave) or dP^T onto -Delta (odd wave), into sX; operands
-      // read two MFMAs ahead
+      // operands read two MFMAs ahead
       constexpr int PD = 2;
       const RowReader<LQ> rd(half ? tdo : tq, lane);
-      f32x16 acc;
       if (half && !DROP) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -1024,85 +1035,80 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
         if (t + PD < NT) a[t + PD] = rd.read(0, t + PD);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (!half) {
+        // P, masked, for both waves of the key block
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        sX[wave][q4][lane] = (f32x4){acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[8 * q4 + 4 * hh]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[4 * q4 + c] = fast_exp2(__builtin_fmaf(acc[4 * q4 + c], sl2e, -l4[c]));
+        }
+        if (CAUSAL && i0 < wk_hi_q) {
+          const int kq = kj_q - i0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kq > 8 * (r >> 2) + 4 * hh + (r & 3)) acc[r] = 0.f;
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          sX[kblk][q4][lane] = (f32x4){acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+      }
     }
     // late waves: the next step's tile has landed (the one after may still
     // be in flight)
     if (late) wait_vm_steps<DMA_PER_STEP, NBUF - 2>(min(NBUF - 2, nsteps - 2 - step));
-    // the pair's tiles are in LDS (the ring's DMA runs on across the barrier)
+    // P is in LDS (the ring's DMA runs on across the barrier)
     barrier_lds_writes();
     if (active) {
-      f32x16 sc, dp;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 x = sX[2 * kblk][q4][lane], y = sX[2 * kblk + 1][q4][lane];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          sc[4 * q4 + c] = x[c];
-          dp[4 * q4 + c] = y[c];
-        }
-      }
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&tvec[8 * q4 + 4 * hh]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          sc[4 * q4 + c] = fast_exp2(__builtin_fmaf(sc[4 * q4 + c], sl2e, -l4[c]));
-      }
-      if (CAUSAL && i0 < wk_hi_q) {
-        const int kq = kj_q - i0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kq > 8 * (r >> 2) + 4 * hh + (r & 3)) sc[r] = 0.f;
-      }
       u32x4 mine;
       if constexpr (DROP)
         mine = quad_transpose(
             byte_transpose(dropout_block(p, w.b, h_step, ((i0 + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2)), li & 3);
+      if (!half) {
+        // (P o D) for dV: dropped values 0, kept ones scaled
+        if constexpr (DROP) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
+          for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * q4 + c;
-          const float pr = sc[r];
-          if constexpr (DROP) {
-            const float dsc = keep_byte(mine[q4], c, p.drop_t) ? p.drop_scale : 0.f;
-            sc[r] = pr * dsc;
-            dp[r] = pr * __builtin_fmaf(dp[r], dsc, d4[c]);
-          } else {
-            dp[r] = pr * dp[r];
+            for (int c = 0; c < 4; ++c) {
+              const int r = 4 * q4 + c;
+              acc[r] = acc[r] * (keep_byte(mine[q4], c, p.drop_t) ? p.drop_scale : 0.f);
+            }
+        }
+      } else {
+        // dS = P o (dP - Delta), with dropout P o (D o dP - Delta)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 pr = sX[kblk][q4][lane];
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * q4 + c;
+            if constexpr (DROP) {
+              const float dsc = keep_byte(mine[q4], c, p.drop_t) ? p.drop_scale : 0.f;
+              acc[r] = pr[c] * __builtin_fmaf(acc[r], dsc, d4[c]);
+            } else {
+              acc[r] = pr[c] * acc[r];
+            }
           }
         }
       }
-      u32x4 bp[NU], bds[NU];
+      u32x4 b[NU];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        bp[u] = pack_operand<DT>(sc, u);
-        bds[u] = pack_operand<DT>(dp, u);
-      }
-      // dV and dK over this wave's column blocks, each transposed operand
-      // read one MFMA ahead
-      const TrReader<LQ> trq(tq, lane), trdo(tdo, lane);
-      constexpr int PD = 1, NO = NU * NCBH;
-      u32x4 tdv[NO], tqv[NO];
+      for (int u = 0; u < NU; ++u) b[u] = pack_operand<DT>(acc, u);
+      // dV += (P o D)^T dO or dK += dS^T Q over every column block, the
+      // transposed operand read two MFMAs ahead
+      const TrReader<LQ> tr(half ? tq : tdo, lane);
+      constexpr int PT = 2, NO = NU * NCB;
+      u32x4 to[NO];
 #pragma unroll
-      for (int o = 0; o < PD; ++o) {
-        tdv[o] = trdo.read(cb0 + o % NCBH, o / NCBH);
-        tqv[o] = trq.read(cb0 + o % NCBH, o / NCBH);
-      }
+      for (int o = 0; o < PT; ++o) to[o] = tr.read(o % NCB, o / NCB);
 #pragma unroll
       for (int o = 0; o < NO; ++o) {
-        const int u = o / NCBH, cb = o % NCBH;
-        const bool ahead = o + PD < NO && (o + PD) % NCBH < nb;
         __builtin_amdgcn_sched_barrier(0);
-        if (cb < nb) adv[cb] = Mfma<DT>::mma(tdv[o], bp[u], adv[cb]);
-        if (ahead) tdv[o + PD] = trdo.read(cb0 + (o + PD) % NCBH, (o + PD) / NCBH);
-        __builtin_amdgcn_sched_barrier(0);
-        if (cb < nb) adk[cb] = Mfma<DT>::mma(tqv[o], bds[u], adk[cb]);
-        if (ahead) tqv[o + PD] = trq.read(cb0 + (o + PD) % NCBH, (o + PD) / NCBH);
+        ad[o % NCB] = Mfma<DT>::mma(to[o], b[o / NCB], ad[o % NCB]);
+        if (o + PT < NO) to[o + PT] = tr.read((o + PT) % NCB, (o + PT) / NCB);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1112,11 +1118,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   if (kj < s.lk) {
     const int64_t row = (int64_t)kj * kvts;
     if constexpr (PART) {
+      // the dK planes, then the dV planes (unscaled)
       float* dkp = p.part + (int64_t)sub * p.part_plane + kvoff + row;
-      store_dkdv_part(p, dkp, dkp + (int64_t)p.kv_split * p.part_plane, cb0, hh, adk, adv, nb);
+      store_row_part(p, half ? dkp : dkp + (int64_t)p.kv_split * p.part_plane, hh, ad);
     } else {
-      store_dkdv<DT, ACC>(p, reinterpret_cast<uint16_t*>(p.dk) + kvoff + row,
-                          reinterpret_cast<uint16_t*>(p.dv) + kvoff + row, cb0, hh, adk, adv, nb);
+      uint16_t* out = reinterpret_cast<uint16_t*>(half ? p.dk : p.dv) + kvoff + row;
+      store_row<DT, ACC>(p, out, 0, hh, ad, half ? p.scale : 1.f);
     }
   }
 }
