@@ -983,7 +983,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   // issues its share of a Q / dO tile's DMA at the start of its own step and
   // waits for it before the barrier that precedes the tile's first read: the
   // early waves tile step + 1 (first read after their next ring barrier),
-  // the late waves tile step + 2 (after their exchange barrier of step + 1).
+  // the late waves tile step + 2 (after their P barrier of step + 1).
   // A tile is read until the late waves' ring barrier of the next step,
   // hence a ring of three.
   if (late) {
@@ -993,7 +993,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   int cm = m_last - 1, chg = 0;
   for (int step = 0; step < nsteps; ++step) {
     // early waves: this step's tile has landed; late waves: the early waves'
-    // S^T / dP^T tiles are in LDS
+    // P tiles are in LDS
     if (!late) wait_vm<0>();
     barrier_lds_writes();
     if (step + 1 + late < nsteps) issue(ibuf);

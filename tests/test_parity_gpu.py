@@ -99,7 +99,7 @@ def _ragged_case(lq, lk, pq, pk, hq, hkv, d, causal, dtype, seed):
 RAGGED = [1, 31, 33, 64, 65, 127, 129, 200, 0, 257]
 
 
-@pytest.mark.parametrize("d", [8, 16, 48, 64, 96, 128, 256])
+@pytest.mark.parametrize("d", [8, 16, 48, 64, 96, 128, 160, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_lengths_all_head_dims(d, causal):
     L = RAGGED
