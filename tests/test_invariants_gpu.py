@@ -48,8 +48,13 @@ def poisoned_run(case):
 
 
 def test_repeat_calls_bitwise_identical(A):
+    from test_parity_gpu import _ragged_case
+    L, P = [300, 1, 129, 0, 257], [304, 8, 136, 8, 264]
+    # the split kernels with odd counts of 32-column blocks (d 144, 208), unspread
+    split = [_ragged_case(L, L, P, P, hq=4, hkv=2, d=d, causal=c, dtype="bf16", seed=d)
+             for d, c in ((144, True), (208, False))]
     for case in (workloads.real_vs_padded(576, causal=True), workloads.gqa_d256_batched(),
-                 workloads.mha_causal_lengths([256, 256])):
+                 workloads.mha_causal_lengths([256, 256]), *split):
         r1 = gpu_run(case)
         r2 = gpu_run(case)
         r3 = poisoned_run(case)
