@@ -513,6 +513,8 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
       u32x4 a[NT];
 #pragma unroll
       for (int t = 0; t < PD; ++t) a[t] = rd.read(0, t);
+      // the product phases at raised wave priority, as in dq_kernel
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         __builtin_amdgcn_sched_barrier(0);
@@ -520,6 +522,7 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
         if (t + PD < NT) a[t + PD] = rd.read(0, t + PD);
       }
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         sX[wave][q4][lane] = (f32x4){t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2], t16[4 * q4 + 3]};
@@ -558,12 +561,14 @@ __global__ __launch_bounds__(512, 1) void dq_split_kernel(AttnParams p) {
       for (int r = 0; r < 16; ++r) sc[r] = DROP ? sc[r] * (dp[r] - dlt) : sc[r] * dp[r];     // dS
       const u32x4 b0 = pack_operand<DT>(sc, 0), b1 = pack_operand<DT>(sc, 1);
       const TrReader<LK> trk(tk, lane);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int cb = 0; cb < NCBH; ++cb)
         if (cb < nb) acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 0), b0, acc[cb]);
 #pragma unroll
       for (int cb = 0; cb < NCBH; ++cb)
         if (cb < nb) acc[cb] = Mfma<DT>::mma(trk.read(cb0 + cb, 1), b1, acc[cb]);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
   if (!late) barrier_lds_writes();
