@@ -903,7 +903,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   const SeqInfo s = w.s;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kblk = wave >> 1, half = wave & 1;
+  // key block of this wave; odd: the V / dK wave of the block (even: K / dV)
+  const int kblk = wave >> 1, odd = wave & 1;
   const int li = lane & 31, hh = lane >> 5;
   const int n0 = w.tile * BN;
   const int kj = n0 + kblk * 32 + li;          // this lane's key (B-operand column)
@@ -965,7 +966,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
   uint32_t ibuf = (uint32_t)late + 1u;
 
   // the full-width operand of this wave's product: K (even waves) or V (odd)
-  const uint16_t* kvb = reinterpret_cast<const uint16_t*>(half ? p.v : p.k) + kvoff;
+  const uint16_t* kvb = reinterpret_cast<const uint16_t*>(odd ? p.v : p.k) + kvoff;
   u32x4 kvreg[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -1019,8 +1020,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
     if (active) {
       // operands read two MFMAs ahead
       constexpr int PD = 2;
-      const RowReader<LQ> rd(half ? tdo : tq, lane);
-      if (half && !DROP) {
+      const RowReader<LQ> rd(odd ? tdo : tq, lane);
+      if (odd && !DROP) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const f32x4 nd = *reinterpret_cast<const f32x4*>(&tvec[64 + 8 * q4 + 4 * hh]);
@@ -1040,7 +1041,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
         if (t + PD < NT) a[t + PD] = rd.read(0, t + PD);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (!half) {
+      if (!odd) {
         // P, masked, for both waves of the key block
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -1070,7 +1071,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
       if constexpr (DROP)
         mine = quad_transpose(
             byte_transpose(dropout_block(p, w.b, h_step, ((i0 + 4 * hh) >> 2) + 2 * (li & 3), kj >> 2)), li & 3);
-      if (!half) {
+      if (!odd) {
         // (P o D) for dV: dropped values 0, kept ones scaled
         if constexpr (DROP) {
 #pragma unroll
@@ -1104,7 +1105,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
       for (int u = 0; u < NU; ++u) b[u] = pack_operand<DT>(acc, u);
       // dV += (P o D)^T dO or dK += dS^T Q over every column block, the
       // transposed operand read two MFMAs ahead
-      const TrReader<LQ> tr(half ? tq : tdo, lane);
+      const TrReader<LQ> tr(odd ? tq : tdo, lane);
       constexpr int PT = 2, NO = NU * NCB;
       u32x4 to[NO];
 #pragma unroll
@@ -1125,10 +1126,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
     if constexpr (PART) {
       // the dK planes, then the dV planes (unscaled)
       float* dkp = p.part + (int64_t)sub * p.part_plane + kvoff + row;
-      store_row_part(p, half ? dkp : dkp + (int64_t)p.kv_split * p.part_plane, hh, ad);
+      store_row_part(p, odd ? dkp : dkp + (int64_t)p.kv_split * p.part_plane, hh, ad);
     } else {
-      uint16_t* out = reinterpret_cast<uint16_t*>(half ? p.dk : p.dv) + kvoff + row;
-      store_row<DT, ACC>(p, out, 0, hh, ad, half ? p.scale : 1.f);
+      uint16_t* out = reinterpret_cast<uint16_t*>(odd ? p.dk : p.dv) + kvoff + row;
+      store_row<DT, ACC>(p, out, 0, hh, ad, odd ? p.scale : 1.f);
     }
   }
 }
