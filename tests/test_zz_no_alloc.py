@@ -92,3 +92,18 @@ def test_noalloc_split_group_within_bar():
         assert_close(name + " (no-alloc vs split)", g, r.float().cpu().numpy(), "bf16", rows)
         assert_close(name + " (no-alloc vs oracle)", g, o, "bf16", rows)
         assert_close(name + " (split vs oracle)", r, o, "bf16", rows)
+
+
+def test_noalloc_split_kernels_twice_second_smaller():
+    """Head dims above 128 (the split dQ and dK/dV kernels, groups small
+    enough that attn_bwd_thd does not spread them): bitwise equal to the
+    workspace call, the second call on a smaller problem."""
+    import bwd_thd_varlen_amd as A
+    A.lib()
+    big = _case([260, 1, 129], [260, 33, 129], [264, 8, 136], [264, 40, 136],
+                hq=4, hkv=2, d=208, causal=False, seed=14)
+    small = _case([70, 9], [70, 9], [72, 16], [72, 16], hq=2, hkv=1, d=160, causal=True, seed=15)
+    for case in (big, small):
+        ref, got = _both(A, case)
+        for name, r, g in (("dq", ref[0], got[0]), ("dk", ref[1], got[1]), ("dv", ref[2], got[2])):
+            assert torch.equal(r, g), f"{name} at d={case.d}: not bitwise equal to attn_bwd_thd"
