@@ -75,7 +75,7 @@ CHUNK_DIMS = [(88, 4, 2), (152, 4, 2), (184, 16, 2), (216, 4, 2), (248, 16, 2)]
 def test_accumulating_chunks_across_head_dims(d, hq, hkv):
     """Chunk pairs whose backward adds into dq / dk / dv; groups of 8 query
     heads also take the partial planes."""
-    dtype = "bf16" if d % 16 == 8 else "fp16"
+    dtype = "bf16" if CHUNK_DIMS.index((d, hq, hkv)) % 2 == 0 else "fp16"
     print(f"[headdim] chunks d={d} hq={hq} hkv={hkv} {dtype}", flush=True)
     L = [300, 77, 513, 1]
     qcuts = [[128, 200], [40], [100, 256, 400], []]
