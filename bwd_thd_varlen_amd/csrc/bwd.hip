@@ -871,7 +871,9 @@ __global__ __launch_bounds__(256, OCC) void dkdv_kernel(AttnParams p) {
 // dim rounded up to 16).
 template <int DT, bool CAUSAL, bool ACC, bool DROP, bool PART, int DE>
 __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(AttnParams p) {
-  constexpr int DPAD = 256, NW = 8, BM = 32, NBUF = 3;
+  // Q / dO tiles 192 columns wide up to d = 192 (a quarter less DMA written
+  // into LDS, which bounds this kernel), 256 above
+  constexpr int DPAD = DE <= 192 ? 192 : 256, NW = 8, BM = 32, NBUF = 3;
   constexpr int BN = 16 * NW;          // keys per workgroup: NW / 2 blocks of 32
   static_assert(BN == kKVTile, "the work lists are built for kKVTile keys per item");
   static_assert(DE % 16 == 0 && DE > 128 && DE <= DPAD, "products over whole 16-wide k chunks");
